@@ -1,0 +1,17 @@
+"""CPU fp64 oracle: TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may import
+this package.  The device library never imports, links or calls it, and this
+package imports nothing from the device library.
+"""
+from .attention import (  # noqa: F401
+    BLOCK,
+    bf16_to_f64,
+    cu_seqlens_from_lengths,
+    e4m3fn_table,
+    e4m3fn_to_f64,
+    gather_kv_rows,
+    paged_decode,
+    ragged_prefill,
+    widen,
+)

@@ -1,0 +1,261 @@
+"""CPU fp64 oracle for paged GQA decode and ragged (MLA) prefill attention.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path imports, calls or links
+this module; only the tests, the smoke check and the benchmark's CPU-baseline
+leg do.  It shares no code with the device library: it reads the storage bits
+produced by the input generator and widens them with its own code.
+
+What it computes is the plain definition of attention, evaluated in float64
+over the logically gathered sequence:
+
+  out[h] = sum_t softmax_t(scale * <q[h], K[t]>) * V[t]
+  lse[h] = log(sum_t exp(scale * <q[h], K[t]>))           (natural log)
+
+Paging, splitting, tiling and block skipping in the device path are only
+faster ways to the same value, so none of them appear here.
+
+Sources (the pages this follows):
+  * FlashMLA "Tensor Shapes Reference", section 1 (flash_mla_with_kvcache):
+    q [B, Hq, 1, D], a paged K/V cache of 64-row blocks, block_table [B, Nblk]
+    mapping a sequence's block index to a physical cache block, seq_lens [B];
+    the last block may be partly filled and the unused slots are ignored by
+    seq_lens.  Same page, "Grouped-Query Attention" diagram: q heads 2g and
+    2g+1 of an 8:4 model read KV head g, i.e. kv head = h // (Hq / Hk).  Same
+    page, "Prefill to Cache Mapping": tokens 64j .. 64j+63 live in
+    block_table[b, j].
+  * Modular "flare_mla_prefill": ragged Q [tokens, heads, 192], K and V
+    [tokens, heads, 128], K_rope [tokens, 1, 64]; the 64 missing elements of
+    each K head are the shared rope key broadcast to all heads; the output has
+    the reduced (V) width; per-sequence valid lengths.
+  * MATE msa_interface: fp8 KV is torch.float8_e4m3fn with per-tensor k_scale
+    and v_scale (the _run_sparse_fwd_kernel argument list); cu_seqlens is
+    [0, cumsum(lengths)] (_make_cu_seqlens); with equal query and key lengths
+    the causal offset kv_len - q_len is 0 (_normalize_qo_offset), so query i
+    sees keys j <= i.
+  * FlashMLA "Tensor Shapes Reference", section 3 (flash_mla_prefill): an
+    optional block-sparse pattern, block-aligned to 64.
+
+Readings where the pages are silent (each also listed in the design notes):
+  * the KV cache is one shared physical pool [NB, Hk, 64, D]; block ids are
+    global; table entries past ceil(L/64) are padding and never read;
+  * the decode query is the newest token and sees all L keys;
+  * block-sparse prefill: key j is visible to query i iff j <= i and
+    mask[b, i // 64, j // 64] != 0 (a diagonal block that is off hides it);
+  * a row with no visible key has out = 0 and lse = -inf;
+  * fp8 values are e4m3fn(byte) * scale, with the pool's per-tensor scale.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional, Sequence
+
+import numpy as np
+
+BLOCK = 64
+
+
+# --------------------------------------------------------------------------
+# Storage formats -> float64
+# --------------------------------------------------------------------------
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bf16 is the top half of an IEEE binary32: widen by shifting the 16 bits up."""
+    b = np.asarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def e4m3fn_table() -> np.ndarray:
+    """Value of each of the 256 OCP fp8 E4M3FN codes (1 sign, 4 exponent bits with
+    bias 7, 3 mantissa bits; no infinities; S.1111.111 is NaN; exponent field 0
+    holds the subnormals m * 2**-9)."""
+    tab = np.empty(256, np.float64)
+    for code in range(256):
+        sign = -1.0 if code & 0x80 else 1.0
+        e = (code >> 3) & 0xF
+        m = code & 0x7
+        if e == 0xF and m == 0x7:
+            tab[code] = math.nan
+        elif e == 0:
+            tab[code] = sign * m * 2.0 ** -9
+        else:
+            tab[code] = sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return tab
+
+
+_E4M3FN = e4m3fn_table()
+
+
+def e4m3fn_to_f64(bits: np.ndarray) -> np.ndarray:
+    return _E4M3FN[np.asarray(bits, dtype=np.uint8)]
+
+
+def widen(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Storage bits (as produced by the input generator) -> float64 values."""
+    if dtype == "f32":
+        return np.asarray(x, dtype=np.float32).astype(np.float64)
+    if dtype == "bf16":
+        return bf16_to_f64(x)
+    if dtype == "e4m3fn":
+        return e4m3fn_to_f64(x)
+    if dtype == "f64":
+        return np.asarray(x, dtype=np.float64)
+    raise ValueError(f"unknown dtype tag {dtype!r}")
+
+
+# --------------------------------------------------------------------------
+# Paged decode
+# --------------------------------------------------------------------------
+
+def gather_kv_rows(pool: np.ndarray, block_table: np.ndarray, b: int, g: int, L: int) -> np.ndarray:
+    """Logical rows 0..L-1 of KV head g of sequence b, in storage format (exact).
+
+    Row t is row t % 64 of physical block block_table[b, t // 64]; only the
+    first ceil(L / 64) entries of the table row are read."""
+    nb = (L + BLOCK - 1) // BLOCK
+    phys = np.asarray(block_table[b, :nb], dtype=np.int64)
+    rows = pool[phys, g]                      # [nb, 64, D]
+    return rows.reshape(nb * BLOCK, pool.shape[-1])[:L]
+
+
+def _softmax_attend(s: np.ndarray, V: np.ndarray):
+    """s: [..., L] scores (with -inf for hidden keys); V: [L, Dv].
+    Returns (out [..., Dv], lse [...]).  No visible key -> out 0, lse -inf."""
+    m = s.max(axis=-1, initial=-np.inf)
+    finite = np.isfinite(m)
+    m_safe = np.where(finite, m, 0.0)
+    w = np.exp(s - m_safe[..., None])          # exp(-inf) = 0 for hidden keys
+    l = w.sum(axis=-1)
+    num = w @ V
+    with np.errstate(invalid="ignore", divide="ignore"):
+        out = np.where((l > 0)[..., None], num / np.where(l > 0, l, 1.0)[..., None], 0.0)
+        lse = np.where(l > 0, m_safe + np.log(np.where(l > 0, l, 1.0)), -np.inf)
+    return out, lse
+
+
+def paged_decode(
+    q: np.ndarray,
+    k_pool: np.ndarray,
+    v_pool: np.ndarray,
+    block_table: np.ndarray,
+    seq_lens: np.ndarray,
+    scale: float,
+    *,
+    q_dtype: str = "f64",
+    kv_dtype: str = "f64",
+    k_scale: float = 1.0,
+    v_scale: float = 1.0,
+    batches: Optional[Sequence[int]] = None,
+):
+    """Single-token decode over a paged KV cache with grouped-query heads.
+
+    q [B, Hq, D]; k_pool, v_pool [NB, Hk, 64, D]; block_table [B, Nblk] int;
+    seq_lens [B].  Inputs are storage bits tagged by q_dtype / kv_dtype (or
+    float64 with tag 'f64').  Returns (out [nb, Hq, D], lse [nb, Hq]) in
+    float64 for the sequences in ``batches`` (default: all, in order)."""
+    B, Hq, D = q.shape
+    Hk = k_pool.shape[1]
+    if Hq % Hk:
+        raise ValueError("Hq must be a multiple of Hk")
+    r = Hq // Hk
+    if batches is None:
+        batches = range(B)
+    batches = list(batches)
+    out = np.zeros((len(batches), Hq, D), np.float64)
+    lse = np.full((len(batches), Hq), -np.inf, np.float64)
+    for i, b in enumerate(batches):
+        L = int(seq_lens[b])
+        qb = widen(q[b], q_dtype)                           # [Hq, D]
+        for g in range(Hk):
+            K = widen(gather_kv_rows(k_pool, block_table, b, g, L), kv_dtype) * k_scale
+            V = widen(gather_kv_rows(v_pool, block_table, b, g, L), kv_dtype) * v_scale
+            heads = slice(g * r, (g + 1) * r)               # kv head g serves q heads g*r .. g*r+r-1
+            s = scale * (qb[heads] @ K.T)                   # [r, L]
+            o, ls = _softmax_attend(s, V)
+            out[i, heads] = o
+            lse[i, heads] = ls
+    return out, lse
+
+
+# --------------------------------------------------------------------------
+# Ragged prefill (causal, optional MLA rope key, optional 64x64 block mask)
+# --------------------------------------------------------------------------
+
+def ragged_prefill(
+    q: np.ndarray,
+    k: np.ndarray,
+    v: np.ndarray,
+    cu_seqlens: np.ndarray,
+    scale: float,
+    *,
+    k_rope: Optional[np.ndarray] = None,
+    block_mask: Optional[np.ndarray] = None,
+    dtype: str = "f64",
+    rows: Optional[Sequence[int]] = None,
+    row_chunk: int = 256,
+):
+    """Causal attention over sequences packed back to back (token-major).
+
+    q [T, Hq, Dn + Dr]; k [T, Hk, Dn]; v [T, Hk, Dv]; k_rope [T, 1, Dr] or None
+    (then Dr = 0); cu_seqlens [B + 1].  Query head h reads KV head h // (Hq/Hk).
+    The score of query i and key j of one sequence is
+        scale * (q[i, h, :Dn] . k[j, g] + q[i, h, Dn:] . k_rope[j, 0])
+    and key j is visible iff j <= i and (no mask or mask[b, i//64, j//64]).
+
+    ``rows``: optional global token indices to evaluate (default all), so that a
+    sample of a large problem can be checked row by row.
+    Returns (out [n, Hq, Dv], lse [n, Hq]) in float64."""
+    Q = widen(q, dtype)
+    K = widen(k, dtype)
+    V = widen(v, dtype)
+    KR = widen(k_rope, dtype) if k_rope is not None else None
+    T, Hq, Dqk = Q.shape
+    Hk, Dn = K.shape[1], K.shape[2]
+    Dr = 0 if KR is None else KR.shape[2]
+    if Dn + Dr != Dqk:
+        raise ValueError("query width must equal K width plus rope width")
+    if Hq % Hk:
+        raise ValueError("Hq must be a multiple of Hk")
+    r = Hq // Hk
+    Dv = V.shape[2]
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    B = cu.shape[0] - 1
+    if rows is None:
+        rows = np.arange(T)
+    rows = np.asarray(rows, dtype=np.int64)
+    out = np.zeros((rows.shape[0], Hq, Dv), np.float64)
+    lse = np.full((rows.shape[0], Hq), -np.inf, np.float64)
+    seq_of_row = np.searchsorted(cu, rows, side="right") - 1
+    for b in range(B):
+        c0, c1 = int(cu[b]), int(cu[b + 1])
+        sel = np.nonzero(seq_of_row == b)[0]
+        if sel.size == 0 or c1 == c0:
+            continue
+        L = c1 - c0
+        j = np.arange(L)
+        for s0 in range(0, sel.size, row_chunk):
+            idx = sel[s0:s0 + row_chunk]
+            gi = rows[idx]                    # global token ids of these queries
+            i = gi - c0                       # local query positions
+            vis = j[None, :] <= i[:, None]    # causal: key j visible to query i iff j <= i
+            if block_mask is not None:
+                vis &= block_mask[b][(i // BLOCK)[:, None], (j // BLOCK)[None, :]] != 0
+            for g in range(Hk):
+                heads = slice(g * r, (g + 1) * r)
+                Qc = Q[gi, heads, :]                        # [n, r, Dqk]
+                s = Qc[:, :, :Dn] @ K[c0:c1, g, :].T        # [n, r, L]
+                if KR is not None:
+                    s = s + Qc[:, :, Dn:] @ KR[c0:c1, 0, :].T
+                s = scale * s
+                s = np.where(vis[:, None, :], s, -np.inf)
+                o, ls = _softmax_attend(s, V[c0:c1, g, :])
+                out[idx, heads] = o
+                lse[idx, heads] = ls
+    return out, lse
+
+
+def cu_seqlens_from_lengths(lengths: Sequence[int]) -> np.ndarray:
+    """[0, cumsum(lengths)] as int32 (length B + 1)."""
+    lens = np.asarray(lengths, dtype=np.int64)
+    cu = np.zeros(lens.shape[0] + 1, np.int64)
+    cu[1:] = np.cumsum(lens)
+    return cu.astype(np.int32)

@@ -1,0 +1,70 @@
+"""Plant plausible mistakes in a copy of the oracle (on the CPU) and check that
+the pins catch every one of them.  The planted copy is built from the oracle's
+own source text with one edit, run through the pin tests, and discarded."""
+import inspect
+import types
+
+import pytest
+
+from oracle import attention as O
+from tests import test_oracle_pins as P
+
+SRC = inspect.getsource(O)
+
+
+def _mutant(old: str, new: str) -> types.ModuleType:
+    assert old in SRC, f"mutation anchor not found: {old!r}"
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(SRC.replace(old, new), "oracle_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+def _bf(): return P.test_decode_matches_bruteforce_on_unpaged_tensors(8, 4)
+def _bf62(): return P.test_decode_matches_bruteforce_on_unpaged_tensors(6, 2)
+
+
+MUTANTS = {
+    "interleaved_head_map": ("heads = slice(g * r, (g + 1) * r)", "heads = slice(g, Hq, Hk)",
+                             [P.test_decode_head_mapping_matches_page_diagram, P.test_prefill_gqa_matches_sdpa]),
+    "block_order_reversed": ("phys = np.asarray(block_table[b, :nb], dtype=np.int64)",
+                             "phys = np.asarray(block_table[b, :nb][::-1], dtype=np.int64)",
+                             [_bf, P.test_gather_follows_page_token_block_mapping]),
+    "rope_term_dropped": ("s = s + Qc[:, :, Dn:] @ KR[c0:c1, 0, :].T", "s = s",
+                          [P.test_prefill_mla_matches_sdpa_with_concatenated_rope_key,
+                           P.test_prefill_matches_bruteforce_with_rope]),
+    "causal_strict": ("vis = j[None, :] <= i[:, None]", "vis = j[None, :] < i[:, None]",
+                      [P.test_prefill_gqa_matches_sdpa, P.test_prefill_first_row_returns_its_own_value_row]),
+    "block_mask_transposed": ("block_mask[b][(i // BLOCK)[:, None], (j // BLOCK)[None, :]]",
+                              "block_mask[b][(j // BLOCK)[None, :], (i // BLOCK)[:, None]]",
+                              [P.test_prefill_block_mask_matches_sdpa_element_mask,
+                               P.test_prefill_matches_bruteforce_with_block_mask]),
+    "k_scale_dropped": ("kv_dtype) * k_scale", "kv_dtype)",
+                        [P.test_decode_fp8_matches_sdpa_on_torch_dequantised_cache]),
+    "v_scale_dropped": ("kv_dtype) * v_scale", "kv_dtype)",
+                        [P.test_decode_fp8_matches_sdpa_on_torch_dequantised_cache]),
+    "decode_scale_dropped": ("s = scale * (qb[heads] @ K.T)", "s = (qb[heads] @ K.T)",
+                             [P.test_decode_matches_torch_sdpa]),
+    "decode_reads_k_for_v": ("V = widen(gather_kv_rows(v_pool,", "V = widen(gather_kv_rows(k_pool,",
+                             [_bf62]),
+    "prefill_scale_dropped": ("s = scale * s", "s = s", [P.test_prefill_gqa_matches_sdpa]),
+    "e4m3_bias_8": ("2.0 ** (e - 7)", "2.0 ** (e - 8)", [P.test_e4m3fn_table_matches_torch_all_codes]),
+    "e4m3_subnormal_scale": ("m * 2.0 ** -9", "m * 2.0 ** -10", [P.test_e4m3fn_closed_form_points]),
+    "e4m3_no_nan": ("if e == 0xF and m == 0x7:", "if False:", [P.test_e4m3fn_closed_form_points]),
+    "bf16_wrong_shift": ("<< np.uint32(16)", "<< np.uint32(15)", [P.test_bf16_widen_matches_torch]),
+    "lse_sign": ("m_safe + np.log(", "m_safe - np.log(", [P.test_decode_matches_torch_sdpa]),
+    "gqa_ratio_inverted_prefill": ("Qc = Q[gi, heads, :]", "Qc = Q[gi, g:g + r, :]",
+                                   [P.test_prefill_gqa_matches_sdpa]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    old, new, catchers = MUTANTS[name]
+    monkeypatch.setattr(P, "O", _mutant(old, new))
+    caught = []
+    for fn in catchers:
+        try:
+            fn()
+        except Exception:        # an assertion, or the mutant breaking outright
+            caught.append(fn.__name__)
+    assert caught, f"mutant {name} passed every pin it was aimed at"
