@@ -1,0 +1,216 @@
+// Host-only planning and validation (no device calls).
+//
+// Decode plan: the FlashMLA tensor-shape reference describes get_mla_metadata
+// as shape/stride validation that materialises nothing, and lists the shape
+// mistakes a caller can make (Hq not a multiple of Hk, sequences longer than
+// Nblk*64, a block size other than 64, non-contiguous inner dims, q and cache
+// of different dtypes).  MATE's planner sizes its schedule from capacities so
+// that execution never reads lengths on the host; the split count here is
+// likewise a function of the descriptor only.
+#include <algorithm>
+#include <cstring>
+#include <string>
+
+#include "status.hpp"
+
+namespace gqap {
+
+std::string& last_error_slot() {
+  static thread_local std::string msg;
+  return msg;
+}
+
+static bool elem_size(int32_t dt, int* out) {
+  switch (dt) {
+    case GQAP_F32: *out = 4; return true;
+    case GQAP_BF16: *out = 2; return true;
+    case GQAP_FP8_E4M3FN: *out = 1; return true;
+    case GQAP_F16: *out = 2; return true;
+    default: return false;
+  }
+}
+
+// A stride in elements keeps 16-byte vector accesses aligned.
+static bool aligned16(int64_t stride_elems, int esz) { return (stride_elems * esz) % 16 == 0; }
+
+static gqap_status check_decode_desc(const gqap_decode_desc_t& d, int* q_esz, int* kv_esz) {
+  if (d.batch < 0 || d.batch > 65535)
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "batch must be in [0, 65535] (got %d)", d.batch);
+  if (d.num_q_heads <= 0 || d.num_kv_heads <= 0)
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "head counts must be positive (Hq=%d, Hk=%d)", d.num_q_heads,
+                d.num_kv_heads);
+  if (d.num_q_heads % d.num_kv_heads)
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "Hq (%d) must be a multiple of Hk (%d)", d.num_q_heads, d.num_kv_heads);
+  if (d.block_size != kBlock)
+    return fail(GQAP_ERR_UNSUPPORTED, "block_size must be %d (got %d)", kBlock, d.block_size);
+  if (d.head_dim != 64 && d.head_dim != 128)
+    return fail(GQAP_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", d.head_dim);
+  if (!elem_size(d.q_dtype, q_esz)) return fail(GQAP_ERR_DTYPE, "unknown q_dtype %d", d.q_dtype);
+  if (!elem_size(d.kv_dtype, kv_esz)) return fail(GQAP_ERR_DTYPE, "unknown kv_dtype %d", d.kv_dtype);
+  if (d.q_dtype == GQAP_F16 || d.kv_dtype == GQAP_F16)
+    return fail(GQAP_ERR_UNSUPPORTED, "fp16 is not implemented");
+  const bool ok_pair = (d.q_dtype == GQAP_F32 && d.kv_dtype == GQAP_F32) ||
+                       (d.q_dtype == GQAP_BF16 && d.kv_dtype == GQAP_BF16) ||
+                       (d.q_dtype == GQAP_BF16 && d.kv_dtype == GQAP_FP8_E4M3FN);
+  if (!ok_pair)
+    return fail(GQAP_ERR_DTYPE, "dtype pair q=%d kv=%d not supported (f32/f32, bf16/bf16, bf16/fp8_e4m3fn)",
+                d.q_dtype, d.kv_dtype);
+  if (d.max_blocks_per_seq <= 0)
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "max_blocks_per_seq must be positive (got %d)", d.max_blocks_per_seq);
+  if (d.num_pool_blocks <= 0)
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "num_pool_blocks must be positive (got %d)", d.num_pool_blocks);
+  if (d.max_seq_len < 0)
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "max_seq_len must be >= 0 (got %d)", d.max_seq_len);
+  if ((int64_t)d.max_seq_len > (int64_t)d.max_blocks_per_seq * kBlock)
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "max_seq_len %d exceeds Nblk*64 = %lld", d.max_seq_len,
+                (long long)d.max_blocks_per_seq * kBlock);
+  const int64_t D = d.head_dim;
+  if (d.q_stride_head < D || (d.num_q_heads > 1 && d.q_stride_batch < d.q_stride_head * d.num_q_heads))
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "q strides (batch %lld, head %lld) overlap for D=%lld",
+                (long long)d.q_stride_batch, (long long)d.q_stride_head, (long long)D);
+  if (d.num_q_heads == 1 && d.q_stride_batch < D)
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "q batch stride %lld < D", (long long)d.q_stride_batch);
+  if (d.out_stride_head < D || (d.num_q_heads > 1 && d.out_stride_batch < d.out_stride_head * d.num_q_heads) ||
+      (d.num_q_heads == 1 && d.out_stride_batch < D))
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "out strides (batch %lld, head %lld) overlap for D=%lld",
+                (long long)d.out_stride_batch, (long long)d.out_stride_head, (long long)D);
+  if (!aligned16(d.q_stride_head, *q_esz) || !aligned16(d.q_stride_batch, *q_esz) ||
+      !aligned16(d.out_stride_head, *q_esz) || !aligned16(d.out_stride_batch, *q_esz))
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "q/out strides must keep rows 16-byte aligned");
+  if (d.kv_stride_head < D * kBlock)
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "kv_stride_head %lld < 64*D: a (block, head) slab must be a contiguous 64 x D tile",
+                (long long)d.kv_stride_head);
+  if (d.kv_stride_block < d.kv_stride_head * d.num_kv_heads)
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "kv_stride_block %lld < Hk * kv_stride_head", (long long)d.kv_stride_block);
+  if (!aligned16(d.kv_stride_head, *kv_esz) || !aligned16(d.kv_stride_block, *kv_esz))
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "kv strides must keep slabs 16-byte aligned");
+  if (d.block_table_stride < d.max_blocks_per_seq)
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "block_table_stride %lld < Nblk %d", (long long)d.block_table_stride,
+                d.max_blocks_per_seq);
+  if (d.num_splits < 0) return fail(GQAP_ERR_INVALID_ARGUMENT, "num_splits must be >= 0");
+  if (d.num_cus < 0) return fail(GQAP_ERR_INVALID_ARGUMENT, "num_cus must be >= 0");
+  return GQAP_OK;
+}
+
+}  // namespace gqap
+
+using namespace gqap;
+
+extern "C" gqap_status gqap_decode_plan(const gqap_decode_desc_t* desc, gqap_decode_plan_t* plan) {
+  if (!desc || !plan) return fail(GQAP_ERR_INVALID_ARGUMENT, "null desc or plan");
+  std::memset(plan, 0, sizeof(*plan));
+  int q_esz = 0, kv_esz = 0;
+  gqap_status st = check_decode_desc(*desc, &q_esz, &kv_esz);
+  if (st != GQAP_OK) return st;
+  const gqap_decode_desc_t& d = *desc;
+  plan->desc = d;
+  plan->ratio = d.num_q_heads / d.num_kv_heads;
+  plan->head_chunks = (int32_t)ceil_div(plan->ratio, 16);
+  plan->kernel = d.kv_dtype == GQAP_F32 ? kDecodeF32Valu
+                 : d.kv_dtype == GQAP_BF16 ? kDecodeBf16Mfma
+                                            : kDecodeFp8Mfma;
+  const int64_t nblk_cap = std::max<int64_t>(1, ceil_div(d.max_seq_len, kBlock));
+  const int cus = d.num_cus ? d.num_cus : kDefaultCUs;
+  int64_t splits;
+  if (d.num_splits > 0) {
+    splits = std::min<int64_t>(d.num_splits, nblk_cap);
+  } else {
+    // Enough work items for several resident workgroups per CU, but keep each
+    // wave of a split on at least two blocks so per-split overhead stays small.
+    const int64_t pairs = std::max<int64_t>(1, (int64_t)d.batch * d.num_kv_heads * plan->head_chunks);
+    const int64_t waves_per_wg = plan->kernel == kDecodeF32Valu ? 1 : kMfmaWaves;
+    const int64_t min_bps = 2 * waves_per_wg;
+    splits = std::max<int64_t>(1, ceil_div(8LL * cus, pairs));
+    int64_t bps = std::max<int64_t>(ceil_div(nblk_cap, splits), std::min<int64_t>(min_bps, nblk_cap));
+    splits = ceil_div(nblk_cap, bps);
+  }
+  plan->blocks_per_split = (int32_t)ceil_div(nblk_cap, splits);
+  plan->num_splits = (int32_t)ceil_div(nblk_cap, plan->blocks_per_split);
+  const int64_t rows = (int64_t)d.batch * d.num_q_heads * plan->num_splits;
+  uint64_t ws = (uint64_t)rows * d.head_dim * sizeof(float);
+  ws = (ws + 255) & ~uint64_t(255);
+  ws += (uint64_t)rows * sizeof(float);
+  plan->workspace_bytes = (ws + 255) & ~uint64_t(255);
+  plan->magic = GQAP_PLAN_MAGIC;
+  return GQAP_OK;
+}
+
+extern "C" gqap_status gqap_decode_validate_host(const gqap_decode_plan_t* plan, const int32_t* block_table_host,
+                                                 const int32_t* seq_lens_host) {
+  if (!plan || plan->magic != GQAP_PLAN_MAGIC) return fail(GQAP_ERR_INVALID_ARGUMENT, "invalid plan");
+  const gqap_decode_desc_t& d = plan->desc;
+  if (d.batch > 0 && (!block_table_host || !seq_lens_host))
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "null host metadata");
+  const int64_t cap = std::min<int64_t>((int64_t)d.max_blocks_per_seq * kBlock, d.max_seq_len);
+  for (int b = 0; b < d.batch; ++b) {
+    const int64_t L = seq_lens_host[b];
+    if (L < 0 || L > cap)
+      return fail(GQAP_ERR_INVALID_ARGUMENT, "seq_lens[%d] = %lld outside [0, %lld]", b, (long long)L,
+                  (long long)cap);
+    const int64_t nb = ceil_div(L, kBlock);
+    for (int64_t j = 0; j < nb; ++j) {
+      const int64_t id = block_table_host[(int64_t)b * d.block_table_stride + j];
+      if (id < 0 || id >= d.num_pool_blocks)
+        return fail(GQAP_ERR_INVALID_ARGUMENT, "block_table[%d, %lld] = %lld outside the pool [0, %d)", b,
+                    (long long)j, (long long)id, d.num_pool_blocks);
+    }
+  }
+  return GQAP_OK;
+}
+
+extern "C" gqap_status gqap_prefill_plan(const gqap_prefill_desc_t* desc, gqap_prefill_plan_t* plan) {
+  if (!desc || !plan) return fail(GQAP_ERR_INVALID_ARGUMENT, "null desc or plan");
+  std::memset(plan, 0, sizeof(*plan));
+  const gqap_prefill_desc_t& d = *desc;
+  if (d.batch < 0) return fail(GQAP_ERR_INVALID_ARGUMENT, "batch must be >= 0");
+  if (d.num_q_heads <= 0 || d.num_kv_heads <= 0)
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "head counts must be positive (Hq=%d, Hk=%d)", d.num_q_heads,
+                d.num_kv_heads);
+  if (d.num_q_heads % d.num_kv_heads)
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "Hq (%d) must be a multiple of Hk (%d)", d.num_q_heads, d.num_kv_heads);
+  if (d.dtype != GQAP_BF16) return fail(GQAP_ERR_DTYPE, "prefill takes bf16 q/k/v (got dtype %d)", d.dtype);
+  if (d.causal != 1) return fail(GQAP_ERR_UNSUPPORTED, "only causal prefill is implemented");
+  const bool mla = d.head_dim_qk == 192 && d.head_dim_rope == 64;
+  const bool plain = d.head_dim_qk == 128 && d.head_dim_rope == 0;
+  if (!mla && !plain)
+    return fail(GQAP_ERR_UNSUPPORTED, "head widths qk=%d rope=%d not supported (128/0 or 192/64)", d.head_dim_qk,
+                d.head_dim_rope);
+  if (d.head_dim_v != 128) return fail(GQAP_ERR_UNSUPPORTED, "head_dim_v must be 128 (got %d)", d.head_dim_v);
+  if (d.total_tokens < 0 || d.max_seq_len < 0)
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "total_tokens and max_seq_len must be >= 0");
+  if (d.max_seq_len > d.total_tokens && d.batch > 0)
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "max_seq_len %d exceeds total_tokens %d", d.max_seq_len, d.total_tokens);
+  const int64_t Dn = d.head_dim_qk - d.head_dim_rope;
+  if (d.q_stride_head < d.head_dim_qk || d.q_stride_token < d.q_stride_head * d.num_q_heads)
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "q strides overlap");
+  if (d.k_stride_head < Dn || d.k_stride_token < d.k_stride_head * d.num_kv_heads)
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "k strides overlap");
+  if (d.v_stride_head < d.head_dim_v || d.v_stride_token < d.v_stride_head * d.num_kv_heads)
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "v strides overlap");
+  if (d.out_stride_head < d.head_dim_v || d.out_stride_token < d.out_stride_head * d.num_q_heads)
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "out strides overlap");
+  if (d.head_dim_rope && d.kr_stride_token < d.head_dim_rope)
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "k_rope token stride < rope width");
+  const int64_t strides[] = {d.q_stride_token, d.q_stride_head, d.k_stride_token, d.k_stride_head,
+                             d.v_stride_token, d.v_stride_head, d.out_stride_token, d.out_stride_head,
+                             d.head_dim_rope ? d.kr_stride_token : 8};
+  for (int64_t s : strides)
+    if (!aligned16(s, 2)) return fail(GQAP_ERR_INVALID_ARGUMENT, "strides must keep rows 16-byte aligned");
+  if (d.has_block_mask != 0 && d.has_block_mask != 1)
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "has_block_mask must be 0 or 1");
+  if (d.has_block_mask && (int64_t)d.mask_blocks < ceil_div(d.max_seq_len, kBlock))
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "mask_blocks %d < ceil(max_seq_len/64)", d.mask_blocks);
+  if (d.num_cus < 0) return fail(GQAP_ERR_INVALID_ARGUMENT, "num_cus must be >= 0");
+  plan->desc = d;
+  plan->ratio = d.num_q_heads / d.num_kv_heads;
+  plan->q_tile_rows = 64;
+  plan->q_tiles = (int32_t)ceil_div(d.max_seq_len, plan->q_tile_rows);
+  plan->kernel = mla ? 2 : 1;
+  plan->workspace_bytes = 0;
+  plan->magic = GQAP_PLAN_MAGIC;
+  return GQAP_OK;
+}
+
+extern "C" const char* gqap_last_error(void) { return last_error_slot().c_str(); }
+
+extern "C" const char* gqap_version(void) { return "gqap 0.1.0 (gfx950)"; }

@@ -1,0 +1,268 @@
+/*
+ * gqap — paged grouped-query attention for AMD MI355X (gfx950).
+ *
+ * A C ABI over hand-written HIP kernels:
+ *   - single-token decode over a paged KV cache with grouped-query heads
+ *     (split over the key axis, then a combine pass), KV in fp32, bf16 or
+ *     OCP fp8 e4m3fn with a per-tensor scale;
+ *   - ragged causal prefill on bf16 matrix cores, with the MLA split head
+ *     (a 128-wide per-head key part plus a 64-wide rope key shared by all
+ *     heads) and an optional 64x64 block-sparse mask;
+ *   - plan / validation calls that run on the host only;
+ *   - a debug gather that exposes the decode kernels' page addressing.
+ *
+ * Conventions for every call
+ *   - Ownership: the caller owns every buffer (device tensors, plan structs,
+ *     workspace).  The library never allocates or frees device memory, never
+ *     synchronises a stream and never reads device memory from the host.
+ *     Inputs are never modified.
+ *   - Pointers named "device" must be device-accessible addresses on the
+ *     current HIP device; pointers named "host" are ordinary host memory.
+ *   - Strides are in elements of the tensor's own dtype.
+ *   - Index tensors are int32.
+ *   - Errors: every call validates before it launches anything.  On error it
+ *     returns a non-zero gqap_status, launches nothing, and records a message
+ *     readable with gqap_last_error() (per host thread).  Faults caused by
+ *     invalid device-side data that the caller did not validate (for example
+ *     a block id outside the pool) are the caller's responsibility; they may
+ *     only surface as GQAP_ERR_HIP if the launch itself reports an error.
+ *   - Streams: `stream` is a hipStream_t passed as void*; NULL means the null
+ *     stream.  All device work is asynchronous on that stream.
+ *
+ * Sources for the operations (pages of the reference material):
+ *   FlashMLA "Tensor Shapes Reference" (flash_mla_with_kvcache,
+ *   get_mla_metadata, flash_mla_prefill, the layout diagrams and the shape
+ *   error table); MATE msa_interface (plan/execute split, int32 metadata,
+ *   cu_seqlens, causal offset, fp8 e4m3fn with k_scale/v_scale, num_splits,
+ *   optional LSE output); Modular flare_mla_prefill (ragged MLA prefill with a
+ *   shared rope key and reduced output width, explicit float scale).
+ */
+#ifndef GQAP_H_
+#define GQAP_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GQAP_BLOCK_SIZE 64      /* paged-cache block rows; fixed at 64 on the pages */
+#define GQAP_PLAN_MAGIC 0x47514150u
+
+typedef enum gqap_status {
+  GQAP_OK = 0,
+  GQAP_ERR_INVALID_ARGUMENT = 1, /* shape, value, stride, pointer or size problem */
+  GQAP_ERR_DTYPE = 2,            /* dtype or dtype combination not allowed */
+  GQAP_ERR_UNSUPPORTED = 3,      /* valid request this library does not implement */
+  GQAP_ERR_HIP = 4               /* a HIP runtime call or launch failed */
+} gqap_status;
+
+typedef enum gqap_dtype {
+  GQAP_F32 = 0,
+  GQAP_BF16 = 1,
+  GQAP_FP8_E4M3FN = 2,           /* OCP fp8 E4M3FN (bias 7, no inf, 0x7F/0xFF NaN) */
+  GQAP_F16 = 3                   /* reserved: always GQAP_ERR_UNSUPPORTED */
+} gqap_dtype;
+
+/* ------------------------------------------------------------------------ */
+/* Paged decode                                                              */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Shapes (FlashMLA tensor-shape reference, section 1, with a shared pool):
+ *   q            [B, Hq, D]            dtype q_dtype; strides q_stride_batch,
+ *                                      q_stride_head; D contiguous.
+ *   k_pool,v_pool[NB, Hk, 64, D]       dtype kv_dtype; strides kv_stride_block,
+ *                                      kv_stride_head; the 64 x D slab of one
+ *                                      (block, head) is contiguous (row stride D).
+ *   block_table  [B, Nblk] int32       row stride block_table_stride; entry
+ *                                      [b, j] is the pool block holding logical
+ *                                      tokens 64j .. 64j+63 of sequence b; only
+ *                                      entries j < ceil(seq_lens[b] / 64) are read.
+ *   seq_lens     [B] int32             0 <= seq_lens[b] <= min(Nblk*64, max_seq_len).
+ *   out          [B, Hq, D]            dtype q_dtype; strides out_stride_*.
+ *   lse          [B, Hq] float32       optional, contiguous, natural log.
+ * Query head h reads KV head h / (Hq / Hk).  The decode query is the newest
+ * token: it sees all seq_lens[b] keys.  seq_lens[b] == 0 gives out = 0 and
+ * lse = -inf.
+ *
+ * Dtype combinations (q / kv): F32/F32, BF16/BF16, BF16/FP8_E4M3FN.
+ * For FP8 KV the value of a stored code c is e4m3fn(c) * k_scale (keys) or
+ * e4m3fn(c) * v_scale (values); for other KV dtypes both scales must be 1.
+ * Supported head_dim: 64 or 128.
+ */
+typedef struct gqap_decode_desc_t {
+  int32_t batch;               /* B >= 0 */
+  int32_t num_q_heads;         /* Hq > 0 */
+  int32_t num_kv_heads;        /* Hk > 0, Hq % Hk == 0 */
+  int32_t head_dim;            /* D */
+  int32_t block_size;          /* must be 64 */
+  int32_t max_blocks_per_seq;  /* Nblk: block_table row width, >= 1 */
+  int32_t num_pool_blocks;     /* NB >= 1 */
+  int32_t max_seq_len;         /* capacity the grid is sized for; <= Nblk*64 */
+  int32_t q_dtype;             /* gqap_dtype; the output has the same dtype */
+  int32_t kv_dtype;            /* gqap_dtype */
+  int64_t q_stride_batch;      /* elements */
+  int64_t q_stride_head;
+  int64_t out_stride_batch;
+  int64_t out_stride_head;
+  int64_t kv_stride_block;     /* elements between pool blocks */
+  int64_t kv_stride_head;      /* elements between heads of one block, >= 64*D */
+  int64_t block_table_stride;  /* int32 elements between block_table rows, >= Nblk */
+  int32_t num_splits;          /* 0 = choose automatically; else the split count */
+  int32_t num_cus;             /* compute units to plan for; 0 = 256 (MI355X) */
+} gqap_decode_desc_t;
+
+/* Plain-old-data plan, filled by gqap_decode_plan and read by the other calls. */
+typedef struct gqap_decode_plan_t {
+  gqap_decode_desc_t desc;
+  int32_t num_splits;          /* splits of the key axis per sequence */
+  int32_t blocks_per_split;    /* 64-row blocks handled by one split */
+  int32_t ratio;               /* Hq / Hk */
+  int32_t head_chunks;         /* ceil(ratio / 16) */
+  uint64_t workspace_bytes;    /* device workspace the decode needs */
+  uint32_t magic;              /* GQAP_PLAN_MAGIC when valid */
+  uint32_t kernel;             /* internal kernel variant */
+} gqap_decode_plan_t;
+
+/*
+ * Validate a decode request and choose its split schedule.  Pure host code:
+ * touches no device and no tensor (get_mla_metadata on the FlashMLA page is
+ * likewise shape/stride validation only).  The schedule depends only on the
+ * descriptor's capacities, never on live lengths, so one plan serves every
+ * call with the same shapes.
+ * Errors: INVALID_ARGUMENT (non-positive sizes, Hq % Hk != 0, max_seq_len >
+ * Nblk*64, strides that overlap or break 16-byte alignment, bad num_splits),
+ * DTYPE (dtype pair not in the list above), UNSUPPORTED (block_size != 64,
+ * head_dim not 64/128, F16).
+ */
+gqap_status gqap_decode_plan(const gqap_decode_desc_t* desc, gqap_decode_plan_t* plan);
+
+/*
+ * Optional deep check of host copies of the metadata (the "coverage up to
+ * max seq_lens" requirement of get_mla_metadata): 0 <= seq_lens[b] <=
+ * min(Nblk*64, max_seq_len), and every entry block_table[b, j] with
+ * j < ceil(seq_lens[b]/64) lies in [0, NB).  Padding entries are not checked.
+ * block_table_host uses the plan's block_table_stride.  Errors:
+ * INVALID_ARGUMENT naming the first offending entry.
+ */
+gqap_status gqap_decode_validate_host(const gqap_decode_plan_t* plan,
+                                      const int32_t* block_table_host,
+                                      const int32_t* seq_lens_host);
+
+/*
+ * Decode attention for one query token per sequence.
+ *   scale:    multiplies q.k (e.g. 1/sqrt(D)); required, no default.
+ *   k_scale, v_scale: per-tensor dequantisation scales (1.0 unless FP8 KV).
+ *   workspace: device buffer of at least plan->workspace_bytes bytes, 256-byte
+ *              aligned; its contents on entry do not matter.
+ * All device pointers must be 16-byte aligned.  Asynchronous on `stream`.
+ */
+gqap_status gqap_paged_decode(const gqap_decode_plan_t* plan,
+                              const void* q, const void* k_pool, const void* v_pool,
+                              const int32_t* block_table, const int32_t* seq_lens,
+                              float scale, float k_scale, float v_scale,
+                              void* out, float* lse,
+                              void* workspace, uint64_t workspace_bytes,
+                              void* stream);
+
+/*
+ * Copy logical rows [0, num_rows) of KV head `kv_head` of sequence `b` from a
+ * paged pool into dst [num_rows, D] (same dtype as the pool, contiguous),
+ * using the same address arithmetic as the decode kernels.  Rows at or past
+ * seq_lens[b] (read on the device) are left untouched.  num_rows is a host
+ * value <= Nblk*64.  Exposed for bit-exact tests of the page addressing.
+ */
+gqap_status gqap_debug_gather_kv(const gqap_decode_plan_t* plan, const void* pool,
+                                 const int32_t* block_table, const int32_t* seq_lens,
+                                 int32_t b, int32_t kv_head, int32_t num_rows,
+                                 void* dst, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Ragged causal prefill (GQA, optional MLA rope key, optional block mask)   */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Token-major ragged layout (Modular flare_mla_prefill; MATE cu_seqlens):
+ *   q       [T, Hq, Dqk]   Dqk = Dn + Dr; strides q_stride_token, q_stride_head
+ *   k       [T, Hk, Dn]    per-head key part (Dn = 128)
+ *   v       [T, Hk, Dv]    Dv = 128
+ *   k_rope  [T, 1, Dr]     shared rope key (Dr = 64), broadcast to every head;
+ *                          NULL iff Dr == 0
+ *   cu_seqlens [B + 1] int32 device: [0, cumsum(seq_len)]; cu_seqlens[B] <= T
+ *   block_mask [B, nb, nb] uint8 device, optional (has_block_mask): entry
+ *                          [b, i, j] != 0 lets query block i see key block j;
+ *                          nb = mask_blocks >= ceil(max_seq_len/64), row
+ *                          stride nb; entries above the diagonal are ignored.
+ *   out     [T, Hq, Dv]    bf16; strides out_stride_*
+ *   lse     [T, Hq] float32 optional, contiguous, natural log
+ * Query i of a sequence sees key j iff j <= i (equal query and key lengths,
+ * so the causal offset is 0) and, with a mask, mask[b, i/64, j/64] != 0.
+ * score(i, j, h) = scale * (q[i,h,:Dn] . k[j,h/(Hq/Hk),:] + q[i,h,Dn:] . k_rope[j,0,:]).
+ * A row with no visible key gets out = 0 and lse = -inf.
+ */
+typedef struct gqap_prefill_desc_t {
+  int32_t batch;               /* B >= 0 */
+  int32_t num_q_heads;         /* Hq */
+  int32_t num_kv_heads;        /* Hk, Hq % Hk == 0 */
+  int32_t head_dim_qk;         /* Dqk: 128 (Dr = 0) or 192 (Dr = 64) */
+  int32_t head_dim_rope;       /* Dr: 0 or 64 */
+  int32_t head_dim_v;          /* Dv: 128 */
+  int32_t total_tokens;        /* T: rows of q/k/v/out */
+  int32_t max_seq_len;         /* capacity the grid is sized for */
+  int32_t dtype;               /* GQAP_BF16 */
+  int32_t causal;              /* must be 1 */
+  int32_t has_block_mask;      /* 0 or 1 */
+  int32_t mask_blocks;         /* nb when has_block_mask */
+  int64_t q_stride_token, q_stride_head;
+  int64_t k_stride_token, k_stride_head;
+  int64_t v_stride_token, v_stride_head;
+  int64_t kr_stride_token;
+  int64_t out_stride_token, out_stride_head;
+  int32_t num_cus;             /* 0 = 256 */
+  int32_t reserved;
+} gqap_prefill_desc_t;
+
+typedef struct gqap_prefill_plan_t {
+  gqap_prefill_desc_t desc;
+  int32_t ratio;               /* Hq / Hk */
+  int32_t q_tiles;             /* ceil(max_seq_len / q_tile_rows) */
+  int32_t q_tile_rows;
+  int32_t kernel;
+  uint64_t workspace_bytes;    /* 0 in this version */
+  uint32_t magic;
+  uint32_t reserved;
+} gqap_prefill_plan_t;
+
+/*
+ * Validate a prefill request.  Pure host code.  Errors: INVALID_ARGUMENT
+ * (sizes, strides, Hq % Hk, mask_blocks too small), DTYPE (not bf16),
+ * UNSUPPORTED (causal == 0, head widths other than 128/192 with rope 0/64,
+ * Dv != 128).
+ */
+gqap_status gqap_prefill_plan(const gqap_prefill_desc_t* desc, gqap_prefill_plan_t* plan);
+
+/*
+ * Ragged causal prefill.  All device pointers 16-byte aligned.  workspace may
+ * be NULL when plan->workspace_bytes == 0.  Asynchronous on `stream`.
+ */
+gqap_status gqap_prefill(const gqap_prefill_plan_t* plan,
+                         const void* q, const void* k, const void* v, const void* k_rope,
+                         const int32_t* cu_seqlens, const uint8_t* block_mask,
+                         float scale, void* out, float* lse,
+                         void* workspace, uint64_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+
+/* Message of the last non-OK status on this host thread ("" if none). */
+const char* gqap_last_error(void);
+
+/* Library version string. */
+const char* gqap_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQAP_H_ */

@@ -1,0 +1,81 @@
+"""Helpers shared by the GPU tests: move generated cases to the device, run the
+library through its C ABI, and widen its outputs for comparison."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import gqa_attention_paged_amd as gq
+
+
+def announce(msg: str) -> None:
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def bits_to_tensor(x: np.ndarray, tag: str) -> torch.Tensor:
+    if tag == "f32":
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    if tag == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16)
+    if tag == "e4m3fn":
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.uint8)).view(torch.float8_e4m3fn)
+    raise ValueError(tag)
+
+
+def tensor_to_f64(t: torch.Tensor) -> np.ndarray:
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        bits = t.view(torch.int16).numpy().view(np.uint16)
+        return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return t.numpy().astype(np.float64)
+
+
+class DeviceDecode:
+    """A decode case resident on the device plus a plan for it."""
+
+    def __init__(self, case, num_splits: int = 0, device: str = "cuda"):
+        self.case = case
+        self.q = bits_to_tensor(case.q, case.q_dtype).to(device)
+        self.k = bits_to_tensor(case.k_pool, case.kv_dtype).to(device)
+        self.v = bits_to_tensor(case.v_pool, case.kv_dtype).to(device)
+        self.bt = torch.from_numpy(np.ascontiguousarray(case.block_table, dtype=np.int32)).to(device)
+        self.sl = torch.from_numpy(np.ascontiguousarray(case.seq_lens, dtype=np.int32)).to(device)
+        self.out = torch.empty_like(self.q)
+        self.lse = torch.empty((case.B, case.Hq), dtype=torch.float32, device=device)
+        max_len = max(1, int(case.seq_lens.max())) if case.B else 1
+        self.desc = gq.decode_desc(self.q, self.k, self.bt, max_seq_len=max_len, out=self.out,
+                                   num_splits=num_splits)
+        self.plan = gq.gqap_decode_plan(self.desc)
+        self.ws = torch.empty(max(256, self.plan.workspace_bytes), dtype=torch.uint8, device=device)
+
+    def run(self, stream=None):
+        c = self.case
+        gq.gqap_paged_decode(self.plan, self.q, self.k, self.v, self.bt, self.sl, c.scale, c.k_scale, c.v_scale,
+                             self.out, self.lse, self.ws, self.plan.workspace_bytes, stream=stream)
+        return self.out, self.lse
+
+    def results(self):
+        torch.cuda.synchronize()
+        return tensor_to_f64(self.out), self.lse.detach().cpu().numpy().astype(np.float64)
+
+
+def max_abs_err(a: np.ndarray, b: np.ndarray) -> float:
+    if a.size == 0:
+        return 0.0
+    d = np.abs(a - b)
+    if np.isnan(d).any():
+        return float("inf")
+    return float(d.max())
+
+
+def lse_err(gpu: np.ndarray, ref: np.ndarray) -> float:
+    """max |a - b| over finite entries; inf if the -inf pattern differs or NaN appears."""
+    if np.isnan(gpu).any():
+        return float("inf")
+    if not np.array_equal(np.isneginf(gpu), np.isneginf(ref)):
+        return float("inf")
+    fin = np.isfinite(ref)
+    return float(np.abs(gpu[fin] - ref[fin]).max()) if fin.any() else 0.0
