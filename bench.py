@@ -107,7 +107,7 @@ def bench_decode(case, steps, warmup, torch, gq, gu, check=True):
         "workload": case.name, "bytes": nbytes, "ms_per_step": ms_step, "ms_kernel": ms_ev,
         "ms_kernel_p10": evs[len(evs) // 10], "ms_kernel_p90": evs[(9 * len(evs)) // 10],
         "gbs_step": nbytes / (ms_step * 1e-3) / 1e9, "gbs_kernel": nbytes / (ms_ev * 1e-3) / 1e9,
-        "splits": plan.num_splits, "blocks_per_split": plan.blocks_per_split, "rotating_copies": nrot,
+        "workers": plan.num_workers, "rotating_copies": nrot,
         "max_abs_err_sample": err,
     }
 
@@ -216,8 +216,7 @@ def main(argv=None) -> int:
             "workload": "paged GQA decode, bf16: B=64, Hq=32, Hk=8, D=128, one query token per sequence, "
                         "seq_lens ~ U{1024..4096}, 64-row blocks, shuffled block_table",
             "kv_bytes_per_step": prim["bytes"],
-            "splits": prim["splits"],
-            "blocks_per_split": prim["blocks_per_split"],
+            "workers": prim["workers"],
             "device": props.name,
             "cus": props.multi_processor_count,
         },

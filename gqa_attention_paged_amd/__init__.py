@@ -48,14 +48,14 @@ class DecodeDesc(ctypes.Structure):
         ("out_stride_batch", ctypes.c_int64), ("out_stride_head", ctypes.c_int64),
         ("kv_stride_block", ctypes.c_int64), ("kv_stride_head", ctypes.c_int64),
         ("block_table_stride", ctypes.c_int64),
-        ("num_splits", ctypes.c_int32), ("num_cus", ctypes.c_int32),
+        ("num_workers", ctypes.c_int32), ("num_cus", ctypes.c_int32),
     ]
 
 
 class DecodePlan(ctypes.Structure):
     _fields_ = [
-        ("desc", DecodeDesc), ("num_splits", ctypes.c_int32), ("blocks_per_split", ctypes.c_int32),
-        ("ratio", ctypes.c_int32), ("head_chunks", ctypes.c_int32), ("workspace_bytes", ctypes.c_uint64),
+        ("desc", DecodeDesc), ("num_workers", ctypes.c_int32), ("ratio", ctypes.c_int32),
+        ("head_chunks", ctypes.c_int32), ("max_pieces", ctypes.c_int32), ("workspace_bytes", ctypes.c_uint64),
         ("magic", ctypes.c_uint32), ("kernel", ctypes.c_uint32),
     ]
 
@@ -207,7 +207,7 @@ def dtype_tag(t) -> int:
     return _TORCH_DTYPE_TAG[key]
 
 
-def decode_desc(q, k_pool, block_table, max_seq_len: int, out=None, num_splits: int = 0,
+def decode_desc(q, k_pool, block_table, max_seq_len: int, out=None, num_workers: int = 0,
                 num_cus: int = 0) -> DecodeDesc:
     """Descriptor for q [B, Hq, D], pool [NB, Hk, 64, D], block_table [B, Nblk]."""
     B, Hq, D = q.shape
@@ -225,7 +225,7 @@ def decode_desc(q, k_pool, block_table, max_seq_len: int, out=None, num_splits: 
     d.out_stride_batch, d.out_stride_head = out.stride(0), out.stride(1)
     d.kv_stride_block, d.kv_stride_head = k_pool.stride(0), k_pool.stride(1)
     d.block_table_stride = block_table.stride(0)
-    d.num_splits = num_splits
+    d.num_workers = num_workers
     d.num_cus = num_cus
     return d
 

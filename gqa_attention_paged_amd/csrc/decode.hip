@@ -1,24 +1,38 @@
-// Split-KV paged GQA decode for gfx950.
+// Paged GQA decode for gfx950: balanced persistent workers + LSE combine.
 //
 // What is computed (FlashMLA tensor-shape reference, section 1 and the GQA
 // diagram): for every sequence b and query head h, attention of the single
 // query q[b, h] over the seq_lens[b] keys and values of KV head h / (Hq/Hk),
-// gathered block by block through block_table.  MATE's decode path schedules
-// the key axis in splits (num_splits); here every split produces a normalised
-// partial output and its log-sum-exp, and a second pass merges the splits.
+// gathered block by block through block_table.
 //
-// Workgroup (split, kv head, sequence), four waves.  Each wave walks every
-// fourth 64-row block of the split with its own online-softmax state; the
-// waves are merged through LDS at the end of the split.  Per block:
-//   K: global -> registers directly in the matrix-core operand layout;
-//   V: global -> registers (contiguous 16-byte chunks) -> LDS (XOR-swizzled)
-//      -> transposed LDS reads that deliver the token-packed operand of P.V;
-//   S^T = K q^T and O^T += V^T P^T on 16x16x32 bf16 MFMA with fp32 accumulate;
-//   the up-to-16 query heads of one KV head share every K/V byte.
+// How (two launches on one stream):
+//  1. decode_worker_*: one wave per worker.  A work unit is one 64-row key
+//     block of one (sequence, KV head, head chunk); units are ordered
+//     sequence-major, then (KV head, head chunk), then block.  The unit list
+//     is cut into num_workers equal contiguous ranges, so every worker
+//     streams the same number of K/V bytes whatever the lengths.  Each
+//     worker finds its first unit with a wave-wide scan of seq_lens (no
+//     separate metadata pass).  Each contiguous run of units of one
+//     (sequence, KV head, head chunk) inside a worker's range is a piece; a
+//     piece ends with a normalised partial output and its base-2 LSE in the
+//     workspace, at slot (piece index + worker index), which is unique
+//     because worker ranges are ordered.
+//  2. decode_combine: merges the pieces of each (sequence, query head) with
+//     weights 2^(lse_piece - max) and writes out (and the natural-log LSE).
+//
+// The bf16/fp8 worker keeps the next block in flight while it computes the
+// current one: K goes straight into (double-buffered) registers in the
+// 16x16x32 MFMA operand layout; V goes into staging registers as contiguous
+// 16-byte rows, is written to an XOR-swizzled LDS tile once the current
+// block's reads of that tile are issued, and comes back through the LDS
+// transpose read as the token-packed operand of P.V.  All loads are plain
+// register loads, so the compiler's wait counts stay exact.  S^T = K q^T and O^T += V^T P^T run on bf16 MFMA with fp32
+// accumulation; the up-to-16 query heads of a KV head share every K/V byte.
 #include "dev.hpp"
 #include "status.hpp"
 
 #include <cmath>
+#include <type_traits>
 
 namespace gqap {
 
@@ -28,20 +42,147 @@ struct DecodeArgs {
   const void* v;
   const int32_t* block_table;
   const int32_t* seq_lens;
-  float* ws_o;    // [B, Hq, S, D] normalised partial outputs
-  float* ws_lse;  // [B, Hq, S] partial log-sum-exp, base 2
+  int32_t* prefix;  // [B + 1] key blocks before each sequence (written by worker 0)
+  float* ws_lse;    // [pieces][16] base 2
+  float* ws_o;      // [pieces][16][D]
   void* out;
   float* lse;
   int64_t q_sb, q_sh, o_sb, o_sh;
   int64_t kv_block_bytes, kv_head_bytes, bt_stride;
-  int32_t B, Hq, Hk, ratio, head_chunks, nsplit, bps;
-  int32_t max_len;         // capacity from the plan; longer seq_lens are clamped to it
+  int32_t B, Hq, Hk, ratio, head_chunks, hkhc, nworkers;
+  int32_t max_len;  // capacity from the plan; longer seq_lens are clamped to it
   float score_scale_log2;  // scale * k_scale * log2(e)
   float score_scale;       // scale * k_scale
   float v_scale;
 };
 
 namespace dev {
+
+// Metadata that no decode kernel writes (seq_lens, block_table) is read
+// through the constant address space: uniform reads become scalar loads,
+// which wait on their own counter and never drain in-flight K/V loads.
+__device__ __forceinline__ int ld_const(const int32_t* p, int64_t i) {
+  return ((const int32_t __attribute__((address_space(4)))*)p)[i];
+}
+
+__device__ __forceinline__ int clamp_len(const DecodeArgs& a, int b) {
+  return min(max(ld_const(a.seq_lens, b), 0), a.max_len);
+}
+
+// Position of one work unit.
+struct Unit {
+  int b;     // sequence
+  int ql;    // kv_head * head_chunks + head_chunk
+  int j;     // key block within the sequence
+  int nblk;  // key blocks of sequence b
+  int L;     // keys of sequence b
+  int phys;  // pool block holding block j
+};
+
+__device__ __forceinline__ int seq_blocks(const DecodeArgs& a, int b) { return (clamp_len(a, b) + 63) >> 6; }
+
+__device__ __forceinline__ void unit_load_seq(const DecodeArgs& a, Unit& u) {
+  u.L = clamp_len(a, u.b);
+  u.nblk = (u.L + 63) >> 6;
+}
+
+__device__ __forceinline__ void unit_load_phys(const DecodeArgs& a, Unit& u) {
+  u.phys = ld_const(a.block_table, (int64_t)u.b * a.bt_stride + u.j);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  const int lane = __lane_id();
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+// Key blocks of sequences [0, b_end), summed by one wave (all lanes get it).
+__device__ __forceinline__ int64_t blocks_before(const DecodeArgs& a, int b_end) {
+  int64_t total = 0;
+  const int lane = __lane_id();
+  for (int b0 = 0; b0 < b_end; b0 += 64) {
+    const int b = b0 + lane;
+    int nb = b < b_end ? seq_blocks(a, b) : 0;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) nb += __shfl_xor(nb, off);
+    total += nb;
+  }
+  return total;
+}
+
+// Sequence holding key-block ordinal t (prefix[b] <= t < prefix[b+1]) and
+// prefix[b], found by one wave scanning seq_lens 64 sequences at a time.
+__device__ __forceinline__ void locate_block(const DecodeArgs& a, int64_t t, int* b_out, int64_t* before_out) {
+  int64_t run = 0;
+  const int lane = __lane_id();
+  for (int b0 = 0; b0 < a.B; b0 += 64) {
+    const int b = b0 + lane;
+    const int nb = b < a.B ? seq_blocks(a, b) : 0;
+    const int incl = wave_incl_scan(nb);
+    const bool hit = nb > 0 && run + incl - nb <= t && t < run + incl;
+    const unsigned long long m = __ballot(hit);
+    if (m) {
+      const int l = __ffsll((long long)m) - 1;
+      *b_out = b0 + l;
+      *before_out = run + __shfl(incl - nb, l);
+      return;
+    }
+    run += __shfl(incl, 63);
+  }
+  *b_out = a.B;
+  *before_out = run;
+}
+
+// Exclusive prefix of the per-sequence block counts -> a.prefix[0..B] (one wave).
+__device__ __forceinline__ void write_prefix(const DecodeArgs& a) {
+  int64_t run = 0;
+  const int lane = __lane_id();
+  for (int b0 = 0; b0 < a.B; b0 += 64) {
+    const int b = b0 + lane;
+    const int nb = b < a.B ? seq_blocks(a, b) : 0;
+    const int incl = wave_incl_scan(nb);
+    if (b < a.B) a.prefix[b] = (int32_t)(run + incl - nb);
+    run += __shfl(incl, 63);
+  }
+  if (lane == 0) a.prefix[a.B] = (int32_t)run;
+}
+
+// First unit of a worker whose range starts at unit ub.
+__device__ __forceinline__ Unit unit_at(const DecodeArgs& a, int64_t ub) {
+  Unit u;
+  int64_t before;
+  locate_block(a, ub / a.hkhc, &u.b, &before);
+  unit_load_seq(a, u);
+  const int rem = (int)(ub - before * a.hkhc);
+  u.ql = rem / u.nblk;
+  u.j = rem - u.ql * u.nblk;
+  unit_load_phys(a, u);
+  return u;
+}
+
+// Next unit in sequence-major order, skipping sequences without keys.  Only
+// called while the worker's range still holds a unit, so b stays below B.
+__device__ __forceinline__ Unit unit_next(const DecodeArgs& a, Unit u) {
+  if (++u.j == u.nblk) {
+    u.j = 0;
+    if (++u.ql == a.hkhc) {
+      u.ql = 0;
+      do {
+        ++u.b;
+      } while (u.b < a.B && seq_blocks(a, u.b) == 0);
+      if (u.b < a.B) unit_load_seq(a, u);
+    }
+  }
+  if (u.b < a.B) unit_load_phys(a, u);
+  return u;
+}
+
+__device__ __forceinline__ bool same_piece(const Unit& x, const Unit& y) { return x.b == y.b && x.ql == y.ql; }
 
 // Token (row of the 64-row block) held by MFMA row m of score tile mt.  The
 // PV operand needs each 16-lane group to hold 8 tokens that the V transpose
@@ -52,10 +193,9 @@ __device__ __forceinline__ int token_of(int mt, int m) {
   return 16 * mt + m;
 }
 
-// Byte offset of (row, byte column c) inside a wave's V tile in LDS.  Rows are
-// RB bytes; pieces of P bytes are XOR-permuted within their row so that the
-// transpose reads (16 or 32 rows at one column) and the staging stores spread
-// over all banks.
+// Byte offset of (row, byte column c) inside a V tile in LDS.  Rows are RB
+// bytes; pieces of P bytes are XOR-permuted within their row so that the
+// transpose reads (16 or 32 rows at one column) spread over all banks.
 template <int RB, int P>
 __device__ __forceinline__ int vswz(int row, int c) {
   constexpr int NP = RB / P;
@@ -69,124 +209,139 @@ __device__ __forceinline__ int vswz(int row, int c) {
 using namespace dev;
 
 template <int D, bool FP8>
-__global__ __launch_bounds__(256, 2) void decode_split_mfma(DecodeArgs a) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_worker_mfma(DecodeArgs a) {
   constexpr int ESZ = FP8 ? 1 : 2;
-  constexpr int RB = D * ESZ;          // bytes per K/V row
-  constexpr int VB = 64 * RB;          // bytes per V slab
-  constexpr int PB = FP8 ? 16 : 32;    // swizzle piece
-  constexpr int KSTEPS = D / 32;       // MFMA k-steps over the head dim
-  constexpr int KLOADS = RB / 64;      // 16-byte loads per row per lane group
-  constexpr int NT = D / 16;           // 16-wide output tiles
-  constexpr int NV = VB / 1024;        // staging loads per lane
-  constexpr int MERGE = 4 * 16 * D * 4 + 2 * 64 * 4;
-  constexpr int SMEM = (4 * VB > MERGE) ? 4 * VB : MERGE;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
+  constexpr int RB = D * ESZ;        // bytes per K/V row
+  constexpr int HB = 32 * RB;        // bytes per half slab (32 rows)
+  constexpr int PB = FP8 ? 16 : 32;  // swizzle piece
+  constexpr int KSTEPS = D / 32;     // MFMA k-steps over the head dim
+  constexpr int KLOADS = RB / 64;    // 16-byte K loads per row and lane group
+  constexpr int NT = D / 16;         // 16-wide output tiles
+  constexpr int NV = HB / 1024;      // 16-byte V loads per lane and half slab
+  __shared__ __attribute__((aligned(1024))) unsigned char vlds[HB];
 
-  const int split = blockIdx.x;
-  const int g = blockIdx.y / a.head_chunks;
-  const int hc = blockIdx.y % a.head_chunks;
-  const int b = blockIdx.z;
-  const int L = min(max(a.seq_lens[b], 0), a.max_len);
-  const int nblk = (L + 63) >> 6;
-  const int j0 = split * a.bps;
-  if (j0 >= nblk) return;  // the combine pass only reads splits that exist
-  const int j1 = min(nblk, j0 + a.bps);
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wv = tid >> 6;
+  const int w = blockIdx.x;
+  const int lane = threadIdx.x;
   const int col = lane & 15;
   const int G = lane >> 4;
-  const int hl = hc * 16 + col;
-  const bool hvalid = hl < a.ratio;
-  const int h = g * a.ratio + hl;
+  if (w == 0) write_prefix(a);  // for the combine pass
+  const int64_t W = blocks_before(a, a.B) * a.hkhc;
+  const int64_t ub = W * w / a.nworkers;
+  const int64_t ue = W * (w + 1) / a.nworkers;
+  if (ub >= ue) return;
+  const int count = (int)(ue - ub);
 
-  // Query of head `col` as the B operand; k-slot layout matches the K loads.
+  const unsigned char* kpool = (const unsigned char*)a.k;
+  const unsigned char* vpool = (const unsigned char*)a.v;
+
+  i32x4 kreg[2][KLOADS];  // K rows of the half about to be scored (two 16-row tiles)
+  i32x4 vst[NV];          // V rows of the next half, on their way to LDS
   bf16x8 qop[KSTEPS];
-  {
-    const unsigned char* qp =
-        (const unsigned char*)a.q + ((int64_t)b * a.q_sb + (int64_t)(hvalid ? h : 0) * a.q_sh) * 2;
+  float m_run, l_run;
+  f32x4 o[NT];
+  f32x4 s[2];
+
+  auto reset = [&]() {
+    m_run = -INFINITY;
+    l_run = 0.f;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+
+  auto slab_offset = [&](const Unit& u) {
+    const int g = u.ql / a.head_chunks;
+    return (int64_t)u.phys * a.kv_block_bytes + (int64_t)g * a.kv_head_bytes;
+  };
+
+  // Query heads of the piece's chunk as the B operand (k slots match the K loads).
+  auto load_q = [&](const Unit& u) {
+    const int g = u.ql / a.head_chunks;
+    const int hc = u.ql - g * a.head_chunks;
+    const int hl = hc * 16 + col;
+    const bool hvalid = hl < a.ratio;
+    const unsigned char* qp = (const unsigned char*)a.q +
+                              ((int64_t)u.b * a.q_sb + (int64_t)(g * a.ratio + (hvalid ? hl : 0)) * a.q_sh) * 2;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
       const int d0 = FP8 ? (64 * (ks >> 1) + 16 * G + 8 * (ks & 1)) : (32 * ks + 8 * G);
-      i32x4 v = hvalid ? load16(qp + 2 * d0) : i32x4{0, 0, 0, 0};
+      const i32x4 v = hvalid ? load16(qp + 2 * d0) : i32x4{0, 0, 0, 0};
       qop[ks] = __builtin_bit_cast(bf16x8, v);
     }
-  }
+  };
 
-  unsigned char* vbuf = smem + wv * VB;
-  const unsigned char* kpool = (const unsigned char*)a.k;
-  const unsigned char* vpool = (const unsigned char*)a.v;
-  const int32_t* bt = a.block_table + (int64_t)b * a.bt_stride;
-
-  float m_run = -INFINITY;
-  float l_run = 0.f;
-  f32x4 o[NT];
+  // K rows of half h of a unit, straight into the MFMA A-operand layout.
+  auto issue_k = [&](const Unit& u, auto hc_) {
+    constexpr int H = decltype(hc_)::value;
+    const unsigned char* kblk = kpool + slab_offset(u);
 #pragma unroll
-  for (int n = 0; n < NT; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  for (int jb = j0 + wv; jb < j1; jb += 4) {
-    const unsigned char* kblk = kv_slab(kpool, bt, jb, g, a.kv_block_bytes, a.kv_head_bytes);
-    const unsigned char* vblk = kv_slab(vpool, bt, jb, g, a.kv_block_bytes, a.kv_head_bytes);
-    const int valid = min(64, L - jb * 64);
-
-    i32x4 vr[NV];
+    for (int t = 0; t < 2; ++t) {
+      const unsigned char* kp = kblk + token_of<FP8>(2 * H + t, col) * RB + 16 * G;
 #pragma unroll
-    for (int i = 0; i < NV; ++i) vr[i] = load16(vblk + 1024 * i + 16 * lane);
-    i32x4 kr[4][KLOADS];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const unsigned char* kp = kblk + token_of<FP8>(mt, col) * RB + 16 * G;
-#pragma unroll
-      for (int p = 0; p < KLOADS; ++p) kr[mt][p] = load16(kp + 64 * p);
+      for (int p = 0; p < KLOADS; ++p) kreg[t][p] = load16(kp + 64 * p);
     }
+  };
 
+  // V rows of half h of a unit as contiguous 16-byte chunks into the staging registers.
+  auto issue_v = [&](const Unit& u, auto hc_) {
+    constexpr int H = decltype(hc_)::value;
+    const unsigned char* vh = vpool + slab_offset(u) + H * HB;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) vst[i] = load16(vh + 1024 * i + 16 * lane);
+  };
+
+  // Staged V rows -> the swizzled LDS tile (rows 0..31 of the half).
+  auto stage_v = [&]() {
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int byte = 1024 * i + 16 * lane;
-      store16(vbuf + vswz<RB, PB>(byte / RB, byte % RB), vr[i]);
+      store16(vlds + vswz<RB, PB>(byte / RB, byte % RB), vst[i]);
     }
+  };
 
-    // S^T[token, head] = K q^T
-    f32x4 s[4];
+  // S^T[token, head] = K q^T for the 32 rows whose K is in kreg.
+  auto qk = [&]() {
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      s[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < 2; ++t) {
+      s[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
         bf16x8 ka;
-        if (FP8) {
-          const i32x4 w = kr[mt][ks >> 1];
-          ka = fp8x8_to_bf16x8(i32x2{w[2 * (ks & 1)], w[2 * (ks & 1) + 1]});
+        if constexpr (FP8) {
+          const i32x4 wv = kreg[t][ks >> 1];
+          ka = fp8x8_to_bf16x8(i32x2{wv[2 * (ks & 1)], wv[2 * (ks & 1) + 1]});
         } else {
-          ka = __builtin_bit_cast(bf16x8, kr[mt][ks]);
+          ka = __builtin_bit_cast(bf16x8, kreg[t][ks]);
         }
-        s[mt] = mfma16x16x32(ka, qop[ks], s[mt]);
+        s[t] = mfma16x16x32(ka, qop[ks], s[t]);
       }
     }
+  };
 
-    // Online softmax in base 2.  Keys past seq_len are dropped by select, so
-    // whatever the padding rows hold never reaches the sums.
+  // Online softmax (base 2) of one half's scores and O^T += V^T P^T from LDS.
+  auto softmax_pv = [&](const Unit& u, auto hc_) {
+    constexpr int H = decltype(hc_)::value;
+    const int valid = min(64, u.L - 64 * u.j) - 32 * H;  // may be <= 0: then the half is all padding
+    // Keys past seq_len are dropped by select: whatever the padding rows hold
+    // never reaches the sums.
     float bmax = -INFINITY;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float x = token_of<FP8>(mt, 4 * G + j) < valid ? s[mt][j] * a.score_scale_log2 : -INFINITY;
-        s[mt][j] = x;
+        const float x = token_of<FP8>(t, 4 * G + j) < valid ? s[t][j] * a.score_scale_log2 : -INFINITY;
+        s[t][j] = x;
         bmax = fmaxf(bmax, x);
       }
-    bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
-    bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
+    bmax = wave_max4(bmax);
     const float m_new = fmaxf(m_run, bmax);
-    const float alpha = exp2f(m_run - m_new);
+    const float alpha = fast_exp2(m_run - m_new);
     float psum = 0.f;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float p = exp2f(s[mt][j] - m_new);
-        s[mt][j] = p;
+        const float p = fast_exp2(s[t][j] - m_new);
+        s[t][j] = p;
         psum += p;
       }
     l_run = l_run * alpha + psum;
@@ -194,145 +349,193 @@ __global__ __launch_bounds__(256, 2) void decode_split_mfma(DecodeArgs a) {
 #pragma unroll
     for (int n = 0; n < NT; ++n) o[n] *= alpha;
 
-    // P^T as the B operand: k-slot e of lane group G is token_of(2ks + e/4, 4G + e%4).
-    bf16x8 pop[2];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      i32x4 w;
-      w[0] = (int)pack_bf16x2(s[2 * ks][0], s[2 * ks][1]);
-      w[1] = (int)pack_bf16x2(s[2 * ks][2], s[2 * ks][3]);
-      w[2] = (int)pack_bf16x2(s[2 * ks + 1][0], s[2 * ks + 1][1]);
-      w[3] = (int)pack_bf16x2(s[2 * ks + 1][2], s[2 * ks + 1][3]);
-      pop[ks] = __builtin_bit_cast(bf16x8, w);
-    }
+    // P^T as the B operand: k-slot e of lane group G is token_of(e/4, 4G + e%4).
+    i32x4 pw;
+    pw[0] = (int)pack_bf16x2_hw(s[0][0], s[0][1]);
+    pw[1] = (int)pack_bf16x2_hw(s[0][2], s[0][3]);
+    pw[2] = (int)pack_bf16x2_hw(s[1][0], s[1][1]);
+    pw[3] = (int)pack_bf16x2_hw(s[1][2], s[1][3]);
+    const bf16x8 pop = __builtin_bit_cast(bf16x8, pw);
 
-    lds_fence();  // this wave's V tile is in LDS
-
-    // O^T[d, head] += V^T P^T
+    // O^T[d, head] += V^T P^T; V rows past seq_len are zeroed after the read.
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
+      bf16x8 va;
+      if constexpr (FP8) {
+        const int t0 = 8 * G;
+        i32x2 wv = lds_read_tr8(vlds + vswz<RB, PB>(t0 + (col >> 1), 16 * n + 8 * (col & 1)));
+        if (valid < 32) {
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        bf16x8 va;
-        if (FP8) {
-          const int t0 = 32 * ks + 8 * G;
-          i32x2 w = lds_read_tr8(vbuf + vswz<RB, PB>(t0 + (col >> 1), 16 * n + 8 * (col & 1)));
-          if (valid < 64) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-              if (t0 + e >= valid) w[e >> 2] &= ~(0xff << (8 * (e & 3)));
-          }
-          va = fp8x8_to_bf16x8(w);
-        } else {
-          i32x4 w;
-#pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            const int t0 = 32 * ks + 16 * half + 4 * G;
-            const i16x4 r = lds_read_tr16(vbuf + vswz<RB, PB>(t0 + (col >> 2), 32 * n + 8 * (col & 3)));
-            uint32_t lo = (uint16_t)r[0] | ((uint32_t)(uint16_t)r[1] << 16);
-            uint32_t hi = (uint16_t)r[2] | ((uint32_t)(uint16_t)r[3] << 16);
-            if (valid < 64) {
-              if (t0 + 0 >= valid) lo &= 0xffff0000u;
-              if (t0 + 1 >= valid) lo &= 0x0000ffffu;
-              if (t0 + 2 >= valid) hi &= 0xffff0000u;
-              if (t0 + 3 >= valid) hi &= 0x0000ffffu;
-            }
-            w[2 * half] = (int)lo;
-            w[2 * half + 1] = (int)hi;
-          }
-          va = __builtin_bit_cast(bf16x8, w);
+          for (int e = 0; e < 8; ++e)
+            if (t0 + e >= valid) wv[e >> 2] &= ~(0xff << (8 * (e & 3)));
         }
-        o[n] = mfma16x16x32(va, pop[ks], o[n]);
+        va = fp8x8_to_bf16x8(wv);
+      } else {
+        i32x4 wv;
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const int t0 = 16 * hf + 4 * G;
+          const i16x4 r = lds_read_tr16(vlds + vswz<RB, PB>(t0 + (col >> 2), 32 * n + 8 * (col & 3)));
+          uint32_t lo = (uint16_t)r[0] | ((uint32_t)(uint16_t)r[1] << 16);
+          uint32_t hi = (uint16_t)r[2] | ((uint32_t)(uint16_t)r[3] << 16);
+          if (valid < 32) {
+            if (t0 + 0 >= valid) lo &= 0xffff0000u;
+            if (t0 + 1 >= valid) lo &= 0x0000ffffu;
+            if (t0 + 2 >= valid) hi &= 0xffff0000u;
+            if (t0 + 3 >= valid) hi &= 0x0000ffffu;
+          }
+          wv[2 * hf] = (int)lo;
+          wv[2 * hf + 1] = (int)hi;
+        }
+        va = __builtin_bit_cast(bf16x8, wv);
       }
+      o[n] = mfma16x16x32(va, pop, o[n]);
     }
-  }
+  };
 
-  // Merge the four waves of this split.
-  float l_tot = l_run + __shfl_xor(l_run, 16);
-  l_tot += __shfl_xor(l_tot, 32);
-  __syncthreads();  // every wave is done with its V tile
-  float* sO = (float*)smem;             // [4 waves][16 heads][D]
-  float* sM = sO + 4 * 16 * D;          // [4][16]
-  float* sL = sM + 64;                  // [4][16]
+  // Normalised partial of the finished piece -> its workspace slot.
+  auto flush = [&](const Unit& u) {
+    const float l_tot = wave_sum4(l_run);
+    const int g = u.ql / a.head_chunks;
+    const int hc = u.ql - g * a.head_chunks;
+    const int rc = min(16, a.ratio - hc * 16);
+    const int64_t slot = (int64_t)u.b * a.hkhc + u.ql + w;
+    if (col < rc) {
+      const float inv = a.v_scale / l_tot;
+      float* dst = a.ws_o + (slot * 16 + col) * D + 4 * G;
 #pragma unroll
-  for (int n = 0; n < NT; ++n)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) sO[(wv * 16 + col) * D + 16 * n + 4 * G + j] = o[n][j];
-  if (G == 0) {
-    sM[wv * 16 + col] = m_run;
-    sL[wv * 16 + col] = l_tot;
-  }
-  __syncthreads();
-  const int rc = min(16, a.ratio - hc * 16);
-  for (int idx = tid; idx < rc * D; idx += 256) {
-    const int hh = idx / D;
-    const int d = idx % D;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, sM[w * 16 + hh]);
-    float den = 0.f, num = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float wt = exp2f(sM[w * 16 + hh] - M);
-      den += sL[w * 16 + hh] * wt;
-      num += sO[(w * 16 + hh) * D + d] * wt;
+      for (int n = 0; n < NT; ++n) *(f32x4*)(dst + 16 * n) = o[n] * inv;
+      if (G == 0) a.ws_lse[slot * 16 + col] = m_run + log2f(l_tot);
     }
-    const int hq = g * a.ratio + hc * 16 + hh;
-    const int64_t row = ((int64_t)b * a.Hq + hq) * a.nsplit + split;
-    a.ws_o[row * D + d] = num / den * a.v_scale;
-    if (d == 0) a.ws_lse[row] = M + log2f(den);
+  };
+
+  using H0 = std::integral_constant<int, 0>;
+  using H1 = std::integral_constant<int, 1>;
+
+  // Pipeline over 32-row halves (half X = current, X+1, X+2 the next two):
+  // K(X+1) is issued as soon as the scores of X have consumed the K
+  // registers, and V(X+2) as soon as V(X+1) has left the staging registers
+  // for the LDS tile (after X's reads of it), so roughly one half of K and V
+  // is always in flight per wave.  The steady-state loop issues
+  // unconditionally (every path into a wait has the same loads outstanding,
+  // which keeps the compiler's wait counts exact); the last unit is peeled.
+  // A new query operand is loaded right after the scores that last used the
+  // old one, ahead of that step's K issue.
+  Unit cur = unit_at(a, ub);
+  reset();
+  load_q(cur);
+  issue_k(cur, H0{});
+  issue_v(cur, H0{});
+  Unit nx = count > 1 ? unit_next(a, cur) : cur;
+  stage_v();
+  issue_v(cur, H1{});
+  int i = 0;
+  for (; i + 1 < count; ++i) {
+    const bool boundary = !same_piece(cur, nx);
+    // first half of cur
+    qk();
+    issue_k(cur, H1{});
+    softmax_pv(cur, H0{});
+    stage_v();
+    issue_v(nx, H0{});
+    // second half of cur
+    qk();
+    if (boundary) load_q(nx);
+    issue_k(nx, H0{});
+    softmax_pv(cur, H1{});
+    stage_v();
+    issue_v(nx, H1{});
+    if (boundary) {
+      flush(cur);
+      reset();
+    }
+    const Unit nx2 = (i + 2 < count) ? unit_next(a, nx) : nx;
+    cur = nx;
+    nx = nx2;
   }
+  qk();
+  issue_k(cur, H1{});
+  softmax_pv(cur, H0{});
+  stage_v();
+  qk();
+  softmax_pv(cur, H1{});
+  flush(cur);
 }
 
-// fp32 path: one wave per (split, kv head, sequence, head chunk), vector ALU.
-// Lane t scores token t of a block (K staged in LDS); lane d accumulates
-// output columns d, d+64 reading V rows straight from the pool (rows past
-// seq_len are never touched).
+// fp32 path: one wave per worker, vector ALU, no prefetch.  Lane t scores
+// token t of a block (K staged in LDS); lane d accumulates output columns
+// d, d+64 reading V rows straight from the pool (rows past seq_len are never
+// touched).
 template <int D>
-__global__ __launch_bounds__(64) void decode_split_f32(DecodeArgs a) {
+__global__ __launch_bounds__(64) void decode_worker_f32(DecodeArgs a) {
   constexpr int DC = D / 64;
   __shared__ float sK[64][D + 1];
   __shared__ float sQ[16][D];
   __shared__ float sP[16][64];
 
-  const int split = blockIdx.x;
-  const int g = blockIdx.y / a.head_chunks;
-  const int hc = blockIdx.y % a.head_chunks;
-  const int b = blockIdx.z;
-  const int L = min(max(a.seq_lens[b], 0), a.max_len);
-  const int nblk = (L + 63) >> 6;
-  const int j0 = split * a.bps;
-  if (j0 >= nblk) return;
-  const int j1 = min(nblk, j0 + a.bps);
+  const int w = blockIdx.x;
   const int lane = threadIdx.x;
-  const int rc = min(16, a.ratio - hc * 16);
-  const int hbase = g * a.ratio + hc * 16;
-
-  const float* q = (const float*)a.q;
-  for (int i = lane; i < 16 * D; i += 64) {
-    const int hh = i / D, d = i % D;
-    sQ[hh][d] = hh < rc ? q[(int64_t)b * a.q_sb + (int64_t)(hbase + hh) * a.q_sh + d] : 0.f;
-  }
-  float m[16], l[16], o[16][DC];
-#pragma unroll
-  for (int hh = 0; hh < 16; ++hh) {
-    m[hh] = -INFINITY;
-    l[hh] = 0.f;
-#pragma unroll
-    for (int c = 0; c < DC; ++c) o[hh][c] = 0.f;
-  }
+  if (w == 0) write_prefix(a);  // for the combine pass
+  const int64_t W = blocks_before(a, a.B) * a.hkhc;
+  const int64_t ub = W * w / a.nworkers;
+  const int64_t ue = W * (w + 1) / a.nworkers;
+  if (ub >= ue) return;
+  const int count = (int)(ue - ub);
   const unsigned char* kpool = (const unsigned char*)a.k;
   const unsigned char* vpool = (const unsigned char*)a.v;
-  const int32_t* bt = a.block_table + (int64_t)b * a.bt_stride;
+  const float* q = (const float*)a.q;
 
-  for (int jb = j0; jb < j1; ++jb) {
-    const float* kblk = (const float*)kv_slab(kpool, bt, jb, g, a.kv_block_bytes, a.kv_head_bytes);
-    const float* vblk = (const float*)kv_slab(vpool, bt, jb, g, a.kv_block_bytes, a.kv_head_bytes);
-    const int valid = min(64, L - jb * 64);
+  float m[16], l[16], o[16][DC];
+  auto reset = [&]() {
+#pragma unroll
+    for (int hh = 0; hh < 16; ++hh) {
+      m[hh] = -INFINITY;
+      l[hh] = 0.f;
+#pragma unroll
+      for (int c = 0; c < DC; ++c) o[hh][c] = 0.f;
+    }
+  };
+  auto load_q = [&](const Unit& u) {
+    const int g = u.ql / a.head_chunks;
+    const int hc = u.ql - g * a.head_chunks;
+    const int rc = min(16, a.ratio - hc * 16);
+    const int hbase = g * a.ratio + hc * 16;
     __syncthreads();
-    for (int i = lane; i < 64 * D; i += 64) {
-      const int t = i / D, d = i % D;
-      sK[t][d] = t < valid ? kblk[i] : 0.f;
+    for (int i = lane; i < 16 * D; i += 64) {
+      const int hh = i / D, d = i % D;
+      sQ[hh][d] = hh < rc ? q[(int64_t)u.b * a.q_sb + (int64_t)(hbase + hh) * a.q_sh + d] : 0.f;
+    }
+    __syncthreads();
+  };
+  auto flush = [&](const Unit& u) {
+    const int g = u.ql / a.head_chunks;
+    const int hc = u.ql - g * a.head_chunks;
+    const int rc = min(16, a.ratio - hc * 16);
+    const int64_t slot = (int64_t)u.b * a.hkhc + u.ql + w;
+#pragma unroll
+    for (int hh = 0; hh < 16; ++hh) {
+      if (hh >= rc) break;
+#pragma unroll
+      for (int c = 0; c < DC; ++c) a.ws_o[(slot * 16 + hh) * D + lane + 64 * c] = o[hh][c] / l[hh] * a.v_scale;
+      if (lane == 0) a.ws_lse[slot * 16 + hh] = m[hh] * kLog2e + log2f(l[hh]);
+    }
+  };
+
+  Unit u = unit_at(a, ub);
+  reset();
+  load_q(u);
+  for (int i = 0; i < count; ++i) {
+    const int g = u.ql / a.head_chunks;
+    const int hc = u.ql - g * a.head_chunks;
+    const int rc = min(16, a.ratio - hc * 16);
+    const int64_t off = (int64_t)u.phys * a.kv_block_bytes + (int64_t)g * a.kv_head_bytes;
+    const float* kblk = (const float*)(kpool + off);
+    const float* vblk = (const float*)(vpool + off);
+    const int valid = min(64, u.L - 64 * u.j);
+    __syncthreads();
+    for (int i2 = lane; i2 < 64 * D; i2 += 64) {
+      const int t = i2 / D, d = i2 % D;
+      sK[t][d] = t < valid ? kblk[i2] : 0.f;
     }
     __syncthreads();
 #pragma unroll
@@ -343,13 +546,13 @@ __global__ __launch_bounds__(64) void decode_split_f32(DecodeArgs a) {
       const float sc = lane < valid ? acc * a.score_scale : -INFINITY;
       float bmax = sc;
 #pragma unroll
-      for (int off = 32; off > 0; off >>= 1) bmax = fmaxf(bmax, __shfl_xor(bmax, off));
+      for (int off2 = 32; off2 > 0; off2 >>= 1) bmax = fmaxf(bmax, __shfl_xor(bmax, off2));
       const float m_new = fmaxf(m[hh], bmax);
       const float alpha = expf(m[hh] - m_new);
       const float p = lane < valid ? expf(sc - m_new) : 0.f;
       float ps = p;
 #pragma unroll
-      for (int off = 32; off > 0; off >>= 1) ps += __shfl_xor(ps, off);
+      for (int off2 = 32; off2 > 0; off2 >>= 1) ps += __shfl_xor(ps, off2);
       l[hh] = l[hh] * alpha + ps;
       m[hh] = m_new;
       sP[hh][lane] = p;
@@ -366,52 +569,101 @@ __global__ __launch_bounds__(64) void decode_split_f32(DecodeArgs a) {
         for (int c = 0; c < DC; ++c) o[hh][c] = fmaf(p, vblk[t * D + lane + 64 * c], o[hh][c]);
       }
     }
-  }
-#pragma unroll
-  for (int hh = 0; hh < 16; ++hh) {
-    if (hh >= rc) break;
-    const int64_t row = ((int64_t)b * a.Hq + hbase + hh) * a.nsplit + split;
-#pragma unroll
-    for (int c = 0; c < DC; ++c) a.ws_o[row * D + lane + 64 * c] = o[hh][c] / l[hh] * a.v_scale;
-    if (lane == 0) a.ws_lse[row] = m[hh] * kLog2e + log2f(l[hh]);
+    if (i + 1 == count) {
+      flush(u);
+      break;
+    }
+    const Unit nx = unit_next(a, u);
+    if (!same_piece(u, nx)) {
+      flush(u);
+      reset();
+      load_q(nx);
+    }
+    u = nx;
   }
 }
 
-// Merge the splits of one (sequence, query head): weights 2^(lse_s - max).
+// Merge the pieces of one (sequence, query head): weights 2^(lse - max).
+// One wave; lane k holds the LSE of piece k (64 pieces per round), and the
+// output rows of all pieces are requested before any arithmetic, so the
+// merge costs one memory round trip for the usual handful of pieces.
 template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(64) void decode_combine(DecodeArgs a) {
   constexpr int DC = D / 64;
   const int bh = blockIdx.x;
   const int b = bh / a.Hq;
-  const int h = bh % a.Hq;
+  const int h = bh - b * a.Hq;
   const int lane = threadIdx.x;
-  const int L = min(max(a.seq_lens[b], 0), a.max_len);
-  const int nblk = (L + 63) >> 6;
-  const int ns = (nblk + a.bps - 1) / a.bps;
-  const float* lse2 = a.ws_lse + (int64_t)bh * a.nsplit;
-  const float* op = a.ws_o + (int64_t)bh * a.nsplit * D;
-  float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, lse2[s]);
-  float den = 0.f;
+  const int g = h / a.ratio;
+  const int hh = h - g * a.ratio;
+  const int hc = hh >> 4;
+  const int col = hh & 15;
+  const int ql = g * a.head_chunks + hc;
+  const int64_t qg = (int64_t)b * a.hkhc + ql;
+  const int pb = ld_const(a.prefix, b);
+  const int nblk = ld_const(a.prefix, b + 1) - pb;
   float acc[DC];
 #pragma unroll
   for (int c = 0; c < DC; ++c) acc[c] = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const float w = exp2f(lse2[s] - M);
-    den += w;
+  float M = -INFINITY, den = 0.f;
+  if (nblk > 0) {
+    const int64_t W = (int64_t)ld_const(a.prefix, a.B) * a.hkhc;
+    const int64_t u0 = (int64_t)pb * a.hkhc + (int64_t)ql * nblk;
+    const int64_t u1 = u0 + nblk;
+    const int64_t P = a.nworkers;
+    const int w0 = (int)(((u0 + 1) * P - 1) / W);  // worker holding unit u0
+    const int w1 = (int)((u1 * P - 1) / W);        // worker holding unit u1 - 1
+    // With fewer units than workers some workers own no unit; they wrote nothing.
+    auto owns_units = [&](int wk) { return W * wk / P < W * (wk + 1) / P; };
+    for (int r0 = w0; r0 <= w1; r0 += 64) {
+      const int wk = r0 + lane;
+      const bool live = wk <= w1 && owns_units(wk);
+      const float lse_k = live ? a.ws_lse[(qg + wk) * 16 + col] : -INFINITY;
+      float m_round = lse_k;
 #pragma unroll
-    for (int c = 0; c < DC; ++c) acc[c] = fmaf(w, op[(int64_t)s * D + lane + 64 * c], acc[c]);
+      for (int off = 32; off > 0; off >>= 1) m_round = fmaxf(m_round, __shfl_xor(m_round, off));
+      const float M_new = fmaxf(M, m_round);
+      const float scale_old = M == -INFINITY ? 0.f : exp2f(M - M_new);
+#pragma unroll
+      for (int c = 0; c < DC; ++c) acc[c] *= scale_old;
+      den *= scale_old;
+      const float wt_k = live ? exp2f(lse_k - M_new) : 0.f;
+      float wsum = wt_k;
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) wsum += __shfl_xor(wsum, off);
+      den += wsum;
+      const int n = min(64, w1 - r0 + 1);
+      // Four pieces per trip, all loads first.  Slots of empty workers are
+      // read (they are inside the workspace) but dropped by select, so stale
+      // contents never reach the sum.
+      for (int k0 = 0; k0 < n; k0 += 4) {
+        float v4[4][DC], w4[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const int k = min(k0 + kk, n - 1);
+          w4[kk] = k0 + kk < n ? __shfl(wt_k, k) : 0.f;
+          const float* op = a.ws_o + ((qg + r0 + k) * 16 + col) * D;
+#pragma unroll
+          for (int c = 0; c < DC; ++c) v4[kk][c] = op[lane + 64 * c];
+        }
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+          for (int c = 0; c < DC; ++c) acc[c] += w4[kk] > 0.f ? w4[kk] * v4[kk][c] : 0.f;
+      }
+      M = M_new;
+    }
   }
   const int64_t obase = (int64_t)b * a.o_sb + (int64_t)h * a.o_sh;
 #pragma unroll
   for (int c = 0; c < DC; ++c) {
-    const float v = ns > 0 ? acc[c] / den : 0.f;
+    const float v = nblk > 0 ? acc[c] / den : 0.f;
     if (OUT_BF16)
       ((uint16_t*)a.out)[obase + lane + 64 * c] = f32_to_bf16(v);
     else
       ((float*)a.out)[obase + lane + 64 * c] = v;
   }
-  if (a.lse && lane == 0) a.lse[bh] = ns > 0 ? (M + log2f(den)) * kLn2 : -INFINITY;
+  if (a.lse && lane == 0) a.lse[bh] = nblk > 0 ? (M + log2f(den)) * kLn2 : -INFINITY;
 }
 
 // Copy logical rows of one (sequence, KV head) out of the pool with the same
@@ -461,15 +713,17 @@ extern "C" gqap_status gqap_paged_decode(const gqap_decode_plan_t* plan, const v
     return fail(GQAP_ERR_INVALID_ARGUMENT, "k_scale/v_scale apply to fp8 KV only and must be 1.0 otherwise");
 
   const int kv_esz = dtype_size(d.kv_dtype);
+  const DecodeWorkspace lay = decode_workspace(d.batch, plan->max_pieces, d.head_dim);
+  char* ws = (char*)workspace;
   DecodeArgs a{};
   a.q = q;
   a.k = k_pool;
   a.v = v_pool;
   a.block_table = block_table;
   a.seq_lens = seq_lens;
-  const int64_t rows = (int64_t)d.batch * d.num_q_heads * plan->num_splits;
-  a.ws_o = (float*)workspace;
-  a.ws_lse = (float*)((char*)workspace + ((rows * d.head_dim * 4 + 255) & ~int64_t(255)));
+  a.prefix = (int32_t*)(ws + lay.prefix);
+  a.ws_lse = (float*)(ws + lay.lse);
+  a.ws_o = (float*)(ws + lay.o);
   a.out = out;
   a.lse = lse;
   a.q_sb = d.q_stride_batch;
@@ -484,40 +738,40 @@ extern "C" gqap_status gqap_paged_decode(const gqap_decode_plan_t* plan, const v
   a.Hk = d.num_kv_heads;
   a.ratio = plan->ratio;
   a.head_chunks = plan->head_chunks;
-  a.nsplit = plan->num_splits;
-  a.bps = plan->blocks_per_split;
+  a.hkhc = d.num_kv_heads * plan->head_chunks;
+  a.nworkers = plan->num_workers;
   a.max_len = d.max_seq_len;
   a.score_scale = scale * k_scale;
   a.score_scale_log2 = scale * k_scale * dev::kLog2e;
   a.v_scale = v_scale;
 
   hipStream_t st = (hipStream_t)stream;
-  const dim3 grid(plan->num_splits, d.num_kv_heads * plan->head_chunks, d.batch);
+  const dim3 grid(plan->num_workers);
   const bool d128 = d.head_dim == 128;
   switch (plan->kernel) {
     case kDecodeF32Valu:
       if (d128)
-        hipLaunchKernelGGL(decode_split_f32<128>, grid, dim3(64), 0, st, a);
+        hipLaunchKernelGGL(decode_worker_f32<128>, grid, dim3(64), 0, st, a);
       else
-        hipLaunchKernelGGL(decode_split_f32<64>, grid, dim3(64), 0, st, a);
+        hipLaunchKernelGGL(decode_worker_f32<64>, grid, dim3(64), 0, st, a);
       break;
     case kDecodeBf16Mfma:
       if (d128)
-        hipLaunchKernelGGL((decode_split_mfma<128, false>), grid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL((decode_worker_mfma<128, false>), grid, dim3(64), 0, st, a);
       else
-        hipLaunchKernelGGL((decode_split_mfma<64, false>), grid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL((decode_worker_mfma<64, false>), grid, dim3(64), 0, st, a);
       break;
     case kDecodeFp8Mfma:
       if (d128)
-        hipLaunchKernelGGL((decode_split_mfma<128, true>), grid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL((decode_worker_mfma<128, true>), grid, dim3(64), 0, st, a);
       else
-        hipLaunchKernelGGL((decode_split_mfma<64, true>), grid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL((decode_worker_mfma<64, true>), grid, dim3(64), 0, st, a);
       break;
     default:
       return fail(GQAP_ERR_INVALID_ARGUMENT, "unknown kernel variant %u", plan->kernel);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(GQAP_ERR_HIP, "decode split launch: %s", hipGetErrorString(e));
+  if (e != hipSuccess) return fail(GQAP_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
   const dim3 cgrid(d.batch * d.num_q_heads);
   const bool bf16_out = d.q_dtype == GQAP_BF16;
   if (d128) {
@@ -548,7 +802,8 @@ extern "C" gqap_status gqap_debug_gather_kv(const gqap_decode_plan_t* plan, cons
     return fail(GQAP_ERR_INVALID_ARGUMENT, "num_rows=%d outside [0, Nblk*64]", num_rows);
   if (num_rows == 0) return GQAP_OK;
   if (!pool || !block_table || !seq_lens || !dst) return fail(GQAP_ERR_INVALID_ARGUMENT, "null device pointer");
-  if (misaligned(pool, 16) || misaligned(dst, 16)) return fail(GQAP_ERR_INVALID_ARGUMENT, "pool/dst must be 16-byte aligned");
+  if (misaligned(pool, 16) || misaligned(dst, 16))
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "pool/dst must be 16-byte aligned");
   const int esz = dtype_size(d.kv_dtype);
   const int row_bytes = d.head_dim * esz;
   const int64_t threads = (int64_t)num_rows * (row_bytes / 16);

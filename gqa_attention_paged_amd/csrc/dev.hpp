@@ -60,6 +60,35 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(i32x2 w) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
+// Two floats -> packed bf16 pair with the hardware round-to-nearest-even convert.
+__device__ __forceinline__ uint32_t pack_bf16x2_hw(float lo, float hi) {
+  typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+  const bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// 2^x with the hardware transcendental (exp2(-inf) = 0).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Max / sum over the four lanes l, l^16, l^32, l^48 (the four 16-lane groups),
+// with the gfx950 lane-swap instructions instead of LDS-routed shuffles.
+__device__ __forceinline__ float wave_max4(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
+                                                  false, false);
+  x = fmaxf(__builtin_bit_cast(float, (uint32_t)a[0]), __builtin_bit_cast(float, (uint32_t)a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
+                                                  false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)b[0]), __builtin_bit_cast(float, (uint32_t)b[1]));
+}
+__device__ __forceinline__ float wave_sum4(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
+                                                  false, false);
+  x = __builtin_bit_cast(float, (uint32_t)a[0]) + __builtin_bit_cast(float, (uint32_t)a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
+                                                  false, false);
+  return __builtin_bit_cast(float, (uint32_t)b[0]) + __builtin_bit_cast(float, (uint32_t)b[1]);
+}
+
 __device__ __forceinline__ i32x4 load16(const void* p) { return *(const i32x4*)p; }
 __device__ __forceinline__ void store16(void* p, i32x4 v) { *(i32x4*)p = v; }
 

@@ -8,6 +8,7 @@
 // that execution never reads lengths on the host; the split count here is
 // likewise a function of the descriptor only.
 #include <algorithm>
+#include <climits>
 #include <cstring>
 #include <string>
 
@@ -87,7 +88,8 @@ static gqap_status check_decode_desc(const gqap_decode_desc_t& d, int* q_esz, in
   if (d.block_table_stride < d.max_blocks_per_seq)
     return fail(GQAP_ERR_INVALID_ARGUMENT, "block_table_stride %lld < Nblk %d", (long long)d.block_table_stride,
                 d.max_blocks_per_seq);
-  if (d.num_splits < 0) return fail(GQAP_ERR_INVALID_ARGUMENT, "num_splits must be >= 0");
+  if (d.num_workers < 0 || d.num_workers > (1 << 20))
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "num_workers must be in [0, 2^20]");
   if (d.num_cus < 0) return fail(GQAP_ERR_INVALID_ARGUMENT, "num_cus must be >= 0");
   return GQAP_OK;
 }
@@ -109,28 +111,12 @@ extern "C" gqap_status gqap_decode_plan(const gqap_decode_desc_t* desc, gqap_dec
   plan->kernel = d.kv_dtype == GQAP_F32 ? kDecodeF32Valu
                  : d.kv_dtype == GQAP_BF16 ? kDecodeBf16Mfma
                                             : kDecodeFp8Mfma;
-  const int64_t nblk_cap = std::max<int64_t>(1, ceil_div(d.max_seq_len, kBlock));
   const int cus = d.num_cus ? d.num_cus : kDefaultCUs;
-  int64_t splits;
-  if (d.num_splits > 0) {
-    splits = std::min<int64_t>(d.num_splits, nblk_cap);
-  } else {
-    // Enough work items for several resident workgroups per CU, but keep each
-    // wave of a split on at least two blocks so per-split overhead stays small.
-    const int64_t pairs = std::max<int64_t>(1, (int64_t)d.batch * d.num_kv_heads * plan->head_chunks);
-    const int64_t waves_per_wg = plan->kernel == kDecodeF32Valu ? 1 : kMfmaWaves;
-    const int64_t min_bps = 2 * waves_per_wg;
-    splits = std::max<int64_t>(1, ceil_div(8LL * cus, pairs));
-    int64_t bps = std::max<int64_t>(ceil_div(nblk_cap, splits), std::min<int64_t>(min_bps, nblk_cap));
-    splits = ceil_div(nblk_cap, bps);
-  }
-  plan->blocks_per_split = (int32_t)ceil_div(nblk_cap, splits);
-  plan->num_splits = (int32_t)ceil_div(nblk_cap, plan->blocks_per_split);
-  const int64_t rows = (int64_t)d.batch * d.num_q_heads * plan->num_splits;
-  uint64_t ws = (uint64_t)rows * d.head_dim * sizeof(float);
-  ws = (ws + 255) & ~uint64_t(255);
-  ws += (uint64_t)rows * sizeof(float);
-  plan->workspace_bytes = (ws + 255) & ~uint64_t(255);
+  plan->num_workers = d.num_workers > 0 ? d.num_workers : cus * decode_waves_per_cu(plan->kernel, d.head_dim);
+  const int64_t pieces = (int64_t)d.batch * d.num_kv_heads * plan->head_chunks + plan->num_workers;
+  if (pieces > INT32_MAX / 16) return fail(GQAP_ERR_INVALID_ARGUMENT, "too many partial slots");
+  plan->max_pieces = (int32_t)pieces;
+  plan->workspace_bytes = decode_workspace(d.batch, pieces, d.head_dim).total;
   plan->magic = GQAP_PLAN_MAGIC;
   return GQAP_OK;
 }

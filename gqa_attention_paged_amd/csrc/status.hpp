@@ -34,7 +34,33 @@ enum DecodeKernel : uint32_t {
   kDecodeFp8Mfma = 3,   // bf16 q / fp8 e4m3fn KV, dequantised to bf16 for the matrix cores
 };
 
-// Workgroup shape of each decode variant (used by the planner and the launcher).
-constexpr int kMfmaWaves = 4;
+// Byte offsets of the decode workspace regions (shared by planner and launcher).
+//   prefix [B + 1] int32          key blocks before each sequence
+//   lse    [pieces][16] float32   base-2 log-sum-exp of each partial
+//   o      [pieces][16][D] float32 normalised partial outputs
+struct DecodeWorkspace {
+  uint64_t prefix, lse, o, total;
+};
+
+inline uint64_t round256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
+
+inline DecodeWorkspace decode_workspace(int64_t B, int64_t pieces, int64_t D) {
+  DecodeWorkspace w;
+  w.prefix = 0;
+  w.lse = round256((uint64_t)(B + 1) * 4);
+  w.o = w.lse + round256((uint64_t)pieces * 16 * 4);
+  w.total = w.o + round256((uint64_t)pieces * 16 * D * 4);
+  return w;
+}
+
+// Resident worker waves per compute unit for each decode variant (LDS and
+// register budgets of the kernels in decode.hip).
+inline int decode_waves_per_cu(uint32_t kernel, int head_dim) {
+  switch (kernel) {
+    case kDecodeF32Valu: return 2;
+    case kDecodeBf16Mfma: return head_dim == 128 ? 4 : 8;  // 1 or 2 waves per SIMD
+    default: return head_dim == 128 ? 4 : 8;              // fp8 KV
+  }
+}
 
 }  // namespace gqap

@@ -110,17 +110,27 @@ typedef struct gqap_decode_desc_t {
   int64_t kv_stride_block;     /* elements between pool blocks */
   int64_t kv_stride_head;      /* elements between heads of one block, >= 64*D */
   int64_t block_table_stride;  /* int32 elements between block_table rows, >= Nblk */
-  int32_t num_splits;          /* 0 = choose automatically; else the split count */
+  int32_t num_workers;         /* 0 = choose automatically; else the worker count */
   int32_t num_cus;             /* compute units to plan for; 0 = 256 (MI355X) */
 } gqap_decode_desc_t;
 
-/* Plain-old-data plan, filled by gqap_decode_plan and read by the other calls. */
+/*
+ * Plain-old-data plan, filled by gqap_decode_plan and read by the other calls.
+ *
+ * Schedule: the key blocks of all (sequence, KV head) pairs form one list of
+ * work units; a device pre-pass reads seq_lens and cuts that list into
+ * num_workers contiguous, equal-length ranges, one per persistent wave.  A
+ * worker's range covers pieces of one or more key axes; each piece leaves a
+ * normalised partial output and its log-sum-exp, and a combine pass merges
+ * the pieces of every (sequence, query head).  The piece count of a sequence
+ * plays the role of the split count (num_splits) of split-KV decoding.
+ */
 typedef struct gqap_decode_plan_t {
   gqap_decode_desc_t desc;
-  int32_t num_splits;          /* splits of the key axis per sequence */
-  int32_t blocks_per_split;    /* 64-row blocks handled by one split */
+  int32_t num_workers;         /* persistent waves sharing the key blocks evenly */
   int32_t ratio;               /* Hq / Hk */
   int32_t head_chunks;         /* ceil(ratio / 16) */
+  int32_t max_pieces;          /* partial-result slots: B*Hk*head_chunks + num_workers */
   uint64_t workspace_bytes;    /* device workspace the decode needs */
   uint32_t magic;              /* GQAP_PLAN_MAGIC when valid */
   uint32_t kernel;             /* internal kernel variant */
@@ -133,7 +143,7 @@ typedef struct gqap_decode_plan_t {
  * descriptor's capacities, never on live lengths, so one plan serves every
  * call with the same shapes.
  * Errors: INVALID_ARGUMENT (non-positive sizes, Hq % Hk != 0, max_seq_len >
- * Nblk*64, strides that overlap or break 16-byte alignment, bad num_splits),
+ * Nblk*64, strides that overlap or break 16-byte alignment, bad num_workers),
  * DTYPE (dtype pair not in the list above), UNSUPPORTED (block_size != 64,
  * head_dim not 64/128, F16).
  */

@@ -36,7 +36,7 @@ def tensor_to_f64(t: torch.Tensor) -> np.ndarray:
 class DeviceDecode:
     """A decode case resident on the device plus a plan for it."""
 
-    def __init__(self, case, num_splits: int = 0, device: str = "cuda"):
+    def __init__(self, case, num_workers: int = 0, device: str = "cuda"):
         self.case = case
         self.q = bits_to_tensor(case.q, case.q_dtype).to(device)
         self.k = bits_to_tensor(case.k_pool, case.kv_dtype).to(device)
@@ -47,7 +47,7 @@ class DeviceDecode:
         self.lse = torch.empty((case.B, case.Hq), dtype=torch.float32, device=device)
         max_len = max(1, int(case.seq_lens.max())) if case.B else 1
         self.desc = gq.decode_desc(self.q, self.k, self.bt, max_seq_len=max_len, out=self.out,
-                                   num_splits=num_splits)
+                                   num_workers=num_workers)
         self.plan = gq.gqap_decode_plan(self.desc)
         self.ws = torch.empty(max(256, self.plan.workspace_bytes), dtype=torch.uint8, device=device)
 

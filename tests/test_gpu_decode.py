@@ -28,10 +28,10 @@ def _oracle(case, batches=None):
                           v_scale=case.v_scale, batches=batches)
 
 
-def _check(gu, case, num_splits=0, batches=None, tol=None):
+def _check(gu, case, num_workers=0, batches=None, tol=None):
     gu.announce(f"decode {case.name} B={case.B} Hq={case.Hq} Hk={case.Hk} D={case.D} kv={case.kv_dtype} "
-                f"splits={num_splits} seed={case.meta.get('seed')}")
-    dd = gu.DeviceDecode(case, num_splits=num_splits)
+                f"workers={num_workers} seed={case.meta.get('seed')}")
+    dd = gu.DeviceDecode(case, num_workers=num_workers)
     dd.run()
     out, lse = dd.results()
     ref_out, ref_lse = _oracle(case, batches)
@@ -40,8 +40,7 @@ def _check(gu, case, num_splits=0, batches=None, tol=None):
     tol = TOL[case.kv_dtype] if tol is None else tol
     e_out = gu.max_abs_err(out, ref_out)
     e_lse = gu.lse_err(lse, ref_lse)
-    gu.announce(f"  max-abs-err out {e_out:.3e} lse {e_lse:.3e} (tol {tol:g}) plan splits={dd.plan.num_splits} "
-                f"bps={dd.plan.blocks_per_split}")
+    gu.announce(f"  max-abs-err out {e_out:.3e} lse {e_lse:.3e} (tol {tol:g}) workers={dd.plan.num_workers}")
     assert e_out <= tol and e_lse <= tol, (e_out, e_lse)
     return dd, out, lse
 
@@ -77,12 +76,12 @@ def test_decode_head_ratios(gu, Hq, Hk):
     _check(gu, case)
 
 
-def test_decode_split_count_invariance_fp32(gu):
+def test_decode_worker_count_invariance_fp32(gu):
     case = gen.make_decode_case(name="splits_f32", seed=61, B=4, Hq=8, Hk=2, D=128, q_dtype="f32",
                                 kv_dtype="f32", seq_lens=[64 * 9 + 5, 1, 300, 64 * 12])
     outs = []
-    for ns in (1, 2, 5, 12, 0):
-        _, out, lse = _check(gu, case, num_splits=ns)
+    for nw in (1, 2, 5, 12, 77, 0):
+        _, out, lse = _check(gu, case, num_workers=nw)
         outs.append((out, lse))
     for out, lse in outs[1:]:
         assert np.abs(out - outs[0][0]).max() <= 1e-6
@@ -90,11 +89,11 @@ def test_decode_split_count_invariance_fp32(gu):
 
 
 @pytest.mark.parametrize("kv", ["bf16", "e4m3fn"])
-def test_decode_split_count_invariance_mfma(gu, kv):
+def test_decode_worker_count_invariance_mfma(gu, kv):
     case = gen.make_decode_case(name=f"splits_{kv}", seed=62, B=4, Hq=16, Hk=2, D=128, q_dtype="bf16",
                                 kv_dtype=kv, seq_lens=[64 * 20 + 5, 3, 900, 64 * 32])
-    for ns in (1, 3, 8, 32, 0):
-        _check(gu, case, num_splits=ns)
+    for nw in (1, 3, 8, 32, 131, 1000, 0):
+        _check(gu, case, num_workers=nw)
 
 
 @pytest.mark.parametrize("kv", ["f32", "bf16", "e4m3fn"])
