@@ -189,7 +189,7 @@ extern "C" gqap_status gqap_prefill_plan(const gqap_prefill_desc_t* desc, gqap_p
   if (d.num_cus < 0) return fail(GQAP_ERR_INVALID_ARGUMENT, "num_cus must be >= 0");
   plan->desc = d;
   plan->ratio = d.num_q_heads / d.num_kv_heads;
-  plan->q_tile_rows = 64;
+  plan->q_tile_rows = 128;
   plan->q_tiles = (int32_t)ceil_div(d.max_seq_len, plan->q_tile_rows);
   plan->kernel = mla ? 2 : 1;
   plan->workspace_bytes = 0;

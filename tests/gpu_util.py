@@ -79,3 +79,33 @@ def lse_err(gpu: np.ndarray, ref: np.ndarray) -> float:
         return float("inf")
     fin = np.isfinite(ref)
     return float(np.abs(gpu[fin] - ref[fin]).max()) if fin.any() else 0.0
+
+
+class DevicePrefill:
+    """A ragged prefill case resident on the device plus a plan for it."""
+
+    def __init__(self, case, device: str = "cuda"):
+        self.case = case
+        self.q = bits_to_tensor(case.q, "bf16").to(device)
+        self.k = bits_to_tensor(case.k, "bf16").to(device)
+        self.v = bits_to_tensor(case.v, "bf16").to(device)
+        self.kr = bits_to_tensor(case.k_rope, "bf16").to(device) if case.k_rope is not None else None
+        self.cu = torch.from_numpy(np.ascontiguousarray(case.cu_seqlens, dtype=np.int32)).to(device)
+        self.mask = (torch.from_numpy(np.ascontiguousarray(case.block_mask, dtype=np.uint8)).to(device)
+                     if case.block_mask is not None else None)
+        T = case.T
+        self.out = torch.empty((T, case.Hq, case.D_v), dtype=torch.bfloat16, device=device)
+        self.lse = torch.empty((T, case.Hq), dtype=torch.float32, device=device)
+        max_len = max(1, int(case.seq_lens.max())) if case.B else 1
+        self.desc = gq.prefill_desc(self.q, self.k, self.v, self.kr, batch=case.B, max_seq_len=max_len,
+                                    block_mask=self.mask, out=self.out)
+        self.plan = gq.gqap_prefill_plan(self.desc)
+
+    def run(self, stream=None):
+        gq.gqap_prefill(self.plan, self.q, self.k, self.v, self.kr, self.cu, self.mask, self.case.scale, self.out,
+                        self.lse, stream=stream)
+        return self.out, self.lse
+
+    def results(self):
+        torch.cuda.synchronize()
+        return tensor_to_f64(self.out), self.lse.detach().cpu().numpy().astype(np.float64)

@@ -1,0 +1,137 @@
+"""Ragged causal prefill on the GPU through the C ABI, against the fp64 oracle.
+
+bf16 inputs: max-abs-err of out and lse against the oracle run on the same
+rounded inputs must stay within 2e-2."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as O
+from workloads import gen
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+
+
+@pytest.fixture(scope="module")
+def gu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    from tests import gpu_util  # imports the HIP library; fails loudly if it is missing
+    return gpu_util
+
+
+def _rows_sample(case, n_mid=64, seed=0):
+    """First and last rows of each sequence, rows around 64/128 boundaries, random rows."""
+    rng = np.random.default_rng(seed)
+    rows = set()
+    for b in range(case.B):
+        c0, c1 = int(case.cu_seqlens[b]), int(case.cu_seqlens[b + 1])
+        if c1 == c0:
+            continue
+        for r in (0, 1, 31, 32, 63, 64, 65, 127, 128, 129):
+            if c0 + r < c1:
+                rows.add(c0 + r)
+        rows.update({c1 - 1, c1 - 2, c1 - 64} & set(range(c0, c1)))
+        rows.update(rng.integers(c0, c1, size=min(n_mid, c1 - c0)).tolist())
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+def _check(gu, case, rows=None, tol=TOL):
+    gu.announce(f"prefill {case.name} lens={list(case.seq_lens)[:8]} Hq={case.Hq} Hk={case.Hk} "
+                f"Dqk={case.D_qk} Dr={case.D_rope} mask={case.block_mask is not None} seed={case.meta.get('seed')}")
+    dp = gu.DevicePrefill(case)
+    dp.run()
+    out, lse = dp.results()
+    ref, ref_lse = O.ragged_prefill(case.q, case.k, case.v, case.cu_seqlens, case.scale, k_rope=case.k_rope,
+                                    block_mask=case.block_mask, dtype="bf16", rows=rows)
+    if rows is not None:
+        out, lse = out[rows], lse[rows]
+    e_out = gu.max_abs_err(out, ref)
+    e_lse = gu.lse_err(lse, ref_lse)
+    gu.announce(f"  max-abs-err out {e_out:.3e} lse {e_lse:.3e} (tol {tol:g}) rows={'all' if rows is None else len(rows)}")
+    assert e_out <= tol and e_lse <= tol, (e_out, e_lse)
+    return dp, out, lse
+
+
+def test_prefill_mla_config_full_size_sampled(gu):
+    case = gen.prefill_mla_bf16()
+    _check(gu, case, rows=_rows_sample(case))
+
+
+def test_prefill_blocksparse_config_full_size_sampled(gu):
+    case = gen.prefill_blocksparse_bf16()
+    _check(gu, case, rows=_rows_sample(case, n_mid=48))
+
+
+@pytest.mark.parametrize("rope", [0, 64])
+def test_prefill_ragged_small(gu, rope):
+    case = gen.make_prefill_case(name=f"ragged_r{rope}", seed=200 + rope, seq_lens=[1, 63, 64, 65, 130, 300, 7],
+                                 Hq=8, Hk=8 if rope else 2, D_qk=128 + rope, D_rope=rope, D_v=128)
+    _check(gu, case)
+
+
+def test_prefill_gqa_ratios(gu):
+    for Hq, Hk in ((8, 1), (16, 4), (4, 4)):
+        case = gen.make_prefill_case(name=f"gqa_{Hq}_{Hk}", seed=210 + Hq, seq_lens=[200, 129], Hq=Hq, Hk=Hk,
+                                     D_qk=128, D_rope=0, D_v=128)
+        _check(gu, case)
+
+
+def test_prefill_block_mask_small_with_hidden_diagonal(gu):
+    case = gen.make_prefill_case(name="mask_small", seed=220, seq_lens=[300, 200], Hq=8, Hk=2, D_qk=128,
+                                 D_rope=0, D_v=128, mask_density=0.4)
+    m = case.block_mask.copy()
+    m[0, 2, :] = 0            # query block 2 of sequence 0 sees nothing: its rows are 0 with lse -inf
+    m[1, 1, 1] = 0            # diagonal off, first column still on
+    case = gen.PrefillCase(**{**case.__dict__, "block_mask": m})
+    dp, out, lse = _check(gu, case)
+    assert np.all(out[128:192] == 0) and np.all(np.isneginf(lse[128:192]))
+
+
+def test_prefill_all_on_mask_equals_dense(gu):
+    case = gen.make_prefill_case(name="dense", seed=230, seq_lens=[257, 190], Hq=8, Hk=2, D_qk=192, D_rope=64,
+                                 D_v=128)
+    gu.announce("prefill all-on mask vs dense")
+    a = gu.DevicePrefill(case)
+    a.run()
+    out1, lse1 = a.results()
+    nb = (int(case.seq_lens.max()) + 63) // 64
+    ones = np.tril(np.ones((case.B, nb, nb), np.uint8))
+    case2 = gen.PrefillCase(**{**case.__dict__, "block_mask": ones})
+    b = gu.DevicePrefill(case2)
+    b.run()
+    out2, lse2 = b.results()
+    assert np.array_equal(out1, out2) and np.array_equal(lse1, lse2)
+
+
+def test_prefill_first_row_is_its_value_row(gu):
+    case = gen.make_prefill_case(name="first_row", seed=240, seq_lens=[5, 1, 70], Hq=4, Hk=4, D_qk=192,
+                                 D_rope=64, D_v=128)
+    gu.announce("prefill first rows")
+    dp = gu.DevicePrefill(case)
+    dp.run()
+    out, _ = dp.results()
+    for b in range(case.B):
+        c0 = int(case.cu_seqlens[b])
+        for h in range(case.Hq):
+            assert np.array_equal(out[c0, h], O.widen(case.v[c0, h], "bf16")), (b, h)
+
+
+def test_prefill_packed_equals_separate(gu):
+    case = gen.make_prefill_case(name="packed", seed=250, seq_lens=[100, 333, 64], Hq=8, Hk=2, D_qk=128,
+                                 D_rope=0, D_v=128)
+    gu.announce("prefill packed vs separate")
+    dp = gu.DevicePrefill(case)
+    dp.run()
+    out, _ = dp.results()
+    for b in range(case.B):
+        c0, c1 = int(case.cu_seqlens[b]), int(case.cu_seqlens[b + 1])
+        sub = gen.PrefillCase(**{**case.__dict__, "seq_lens": case.seq_lens[b:b + 1],
+                                 "cu_seqlens": np.array([0, c1 - c0], np.int32), "q": case.q[c0:c1],
+                                 "k": case.k[c0:c1], "v": case.v[c0:c1]})
+        sp = gu.DevicePrefill(sub)
+        sp.run()
+        o1, _ = sp.results()
+        assert np.array_equal(o1, out[c0:c1]), b
