@@ -162,6 +162,8 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-primary", action="store_true", help="measure only the primary decode workload")
+    ap.add_argument("--only", default=None,
+                    help="measure one workload by name (for profiling) and print its record instead")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (this library has no "
@@ -176,6 +178,13 @@ def main(argv=None) -> int:
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     props = torch.cuda.get_device_properties(0)
+
+    if args.only:
+        mk = gen.CONFIGS[args.only]
+        c = mk()
+        fn = bench_prefill if isinstance(c, gen.PrefillCase) else bench_decode
+        print(json.dumps(fn(c, args.steps, args.warmup, torch, gq, gu)), flush=True)
+        return 0
 
     case = gen.decode_gqa_bf16()
     prim = bench_decode(case, args.steps, args.warmup, torch, gq, gu)

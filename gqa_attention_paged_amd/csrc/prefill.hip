@@ -27,6 +27,7 @@
 #include "status.hpp"
 
 #include <cmath>
+#include <type_traits>
 
 namespace gqap {
 
@@ -75,22 +76,26 @@ using namespace dev;
 
 template <int DR>
 __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
-  constexpr int DN = 128;                 // per-head key width
-  constexpr int DV = 128;                 // value / output width
-  constexpr int KSN = DN / 16;            // k-steps over the nope part
-  constexpr int KSR = DR / 16;            // k-steps over the rope part
-  constexpr int KB = 64 * DN * 2;         // K tile bytes
-  constexpr int RB = 64 * (DR ? DR : 8) * 2;  // rope tile bytes (unused when DR == 0)
-  constexpr int VB = 64 * DV * 2;         // V tile bytes
-  constexpr int STAGE = KB + (DR ? RB : 0) + VB;
-  constexpr int KLD = KB / 16 / 256;      // 16-byte staging loads per thread: K
-  constexpr int RLD = DR ? RB / 16 / 256 : 0;
-  constexpr int VLD = VB / 16 / 256;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE];
+  constexpr int DN = 128;                     // per-head key width
+  constexpr int DV = 128;                     // value / output width
+  constexpr int KSN = DN / 16;                // k-steps over the nope part
+  constexpr int KSR = DR / 16;                // k-steps over the rope part
+  constexpr int KB = 64 * DN * 2;             // K tile bytes
+  constexpr int RB = DR ? 64 * DR * 2 : 0;    // rope tile bytes
+  constexpr int VB = 64 * DV * 2;             // V tile bytes
+  constexpr int KLD = KB / 16 / 256;          // 16-byte staging loads per thread: K
+  constexpr int RLD = RB / 16 / 256;          //   rope
+  constexpr int VLD = VB / 16 / 256;          //   V
+  // LDS: both K buffers, then both rope buffers, then both V buffers, so that
+  // every read offset from its region base fits the 16-bit immediate.
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * (KB + RB + VB)];
+  unsigned char* const ks_base = smem;
+  unsigned char* const rs_base = smem + 2 * KB;
+  unsigned char* const vs_base = smem + 2 * KB + 2 * RB;
 
   // Work item: deepest query tile first; heads of one KV group on one XCD.
-  const int x = blockIdx.x;                   // 0 .. Hq-1
-  const int hpx = a.Hq >> 3;                  // heads per XCD slot (Hq % 8 == 0), else identity
+  const int x = blockIdx.x;
+  const int hpx = a.Hq >> 3;
   const int h = (a.Hq & 7) ? x : (x & 7) * hpx + (x >> 3);
   const int b = blockIdx.y;
   const int qt = a.q_tiles - 1 - (int)blockIdx.z;
@@ -115,11 +120,11 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
   bf16x8 qop[KSN + KSR];
   {
     const bool ok = qrow < L;
-    const uint16_t* qp = a.q + (int64_t)(c0 + (ok ? qrow : 0)) * a.q_st + (int64_t)h * a.q_sh;
+    const uint16_t* qp = a.q + (int64_t)(c0 + (ok ? qrow : 0)) * a.q_st + (int64_t)h * a.q_sh + 8 * hh;
 #pragma unroll
     for (int s = 0; s < KSN + KSR; ++s) {
-      const i32x4 v = ok ? load16(qp + 16 * s + 8 * hh) : i32x4{0, 0, 0, 0};
-      qop[s] = __builtin_bit_cast(bf16x8, v);
+      const i32x4 v = load16(qp + 16 * s);
+      qop[s] = __builtin_bit_cast(bf16x8, ok ? v : i32x4{0, 0, 0, 0});
     }
   }
 
@@ -129,12 +134,9 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
   const int qb1 = min(qb0 + 1, (L - 1) >> 6);
   const uint8_t* mrow0 = a.mask ? a.mask + ((int64_t)b * a.mask_nb + qb0) * a.mask_nb : nullptr;
   const uint8_t* mrow1 = a.mask ? a.mask + ((int64_t)b * a.mask_nb + qb1) * a.mask_nb : nullptr;
-  // A key tile is needed if either query block sees it (causal order first).
   auto tile_needed = [&](int kt) {
     if (!a.mask) return true;
-    const bool v0 = kt <= qb0 && mrow0[kt];
-    const bool v1 = kt <= qb1 && mrow1[kt];
-    return v0 || v1;
+    return (kt <= qb0 && mrow0[kt]) || (kt <= qb1 && mrow1[kt]);
   };
   auto next_tile = [&](int kt) {
     ++kt;
@@ -143,104 +145,143 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
   };
   const int wqb = r0 >> 6;                   // this wave's query block
   const uint8_t* mroww = a.mask ? a.mask + ((int64_t)b * a.mask_nb + wqb) * a.mask_nb : nullptr;
+  auto wave_sees = [&](int kt) {
+    if (!wave_rows || kt * 64 > rlast) return false;
+    return !a.mask || mroww[kt];
+  };
 
-  // Staging: thread tid moves chunks tid + 256 i of each tile.
+  // Staging: thread tid moves 16-byte chunks tid + 256 i of each tile; the
+  // row of chunk i is row0 + 16 i (K, V) or row0r + 32 i (rope).
+  const int row0 = tid >> 4, ch = tid & 15;
+  const int row0r = tid >> 3, chr = tid & 7;
+  // Tile bases are uniform (scalar) pointers; each lane adds one fixed 32-bit
+  // byte offset, so the loads use the scalar-base addressing form.
+  const int64_t kstr = a.k_st * 2, vstr = a.v_st * 2, rstr = a.kr_st * 2;  // row strides in bytes
+  const unsigned char* kg = (const unsigned char*)(a.k + (int64_t)c0 * a.k_st + (int64_t)g * a.k_sh);
+  const unsigned char* vg = (const unsigned char*)(a.v + (int64_t)c0 * a.v_st + (int64_t)g * a.v_sh);
+  const unsigned char* rg = DR ? (const unsigned char*)(a.kr + (int64_t)c0 * a.kr_st) : nullptr;
+  const uint32_t koff = (uint32_t)(row0 * kstr) + 16u * ch;
+  const uint32_t voff = (uint32_t)(row0 * vstr) + 16u * ch;
+  const uint32_t roff = DR ? (uint32_t)(row0r * rstr) + 16u * chr : 0u;
   i32x4 kst[KLD], rst[RLD > 0 ? RLD : 1], vst[VLD];
   auto load_tile = [&](int kt) {
+    const int key0 = kt * 64;
+    const unsigned char* kt_k = kg + key0 * kstr;
+    const unsigned char* kt_v = vg + key0 * vstr;
+    const unsigned char* kt_r = DR ? rg + key0 * rstr : nullptr;
+    if (key0 + 64 <= L) {  // whole tile inside the sequence
 #pragma unroll
-    for (int i = 0; i < KLD; ++i) {
-      const int chunk = tid + 256 * i;
-      const int row = chunk >> 4, c = chunk & 15;
-      const int key = kt * 64 + row;
-      kst[i] = key < L ? load16(a.k + (int64_t)(c0 + key) * a.k_st + (int64_t)g * a.k_sh + 8 * c)
-                       : i32x4{0, 0, 0, 0};
-    }
-    if constexpr (DR > 0) {
+      for (int i = 0; i < KLD; ++i) kst[i] = load16(kt_k + 16 * i * kstr + koff);
+#pragma unroll
+      for (int i = 0; i < RLD; ++i) rst[i] = load16(kt_r + 32 * i * rstr + roff);
+#pragma unroll
+      for (int i = 0; i < VLD; ++i) vst[i] = load16(kt_v + 16 * i * vstr + voff);
+    } else {  // ragged end: rows past the sequence read row L-1 and are zeroed
+#pragma unroll
+      for (int i = 0; i < KLD; ++i) {
+        const int key = key0 + row0 + 16 * i;
+        const i32x4 v = load16(kg + (int64_t)min(key, L - 1) * kstr + 16 * ch);
+        kst[i] = key < L ? v : i32x4{0, 0, 0, 0};
+      }
 #pragma unroll
       for (int i = 0; i < RLD; ++i) {
-        const int chunk = tid + 256 * i;
-        const int row = chunk >> 3, c = chunk & 7;
-        const int key = kt * 64 + row;
-        rst[i] = key < L ? load16(a.kr + (int64_t)(c0 + key) * a.kr_st + 8 * c) : i32x4{0, 0, 0, 0};
+        const int key = key0 + row0r + 32 * i;
+        const i32x4 v = load16(rg + (int64_t)min(key, L - 1) * rstr + 16 * chr);
+        rst[i] = key < L ? v : i32x4{0, 0, 0, 0};
       }
-    }
 #pragma unroll
-    for (int i = 0; i < VLD; ++i) {
-      const int chunk = tid + 256 * i;
-      const int row = chunk >> 4, c = chunk & 15;
-      const int key = kt * 64 + row;
-      vst[i] = key < L ? load16(a.v + (int64_t)(c0 + key) * a.v_st + (int64_t)g * a.v_sh + 8 * c)
-                       : i32x4{0, 0, 0, 0};
+      for (int i = 0; i < VLD; ++i) {
+        const int key = key0 + row0 + 16 * i;
+        const i32x4 v = load16(vg + (int64_t)min(key, L - 1) * vstr + 16 * ch);
+        vst[i] = key < L ? v : i32x4{0, 0, 0, 0};
+      }
     }
   };
-  auto store_tile = [&](int buf) {
-    unsigned char* st = smem + buf * STAGE;
+  // LDS write positions of this thread's chunks (swizzled), per buffer offset.
+  const int kw = kswz<16>(row0, ch);            // + 4096 i (16 rows) + KB * buf
+  const int rw = DR ? kswz<8>(row0r, chr) : 0;  // + 4096 i (32 rows) + RB * buf
+  const int vw = vswz256(row0, ch << 4);        // + 4096 i + VB * buf
+  auto store_tile = [&](auto bufc) {
+    constexpr int BUF = decltype(bufc)::value;
 #pragma unroll
-    for (int i = 0; i < KLD; ++i) {
-      const int chunk = tid + 256 * i;
-      store16(st + kswz<16>(chunk >> 4, chunk & 15), kst[i]);
-    }
-    if constexpr (DR > 0) {
+    for (int i = 0; i < KLD; ++i) store16(ks_base + BUF * KB + kw + 4096 * i, kst[i]);
 #pragma unroll
-      for (int i = 0; i < RLD; ++i) {
-        const int chunk = tid + 256 * i;
-        store16(st + KB + kswz<8>(chunk >> 3, chunk & 7), rst[i]);
-      }
-    }
+    for (int i = 0; i < RLD; ++i) store16(rs_base + BUF * RB + rw + 4096 * i, rst[i]);
 #pragma unroll
-    for (int i = 0; i < VLD; ++i) {
-      const int chunk = tid + 256 * i;
-      store16(st + KB + (DR ? RB : 0) + vswz256(chunk >> 4, (chunk & 15) << 4), vst[i]);
-    }
+    for (int i = 0; i < VLD; ++i) store16(vs_base + BUF * VB + vw + 4096 * i, vst[i]);
   };
 
-  float m_run = -INFINITY, l_run = 0.f;  // per query (both halves of a query agree)
+  // Per-lane LDS read offsets; the tile half t, k-step and buffer parts are
+  // immediates.  K: chunk (2s + hh) ^ (row & 15) = 2 (s ^ m) + ((hh ^ row) & 1).
+  int kra[KSN];
+  {
+    const int m = (l32 & 15) >> 1;
+    const int lo = ((hh ^ l32) & 1) << 4;
+#pragma unroll
+    for (int s2 = 0; s2 < KSN; ++s2) kra[s2] = l32 * 256 + ((s2 ^ m) << 5) + lo;
+  }
+  int rra[KSR > 0 ? KSR : 1];
+  if constexpr (DR > 0) {
+    const int m = (l32 >> 1) & 7;
+#pragma unroll
+    for (int s2 = 0; s2 < KSR; ++s2) rra[s2] = l32 * 128 + (((2 * s2 + hh) ^ m) << 4);
+  }
+  // V^T transpose reads: 16-lane group gamma takes d = 32 dt + 16 (gamma & 1) + i
+  // from rows kb + li/4, kb = 16 ks + 8 part + 4 hh; kb & 7 == 4 hh.
+  int vra[4];
+  {
+    const int gam = lane >> 4, li = lane & 15;
+    const int row = 4 * hh + (li >> 2);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+      vra[dt] = row * 256 + (((2 * dt + (gam & 1)) ^ (row & 7)) << 5) + 8 * (li & 3);
+  }
+
+  float m_run = -INFINITY, l_run = 0.f;  // base-2 scaled max; this lane's half of the row sum
   f32x16_t o[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) o[t] = f32x16_t{};
+  const float c = a.scale_log2;
 
-  auto compute_tile = [&](int kt, int buf) {
-    const unsigned char* st = smem + buf * STAGE;
+  auto compute_tile = [&](int kt, auto bufc) {
+    constexpr int BUF = decltype(bufc)::value;
+    const unsigned char* kb = ks_base + BUF * KB;
+    const unsigned char* rb = rs_base + BUF * RB;
+    const unsigned char* vb = vs_base + BUF * VB;
     // S^T tile t (keys 32t .. 32t+31 of the tile) x 32 queries.
     f32x16_t s[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       s[t] = f32x16_t{};
-      const int krow = 32 * t + l32;
 #pragma unroll
-      for (int ss = 0; ss < KSN; ++ss) {
-        const bf16x8 ka = __builtin_bit_cast(bf16x8, load16(st + kswz<16>(krow, 2 * ss + hh)));
-        s[t] = mfma32x32x16(ka, qop[ss], s[t]);
-      }
+      for (int ss = 0; ss < KSN; ++ss)
+        s[t] = mfma32x32x16(__builtin_bit_cast(bf16x8, load16(kb + t * 8192 + kra[ss])), qop[ss], s[t]);
       if constexpr (DR > 0) {
 #pragma unroll
-        for (int ss = 0; ss < KSR; ++ss) {
-          const bf16x8 ka = __builtin_bit_cast(bf16x8, load16(st + KB + kswz<8>(krow, 2 * ss + hh)));
-          s[t] = mfma32x32x16(ka, qop[KSN + ss], s[t]);
-        }
+        for (int ss = 0; ss < KSR; ++ss)
+          s[t] = mfma32x32x16(__builtin_bit_cast(bf16x8, load16(rb + t * 4096 + rra[ss])), qop[KSN + ss], s[t]);
       }
     }
-    // Scale, mask (causal, ragged end) by select, running max.
-    const bool need_mask = kt * 64 + 63 > r0;  // tile reaches past this wave's first row
+    // Causal mask by select (only on tiles reaching past the wave's first row).
+    if (kt * 64 + 63 > r0) {
+      const int rel = qrow - kt * 64 - hh * 4;  // key offset + hh*4 must stay <= rel
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if (32 * t + (j >> 2) * 8 + (j & 3) > rel) s[t][j] = -INFINITY;
+    }
     float tmax = -INFINITY;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        float x = s[t][j] * a.scale_log2;
-        if (need_mask) {
-          const int key = kt * 64 + 32 * t + (j >> 2) * 8 + hh * 4 + (j & 3);
-          x = key <= qrow ? x : -INFINITY;
-        }
-        s[t][j] = x;
-        tmax = fmaxf(tmax, x);
-      }
+      for (int j = 0; j < 16; ++j) tmax = fmaxf(tmax, s[t][j]);
     {
       const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, tmax),
                                                        __builtin_bit_cast(uint32_t, tmax), false, false);
       tmax = fmaxf(__builtin_bit_cast(float, (uint32_t)sw[0]), __builtin_bit_cast(float, (uint32_t)sw[1]));
     }
-    const float m_new = fmaxf(m_run, tmax);
+    const float m_new = fmaxf(m_run, tmax * c);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;  // a row with nothing visible yet
     const float alpha = fast_exp2(m_run - m_use);
     float psum = 0.f;
@@ -248,14 +289,16 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const float p = fast_exp2(s[t][j] - m_use);
+        const float p = fast_exp2(fmaf(s[t][j], c, -m_use));
         s[t][j] = p;
         psum += p;
       }
-    l_run = l_run * alpha + psum;  // this lane's half of the row sum
+    l_run = fmaf(l_run, alpha, psum);
     m_run = m_new;
+    if (__any(alpha != 1.f)) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) o[t] *= alpha;
+      for (int t = 0; t < 4; ++t) o[t] *= alpha;
+    }
     // P^T operands: k-step ks covers keys 16 ks + {4hh .. 4hh+3, 8+4hh .. 8+4hh+3},
     // which are D registers 8 (ks % 2) .. +7 of score tile ks / 2.
     bf16x8 pop[4];
@@ -267,50 +310,43 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
         w[e] = (int)pack_bf16x2_hw(s[ks >> 1][8 * (ks & 1) + 2 * e], s[ks >> 1][8 * (ks & 1) + 2 * e + 1]);
       pop[ks] = __builtin_bit_cast(bf16x8, w);
     }
-    // O^T[d, q] += V^T P^T.  16-lane group gamma reads d = 32 dt + 16 (gamma & 1) + i
-    // at keys kb .. kb+3 through the transpose read.
-    const unsigned char* vt = st + KB + (DR ? RB : 0);
-    const int gam = lane >> 4;
-    const int li = lane & 15;
+    // O^T[d, q] += V^T P^T, V^T from two transpose reads per k-step.
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
-      const int db = 32 * dt + 16 * (gam & 1);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        i32x4 w;
-#pragma unroll
-        for (int part = 0; part < 2; ++part) {
-          const int kb = 16 * ks + 8 * part + 4 * hh;
-          const i16x4 r = lds_read_tr16(vt + vswz256(kb + (li >> 2), 2 * (db + 4 * (li & 3))));
-          w[2 * part] = (int)((uint16_t)r[0] | ((uint32_t)(uint16_t)r[1] << 16));
-          w[2 * part + 1] = (int)((uint16_t)r[2] | ((uint32_t)(uint16_t)r[3] << 16));
-        }
+        const i16x4 lo = lds_read_tr16(vb + vra[dt] + (16 * ks) * 256);
+        const i16x4 hi = lds_read_tr16(vb + vra[dt] + (16 * ks + 8) * 256);
+        typedef __attribute__((__vector_size__(8 * sizeof(short)))) short i16x8;
+        const i16x8 w = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         o[dt] = mfma32x32x16(__builtin_bit_cast(bf16x8, w), pop[ks], o[dt]);
       }
     }
   };
 
-  // A wave computes a loaded tile only if its own rows see some key of it.
-  auto wave_sees = [&](int kt) {
-    if (!wave_rows || kt * 64 > rlast) return false;
-    return !a.mask || mroww[kt];
-  };
-
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
   int kt = tile_needed(0) ? 0 : next_tile(0);
-  int buf = 0;
   if (kt < nkt) {
     load_tile(kt);
-    store_tile(0);
+    store_tile(B0{});
   }
   __syncthreads();
+  // Two tiles per trip so the LDS buffer index is static.
   while (kt < nkt) {
-    const int kn = next_tile(kt);
+    int kn = next_tile(kt);
     if (kn < nkt) load_tile(kn);
-    if (wave_sees(kt)) compute_tile(kt, buf);
-    if (kn < nkt) store_tile(buf ^ 1);
+    if (wave_sees(kt)) compute_tile(kt, B0{});
+    if (kn < nkt) store_tile(B1{});
     __syncthreads();
     kt = kn;
-    buf ^= 1;
+    if (kt >= nkt) break;
+    kn = next_tile(kt);
+    if (kn < nkt) load_tile(kn);
+    if (wave_sees(kt)) compute_tile(kt, B1{});
+    if (kn < nkt) store_tile(B0{});
+    __syncthreads();
+    kt = kn;
   }
 
   // Epilogue: combine the two halves of each row sum, normalise, store.
