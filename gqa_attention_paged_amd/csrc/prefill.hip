@@ -64,10 +64,14 @@ __device__ __forceinline__ int kswz(int row, int c) {
   }
 }
 
-// V tile (64 rows x 256 bytes): 32-byte pieces permuted by row, for the
-// transpose reads (4 rows x 32 bytes per 16 lanes).
+// V tile (64 rows x 256 bytes): 32-byte pieces XOR-permuted by a function
+// of the row.  A transpose read has four 16-lane groups; groups 0 and 1 read
+// rows 8k..8k+3 at pieces P and P^1, groups 2 and 3 rows 8k+4..8k+7.  The
+// mask 2*(row & 3) + ((row >> 2) & 1) sends the first two groups to the even
+// and the odd pieces respectively, so each half-wave covers all 64 banks.
+__device__ __forceinline__ int vmask(int row) { return 2 * (row & 3) + ((row >> 2) & 1); }
 __device__ __forceinline__ int vswz256(int row, int c) {
-  return row * 256 + ((((c >> 5) ^ (row & 7))) << 5) + (c & 31);
+  return row * 256 + (((c >> 5) ^ vmask(row)) << 5) + (c & 31);
 }
 
 }  // namespace dev
@@ -132,24 +136,46 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
   const int nkt = (min(L, q0 + 128) + 63) >> 6;
   const int qb0 = q0 >> 6;                   // the workgroup's two query blocks
   const int qb1 = min(qb0 + 1, (L - 1) >> 6);
-  const uint8_t* mrow0 = a.mask ? a.mask + ((int64_t)b * a.mask_nb + qb0) * a.mask_nb : nullptr;
-  const uint8_t* mrow1 = a.mask ? a.mask + ((int64_t)b * a.mask_nb + qb1) * a.mask_nb : nullptr;
-  auto tile_needed = [&](int kt) {
-    if (!a.mask) return true;
-    return (kt <= qb0 && mrow0[kt]) || (kt <= qb1 && mrow1[kt]);
-  };
-  auto next_tile = [&](int kt) {
-    ++kt;
-    while (kt < nkt && !tile_needed(kt)) ++kt;
-    return kt;
-  };
   const int wqb = r0 >> 6;                   // this wave's query block
-  const uint8_t* mroww = a.mask ? a.mask + ((int64_t)b * a.mask_nb + wqb) * a.mask_nb : nullptr;
+  // Tile schedule as bit words: bit i of word w is key tile 64 w + i.  `need`
+  // = loaded by the workgroup (either query block sees it), `see` = this
+  // wave's own query block sees it (mask part only).  Built with one load
+  // per lane and a ballot once per 64 tiles, so the tile loop itself never
+  // waits on memory for the mask.
+  uint64_t need_word = 0, see_word = 0;
+  int word_idx = -1;
+  auto load_words = [&](int wi) {
+    const int kt = wi * 64 + lane;
+    bool need = kt < nkt, see = kt < nkt;
+    if (a.mask && kt < nkt) {
+      const uint8_t* mb = a.mask + (int64_t)b * a.mask_nb * a.mask_nb;
+      const bool v0 = kt <= qb0 && mb[(int64_t)qb0 * a.mask_nb + kt];
+      const bool v1 = kt <= qb1 && mb[(int64_t)qb1 * a.mask_nb + kt];
+      need = v0 || v1;
+      see = kt <= wqb && mb[(int64_t)wqb * a.mask_nb + kt];
+    }
+    need_word = __ballot(need);
+    see_word = __ballot(see);
+    word_idx = wi;
+  };
+  // First needed tile at or after kt (nkt if none).
+  auto first_needed = [&](int kt) {
+    while (kt < nkt) {
+      if ((kt >> 6) != word_idx) load_words(kt >> 6);
+      const uint64_t bits = need_word >> (kt & 63);
+      if (bits) return kt + (int)__builtin_ctzll(bits);
+      kt = (kt | 63) + 1;
+    }
+    return nkt;
+  };
+  auto next_tile = [&](int kt) { return a.mask ? first_needed(kt + 1) : kt + 1; };
+  // A wave computes a loaded tile only if its own rows see some key of it.
+  // Called only for the tile just returned by first_needed / next_tile, so
+  // see_word is the word holding kt.
   auto wave_sees = [&](int kt) {
     if (!wave_rows || kt * 64 > rlast) return false;
-    return !a.mask || mroww[kt];
+    return !a.mask || ((see_word >> (kt & 63)) & 1);
   };
-
   // Staging: thread tid moves 16-byte chunks tid + 256 i of each tile; the
   // row of chunk i is row0 + 16 i (K, V) or row0r + 32 i (rope).
   const int row0 = tid >> 4, ch = tid & 15;
@@ -227,14 +253,14 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
     for (int s2 = 0; s2 < KSR; ++s2) rra[s2] = l32 * 128 + (((2 * s2 + hh) ^ m) << 4);
   }
   // V^T transpose reads: 16-lane group gamma takes d = 32 dt + 16 (gamma & 1) + i
-  // from rows kb + li/4, kb = 16 ks + 8 part + 4 hh; kb & 7 == 4 hh.
+  // from rows kb + li/4, kb = 16 ks + 8 part + 4 hh, so row & 7 = 4 hh + li/4.
   int vra[4];
   {
     const int gam = lane >> 4, li = lane & 15;
     const int row = 4 * hh + (li >> 2);
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
-      vra[dt] = row * 256 + (((2 * dt + (gam & 1)) ^ (row & 7)) << 5) + 8 * (li & 3);
+      vra[dt] = row * 256 + (((2 * dt + (gam & 1)) ^ vmask(row)) << 5) + 8 * (li & 3);
   }
 
   float m_run = -INFINITY, l_run = 0.f;  // base-2 scaled max; this lane's half of the row sum
@@ -326,24 +352,27 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
 
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
-  int kt = tile_needed(0) ? 0 : next_tile(0);
+  int kt = a.mask ? first_needed(0) : 0;
   if (kt < nkt) {
     load_tile(kt);
     store_tile(B0{});
   }
   __syncthreads();
-  // Two tiles per trip so the LDS buffer index is static.
+  // Two tiles per trip so the LDS buffer index is static.  wave_sees(kt) is
+  // read before next_tile() may move the bit words on to the next 64 tiles.
   while (kt < nkt) {
+    bool sees = wave_sees(kt);
     int kn = next_tile(kt);
     if (kn < nkt) load_tile(kn);
-    if (wave_sees(kt)) compute_tile(kt, B0{});
+    if (sees) compute_tile(kt, B0{});
     if (kn < nkt) store_tile(B1{});
     __syncthreads();
     kt = kn;
     if (kt >= nkt) break;
+    sees = wave_sees(kt);
     kn = next_tile(kt);
     if (kn < nkt) load_tile(kn);
-    if (wave_sees(kt)) compute_tile(kt, B1{});
+    if (sees) compute_tile(kt, B1{});
     if (kn < nkt) store_tile(B0{});
     __syncthreads();
     kt = kn;
