@@ -87,15 +87,14 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
   constexpr int KB = 64 * DN * 2;             // K tile bytes
   constexpr int RB = DR ? 64 * DR * 2 : 0;    // rope tile bytes
   constexpr int VB = 64 * DV * 2;             // V tile bytes
-  constexpr int KLD = KB / 16 / 256;          // 16-byte staging loads per thread: K
-  constexpr int RLD = RB / 16 / 256;          //   rope
-  constexpr int VLD = VB / 16 / 256;          //   V
-  // LDS: both K buffers, then both rope buffers, then both V buffers, so that
-  // every read offset from its region base fits the 16-bit immediate.
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * (KB + RB + VB)];
-  unsigned char* const ks_base = smem;
-  unsigned char* const rs_base = smem + 2 * KB;
-  unsigned char* const vs_base = smem + 2 * KB + 2 * RB;
+  constexpr int KLD = KB / 1024 / 4;          // 1 KB loads-to-LDS per wave and tile: K
+  constexpr int RLD = RB / 1024 / 4;          //   rope
+  constexpr int VLD = VB / 1024 / 4;          //   V
+  // LDS: one array per tile buffer, so the compiler can tell the buffer being
+  // filled by the direct-to-LDS loads from the one being read.
+  __shared__ __attribute__((aligned(1024))) unsigned char kbuf0[KB], kbuf1[KB];
+  __shared__ __attribute__((aligned(1024))) unsigned char rbuf0[RB ? RB : 16], rbuf1[RB ? RB : 16];
+  __shared__ __attribute__((aligned(1024))) unsigned char vbuf0[VB], vbuf1[VB];
 
   // Work item: deepest query tile first; heads of one KV group on one XCD.
   const int x = blockIdx.x;
@@ -176,66 +175,66 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
     if (!wave_rows || kt * 64 > rlast) return false;
     return !a.mask || ((see_word >> (kt & 63)) & 1);
   };
-  // Staging: thread tid moves 16-byte chunks tid + 256 i of each tile; the
-  // row of chunk i is row0 + 16 i (K, V) or row0r + 32 i (rope).
+  // Tile loads go straight to LDS (global_load_lds_dwordx4): wave w's i-th
+  // load fills the 1 KB LDS segment 4 i + w, lane l the 16 bytes at 16 l of
+  // it.  For K and V a segment is rows 16 i + tid/16 (4 rows of 256 bytes),
+  // for the rope part rows 32 i + tid/8 (8 rows of 128 bytes).  The LDS
+  // swizzle is applied on the global side: the lane that fills LDS chunk c'
+  // of a row fetches the chunk that the read swizzle expects there.
   const int row0 = tid >> 4, ch = tid & 15;
   const int row0r = tid >> 3, chr = tid & 7;
+  const int kch = ch ^ (row0 & 15);                                    // K: c' = c ^ (row & 15)
+  const int vch = (((ch >> 1) ^ vmask(row0)) << 1) | (ch & 1);         // V: 32-byte pieces ^ vmask(row)
+  const int rch = chr ^ ((row0r >> 1) & 7);                            // rope: c' = c ^ ((row >> 1) & 7)
   // Tile bases are uniform (scalar) pointers; each lane adds one fixed 32-bit
   // byte offset, so the loads use the scalar-base addressing form.
   const int64_t kstr = a.k_st * 2, vstr = a.v_st * 2, rstr = a.kr_st * 2;  // row strides in bytes
   const unsigned char* kg = (const unsigned char*)(a.k + (int64_t)c0 * a.k_st + (int64_t)g * a.k_sh);
   const unsigned char* vg = (const unsigned char*)(a.v + (int64_t)c0 * a.v_st + (int64_t)g * a.v_sh);
   const unsigned char* rg = DR ? (const unsigned char*)(a.kr + (int64_t)c0 * a.kr_st) : nullptr;
-  const uint32_t koff = (uint32_t)(row0 * kstr) + 16u * ch;
-  const uint32_t voff = (uint32_t)(row0 * vstr) + 16u * ch;
-  const uint32_t roff = DR ? (uint32_t)(row0r * rstr) + 16u * chr : 0u;
-  i32x4 kst[KLD], rst[RLD > 0 ? RLD : 1], vst[VLD];
-  auto load_tile = [&](int kt) {
-    const int key0 = kt * 64;
-    const unsigned char* kt_k = kg + key0 * kstr;
-    const unsigned char* kt_v = vg + key0 * vstr;
-    const unsigned char* kt_r = DR ? rg + key0 * rstr : nullptr;
-    if (key0 + 64 <= L) {  // whole tile inside the sequence
-#pragma unroll
-      for (int i = 0; i < KLD; ++i) kst[i] = load16(kt_k + 16 * i * kstr + koff);
-#pragma unroll
-      for (int i = 0; i < RLD; ++i) rst[i] = load16(kt_r + 32 * i * rstr + roff);
-#pragma unroll
-      for (int i = 0; i < VLD; ++i) vst[i] = load16(kt_v + 16 * i * vstr + voff);
-    } else {  // ragged end: rows past the sequence read row L-1 and are zeroed
-#pragma unroll
-      for (int i = 0; i < KLD; ++i) {
-        const int key = key0 + row0 + 16 * i;
-        const i32x4 v = load16(kg + (int64_t)min(key, L - 1) * kstr + 16 * ch);
-        kst[i] = key < L ? v : i32x4{0, 0, 0, 0};
-      }
-#pragma unroll
-      for (int i = 0; i < RLD; ++i) {
-        const int key = key0 + row0r + 32 * i;
-        const i32x4 v = load16(rg + (int64_t)min(key, L - 1) * rstr + 16 * chr);
-        rst[i] = key < L ? v : i32x4{0, 0, 0, 0};
-      }
-#pragma unroll
-      for (int i = 0; i < VLD; ++i) {
-        const int key = key0 + row0 + 16 * i;
-        const i32x4 v = load16(vg + (int64_t)min(key, L - 1) * vstr + 16 * ch);
-        vst[i] = key < L ? v : i32x4{0, 0, 0, 0};
-      }
-    }
+  const uint32_t koff = (uint32_t)(row0 * kstr) + 16u * kch;
+  const uint32_t voff = (uint32_t)(row0 * vstr) + 16u * vch;
+  const uint32_t roff = DR ? (uint32_t)(row0r * rstr) + 16u * rch : 0u;
+  const int wseg = __builtin_amdgcn_readfirstlane(wv) * 1024;
+  auto dma = [&](const unsigned char* gp, unsigned char* lp) {
+    __builtin_amdgcn_global_load_lds((const void*)gp, (GQAP_LDS void*)lp, 16, 0, 0);
   };
-  // LDS write positions of this thread's chunks (swizzled), per buffer offset.
-  const int kw = kswz<16>(row0, ch);            // + 4096 i (16 rows) + KB * buf
-  const int rw = DR ? kswz<8>(row0r, chr) : 0;  // + 4096 i (32 rows) + RB * buf
-  const int vw = vswz256(row0, ch << 4);        // + 4096 i + VB * buf
-  auto store_tile = [&](auto bufc) {
+  // Rows past the end of the sequence read row L-1 instead: every key past L
+  // is causally hidden from every query of the sequence, so its score is
+  // replaced by -inf and its probability is exactly 0.
+  auto load_tile = [&](int kt, auto bufc) {
     constexpr int BUF = decltype(bufc)::value;
+    unsigned char* kd = BUF ? kbuf1 : kbuf0;
+    unsigned char* rd = BUF ? rbuf1 : rbuf0;
+    unsigned char* vd = BUF ? vbuf1 : vbuf0;
+    const int key0 = kt * 64;
+    if (key0 + 64 <= L) {  // whole tile inside the sequence
+      const unsigned char* kt_k = kg + key0 * kstr;
+      const unsigned char* kt_v = vg + key0 * vstr;
+      const unsigned char* kt_r = DR ? rg + key0 * rstr : nullptr;
 #pragma unroll
-    for (int i = 0; i < KLD; ++i) store16(ks_base + BUF * KB + kw + 4096 * i, kst[i]);
+      for (int i = 0; i < KLD; ++i) dma(kt_k + 16 * i * kstr + koff, kd + 4096 * i + wseg);
 #pragma unroll
-    for (int i = 0; i < RLD; ++i) store16(rs_base + BUF * RB + rw + 4096 * i, rst[i]);
+      for (int i = 0; i < RLD; ++i) dma(kt_r + 32 * i * rstr + roff, rd + 4096 * i + wseg);
 #pragma unroll
-    for (int i = 0; i < VLD; ++i) store16(vs_base + BUF * VB + vw + 4096 * i, vst[i]);
+      for (int i = 0; i < VLD; ++i) dma(kt_v + 16 * i * vstr + voff, vd + 4096 * i + wseg);
+    } else {
+#pragma unroll
+      for (int i = 0; i < KLD; ++i)
+        dma(kg + (int64_t)min(key0 + row0 + 16 * i, L - 1) * kstr + 16 * kch, kd + 4096 * i + wseg);
+#pragma unroll
+      for (int i = 0; i < RLD; ++i)
+        dma(rg + (int64_t)min(key0 + row0r + 32 * i, L - 1) * rstr + 16 * rch, rd + 4096 * i + wseg);
+#pragma unroll
+      for (int i = 0; i < VLD; ++i)
+        dma(vg + (int64_t)min(key0 + row0 + 16 * i, L - 1) * vstr + 16 * vch, vd + 4096 * i + wseg);
+    }
+    // Keep the loads at the top of the tile so they overlap its math.
+    __builtin_amdgcn_sched_barrier(0);
   };
+  // Waits for this thread's tile loads; the barrier that follows publishes
+  // every thread's.
+  auto loads_done = [] { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
   // Per-lane LDS read offsets; the tile half t, k-step and buffer parts are
   // immediates.  K: chunk (2s + hh) ^ (row & 15) = 2 (s ^ m) + ((hh ^ row) & 1).
@@ -271,23 +270,35 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
 
   auto compute_tile = [&](int kt, auto bufc) {
     constexpr int BUF = decltype(bufc)::value;
-    const unsigned char* kb = ks_base + BUF * KB;
-    const unsigned char* rb = rs_base + BUF * RB;
-    const unsigned char* vb = vs_base + BUF * VB;
-    // S^T tile t (keys 32t .. 32t+31 of the tile) x 32 queries.
-    f32x16_t s[2];
+    const unsigned char* kb = BUF ? kbuf1 : kbuf0;
+    const unsigned char* rb = BUF ? rbuf1 : rbuf0;
+    const unsigned char* vb = BUF ? vbuf1 : vbuf0;
+    // S^T tile t (keys 32t .. 32t+31 of the tile) x 32 queries: 2 NS MFMAs
+    // whose K operands are read from LDS PF steps ahead.
+    constexpr int NS = KSN + KSR;
+    constexpr int PF = 8;
+    auto kfrag = [&](int idx) {
+      const int t = idx / NS, ss = idx % NS;
+      return ss < KSN ? load16(kb + t * 8192 + kra[ss]) : load16(rb + t * 4096 + rra[ss - KSN]);
+    };
+    f32x16_t s[2] = {f32x16_t{}, f32x16_t{}};
+    i32x4 kf[PF];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      s[t] = f32x16_t{};
+    for (int i = 0; i < PF; ++i) kf[i] = kfrag(i);
 #pragma unroll
-      for (int ss = 0; ss < KSN; ++ss)
-        s[t] = mfma32x32x16(__builtin_bit_cast(bf16x8, load16(kb + t * 8192 + kra[ss])), qop[ss], s[t]);
-      if constexpr (DR > 0) {
-#pragma unroll
-        for (int ss = 0; ss < KSR; ++ss)
-          s[t] = mfma32x32x16(__builtin_bit_cast(bf16x8, load16(rb + t * 4096 + rra[ss])), qop[KSN + ss], s[t]);
-      }
+    for (int idx = 0; idx < 2 * NS; ++idx) {
+      const i32x4 cur = kf[idx % PF];
+      if (idx + PF < 2 * NS) kf[idx % PF] = kfrag(idx + PF);
+      s[idx / NS] = mfma32x32x16(__builtin_bit_cast(bf16x8, cur), qop[idx % NS], s[idx / NS]);
     }
+    // Issue order: PF reads, then one MFMA and one read at a time.
+    __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
+#pragma unroll
+    for (int idx = 0; idx < 2 * NS - PF; ++idx) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, PF, 0);
     // Causal mask by select (only on tiles reaching past the wave's first row).
     if (kt * 64 + 63 > r0) {
       const int rel = qrow - kt * 64 - hh * 4;  // key offset + hh*4 must stay <= rel
@@ -336,44 +347,57 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
         w[e] = (int)pack_bf16x2_hw(s[ks >> 1][8 * (ks & 1) + 2 * e], s[ks >> 1][8 * (ks & 1) + 2 * e + 1]);
       pop[ks] = __builtin_bit_cast(bf16x8, w);
     }
-    // O^T[d, q] += V^T P^T, V^T from two transpose reads per k-step.
+    // O^T[d, q] += V^T P^T, V^T from two transpose reads per k-step, read
+    // PV steps ahead of the MFMA that consumes them.
+    typedef __attribute__((__vector_size__(8 * sizeof(short)))) short i16x8;
+    constexpr int PV = 4;
+    auto vfrag = [&](int idx) {
+      const int dt = idx >> 2, ks = idx & 3;
+      const i16x4 lo = lds_read_tr16(vb + vra[dt] + (16 * ks) * 256);
+      const i16x4 hi = lds_read_tr16(vb + vra[dt] + (16 * ks + 8) * 256);
+      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    i16x8 vf[PV];
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
+    for (int i = 0; i < PV; ++i) vf[i] = vfrag(i);
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const i16x4 lo = lds_read_tr16(vb + vra[dt] + (16 * ks) * 256);
-        const i16x4 hi = lds_read_tr16(vb + vra[dt] + (16 * ks + 8) * 256);
-        typedef __attribute__((__vector_size__(8 * sizeof(short)))) short i16x8;
-        const i16x8 w = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[dt] = mfma32x32x16(__builtin_bit_cast(bf16x8, w), pop[ks], o[dt]);
-      }
+    for (int idx = 0; idx < 16; ++idx) {
+      const i16x8 cur = vf[idx % PV];
+      if (idx + PV < 16) vf[idx % PV] = vfrag(idx + PV);
+      o[idx >> 2] = mfma32x32x16(__builtin_bit_cast(bf16x8, cur), pop[idx & 3], o[idx >> 2]);
     }
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * PV, 0);
+#pragma unroll
+    for (int idx = 0; idx < 16 - PV; ++idx) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, PV, 0);
   };
 
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
   int kt = a.mask ? first_needed(0) : 0;
-  if (kt < nkt) {
-    load_tile(kt);
-    store_tile(B0{});
-  }
+  if (kt < nkt) load_tile(kt, B0{});
+  loads_done();
   __syncthreads();
   // Two tiles per trip so the LDS buffer index is static.  wave_sees(kt) is
   // read before next_tile() may move the bit words on to the next 64 tiles.
+  // A buffer is refilled only after the barrier that ends the reads of it.
   while (kt < nkt) {
     bool sees = wave_sees(kt);
     int kn = next_tile(kt);
-    if (kn < nkt) load_tile(kn);
+    if (kn < nkt) load_tile(kn, B1{});
     if (sees) compute_tile(kt, B0{});
-    if (kn < nkt) store_tile(B1{});
+    loads_done();
     __syncthreads();
     kt = kn;
     if (kt >= nkt) break;
     sees = wave_sees(kt);
     kn = next_tile(kt);
-    if (kn < nkt) load_tile(kn);
+    if (kn < nkt) load_tile(kn, B0{});
     if (sees) compute_tile(kt, B1{});
-    if (kn < nkt) store_tile(B0{});
+    loads_done();
     __syncthreads();
     kt = kn;
   }
