@@ -191,6 +191,11 @@ extern "C" gqap_status gqap_prefill_plan(const gqap_prefill_desc_t* desc, gqap_p
   plan->ratio = d.num_q_heads / d.num_kv_heads;
   plan->q_tile_rows = 128;
   plan->q_tiles = (int32_t)ceil_div(d.max_seq_len, plan->q_tile_rows);
+  // One workgroup of 256 work-items per (head, sequence, query tile) slot;
+  // the launch must stay under 2^32 work-items.
+  if ((int64_t)d.num_q_heads * d.batch * plan->q_tiles >= ((int64_t)1 << 24))
+    return fail(GQAP_ERR_UNSUPPORTED, "Hq * batch * ceil(max_seq_len/128) = %lld workgroups exceeds 2^24",
+                (long long)d.num_q_heads * d.batch * plan->q_tiles);
   plan->kernel = mla ? 2 : 1;
   plan->workspace_bytes = 0;
   plan->magic = GQAP_PLAN_MAGIC;

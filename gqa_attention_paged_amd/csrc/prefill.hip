@@ -96,21 +96,48 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
   __shared__ __attribute__((aligned(1024))) unsigned char rbuf0[RB ? RB : 16], rbuf1[RB ? RB : 16];
   __shared__ __attribute__((aligned(1024))) unsigned char vbuf0[VB], vbuf1[VB];
 
-  // Work item: deepest query tile first; heads of one KV group on one XCD.
-  const int x = blockIdx.x;
+  // Work item.  The grid is one-dimensional, Hq workgroups per (query tile,
+  // sequence) pair; pairs are ranked deepest query tile first, then by
+  // sequence, and only pairs that exist (query tile inside its sequence) are
+  // ranked, so all real work precedes the empty tail of the grid and is
+  // spread evenly over the dispatcher's shader engines.  Within a pair the
+  // heads of one KV group share an XCD (workgroup i runs on XCD i % 8).
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int x = blockIdx.x % a.Hq;
+  const int pair = blockIdx.x / a.Hq;
   const int hpx = a.Hq >> 3;
   const int h = (a.Hq & 7) ? x : (x & 7) * hpx + (x >> 3);
-  const int b = blockIdx.y;
-  const int qt = a.q_tiles - 1 - (int)blockIdx.z;
+  int b, qt;
+  if (a.B <= 64) {
+    int nq = 0;  // query tiles of sequence `lane`
+    if (lane < a.B) nq = (min(a.cu[lane + 1] - a.cu[lane], a.max_len) + 127) >> 7;
+    b = -1;
+    qt = -1;
+    int before = 0;
+    for (int t = a.q_tiles - 1; t >= 0; --t) {
+      uint64_t m = __ballot(nq > t);
+      const int cnt = __builtin_popcountll(m);
+      if (pair < before + cnt) {
+        for (int k = pair - before; k > 0; --k) m &= m - 1;  // drop the lower set bits
+        b = __builtin_ctzll(m);
+        qt = t;
+        break;
+      }
+      before += cnt;
+    }
+    if (qt < 0) return;  // past the last real pair
+  } else {
+    b = pair % a.B;
+    qt = a.q_tiles - 1 - pair / a.B;
+  }
   const int c0 = a.cu[b];
   const int L = min(a.cu[b + 1] - c0, a.max_len);  // capacity from the plan
   const int q0 = qt * 128;
   if (q0 >= L) return;
   const int g = h / a.ratio;
 
-  const int tid = threadIdx.x;
   const int wv = tid >> 6;
-  const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hh = lane >> 5;
   const int r0 = q0 + 32 * wv;               // first query row of this wave (local)
@@ -318,9 +345,22 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
                                                        __builtin_bit_cast(uint32_t, tmax), false, false);
       tmax = fmaxf(__builtin_bit_cast(float, (uint32_t)sw[0]), __builtin_bit_cast(float, (uint32_t)sw[1]));
     }
-    const float m_new = fmaxf(m_run, tmax * c);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;  // a row with nothing visible yet
-    const float alpha = fast_exp2(m_run - m_use);
+    // The reference point m_run of the exponentials moves only when a score
+    // passes it by more than 2^8, so probabilities stay <= 256 (exact range
+    // for bf16 and fp32) and the accumulator is rescaled a few times per row
+    // instead of on every tile.  The result does not depend on where the
+    // reference point sits: out = sum p v / sum p and lse = m_run + log2(sum p).
+    const float tm = tmax * c;
+    const bool grow = tm > m_run + 8.f;  // also true on the first visible key (m_run = -inf)
+    if (__any(grow)) {
+      const float m_new = grow ? tm : m_run;
+      const float alpha = grow ? fast_exp2(m_run - m_new) : 1.f;  // exp2(-inf) = 0 on the first
+      l_run *= alpha;
+      m_run = m_new;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) o[t] *= alpha;
+    }
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;  // a row with nothing visible yet
     float psum = 0.f;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -330,12 +370,7 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
         s[t][j] = p;
         psum += p;
       }
-    l_run = fmaf(l_run, alpha, psum);
-    m_run = m_new;
-    if (__any(alpha != 1.f)) {
-#pragma unroll
-      for (int t = 0; t < 4; ++t) o[t] *= alpha;
-    }
+    l_run += psum;
     // P^T operands: k-step ks covers keys 16 ks + {4hh .. 4hh+3, 8+4hh .. 8+4hh+3},
     // which are D registers 8 (ks % 2) .. +7 of score tile ks / 2.
     bf16x8 pop[4];
@@ -476,7 +511,7 @@ extern "C" gqap_status gqap_prefill(const gqap_prefill_plan_t* plan, const void*
   a.mask_nb = d.mask_blocks;
   a.max_len = d.max_seq_len;
   a.scale_log2 = scale * dev::kLog2e;
-  const dim3 grid(d.num_q_heads, d.batch, plan->q_tiles);
+  const dim3 grid((unsigned)d.num_q_heads * (unsigned)d.batch * (unsigned)plan->q_tiles);
   hipStream_t st = (hipStream_t)stream;
   if (d.head_dim_rope == 64)
     hipLaunchKernelGGL(prefill_fwd<64>, grid, dim3(256), 0, st, a);
