@@ -1,0 +1,244 @@
+"""The C ABI on the host: the library loads, exports every function that
+include/gqap.h declares, its structures have the layout the binding assumes,
+and planning / host validation reject exactly the calls they document.
+No device calls are made here."""
+import ctypes
+import os
+import re
+import shutil
+import subprocess
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gqap.h")
+GOLDEN = os.path.join(ROOT, "tests", "golden", "precall_checks.txt")
+
+
+@pytest.fixture(scope="module")
+def gq():
+    import gqa_attention_paged_amd as m  # raises ImportError when the library is not built
+    return m
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(gqap_[a-z_0-9]+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_binding_functions(gq):
+    decl = declared_functions()
+    assert decl, "no functions parsed from the header"
+    assert sorted(gq.C_FUNCTIONS) == decl
+
+
+def test_library_exports_every_declared_symbol(gq):
+    lib = ctypes.CDLL(gq.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    nm = shutil.which("nm")
+    if nm:
+        out = subprocess.run([nm, "-D", "--defined-only", gq.LIB_PATH], capture_output=True, text=True).stdout
+        exported = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
+        for name in declared_functions():
+            assert name in exported, name
+
+
+def test_version_string(gq):
+    assert "gfx950" in gq.gqap_version()
+
+
+LAYOUT_PROGRAM = r"""
+#include <stddef.h>
+#include <stdio.h>
+#include "gqap.h"
+#define F(T, f) printf(#T " " #f " %zu\n", offsetof(T, f));
+int main(void) {
+  printf("gqap_decode_desc_t sizeof %zu\n", sizeof(gqap_decode_desc_t));
+  printf("gqap_decode_plan_t sizeof %zu\n", sizeof(gqap_decode_plan_t));
+  printf("gqap_prefill_desc_t sizeof %zu\n", sizeof(gqap_prefill_desc_t));
+  printf("gqap_prefill_plan_t sizeof %zu\n", sizeof(gqap_prefill_plan_t));
+  %FIELDS%
+  return 0;
+}
+"""
+
+
+def test_struct_layout_matches_the_c_compiler(gq, tmp_path):
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if not cc:
+        pytest.skip("no C compiler")
+    structs = {"gqap_decode_desc_t": gq.DecodeDesc, "gqap_decode_plan_t": gq.DecodePlan,
+               "gqap_prefill_desc_t": gq.PrefillDesc, "gqap_prefill_plan_t": gq.PrefillPlan}
+    fields = "\n  ".join(f"F({cn}, {f})" for cn, py in structs.items() for f, _ in py._fields_)
+    src = tmp_path / "layout.c"
+    src.write_text(LAYOUT_PROGRAM.replace("%FIELDS%", fields))
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"), str(src), "-o",
+                    str(exe)], check=True)
+    got = {}
+    for ln in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.splitlines():
+        t, f, v = ln.split()
+        got[(t, f)] = int(v)
+    for cn, py in structs.items():
+        assert got[(cn, "sizeof")] == ctypes.sizeof(py), cn
+        for f, _ in py._fields_:
+            assert got[(cn, f)] == getattr(py, f).offset, (cn, f)
+
+
+# ---------------------------------------------------------------- decode planning
+
+def baseline_decode_desc(gq):
+    """B=64, Hq=32, Hk=8, D=128, 64 blocks per sequence, capacity 4096, bf16,
+    contiguous [B, Hq, D] q/out and [NB, Hk, 64, D] pools."""
+    d = gq.DecodeDesc()
+    d.batch, d.num_q_heads, d.num_kv_heads, d.head_dim = 64, 32, 8, 128
+    d.block_size, d.max_blocks_per_seq, d.num_pool_blocks, d.max_seq_len = 64, 64, 4096, 4096
+    d.q_dtype = d.kv_dtype = gq.BF16
+    d.q_stride_head, d.q_stride_batch = 128, 32 * 128
+    d.out_stride_head, d.out_stride_batch = 128, 32 * 128
+    d.kv_stride_head, d.kv_stride_block = 64 * 128, 8 * 64 * 128
+    d.block_table_stride = 64
+    return d
+
+
+def golden_cases():
+    cases = []
+    for ln in open(GOLDEN):
+        ln = ln.split("#", 1)[0].strip()
+        if not ln:
+            continue
+        lhs, want = [p.strip() for p in ln.split("->")]
+        parts = lhs.split()
+        cases.append((parts[0], dict(p.split("=") for p in parts[1:]), want))
+    return cases
+
+
+@pytest.mark.parametrize("name,overrides,want", golden_cases(), ids=[c[0] for c in golden_cases()])
+def test_decode_plan_precall_checks(gq, name, overrides, want):
+    d = baseline_decode_desc(gq)
+    for k, v in overrides.items():
+        setattr(d, k, getattr(gq, v) if v in ("F32", "BF16", "FP8_E4M3FN", "F16") else int(v))
+    status = gq.lib().gqap_decode_plan(ctypes.byref(d), ctypes.byref(gq.DecodePlan()))
+    assert gq.STATUS_NAMES[status] == want, (name, gq.gqap_last_error())
+    if want != "OK":
+        assert gq.gqap_last_error(), "an error status leaves a message"
+
+
+def test_decode_plan_is_a_function_of_the_descriptor(gq):
+    d = baseline_decode_desc(gq)
+    p = gq.gqap_decode_plan(d)
+    assert p.magic == gq.PLAN_MAGIC and p.ratio == 4
+    assert p.num_workers == 256 * 4        # D=128 bf16: four persistent waves per compute unit
+    assert p.head_chunks == 1
+    assert p.max_pieces == 64 * 8 * 1 + p.num_workers
+    # prefix (B+1 ints), lse (pieces x 16 floats), partial outputs (pieces x 16 x D floats), 256-byte rounded
+    r = lambda n: (n + 255) // 256 * 256
+    assert p.workspace_bytes == r(4 * 65) + r(4 * 16 * p.max_pieces) + r(4 * 16 * 128 * p.max_pieces)
+    d.num_workers = 77
+    assert gq.gqap_decode_plan(d).num_workers == 77
+    d.num_workers, d.num_cus = 0, 80
+    assert gq.gqap_decode_plan(d).num_workers == 80 * 4
+    d.q_dtype = d.kv_dtype = gq.F32
+    d.num_cus = 0
+    assert gq.gqap_decode_plan(d).num_workers == 256 * 2
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("head_dim", 96, "UNSUPPORTED"), ("q_dtype", 7, "DTYPE"), ("kv_dtype", 3, "UNSUPPORTED"),
+    ("max_blocks_per_seq", 0, "INVALID_ARGUMENT"), ("num_workers", -1, "INVALID_ARGUMENT"),
+    ("batch", 65536, "INVALID_ARGUMENT"), ("kv_stride_head", 64 * 100, "INVALID_ARGUMENT"),
+])
+def test_decode_plan_rejects(gq, field, value, status):
+    d = baseline_decode_desc(gq)
+    setattr(d, field, value)
+    got = gq.lib().gqap_decode_plan(ctypes.byref(d), ctypes.byref(gq.DecodePlan()))
+    assert gq.STATUS_NAMES[got] == status, gq.gqap_last_error()
+
+
+def test_decode_plan_accepts_an_empty_batch(gq):
+    d = baseline_decode_desc(gq)
+    d.batch = 0
+    assert gq.gqap_decode_plan(d).magic == gq.PLAN_MAGIC
+
+
+def test_validate_host_metadata(gq):
+    d = baseline_decode_desc(gq)
+    d.batch, d.num_pool_blocks = 2, 10
+    p = gq.gqap_decode_plan(d)
+    bt = np.full((2, 64), -1, np.int32)
+    bt[0, :3] = [4, 9, 0]
+    bt[1, :1] = [7]
+    gq.gqap_decode_validate_host(p, bt, np.array([130, 64], np.int32))      # 3 blocks and 1 block: fine
+    with pytest.raises(gq.GqapError, match="block_table"):
+        gq.gqap_decode_validate_host(p, bt, np.array([130, 65], np.int32))  # needs a second block: -1
+    bt[0, 1] = 10
+    with pytest.raises(gq.GqapError, match="outside the pool"):
+        gq.gqap_decode_validate_host(p, bt, np.array([130, 64], np.int32))
+    bt[0, 1] = 9
+    with pytest.raises(gq.GqapError, match="seq_lens"):
+        gq.gqap_decode_validate_host(p, bt, np.array([4097, 0], np.int32))
+    with pytest.raises(gq.GqapError, match="seq_lens"):
+        gq.gqap_decode_validate_host(p, bt, np.array([-1, 0], np.int32))
+
+
+def test_calls_reject_a_plan_that_was_never_made(gq):
+    bad = gq.DecodePlan()
+    st = gq.lib().gqap_paged_decode(ctypes.byref(bad), None, None, None, None, None, 1.0, 1.0, 1.0, None, None,
+                                    None, 0, None)
+    assert gq.STATUS_NAMES[st] == "INVALID_ARGUMENT"
+    st = gq.lib().gqap_prefill(ctypes.byref(gq.PrefillPlan()), None, None, None, None, None, None, 1.0, None, None,
+                               None, 0, None)
+    assert gq.STATUS_NAMES[st] == "INVALID_ARGUMENT"
+
+
+# ---------------------------------------------------------------- prefill planning
+
+def baseline_prefill_desc(gq, mla=True):
+    d = gq.PrefillDesc()
+    Dqk, Dr = (192, 64) if mla else (128, 0)
+    d.batch, d.num_q_heads, d.num_kv_heads = 4, 16, 16 if mla else 8
+    d.head_dim_qk, d.head_dim_rope, d.head_dim_v = Dqk, Dr, 128
+    d.total_tokens, d.max_seq_len, d.dtype, d.causal = 6584, 3000, gq.BF16, 1
+    d.q_stride_head, d.q_stride_token = Dqk, Dqk * d.num_q_heads
+    d.k_stride_head, d.k_stride_token = Dqk - Dr, (Dqk - Dr) * d.num_kv_heads
+    d.v_stride_head, d.v_stride_token = 128, 128 * d.num_kv_heads
+    d.kr_stride_token = Dr if Dr else 0
+    d.out_stride_head, d.out_stride_token = 128, 128 * d.num_q_heads
+    return d
+
+
+def test_prefill_plan_baseline(gq):
+    p = gq.gqap_prefill_plan(baseline_prefill_desc(gq))
+    assert p.magic == gq.PLAN_MAGIC and p.q_tile_rows == 128 and p.q_tiles == 24 and p.workspace_bytes == 0
+    p = gq.gqap_prefill_plan(baseline_prefill_desc(gq, mla=False))
+    assert p.ratio == 2
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("head_dim_rope", 0, "UNSUPPORTED"),        # 192 wide without the rope split
+    ("head_dim_v", 64, "UNSUPPORTED"),
+    ("dtype", 0, "DTYPE"),
+    ("causal", 0, "UNSUPPORTED"),
+    ("num_kv_heads", 3, "INVALID_ARGUMENT"),
+    ("max_seq_len", 7000, "INVALID_ARGUMENT"),  # longer than the packed token count
+    ("k_stride_token", 100, "INVALID_ARGUMENT"),
+    ("q_stride_head", 200, "INVALID_ARGUMENT"),  # 16 heads of 200 overrun the 3072-element token stride
+    ("has_block_mask", 2, "INVALID_ARGUMENT"),
+    ("batch", -1, "INVALID_ARGUMENT"),
+])
+def test_prefill_plan_rejects(gq, field, value, status):
+    d = baseline_prefill_desc(gq)
+    setattr(d, field, value)
+    got = gq.lib().gqap_prefill_plan(ctypes.byref(d), ctypes.byref(gq.PrefillPlan()))
+    assert gq.STATUS_NAMES[got] == status, gq.gqap_last_error()
+
+
+def test_prefill_plan_block_mask_extent(gq):
+    d = baseline_prefill_desc(gq)
+    d.has_block_mask, d.mask_blocks = 1, 46                  # ceil(3000 / 64) = 47 needed
+    assert gq.lib().gqap_prefill_plan(ctypes.byref(d), ctypes.byref(gq.PrefillPlan())) != 0
+    d.mask_blocks = 47
+    assert gq.gqap_prefill_plan(d).magic == gq.PLAN_MAGIC
