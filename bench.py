@@ -33,9 +33,17 @@ METRIC = "paged decode KV-read GB/s (% HBM peak); MLA prefill TFLOP/s (% MFMA pe
 ROT_BYTES = 768 << 20          # keep the rotating copies larger than the last-level cache
 
 
-def _kernel_source_hash() -> str:
+# Sources whose text decides each measured kernel's code (a change makes the
+# stored hardware-counter traffic for that kernel stale).
+KERNEL_SOURCES = {
+    "decode": ("dev.hpp", "status.hpp", "decode.hip"),
+    "prefill": ("dev.hpp", "status.hpp", "prefill.hip"),
+}
+
+
+def _kernel_source_hash(kind: str = "decode") -> str:
     h = hashlib.sha256()
-    for f in ("dev.hpp", "decode.hip", "prefill.hip"):
+    for f in KERNEL_SOURCES[kind]:
         p = os.path.join(ROOT, "gqa_attention_paged_amd", "csrc", f)
         if os.path.exists(p):
             with open(p, "rb") as fh:
@@ -43,21 +51,110 @@ def _kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def _traffic(kernel: str, per_launch_units: float):
-    """HBM bytes per launch from the committed PMC summary, or None when the
-    summary is missing or was taken on a different kernel source."""
+def _kind_of(workload: str) -> str:
+    return "prefill" if workload.startswith("prefill") else "decode"
+
+
+def _traffic(workload: str):
+    """HBM bytes per launch of the workload's dominant kernel from the
+    committed counter summary (profiles/traffic.json), or None when it is
+    missing or was taken on a different kernel source."""
     p = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(p):
         return None
     try:
         with open(p) as fh:
             t = json.load(fh)
-        ent = t.get(kernel)
-        if not ent or ent.get("source_hash") != _kernel_source_hash():
+        ent = t.get("workloads", {}).get(workload)
+        if not ent or ent.get("source_hash") != _kernel_source_hash(_kind_of(workload)):
             return None
         return ent["hbm_bytes_per_launch"]
-    except Exception:
+    except (OSError, ValueError, KeyError):
         return None
+
+
+# Dominant kernel of each workload, as rocprofv3 names it (substring match).
+DOMINANT_KERNEL = {
+    "decode_gqa_bf16": "decode_worker_mfma<128, false>",
+    "decode_long_fp8": "decode_worker_mfma<128, true>",
+    "decode_tiny_fp32": "decode_worker_f32",
+    "prefill_mla_bf16": "prefill_fwd<64>",
+    "prefill_blocksparse_bf16": "prefill_fwd<0>",
+}
+COPY_KERNEL = "neg_kernel"   # torch.neg(out=) over float32: reads and writes each byte once
+
+
+def _counter_per_dispatch(csv_dir: str, counter: str):
+    """{kernel name: [value per dispatch]} from a rocprofv3 counter CSV."""
+    import csv
+    import glob
+    per = {}
+    files = glob.glob(os.path.join(csv_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no *counter_collection.csv under {csv_dir}")
+    for fn in files:
+        with open(fn) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] != counter:
+                    continue
+                key = (r["Kernel_Name"], r["Dispatch_Id"])
+                per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    out = {}
+    for (name, _), v in per.items():
+        out.setdefault(name, []).append(v)
+    return out
+
+
+def _mean_for(per, pattern: str) -> float:
+    vals = [v for name, vs in per.items() if pattern in name for v in vs]
+    if not vals:
+        raise SystemExit(f"no dispatch of a kernel matching {pattern!r}; kernels seen: {sorted(per)[:8]}")
+    return sum(vals) / len(vals)
+
+
+def pmc_summary(fetch_dir: str, write_dir: str, workload: str, copy_bytes: int, out_path: str) -> dict:
+    """Turn a FETCH_SIZE run and a WRITE_SIZE run (KiB per dispatch) into HBM
+    bytes per launch of the workload's dominant kernel, each counter scaled
+    by what it reads for the plain copy kernel of `copy_bytes` bytes."""
+    from workloads import gen
+    fetch = _counter_per_dispatch(fetch_dir, "FETCH_SIZE")
+    write = _counter_per_dispatch(write_dir, "WRITE_SIZE")
+    f_copy, w_copy = _mean_for(fetch, COPY_KERNEL), _mean_for(write, COPY_KERNEL)
+    k_fetch = copy_bytes / (f_copy * 1024.0)
+    k_write = copy_bytes / (w_copy * 1024.0)
+    kern = DOMINANT_KERNEL[workload]
+    f_k, w_k = _mean_for(fetch, kern), _mean_for(write, kern)
+    case = gen.CONFIGS[workload]()
+    alg = case.kv_bytes() if hasattr(case, "kv_bytes") else None
+    ent = {
+        "kernel": kern, "source_hash": _kernel_source_hash(_kind_of(workload)),
+        "fetch_kib_per_dispatch": f_k, "write_kib_per_dispatch": w_k,
+        "copy_bytes": copy_bytes, "copy_fetch_kib": f_copy, "copy_write_kib": w_copy,
+        "fetch_scale": k_fetch, "write_scale": k_write,
+        "hbm_bytes_per_launch": f_k * 1024.0 * k_fetch + w_k * 1024.0 * k_write,
+        "algorithmic_bytes_per_launch": alg,
+    }
+    t = {"workloads": {}}
+    if os.path.exists(out_path):
+        with open(out_path) as fh:
+            t = json.load(fh)
+    t.setdefault("workloads", {})[workload] = ent
+    with open(out_path, "w") as fh:
+        json.dump(t, fh, indent=1, sort_keys=True)
+        fh.write("\n")
+    return ent
+
+
+def stats_summary(stats_csv: str, command: str) -> str:
+    """A short text table of a rocprofv3 --stats kernel summary."""
+    import csv
+    with open(stats_csv) as fh:
+        rows = list(csv.DictReader(fh))
+    lines = [f"command: {command}", "", f"{'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'pct':>6}  kernel"]
+    for r in rows:
+        lines.append(f"{int(r['Calls']):>6} {float(r['AverageNs']) / 1e3:>10.2f} {float(r['MinNs']) / 1e3:>10.2f} "
+                     f"{float(r['MaxNs']) / 1e3:>10.2f} {float(r['Percentage']):>6.2f}  {r['Name'][:110]}")
+    return "\n".join(lines) + "\n"
 
 
 def _timed_loop(run, steps: int, warmup: int, torch):
@@ -164,7 +261,23 @@ def main(argv=None) -> int:
     ap.add_argument("--only-primary", action="store_true", help="measure only the primary decode workload")
     ap.add_argument("--only", default=None,
                     help="measure one workload by name (for profiling) and print its record instead")
+    ap.add_argument("--copy-calibration-bytes", type=int, default=0,
+                    help="after the workload, run a plain float32 copy kernel (torch.neg) over this many bytes "
+                         "three times: the known-size reference for hardware byte counters")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None,
+                    help="summarise a FETCH_SIZE run and a WRITE_SIZE run of `--only WORKLOAD "
+                         "--copy-calibration-bytes N` into profiles/traffic.json (no GPU needed)")
+    ap.add_argument("--stats-summary", nargs=2, metavar=("KERNEL_STATS_CSV", "COMMAND"), default=None,
+                    help="print a rocprofv3 --stats kernel summary as a short text table (no GPU needed)")
     args = ap.parse_args(argv)
+    if args.pmc_summary:
+        ent = pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.only, args.copy_calibration_bytes,
+                          os.path.join(ROOT, "profiles", "traffic.json"))
+        print(json.dumps(ent, indent=1))
+        return 0
+    if args.stats_summary:
+        print(stats_summary(*args.stats_summary), end="")
+        return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (this library has no "
               "multi-GPU path: each GPU would run the same kernels on its own share).", file=sys.stderr)
@@ -184,6 +297,13 @@ def main(argv=None) -> int:
         c = mk()
         fn = bench_prefill if isinstance(c, gen.PrefillCase) else bench_decode
         print(json.dumps(fn(c, args.steps, args.warmup, torch, gq, gu)), flush=True)
+        if args.copy_calibration_bytes:
+            n = args.copy_calibration_bytes // 4
+            src = torch.ones(n, dtype=torch.float32, device="cuda")
+            dst = torch.empty_like(src)
+            for _ in range(3):
+                torch.neg(src, out=dst)
+            torch.cuda.synchronize()
         return 0
 
     case = gen.decode_gqa_bf16()
@@ -194,7 +314,7 @@ def main(argv=None) -> int:
         r4 = bench_decode(c4, args.steps, args.warmup, torch, gq, gu)
         r4["roofline"] = {"bound": "hbm", "achieved": r4["gbs_kernel"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                           "frac": r4["gbs_kernel"] / HBM_PEAK_GBS,
-                          "traffic": _traffic("decode_long_fp8", 1)}
+                          "traffic": _traffic("decode_long_fp8")}
         secondary.append(r4)
         del c4
         if hasattr(gu, "DevicePrefill"):
@@ -203,7 +323,7 @@ def main(argv=None) -> int:
                 rp = bench_prefill(pc, args.steps, args.warmup, torch, gq, gu)
                 rp["roofline"] = {"bound": "mfma", "achieved": rp["tflops_kernel"], "peak": BF16_MFMA_PEAK_TFLOPS,
                                   "unit": "TFLOP/s", "frac": rp["tflops_kernel"] / BF16_MFMA_PEAK_TFLOPS,
-                                  "traffic": None}
+                                  "traffic": _traffic(pc.name)}
                 secondary.append(rp)
                 del pc
 
@@ -235,11 +355,11 @@ def main(argv=None) -> int:
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(prim["gbs_kernel"] / HBM_PEAK_GBS, 4),
-            "traffic": _traffic("decode_gqa_bf16", 1),
+            "traffic": _traffic("decode_gqa_bf16"),
         },
         "cpu_baseline": cpu,
         "secondary": secondary,
-        "kernel_source_hash": _kernel_source_hash(),
+        "kernel_source_hash": {k: _kernel_source_hash(k) for k in KERNEL_SOURCES},
     }
     print(json.dumps(line), flush=True)
     return 0

@@ -249,13 +249,18 @@ typedef struct gqap_prefill_plan_t {
  * Validate a prefill request.  Pure host code.  Errors: INVALID_ARGUMENT
  * (sizes, strides, Hq % Hk, mask_blocks too small), DTYPE (not bf16),
  * UNSUPPORTED (causal == 0, head widths other than 128/192 with rope 0/64,
- * Dv != 128).
+ * Dv != 128, or Hq * batch * ceil(max_seq_len/128) >= 2^24 workgroups).
  */
 gqap_status gqap_prefill_plan(const gqap_prefill_desc_t* desc, gqap_prefill_plan_t* plan);
 
 /*
  * Ragged causal prefill.  All device pointers 16-byte aligned.  workspace may
  * be NULL when plan->workspace_bytes == 0.  Asynchronous on `stream`.
+ * Sequences longer than the plan's max_seq_len are truncated to it.  Only
+ * rows inside each sequence are read: a key tile that runs past the end
+ * repeats the sequence's last row, whose probability is then exactly 0, so
+ * K/V are expected to be finite (an infinite value in a sequence's last V
+ * row would also reach the other rows of its last 64-key tile).
  */
 gqap_status gqap_prefill(const gqap_prefill_plan_t* plan,
                          const void* q, const void* k, const void* v, const void* k_rope,
