@@ -295,11 +295,31 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
   for (int t = 0; t < 4; ++t) o[t] = f32x16_t{};
   const float c = a.scale_log2;
 
-  auto compute_tile = [&](int kt, auto bufc) {
+  // compute_tile(kt, BUF, WL, kn): the math of tile kt from buffer BUF; with
+  // WL, the loads of tile kn (a whole tile inside the sequence) into the
+  // other buffer are issued between its first MFMAs, so that their issue
+  // stalls overlap the matrix work instead of preceding it.
+  auto compute_tile = [&](int kt, auto bufc, auto wlc, int kn) {
     constexpr int BUF = decltype(bufc)::value;
+    constexpr bool WL = decltype(wlc)::value;
     const unsigned char* kb = BUF ? kbuf1 : kbuf0;
     const unsigned char* rb = BUF ? rbuf1 : rbuf0;
     const unsigned char* vb = BUF ? vbuf1 : vbuf0;
+    unsigned char* kd = BUF ? kbuf0 : kbuf1;
+    unsigned char* rd = BUF ? rbuf0 : rbuf1;
+    unsigned char* vd = BUF ? vbuf0 : vbuf1;
+    constexpr int NLD = KLD + RLD + VLD;
+    const unsigned char* kt_k = kg + kn * 64 * kstr;
+    const unsigned char* kt_v = vg + kn * 64 * vstr;
+    const unsigned char* kt_r = DR ? rg + kn * 64 * rstr : nullptr;
+    auto issue_load = [&](int i) {
+      if (i < KLD)
+        dma(kt_k + 16 * i * kstr + koff, kd + 4096 * i + wseg);
+      else if (i < KLD + RLD)
+        dma(kt_r + 32 * (i - KLD) * rstr + roff, rd + 4096 * (i - KLD) + wseg);
+      else
+        dma(kt_v + 16 * (i - KLD - RLD) * vstr + voff, vd + 4096 * (i - KLD - RLD) + wseg);
+    };
     // S^T tile t (keys 32t .. 32t+31 of the tile) x 32 queries: 2 NS MFMAs
     // whose K operands are read from LDS PF steps ahead.
     constexpr int NS = KSN + KSR;
@@ -317,15 +337,17 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
       const i32x4 cur = kf[idx % PF];
       if (idx + PF < 2 * NS) kf[idx % PF] = kfrag(idx + PF);
       s[idx / NS] = mfma32x32x16(__builtin_bit_cast(bf16x8, cur), qop[idx % NS], s[idx / NS]);
+      if (WL && idx < NLD) issue_load(idx);
     }
-    // Issue order: PF reads, then one MFMA and one read at a time.
+    // Issue order: PF reads, then per MFMA one read (and one tile load
+    // while any is left).
     __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
 #pragma unroll
-    for (int idx = 0; idx < 2 * NS - PF; ++idx) {
+    for (int idx = 0; idx < 2 * NS; ++idx) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (idx + PF < 2 * NS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (WL && idx < NLD) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, PF, 0);
     // Causal mask by select (only on tiles reaching past the wave's first row).
     if (kt * 64 + 63 > r0) {
       const int rel = qrow - kt * 64 - hh * 4;  // key offset + hh*4 must stay <= rel
@@ -416,24 +438,35 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
   if (kt < nkt) load_tile(kt, B0{});
   loads_done();
   __syncthreads();
+  using WL0 = std::integral_constant<bool, false>;
+  using WL1 = std::integral_constant<bool, true>;
+  // One tile: the loads of the next needed tile kn go into the other buffer,
+  // interleaved with this tile's matrix work when this wave computes and kn
+  // lies wholly inside the sequence, else up front.
+  auto step = [&](int kt, bool sees, int kn, auto bufc, auto nbufc) {
+    const bool more = kn < nkt;
+    const bool inside = more && kn * 64 + 64 <= L;
+    if (sees && inside) {
+      compute_tile(kt, bufc, WL1{}, kn);
+    } else {
+      if (more) load_tile(kn, nbufc);
+      if (sees) compute_tile(kt, bufc, WL0{}, kn);
+    }
+    loads_done();
+    __syncthreads();
+  };
   // Two tiles per trip so the LDS buffer index is static.  wave_sees(kt) is
   // read before next_tile() may move the bit words on to the next 64 tiles.
   // A buffer is refilled only after the barrier that ends the reads of it.
   while (kt < nkt) {
     bool sees = wave_sees(kt);
     int kn = next_tile(kt);
-    if (kn < nkt) load_tile(kn, B1{});
-    if (sees) compute_tile(kt, B0{});
-    loads_done();
-    __syncthreads();
+    step(kt, sees, kn, B0{}, B1{});
     kt = kn;
     if (kt >= nkt) break;
     sees = wave_sees(kt);
     kn = next_tile(kt);
-    if (kn < nkt) load_tile(kn, B0{});
-    if (sees) compute_tile(kt, B1{});
-    loads_done();
-    __syncthreads();
+    step(kt, sees, kn, B1{}, B0{});
     kt = kn;
   }
 
