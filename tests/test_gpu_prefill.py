@@ -135,3 +135,31 @@ def test_prefill_packed_equals_separate(gu):
         sp.run()
         o1, _ = sp.results()
         assert np.array_equal(o1, out[c0:c1]), b
+
+
+def test_prefill_more_than_64_sequences(gu):
+    """Batches above 64 sequences take the plain (sequence, query tile) grid order."""
+    rng = np.random.default_rng(260)
+    lens = rng.integers(0, 300, size=70).tolist()
+    lens[:6] = [0, 1, 128, 129, 257, 64]
+    case = gen.make_prefill_case(name="b70", seed=260, seq_lens=lens, Hq=4, Hk=2, D_qk=128, D_rope=0, D_v=128)
+    _check(gu, case)
+
+
+def test_prefill_more_than_64_sequences_with_mask(gu):
+    rng = np.random.default_rng(261)
+    lens = rng.integers(1, 400, size=66).tolist()
+    case = gen.make_prefill_case(name="b66_mask", seed=261, seq_lens=lens, Hq=2, Hk=1, D_qk=192, D_rope=64,
+                                 D_v=128, mask_density=0.4)
+    _check(gu, case)
+
+
+def test_prefill_empty_sequences_in_the_batch(gu):
+    case = gen.make_prefill_case(name="empties", seed=262, seq_lens=[0, 5, 0, 200, 0, 129], Hq=4, Hk=4, D_qk=192,
+                                 D_rope=64, D_v=128)
+    _check(gu, case)
+
+
+def test_prefill_single_long_sequence_sampled(gu):
+    case = gen.make_prefill_case(name="long1", seed=263, seq_lens=[5000], Hq=2, Hk=1, D_qk=192, D_rope=64, D_v=128)
+    _check(gu, case, rows=_rows_sample(case, n_mid=96))
