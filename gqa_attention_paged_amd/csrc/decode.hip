@@ -615,6 +615,32 @@ __global__ __launch_bounds__(64) void decode_combine(DecodeArgs a) {
     const int w1 = (int)((u1 * P - 1) / W);        // worker holding unit u1 - 1
     // With fewer units than workers some workers own no unit; they wrote nothing.
     auto owns_units = [&](int wk) { return W * wk / P < W * (wk + 1) / P; };
+    if (w1 - w0 < 4) {
+      // Up to four pieces (the usual case): their LSEs and rows are requested
+      // together, so the merge costs a single memory round trip.
+      const int n = w1 - w0 + 1;
+      const bool live = lane < n && owns_units(w0 + lane);
+      const float lse_k = live ? a.ws_lse[(qg + w0 + lane) * 16 + col] : -INFINITY;
+      float v4[4][DC];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const float* op = a.ws_o + ((qg + w0 + min(kk, n - 1)) * 16 + col) * D;
+#pragma unroll
+        for (int c = 0; c < DC; ++c) v4[kk][c] = op[lane + 64 * c];
+      }
+      M = lse_k;
+#pragma unroll
+      for (int off = 2; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+      M = __shfl(M, 0);
+      const float wt_k = live ? exp2f(lse_k - M) : 0.f;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const float w = __shfl(wt_k, kk);  // 0 for kk >= n or a piece-less worker
+        den += w;
+#pragma unroll
+        for (int c = 0; c < DC; ++c) acc[c] += w > 0.f ? w * v4[kk][c] : 0.f;
+      }
+    } else
     for (int r0 = w0; r0 <= w1; r0 += 64) {
       const int wk = r0 + lane;
       const bool live = wk <= w1 && owns_units(wk);
