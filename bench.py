@@ -158,21 +158,26 @@ def stats_summary(stats_csv: str, command: str) -> str:
 
 
 def _timed_loop(run, steps: int, warmup: int, torch):
-    """Warm up, then time exactly `steps` calls; per-call HIP events on the
-    current stream give the kernel-side duration."""
+    """Warm up, then time exactly `steps` calls with nothing else in the loop
+    (wall clock, synchronised on both sides).  A second pass of the same
+    `steps` calls brackets each call with HIP events on the current stream
+    (the stream the library launches on) for the per-call duration and its
+    spread; those events stay out of the first, timed pass."""
     for i in range(warmup):
         run(i)
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        run(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for i in range(steps):
         starts[i].record()
         run(i)
         ends[i].record()
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
     ev_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     return (t1 - t0) * 1e3 / steps, sum(ev_ms) / len(ev_ms), sorted(ev_ms)
 
