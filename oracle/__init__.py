@@ -6,6 +6,8 @@ package imports nothing from the device library.
 """
 from .attention import (  # noqa: F401
     BLOCK,
+    append_kv,
+    chunk_prefill,
     bf16_to_f64,
     cu_seqlens_from_lengths,
     e4m3fn_table,

@@ -35,6 +35,14 @@ Sources (the pages this follows):
   * FlashMLA "Tensor Shapes Reference", section 3 (flash_mla_prefill): an
     optional block-sparse pattern, block-aligned to 64.
 
+  * FlashMLA "Tensor Shapes Reference", section 4 (mha_fwd_kvcache) and its
+    "Prefill to Cache Mapping" diagram: a prefill writes its keys and values
+    into the paged cache, tokens 64j .. 64j+63 of a sequence going to
+    block_table[b, j].  MATE msa_interface: without an explicit offset the
+    query chunk is aligned to the end of the keys (_normalize_qo_offset gives
+    kv_len - q_len), and a causal query i then uses keys up to i + offset
+    (_resolve_seqused_k).
+
 Readings where the pages are silent (each also listed in the design notes):
   * the KV cache is one shared physical pool [NB, Hk, 64, D]; block ids are
     global; table entries past ceil(L/64) are padding and never read;
@@ -42,7 +50,10 @@ Readings where the pages are silent (each also listed in the design notes):
   * block-sparse prefill: key j is visible to query i iff j <= i and
     mask[b, i // 64, j // 64] != 0 (a diagonal block that is off hides it);
   * a row with no visible key has out = 0 and lse = -inf;
-  * fp8 values are e4m3fn(byte) * scale, with the pool's per-tensor scale.
+  * fp8 values are e4m3fn(byte) * scale, with the pool's per-tensor scale;
+  * chunked prefill: a sequence holds kv_len keys in the paged cache, the last
+    q_len of which are the chunk's own tokens (appended at logical positions
+    kv_len - q_len + i); query i sees key j iff j <= kv_len - q_len + i.
 """
 from __future__ import annotations
 
@@ -259,3 +270,100 @@ def cu_seqlens_from_lengths(lengths: Sequence[int]) -> np.ndarray:
     cu = np.zeros(lens.shape[0] + 1, np.int64)
     cu[1:] = np.cumsum(lens)
     return cu.astype(np.int32)
+
+
+# --------------------------------------------------------------------------
+# Chunked prefill against a paged KV cache
+# --------------------------------------------------------------------------
+
+def append_kv(
+    k_new: np.ndarray,
+    v_new: np.ndarray,
+    k_pool: np.ndarray,
+    v_pool: np.ndarray,
+    block_table: np.ndarray,
+    cu_seqlens_q: np.ndarray,
+    kv_lens: np.ndarray,
+):
+    """Write a chunk's keys and values into the paged cache (storage bits, exact).
+
+    k_new, v_new [T, Hk, D] hold the chunk tokens of all sequences back to back
+    (cu_seqlens_q); sequence b's chunk is the last q_len_b = cu[b+1] - cu[b] of
+    its kv_lens[b] keys, so its token i goes to logical position
+    p = kv_lens[b] - q_len_b + i: row p % 64 of pool block block_table[b, p // 64]
+    (FlashMLA tensor-shape reference, section 4, "Prefill to Cache Mapping").
+    Returns new pools; the inputs are not modified."""
+    kp = np.array(k_pool, copy=True)
+    vp = np.array(v_pool, copy=True)
+    cu = np.asarray(cu_seqlens_q, dtype=np.int64)
+    for b in range(cu.shape[0] - 1):
+        ql = int(cu[b + 1] - cu[b])
+        first = int(kv_lens[b]) - ql
+        for i in range(ql):
+            p = first + i
+            if p < 0:
+                continue
+            blk = int(block_table[b, p // BLOCK])
+            kp[blk, :, p % BLOCK] = k_new[cu[b] + i]
+            vp[blk, :, p % BLOCK] = v_new[cu[b] + i]
+    return kp, vp
+
+
+def chunk_prefill(
+    q: np.ndarray,
+    k_pool: np.ndarray,
+    v_pool: np.ndarray,
+    block_table: np.ndarray,
+    cu_seqlens_q: np.ndarray,
+    kv_lens: np.ndarray,
+    scale: float,
+    *,
+    dtype: str = "f64",
+    rows: Optional[Sequence[int]] = None,
+    row_chunk: int = 256,
+):
+    """Causal attention of a chunk of new queries to a paged KV cache.
+
+    q [T, Hq, D] (chunks packed back to back, cu_seqlens_q [B + 1]); k_pool,
+    v_pool [NB, Hk, 64, D]; block_table [B, Nblk]; kv_lens [B] counts every
+    key of sequence b, the chunk's own tokens included.  With q_len_b =
+    cu[b+1] - cu[b] and offset o_b = kv_lens[b] - q_len_b (the chunk aligned to
+    the end of the keys), query i sees logical key j iff j < kv_lens[b] and
+    j <= o_b + i.  Keys are gathered from the pool exactly as in decode.
+    ``rows``: optional global query indices to evaluate (default all).
+    Returns (out [n, Hq, D], lse [n, Hq]) in float64."""
+    Q = widen(q, dtype)
+    T, Hq, D = Q.shape
+    Hk = k_pool.shape[1]
+    if Hq % Hk:
+        raise ValueError("Hq must be a multiple of Hk")
+    r = Hq // Hk
+    cu = np.asarray(cu_seqlens_q, dtype=np.int64)
+    B = cu.shape[0] - 1
+    if rows is None:
+        rows = np.arange(T)
+    rows = np.asarray(rows, dtype=np.int64)
+    out = np.zeros((rows.shape[0], Hq, D), np.float64)
+    lse = np.full((rows.shape[0], Hq), -np.inf, np.float64)
+    seq_of_row = np.searchsorted(cu, rows, side="right") - 1
+    for b in range(B):
+        sel = np.nonzero(seq_of_row == b)[0]
+        Lk = int(kv_lens[b])
+        if sel.size == 0 or Lk == 0:
+            continue
+        off = Lk - int(cu[b + 1] - cu[b])
+        j = np.arange(Lk)
+        for g in range(Hk):
+            K = widen(gather_kv_rows(k_pool, block_table, b, g, Lk), dtype)
+            V = widen(gather_kv_rows(v_pool, block_table, b, g, Lk), dtype)
+            heads = slice(g * r, (g + 1) * r)
+            for s0 in range(0, sel.size, row_chunk):
+                idx = sel[s0:s0 + row_chunk]
+                i = rows[idx] - cu[b]                      # local query index in the chunk
+                vis = j[None, :] <= (off + i)[:, None]     # bottom-right aligned causal bound
+                s = scale * (Q[rows[idx], heads, :] @ K.T)  # [n, r, Lk]
+                s = np.where(vis[:, None, :], s, -np.inf)
+                o, ls = _softmax_attend(s, V)
+                out[idx, heads] = o
+                lse[idx, heads] = ls
+    return out, lse

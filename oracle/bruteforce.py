@@ -79,3 +79,31 @@ def prefill(q, k, v, seq_lens, scale, *, k_rope=None, block_mask: Optional[objec
         outs.append(ob)
         lses.append(lb)
     return outs, lses
+
+
+def chunk_prefill(q, k, v, offsets, scale):
+    """Per-sequence lists: q[b] [n_b, Hq, D] (the chunk's queries), k[b], v[b]
+    [Lk_b, Hk, D] (every logical key of the sequence), offsets[b] = Lk_b - n_b.
+    Query i sees key j iff j < Lk_b and j <= offsets[b] + i."""
+    outs, lses = [], []
+    for b in range(len(q)):
+        qb, kb, vb = q[b], k[b], v[b]
+        n, Hq = qb.shape[0], qb.shape[1]
+        Lk, Hk = kb.shape[0], kb.shape[1]
+        ob = [[None] * Hq for _ in range(n)]
+        lb = [[None] * Hq for _ in range(n)]
+        for i in range(n):
+            for h in range(Hq):
+                g = (h * Hk) // Hq
+                keys, vals = [], []
+                for jj in range(Lk):
+                    if jj <= offsets[b] + i:
+                        keys.append([float(x) for x in kb[jj, g]])
+                        vals.append([float(x) for x in vb[jj, g]])
+                if not keys:
+                    ob[i][h], lb[i][h] = [0.0] * vb.shape[2], -math.inf
+                else:
+                    ob[i][h], lb[i][h] = _attend([float(x) for x in qb[i, h]], keys, vals, scale)
+        outs.append(ob)
+        lses.append(lb)
+    return outs, lses
