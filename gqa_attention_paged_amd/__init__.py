@@ -28,7 +28,8 @@ PLAN_MAGIC = 0x47514150
 
 C_FUNCTIONS = (
     "gqap_decode_plan", "gqap_decode_validate_host", "gqap_paged_decode", "gqap_debug_gather_kv",
-    "gqap_prefill_plan", "gqap_prefill", "gqap_last_error", "gqap_version",
+    "gqap_prefill_plan", "gqap_prefill", "gqap_chunk_plan", "gqap_chunk_validate_host", "gqap_append_kv",
+    "gqap_chunk_prefill", "gqap_last_error", "gqap_version",
 )
 
 
@@ -83,6 +84,28 @@ class PrefillPlan(ctypes.Structure):
     ]
 
 
+class ChunkDesc(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("block_size", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
+        ("num_pool_blocks", ctypes.c_int32), ("total_q_tokens", ctypes.c_int32), ("max_q_len", ctypes.c_int32),
+        ("max_kv_len", ctypes.c_int32), ("dtype", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+        ("q_stride_token", ctypes.c_int64), ("q_stride_head", ctypes.c_int64),
+        ("new_stride_token", ctypes.c_int64), ("new_stride_head", ctypes.c_int64),
+        ("out_stride_token", ctypes.c_int64), ("out_stride_head", ctypes.c_int64),
+        ("kv_stride_block", ctypes.c_int64), ("kv_stride_head", ctypes.c_int64),
+        ("block_table_stride", ctypes.c_int64),
+    ]
+
+
+class ChunkPlan(ctypes.Structure):
+    _fields_ = [
+        ("desc", ChunkDesc), ("ratio", ctypes.c_int32), ("q_tiles", ctypes.c_int32),
+        ("q_tile_rows", ctypes.c_int32), ("kernel", ctypes.c_int32), ("workspace_bytes", ctypes.c_uint64),
+        ("magic", ctypes.c_uint32), ("reserved", ctypes.c_uint32),
+    ]
+
+
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built: run `python __graft_entry__.py` (build()) first")
@@ -102,6 +125,14 @@ def _load() -> ctypes.CDLL:
     lib.gqap_prefill_plan.restype = st
     lib.gqap_prefill.argtypes = [ctypes.POINTER(PrefillPlan), vp, vp, vp, vp, vp, vp, f32, vp, vp, vp, u64, vp]
     lib.gqap_prefill.restype = st
+    lib.gqap_chunk_plan.argtypes = [ctypes.POINTER(ChunkDesc), ctypes.POINTER(ChunkPlan)]
+    lib.gqap_chunk_plan.restype = st
+    lib.gqap_chunk_validate_host.argtypes = [ctypes.POINTER(ChunkPlan), vp, vp, vp]
+    lib.gqap_chunk_validate_host.restype = st
+    lib.gqap_append_kv.argtypes = [ctypes.POINTER(ChunkPlan), vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.gqap_append_kv.restype = st
+    lib.gqap_chunk_prefill.argtypes = [ctypes.POINTER(ChunkPlan), vp, vp, vp, vp, vp, vp, f32, vp, vp, vp, u64, vp]
+    lib.gqap_chunk_prefill.restype = st
     lib.gqap_last_error.argtypes = []
     lib.gqap_last_error.restype = ctypes.c_char_p
     lib.gqap_version.argtypes = []
@@ -194,6 +225,36 @@ def gqap_prefill(plan: PrefillPlan, q, k, v, k_rope, cu_seqlens, block_mask, sca
                              _stream(stream)))
 
 
+def gqap_chunk_plan(desc: ChunkDesc) -> ChunkPlan:
+    plan = ChunkPlan()
+    _check(_lib.gqap_chunk_plan(ctypes.byref(desc), ctypes.byref(plan)))
+    return plan
+
+
+def gqap_chunk_validate_host(plan: ChunkPlan, block_table_host, cu_seqlens_q_host, kv_lens_host) -> None:
+    """Host arrays (numpy int32, C-contiguous with the plan's row stride)."""
+    import numpy as np
+    bt = np.ascontiguousarray(block_table_host, dtype=np.int32)
+    cu = np.ascontiguousarray(cu_seqlens_q_host, dtype=np.int32)
+    kl = np.ascontiguousarray(kv_lens_host, dtype=np.int32)
+    _check(_lib.gqap_chunk_validate_host(ctypes.byref(plan), bt.ctypes.data, cu.ctypes.data, kl.ctypes.data))
+
+
+def gqap_append_kv(plan: ChunkPlan, k_new, v_new, k_pool, v_pool, block_table, cu_seqlens_q, kv_lens,
+                   stream=None) -> None:
+    _check(_lib.gqap_append_kv(ctypes.byref(plan), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool),
+                               _ptr(block_table), _ptr(cu_seqlens_q), _ptr(kv_lens), _stream(stream)))
+
+
+def gqap_chunk_prefill(plan: ChunkPlan, q, k_pool, v_pool, block_table, cu_seqlens_q, kv_lens, scale: float,
+                       out, lse=None, workspace=None, workspace_bytes: Optional[int] = None, stream=None) -> None:
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.gqap_chunk_prefill(ctypes.byref(plan), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
+                                   _ptr(cu_seqlens_q), _ptr(kv_lens), scale, _ptr(out), _ptr(lse),
+                                   _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
 # ------------------------------------------------------------------ descriptors from tensors
 
 _TORCH_DTYPE_TAG = {"torch.float32": F32, "torch.bfloat16": BF16, "torch.float8_e4m3fn": FP8_E4M3FN,
@@ -253,4 +314,28 @@ def prefill_desc(q, k, v, k_rope, batch: int, max_seq_len: int, block_mask=None,
     d.kr_stride_token = 0 if k_rope is None else k_rope.stride(0)
     d.out_stride_token, d.out_stride_head = out.stride(0), out.stride(1)
     d.num_cus = num_cus
+    return d
+
+
+def chunk_desc(q, k_new, k_pool, block_table, batch: int, max_q_len: int, max_kv_len: int,
+               out=None) -> ChunkDesc:
+    """Descriptor for q [T, Hq, D], k_new / v_new [T, Hk, D], pool [NB, Hk, 64, D],
+    block_table [B, Nblk]."""
+    T, Hq, D = q.shape
+    NB, Hk, blk, _ = k_pool.shape
+    out = q if out is None else out
+    d = ChunkDesc()
+    d.batch, d.num_q_heads, d.num_kv_heads, d.head_dim = batch, Hq, Hk, D
+    d.block_size = blk
+    d.max_blocks_per_seq = block_table.shape[1]
+    d.num_pool_blocks = NB
+    d.total_q_tokens = T
+    d.max_q_len = max_q_len
+    d.max_kv_len = max_kv_len
+    d.dtype = dtype_tag(q)
+    d.q_stride_token, d.q_stride_head = q.stride(0), q.stride(1)
+    d.new_stride_token, d.new_stride_head = k_new.stride(0), k_new.stride(1)
+    d.out_stride_token, d.out_stride_head = out.stride(0), out.stride(1)
+    d.kv_stride_block, d.kv_stride_head = k_pool.stride(0), k_pool.stride(1)
+    d.block_table_stride = block_table.stride(0)
     return d

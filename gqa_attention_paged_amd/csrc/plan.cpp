@@ -202,6 +202,96 @@ extern "C" gqap_status gqap_prefill_plan(const gqap_prefill_desc_t* desc, gqap_p
   return GQAP_OK;
 }
 
+// Chunked prefill against the paged cache (FlashMLA tensor-shape reference,
+// section 4: a prefill with a KV cache writes into 64-row pages).  The same
+// shape rules as decode for the cache, ragged token-major rows for the chunk.
+extern "C" gqap_status gqap_chunk_plan(const gqap_chunk_desc_t* desc, gqap_chunk_plan_t* plan) {
+  if (!desc || !plan) return fail(GQAP_ERR_INVALID_ARGUMENT, "null desc or plan");
+  std::memset(plan, 0, sizeof(*plan));
+  const gqap_chunk_desc_t& d = *desc;
+  if (d.batch < 0) return fail(GQAP_ERR_INVALID_ARGUMENT, "batch must be >= 0");
+  if (d.num_q_heads <= 0 || d.num_kv_heads <= 0)
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "head counts must be positive (Hq=%d, Hk=%d)", d.num_q_heads,
+                d.num_kv_heads);
+  if (d.num_q_heads % d.num_kv_heads)
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "Hq (%d) must be a multiple of Hk (%d)", d.num_q_heads, d.num_kv_heads);
+  if (d.block_size != kBlock) return fail(GQAP_ERR_UNSUPPORTED, "block_size must be %d (got %d)", kBlock, d.block_size);
+  if (d.head_dim != 128) return fail(GQAP_ERR_UNSUPPORTED, "head_dim must be 128 (got %d)", d.head_dim);
+  if (d.dtype != GQAP_BF16) return fail(GQAP_ERR_DTYPE, "chunked prefill takes bf16 tensors (got dtype %d)", d.dtype);
+  if (d.max_blocks_per_seq <= 0)
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "max_blocks_per_seq must be positive (got %d)", d.max_blocks_per_seq);
+  if (d.num_pool_blocks <= 0)
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "num_pool_blocks must be positive (got %d)", d.num_pool_blocks);
+  if (d.total_q_tokens < 0 || d.max_q_len < 0 || d.max_kv_len < 0)
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "total_q_tokens, max_q_len and max_kv_len must be >= 0");
+  if ((int64_t)d.max_kv_len > (int64_t)d.max_blocks_per_seq * kBlock)
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "max_kv_len %d exceeds Nblk*64 = %lld", d.max_kv_len,
+                (long long)d.max_blocks_per_seq * kBlock);
+  if (d.max_q_len > d.max_kv_len)
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "max_q_len %d exceeds max_kv_len %d (a chunk's tokens are among its keys)",
+                d.max_q_len, d.max_kv_len);
+  const int64_t D = d.head_dim, Hq = d.num_q_heads, Hk = d.num_kv_heads;
+  if (d.q_stride_head < D || d.q_stride_token < d.q_stride_head * Hq)
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "q strides overlap");
+  if (d.new_stride_head < D || d.new_stride_token < d.new_stride_head * Hk)
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "k_new/v_new strides overlap");
+  if (d.out_stride_head < D || d.out_stride_token < d.out_stride_head * Hq)
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "out strides overlap");
+  if (d.kv_stride_head < D * kBlock)
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "kv_stride_head %lld < 64*D: a (block, head) slab must be a contiguous 64 x D tile",
+                (long long)d.kv_stride_head);
+  if (d.kv_stride_block < d.kv_stride_head * Hk)
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "kv_stride_block %lld < Hk * kv_stride_head", (long long)d.kv_stride_block);
+  if (d.block_table_stride < d.max_blocks_per_seq)
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "block_table_stride %lld < Nblk %d", (long long)d.block_table_stride,
+                d.max_blocks_per_seq);
+  const int64_t strides[] = {d.q_stride_token, d.q_stride_head, d.new_stride_token, d.new_stride_head,
+                             d.out_stride_token, d.out_stride_head, d.kv_stride_block, d.kv_stride_head};
+  for (int64_t st : strides)
+    if (!aligned16(st, 2)) return fail(GQAP_ERR_INVALID_ARGUMENT, "strides must keep rows 16-byte aligned");
+  plan->desc = d;
+  plan->ratio = d.num_q_heads / d.num_kv_heads;
+  plan->q_tile_rows = 128;
+  plan->q_tiles = (int32_t)ceil_div(d.max_q_len, plan->q_tile_rows);
+  // One workgroup of 256 work-items per (head, sequence, query tile) slot;
+  // the launch must stay under 2^32 work-items.
+  if ((int64_t)d.num_q_heads * d.batch * plan->q_tiles >= ((int64_t)1 << 24))
+    return fail(GQAP_ERR_UNSUPPORTED, "Hq * batch * ceil(max_q_len/128) = %lld workgroups exceeds 2^24",
+                (long long)d.num_q_heads * d.batch * plan->q_tiles);
+  plan->kernel = 1;
+  plan->workspace_bytes = 0;
+  plan->magic = GQAP_PLAN_MAGIC;
+  return GQAP_OK;
+}
+
+extern "C" gqap_status gqap_chunk_validate_host(const gqap_chunk_plan_t* plan, const int32_t* block_table_host,
+                                                const int32_t* cu_seqlens_q_host, const int32_t* kv_lens_host) {
+  if (!plan || plan->magic != GQAP_PLAN_MAGIC) return fail(GQAP_ERR_INVALID_ARGUMENT, "invalid plan");
+  const gqap_chunk_desc_t& d = plan->desc;
+  if (!cu_seqlens_q_host || (d.batch > 0 && (!block_table_host || !kv_lens_host)))
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "null host metadata");
+  if (cu_seqlens_q_host[0] != 0) return fail(GQAP_ERR_INVALID_ARGUMENT, "cu_seqlens_q[0] = %d, not 0", cu_seqlens_q_host[0]);
+  for (int b = 0; b < d.batch; ++b) {
+    const int64_t ql = (int64_t)cu_seqlens_q_host[b + 1] - cu_seqlens_q_host[b];
+    const int64_t kl = kv_lens_host[b];
+    if (ql < 0 || cu_seqlens_q_host[b + 1] > d.total_q_tokens)
+      return fail(GQAP_ERR_INVALID_ARGUMENT, "cu_seqlens_q[%d..%d] = %d..%d decreases or passes T = %d", b, b + 1,
+                  cu_seqlens_q_host[b], cu_seqlens_q_host[b + 1], d.total_q_tokens);
+    if (ql > d.max_q_len)
+      return fail(GQAP_ERR_INVALID_ARGUMENT, "chunk %d has %lld tokens > max_q_len %d", b, (long long)ql, d.max_q_len);
+    if (kl < ql || kl > d.max_kv_len)
+      return fail(GQAP_ERR_INVALID_ARGUMENT, "kv_lens[%d] = %lld outside [q_len %lld, max_kv_len %d]", b,
+                  (long long)kl, (long long)ql, d.max_kv_len);
+    for (int64_t j = 0; j < ceil_div(kl, kBlock); ++j) {
+      const int64_t id = block_table_host[(int64_t)b * d.block_table_stride + j];
+      if (id < 0 || id >= d.num_pool_blocks)
+        return fail(GQAP_ERR_INVALID_ARGUMENT, "block_table[%d, %lld] = %lld outside the pool [0, %d)", b,
+                    (long long)j, (long long)id, d.num_pool_blocks);
+    }
+  }
+  return GQAP_OK;
+}
+
 extern "C" const char* gqap_last_error(void) { return last_error_slot().c_str(); }
 
 extern "C" const char* gqap_version(void) { return "gqap 0.1.0 (gfx950)"; }

@@ -43,6 +43,14 @@ struct PrefillArgs {
   int64_t q_st, q_sh, k_st, k_sh, v_st, v_sh, kr_st, o_st, o_sh;
   int32_t B, Hq, Hk, ratio, q_tiles, mask_nb, max_len;
   float scale_log2;  // scale * log2(e)
+  // Chunked prefill against the paged cache: k and v are the pools, the
+  // query rows of sequence b are the last of its kvlens[b] keys.
+  const int32_t* kvlens;
+  const int32_t* bt;
+  int64_t bt_st;      // block_table row stride (int32 elements)
+  int64_t kv_sb;      // elements between pool blocks
+  int64_t kv_sh;      // elements between heads of a block
+  int32_t max_kv;     // capacity: keys per sequence
 };
 
 namespace dev {
@@ -78,7 +86,7 @@ __device__ __forceinline__ int vswz256(int row, int c) {
 
 using namespace dev;
 
-template <int DR>
+template <int DR, bool PAGED>
 __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
   constexpr int DN = 128;                     // per-head key width
   constexpr int DV = 128;                     // value / output width
@@ -132,7 +140,15 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
     qt = a.q_tiles - 1 - pair / a.B;
   }
   const int c0 = a.cu[b];
-  const int L = min(a.cu[b + 1] - c0, a.max_len);  // capacity from the plan
+  const int L = min(a.cu[b + 1] - c0, a.max_len);  // query rows (capacity from the plan)
+  // Keys: the sequence itself, or with PAGED its Lk cached keys, the query
+  // rows being the last L of them (offset off = Lk - L), so query i sees key
+  // j iff j <= off + i.
+  int Lk = L, off = 0;
+  if constexpr (PAGED) {
+    Lk = min(a.kvlens[b], a.max_kv);
+    off = Lk - L;
+  }
   const int q0 = qt * 128;
   if (q0 >= L) return;
   const int g = h / a.ratio;
@@ -144,6 +160,7 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
   const int qrow = r0 + l32;                 // this lane's query row
   const bool wave_rows = r0 < L;
   const int rlast = min(L, r0 + 32) - 1;     // last valid row of the wave
+  const int klast = off + rlast;             // last key visible to the wave
 
   // The wave's queries as the B operand: lane (query l32, half hh) holds
   // d = 16 s + 8 hh .. +7 for k-step s (s < KSN: nope part, then rope).
@@ -158,8 +175,8 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
     }
   }
 
-  // Key tiles this workgroup must visit: keys < min(L, q0 + 128).
-  const int nkt = (min(L, q0 + 128) + 63) >> 6;
+  // Key tiles this workgroup must visit: keys < min(Lk, off + q0 + 128).
+  const int nkt = max(0, min(Lk, off + q0 + 128) + 63) >> 6;
   const int qb0 = q0 >> 6;                   // the workgroup's two query blocks
   const int qb1 = min(qb0 + 1, (L - 1) >> 6);
   const int wqb = r0 >> 6;                   // this wave's query block
@@ -199,7 +216,7 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
   // Called only for the tile just returned by first_needed / next_tile, so
   // see_word is the word holding kt.
   auto wave_sees = [&](int kt) {
-    if (!wave_rows || kt * 64 > rlast) return false;
+    if (!wave_rows || kt * 64 > klast) return false;
     return !a.mask || ((see_word >> (kt & 63)) & 1);
   };
   // Tile loads go straight to LDS (global_load_lds_dwordx4): wave w's i-th
@@ -226,8 +243,35 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
   auto dma = [&](const unsigned char* gp, unsigned char* lp) {
     __builtin_amdgcn_global_load_lds((const void*)gp, (GQAP_LDS void*)lp, 16, 0, 0);
   };
-  // Rows past the end of the sequence read row L-1 instead: every key past L
-  // is causally hidden from every query of the sequence, so its score is
+  // First byte of key tile kt of K / V.  With PAGED a tile is one page: the
+  // 64 x D slab of pool block block_table[b, kt] for KV head g (FlashMLA
+  // tensor-shape reference, section 1: tokens 64j .. 64j+63 live in
+  // block_table[b, j]).  The table entries are read 64 tiles at a time, one
+  // per lane, and picked out with readlane.
+  int32_t bt_word = 0;
+  int bt_idx = -1;
+  auto page_of = [&](int kt) {
+    if ((kt >> 6) != bt_idx) {
+      bt_idx = kt >> 6;
+      const int j = bt_idx * 64 + lane;
+      bt_word = j < nkt ? a.bt[(int64_t)b * a.bt_st + j] : 0;
+    }
+    return __builtin_amdgcn_readlane(bt_word, kt & 63);
+  };
+  auto tile_k = [&](int kt) -> const unsigned char* {
+    if constexpr (PAGED)
+      return (const unsigned char*)a.k + ((int64_t)page_of(kt) * a.kv_sb + (int64_t)g * a.kv_sh) * 2;
+    else
+      return kg + (int64_t)kt * 64 * kstr;
+  };
+  auto tile_v = [&](int kt) -> const unsigned char* {
+    if constexpr (PAGED)
+      return (const unsigned char*)a.v + ((int64_t)page_of(kt) * a.kv_sb + (int64_t)g * a.kv_sh) * 2;
+    else
+      return vg + (int64_t)kt * 64 * vstr;
+  };
+  // Rows past the last key read row Lk-1 instead: every key past Lk is
+  // causally hidden from every query of the sequence, so its score is
   // replaced by -inf and its probability is exactly 0.
   auto load_tile = [&](int kt, auto bufc) {
     constexpr int BUF = decltype(bufc)::value;
@@ -235,10 +279,10 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
     unsigned char* rd = BUF ? rbuf1 : rbuf0;
     unsigned char* vd = BUF ? vbuf1 : vbuf0;
     const int key0 = kt * 64;
-    if (key0 + 64 <= L) {  // whole tile inside the sequence
-      const unsigned char* kt_k = kg + key0 * kstr;
-      const unsigned char* kt_v = vg + key0 * vstr;
-      const unsigned char* kt_r = DR ? rg + key0 * rstr : nullptr;
+    const unsigned char* kt_k = tile_k(kt);
+    const unsigned char* kt_v = tile_v(kt);
+    const unsigned char* kt_r = DR ? rg + key0 * rstr : nullptr;
+    if (key0 + 64 <= Lk) {  // whole tile inside the keys
 #pragma unroll
       for (int i = 0; i < KLD; ++i) dma(kt_k + 16 * i * kstr + koff, kd + 4096 * i + wseg);
 #pragma unroll
@@ -248,13 +292,13 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
     } else {
 #pragma unroll
       for (int i = 0; i < KLD; ++i)
-        dma(kg + (int64_t)min(key0 + row0 + 16 * i, L - 1) * kstr + 16 * kch, kd + 4096 * i + wseg);
+        dma(kt_k + (int64_t)min(row0 + 16 * i, Lk - 1 - key0) * kstr + 16 * kch, kd + 4096 * i + wseg);
 #pragma unroll
       for (int i = 0; i < RLD; ++i)
-        dma(rg + (int64_t)min(key0 + row0r + 32 * i, L - 1) * rstr + 16 * rch, rd + 4096 * i + wseg);
+        dma(kt_r + (int64_t)min(row0r + 32 * i, Lk - 1 - key0) * rstr + 16 * rch, rd + 4096 * i + wseg);
 #pragma unroll
       for (int i = 0; i < VLD; ++i)
-        dma(vg + (int64_t)min(key0 + row0 + 16 * i, L - 1) * vstr + 16 * vch, vd + 4096 * i + wseg);
+        dma(kt_v + (int64_t)min(row0 + 16 * i, Lk - 1 - key0) * vstr + 16 * vch, vd + 4096 * i + wseg);
     }
     // Keep the loads at the top of the tile so they overlap its math.
     __builtin_amdgcn_sched_barrier(0);
@@ -309,8 +353,8 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
     unsigned char* rd = BUF ? rbuf0 : rbuf1;
     unsigned char* vd = BUF ? vbuf0 : vbuf1;
     constexpr int NLD = KLD + RLD + VLD;
-    const unsigned char* kt_k = kg + kn * 64 * kstr;
-    const unsigned char* kt_v = vg + kn * 64 * vstr;
+    const unsigned char* kt_k = WL ? tile_k(kn) : nullptr;
+    const unsigned char* kt_v = WL ? tile_v(kn) : nullptr;
     const unsigned char* kt_r = DR ? rg + kn * 64 * rstr : nullptr;
     auto issue_load = [&](int i) {
       if (i < KLD)
@@ -349,8 +393,8 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
       if (WL && idx < NLD) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
     // Causal mask by select (only on tiles reaching past the wave's first row).
-    if (kt * 64 + 63 > r0) {
-      const int rel = qrow - kt * 64 - hh * 4;  // key offset + hh*4 must stay <= rel
+    if (kt * 64 + 63 > off + r0) {
+      const int rel = off + qrow - kt * 64 - hh * 4;  // key offset + hh*4 must stay <= rel
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -445,7 +489,7 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
   // lies wholly inside the sequence, else up front.
   auto step = [&](int kt, bool sees, int kn, auto bufc, auto nbufc) {
     const bool more = kn < nkt;
-    const bool inside = more && kn * 64 + 64 <= L;
+    const bool inside = more && kn * 64 + 64 <= Lk;
     if (sees && inside) {
       compute_tile(kt, bufc, WL1{}, kn);
     } else {
@@ -493,6 +537,47 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
     }
   if (a.lse && hh == 0)
     a.lse[(int64_t)(c0 + qrow) * a.Hq + h] = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
+}
+
+// Append a chunk's keys and values to the paged cache (FlashMLA tensor-shape
+// reference, section 4, "Prefill to Cache Mapping": token p of a sequence is
+// row p % 64 of block block_table[b, p / 64]).  The chunk of sequence b is
+// the last q_len of its kv_len keys, so its token i lands at p = kv_len -
+// q_len + i.  One thread per 16-byte piece of a (token, KV head) row.
+struct AppendArgs {
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  uint16_t* k_pool;
+  uint16_t* v_pool;
+  const int32_t* bt;
+  const int32_t* cu;
+  const int32_t* kvlens;
+  int64_t new_st, new_sh, kv_sb, kv_sh, bt_st;
+  int64_t rows;     // T * Hk
+  int32_t B, Hk, max_kv;
+};
+
+__global__ __launch_bounds__(256) void append_kv(AppendArgs a) {
+  constexpr int D = 128;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = gid >> 4;
+  const int piece = (int)(gid & 15);
+  if (row >= a.rows) return;
+  const int t = (int)(row / a.Hk), g = (int)(row - (int64_t)t * a.Hk);
+  if (t >= a.cu[a.B]) return;  // rows past the last chunk
+  int lo = 0, hi = a.B;        // the sequence b with cu[b] <= t < cu[b + 1]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (a.cu[mid] <= t) lo = mid; else hi = mid;
+  }
+  const int b = lo;
+  const int p = a.kvlens[b] - (a.cu[b + 1] - a.cu[b]) + (t - a.cu[b]);
+  if (p < 0 || p >= a.max_kv) return;  // outside the keys the plan covers
+  const int64_t page = a.bt[(int64_t)b * a.bt_st + (p >> 6)];
+  const int64_t dst = page * a.kv_sb + (int64_t)g * a.kv_sh + (int64_t)(p & 63) * D + 8 * piece;
+  const int64_t src = (int64_t)t * a.new_st + (int64_t)g * a.new_sh + 8 * piece;
+  dev::store16(a.k_pool + dst, dev::load16(a.k_new + src));
+  dev::store16(a.v_pool + dst, dev::load16(a.v_new + src));
 }
 
 static bool misaligned16(const void* p) { return ((uintptr_t)p) & 15; }
@@ -547,10 +632,102 @@ extern "C" gqap_status gqap_prefill(const gqap_prefill_plan_t* plan, const void*
   const dim3 grid((unsigned)d.num_q_heads * (unsigned)d.batch * (unsigned)plan->q_tiles);
   hipStream_t st = (hipStream_t)stream;
   if (d.head_dim_rope == 64)
-    hipLaunchKernelGGL(prefill_fwd<64>, grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((prefill_fwd<64, false>), grid, dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL(prefill_fwd<0>, grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((prefill_fwd<0, false>), grid, dim3(256), 0, st, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(GQAP_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
+  return GQAP_OK;
+}
+
+extern "C" gqap_status gqap_append_kv(const gqap_chunk_plan_t* plan, const void* k_new, const void* v_new,
+                                      void* k_pool, void* v_pool, const int32_t* block_table,
+                                      const int32_t* cu_seqlens_q, const int32_t* kv_lens, void* stream) {
+  if (!plan || plan->magic != GQAP_PLAN_MAGIC) return fail(GQAP_ERR_INVALID_ARGUMENT, "invalid chunk plan");
+  const gqap_chunk_desc_t& d = plan->desc;
+  if (d.batch == 0 || d.total_q_tokens == 0) return GQAP_OK;
+  if (!k_new || !v_new || !k_pool || !v_pool || !block_table || !cu_seqlens_q || !kv_lens)
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "null device pointer");
+  if (misaligned16(k_new) || misaligned16(v_new) || misaligned16(k_pool) || misaligned16(v_pool) ||
+      ((uintptr_t)block_table & 3) || ((uintptr_t)cu_seqlens_q & 3) || ((uintptr_t)kv_lens & 3))
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "device pointers must be 16-byte aligned (index arrays 4-byte)");
+  AppendArgs a{};
+  a.k_new = (const uint16_t*)k_new;
+  a.v_new = (const uint16_t*)v_new;
+  a.k_pool = (uint16_t*)k_pool;
+  a.v_pool = (uint16_t*)v_pool;
+  a.bt = block_table;
+  a.cu = cu_seqlens_q;
+  a.kvlens = kv_lens;
+  a.new_st = d.new_stride_token;
+  a.new_sh = d.new_stride_head;
+  a.kv_sb = d.kv_stride_block;
+  a.kv_sh = d.kv_stride_head;
+  a.bt_st = d.block_table_stride;
+  a.rows = (int64_t)d.total_q_tokens * d.num_kv_heads;
+  a.B = d.batch;
+  a.Hk = d.num_kv_heads;
+  a.max_kv = d.max_kv_len;
+  const int64_t blocks = (a.rows * 16 + 255) / 256;
+  if (blocks >= ((int64_t)1 << 31)) return fail(GQAP_ERR_UNSUPPORTED, "chunk too large for one append launch");
+  hipLaunchKernelGGL(append_kv, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(GQAP_ERR_HIP, "append launch: %s", hipGetErrorString(e));
+  return GQAP_OK;
+}
+
+extern "C" gqap_status gqap_chunk_prefill(const gqap_chunk_plan_t* plan, const void* q, const void* k_pool,
+                                          const void* v_pool, const int32_t* block_table,
+                                          const int32_t* cu_seqlens_q, const int32_t* kv_lens, float scale,
+                                          void* out, float* lse, void* workspace, uint64_t workspace_bytes,
+                                          void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  if (!plan || plan->magic != GQAP_PLAN_MAGIC) return fail(GQAP_ERR_INVALID_ARGUMENT, "invalid chunk plan");
+  const gqap_chunk_desc_t& d = plan->desc;
+  if (d.batch == 0 || plan->q_tiles == 0) return GQAP_OK;
+  if (!q || !k_pool || !v_pool || !block_table || !cu_seqlens_q || !kv_lens || !out)
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "null device pointer");
+  if (misaligned16(q) || misaligned16(k_pool) || misaligned16(v_pool) || misaligned16(out) ||
+      ((uintptr_t)block_table & 3) || ((uintptr_t)cu_seqlens_q & 3) || ((uintptr_t)kv_lens & 3) ||
+      (lse && ((uintptr_t)lse & 3)))
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "device pointers must be 16-byte aligned (index arrays, lse 4-byte)");
+  if (!std::isfinite(scale)) return fail(GQAP_ERR_INVALID_ARGUMENT, "scale must be finite");
+  PrefillArgs a{};
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k_pool;
+  a.v = (const uint16_t*)v_pool;
+  a.kr = nullptr;
+  a.cu = cu_seqlens_q;
+  a.mask = nullptr;
+  a.out = (uint16_t*)out;
+  a.lse = lse;
+  a.q_st = d.q_stride_token;
+  a.q_sh = d.q_stride_head;
+  a.k_st = d.head_dim;  // rows of a page slab are contiguous
+  a.k_sh = 0;
+  a.v_st = d.head_dim;
+  a.v_sh = 0;
+  a.kr_st = 0;
+  a.o_st = d.out_stride_token;
+  a.o_sh = d.out_stride_head;
+  a.B = d.batch;
+  a.Hq = d.num_q_heads;
+  a.Hk = d.num_kv_heads;
+  a.ratio = plan->ratio;
+  a.q_tiles = plan->q_tiles;
+  a.mask_nb = 0;
+  a.max_len = d.max_q_len;
+  a.scale_log2 = scale * dev::kLog2e;
+  a.kvlens = kv_lens;
+  a.bt = block_table;
+  a.bt_st = d.block_table_stride;
+  a.kv_sb = d.kv_stride_block;
+  a.kv_sh = d.kv_stride_head;
+  a.max_kv = d.max_kv_len;
+  const dim3 grid((unsigned)d.num_q_heads * (unsigned)d.batch * (unsigned)plan->q_tiles);
+  hipLaunchKernelGGL((prefill_fwd<0, true>), grid, dim3(256), 0, (hipStream_t)stream, a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(GQAP_ERR_HIP, "chunk prefill launch: %s", hipGetErrorString(e));
   return GQAP_OK;
 }

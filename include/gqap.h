@@ -269,6 +269,113 @@ gqap_status gqap_prefill(const gqap_prefill_plan_t* plan,
                          void* workspace, uint64_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* Chunked prefill against a paged KV cache                                  */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * A chunk of new tokens of every sequence attends to the keys already in the
+ * paged cache and to itself.  A prefill with a KV cache writes the chunk's
+ * keys and values into the cache, tokens 64j .. 64j+63 of a sequence going to
+ * block_table[b, j] (FlashMLA tensor-shape reference, section 4, and its
+ * "Prefill to Cache Mapping"); the chunk is aligned to the end of the keys,
+ * so with kv_len keys in all, the last q_len of them the chunk's own, query i
+ * uses the keys up to kv_len - q_len + i (MATE msa_interface,
+ * _normalize_qo_offset and _resolve_seqused_k).
+ *
+ * Shapes (bf16 tensors, D = 128 contiguous):
+ *   q             [T, Hq, D]       strides q_stride_token, q_stride_head
+ *   k_new, v_new  [T, Hk, D]       the chunk's keys and values; strides
+ *                                  new_stride_token, new_stride_head
+ *   k_pool,v_pool [NB, Hk, 64, D]  strides kv_stride_block, kv_stride_head;
+ *                                  each (block, head) 64 x D slab contiguous
+ *   block_table   [B, Nblk] int32  row stride block_table_stride; entries
+ *                                  j < ceil(kv_lens[b] / 64) are used
+ *   cu_seqlens_q  [B + 1] int32    chunk b is rows cu[b] .. cu[b+1]-1 of q,
+ *                                  k_new, v_new and out; cu[B] <= T
+ *   kv_lens       [B] int32        keys of sequence b with its chunk included:
+ *                                  q_len_b = cu[b+1] - cu[b] <= kv_lens[b] <=
+ *                                  max_kv_len, q_len_b <= max_q_len
+ *   out           [T, Hq, D]       strides out_stride_*
+ *   lse           [T, Hq] float32  optional, contiguous, natural log
+ * Query i of chunk b sees key j iff j <= kv_lens[b] - q_len_b + i; query head
+ * h reads KV head h / (Hq / Hk).
+ */
+typedef struct gqap_chunk_desc_t {
+  int32_t batch;               /* B >= 0 */
+  int32_t num_q_heads;         /* Hq > 0 */
+  int32_t num_kv_heads;        /* Hk > 0, Hq % Hk == 0 */
+  int32_t head_dim;            /* D: 128 */
+  int32_t block_size;          /* must be 64 */
+  int32_t max_blocks_per_seq;  /* Nblk >= ceil(max_kv_len / 64) */
+  int32_t num_pool_blocks;     /* NB >= 1 */
+  int32_t total_q_tokens;      /* T: rows of q, k_new, v_new, out */
+  int32_t max_q_len;           /* capacity the grid is sized for */
+  int32_t max_kv_len;          /* capacity; <= Nblk * 64 */
+  int32_t dtype;               /* GQAP_BF16 */
+  int32_t reserved0;
+  int64_t q_stride_token, q_stride_head;
+  int64_t new_stride_token, new_stride_head;
+  int64_t out_stride_token, out_stride_head;
+  int64_t kv_stride_block;     /* elements between pool blocks */
+  int64_t kv_stride_head;      /* elements between heads of a block, >= 64*D */
+  int64_t block_table_stride;  /* int32 elements between rows, >= Nblk */
+} gqap_chunk_desc_t;
+
+typedef struct gqap_chunk_plan_t {
+  gqap_chunk_desc_t desc;
+  int32_t ratio;               /* Hq / Hk */
+  int32_t q_tiles;             /* ceil(max_q_len / q_tile_rows) */
+  int32_t q_tile_rows;
+  int32_t kernel;
+  uint64_t workspace_bytes;    /* 0 in this version */
+  uint32_t magic;
+  uint32_t reserved;
+} gqap_chunk_plan_t;
+
+/*
+ * Validate a chunked-prefill request.  Pure host code.  Errors:
+ * INVALID_ARGUMENT (sizes, strides that overlap or break 16-byte alignment,
+ * Hq % Hk, max_kv_len > Nblk * 64, max_q_len > max_kv_len), DTYPE (not bf16),
+ * UNSUPPORTED (block_size != 64, D != 128, Hq * batch * ceil(max_q_len / 128)
+ * >= 2^24 workgroups).
+ */
+gqap_status gqap_chunk_plan(const gqap_chunk_desc_t* desc, gqap_chunk_plan_t* plan);
+
+/*
+ * Optional deep check of host copies of the metadata: cu_seqlens_q starts at
+ * 0, never decreases and ends at most at T; 0 <= q_len_b <= min(kv_lens[b],
+ * max_q_len); kv_lens[b] <= max_kv_len; every used block_table entry lies in
+ * [0, NB).  Errors: INVALID_ARGUMENT naming the first offending entry.
+ */
+gqap_status gqap_chunk_validate_host(const gqap_chunk_plan_t* plan, const int32_t* block_table_host,
+                                     const int32_t* cu_seqlens_q_host, const int32_t* kv_lens_host);
+
+/*
+ * Write the chunk's keys and values into the paged cache: token i of chunk b
+ * goes to logical position p = kv_lens[b] - q_len_b + i, i.e. row p % 64 of
+ * pool block block_table[b, p / 64], for every KV head.  Nothing else in the
+ * pools changes.  Asynchronous on `stream`; 16-byte aligned pointers.
+ */
+gqap_status gqap_append_kv(const gqap_chunk_plan_t* plan, const void* k_new, const void* v_new,
+                           void* k_pool, void* v_pool, const int32_t* block_table,
+                           const int32_t* cu_seqlens_q, const int32_t* kv_lens, void* stream);
+
+/*
+ * Attention of each chunk to its sequence's cached keys (the chunk's own
+ * included, so gqap_append_kv runs first).  Only key rows j < kv_lens[b] are
+ * used; a key tile that runs past kv_lens[b] repeats row kv_lens[b] - 1,
+ * whose probability is then exactly 0.  A query with no visible key gets
+ * out = 0 and lse = -inf.  workspace may be NULL when plan->workspace_bytes
+ * == 0.  Asynchronous on `stream`; 16-byte aligned pointers (lse, cu_seqlens_q
+ * and kv_lens 4-byte).
+ */
+gqap_status gqap_chunk_prefill(const gqap_chunk_plan_t* plan, const void* q, const void* k_pool,
+                               const void* v_pool, const int32_t* block_table,
+                               const int32_t* cu_seqlens_q, const int32_t* kv_lens, float scale,
+                               void* out, float* lse, void* workspace, uint64_t workspace_bytes,
+                               void* stream);
+
+/* ------------------------------------------------------------------------ */
 
 /* Message of the last non-OK status on this host thread ("" if none). */
 const char* gqap_last_error(void);

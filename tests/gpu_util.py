@@ -109,3 +109,46 @@ class DevicePrefill:
     def results(self):
         torch.cuda.synchronize()
         return tensor_to_f64(self.out), self.lse.detach().cpu().numpy().astype(np.float64)
+
+
+class DeviceChunk:
+    """A chunked-prefill case on the device (cache with the prefixes filled)
+    plus a plan for it."""
+
+    def __init__(self, case, device: str = "cuda"):
+        self.case = case
+        self.q = bits_to_tensor(case.q, "bf16").to(device)
+        self.k_new = bits_to_tensor(case.k_new, "bf16").to(device)
+        self.v_new = bits_to_tensor(case.v_new, "bf16").to(device)
+        self.k_pool = bits_to_tensor(case.k_pool, "bf16").to(device)
+        self.v_pool = bits_to_tensor(case.v_pool, "bf16").to(device)
+        self.bt = torch.from_numpy(np.ascontiguousarray(case.block_table, dtype=np.int32)).to(device)
+        self.cu = torch.from_numpy(np.ascontiguousarray(case.cu_seqlens_q, dtype=np.int32)).to(device)
+        self.kvl = torch.from_numpy(np.ascontiguousarray(case.kv_lens, dtype=np.int32)).to(device)
+        T = case.T
+        self.out = torch.empty((T, case.Hq, case.D), dtype=torch.bfloat16, device=device)
+        self.lse = torch.empty((T, case.Hq), dtype=torch.float32, device=device)
+        max_q = max(1, int(case.q_lens.max())) if case.B else 1
+        max_kv = max(max_q, int(case.kv_lens.max())) if case.B else 1
+        self.desc = gq.chunk_desc(self.q, self.k_new, self.k_pool, self.bt, batch=case.B, max_q_len=max_q,
+                                  max_kv_len=max_kv, out=self.out)
+        self.plan = gq.gqap_chunk_plan(self.desc)
+        gq.gqap_chunk_validate_host(self.plan, case.block_table, case.cu_seqlens_q, case.kv_lens)
+
+    def append(self, stream=None):
+        gq.gqap_append_kv(self.plan, self.k_new, self.v_new, self.k_pool, self.v_pool, self.bt, self.cu, self.kvl,
+                          stream=stream)
+
+    def run(self, stream=None):
+        gq.gqap_chunk_prefill(self.plan, self.q, self.k_pool, self.v_pool, self.bt, self.cu, self.kvl,
+                              self.case.scale, self.out, self.lse, stream=stream)
+        return self.out, self.lse
+
+    def results(self):
+        torch.cuda.synchronize()
+        return tensor_to_f64(self.out), self.lse.detach().cpu().numpy().astype(np.float64)
+
+    def pools_bits(self):
+        torch.cuda.synchronize()
+        return (self.k_pool.detach().cpu().view(torch.int16).numpy().view(np.uint16),
+                self.v_pool.detach().cpu().view(torch.int16).numpy().view(np.uint16))

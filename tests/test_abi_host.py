@@ -60,6 +60,8 @@ int main(void) {
   printf("gqap_decode_plan_t sizeof %zu\n", sizeof(gqap_decode_plan_t));
   printf("gqap_prefill_desc_t sizeof %zu\n", sizeof(gqap_prefill_desc_t));
   printf("gqap_prefill_plan_t sizeof %zu\n", sizeof(gqap_prefill_plan_t));
+  printf("gqap_chunk_desc_t sizeof %zu\n", sizeof(gqap_chunk_desc_t));
+  printf("gqap_chunk_plan_t sizeof %zu\n", sizeof(gqap_chunk_plan_t));
   %FIELDS%
   return 0;
 }
@@ -71,7 +73,8 @@ def test_struct_layout_matches_the_c_compiler(gq, tmp_path):
     if not cc:
         pytest.skip("no C compiler")
     structs = {"gqap_decode_desc_t": gq.DecodeDesc, "gqap_decode_plan_t": gq.DecodePlan,
-               "gqap_prefill_desc_t": gq.PrefillDesc, "gqap_prefill_plan_t": gq.PrefillPlan}
+               "gqap_prefill_desc_t": gq.PrefillDesc, "gqap_prefill_plan_t": gq.PrefillPlan,
+               "gqap_chunk_desc_t": gq.ChunkDesc, "gqap_chunk_plan_t": gq.ChunkPlan}
     fields = "\n  ".join(f"F({cn}, {f})" for cn, py in structs.items() for f, _ in py._fields_)
     src = tmp_path / "layout.c"
     src.write_text(LAYOUT_PROGRAM.replace("%FIELDS%", fields))
@@ -242,3 +245,79 @@ def test_prefill_plan_block_mask_extent(gq):
     assert gq.lib().gqap_prefill_plan(ctypes.byref(d), ctypes.byref(gq.PrefillPlan())) != 0
     d.mask_blocks = 47
     assert gq.gqap_prefill_plan(d).magic == gq.PLAN_MAGIC
+
+
+# ---------------------------------------------------------------- chunked prefill planning
+
+def baseline_chunk_desc(gq):
+    """8 sequences, chunks of up to 512 tokens, up to 6656 keys; pool [464, 8, 64, 128]."""
+    d = gq.ChunkDesc()
+    d.batch, d.num_q_heads, d.num_kv_heads, d.head_dim = 8, 32, 8, 128
+    d.block_size, d.max_blocks_per_seq, d.num_pool_blocks = 64, 104, 464
+    d.total_q_tokens, d.max_q_len, d.max_kv_len, d.dtype = 4096, 512, 6656, gq.BF16
+    d.q_stride_head, d.q_stride_token = 128, 128 * 32
+    d.new_stride_head, d.new_stride_token = 128, 128 * 8
+    d.out_stride_head, d.out_stride_token = 128, 128 * 32
+    d.kv_stride_head, d.kv_stride_block = 64 * 128, 8 * 64 * 128
+    d.block_table_stride = 104
+    return d
+
+
+def test_chunk_plan_baseline(gq):
+    p = gq.gqap_chunk_plan(baseline_chunk_desc(gq))
+    assert p.magic == gq.PLAN_MAGIC and p.ratio == 4 and p.q_tile_rows == 128 and p.q_tiles == 4
+    assert p.workspace_bytes == 0
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("head_dim", 64, "UNSUPPORTED"),
+    ("block_size", 32, "UNSUPPORTED"),
+    ("dtype", 0, "DTYPE"),
+    ("num_kv_heads", 5, "INVALID_ARGUMENT"),
+    ("max_kv_len", 104 * 64 + 1, "INVALID_ARGUMENT"),   # past Nblk * 64
+    ("max_q_len", 7000, "INVALID_ARGUMENT"),            # more chunk tokens than keys
+    ("kv_stride_head", 64 * 128 - 8, "INVALID_ARGUMENT"),
+    ("new_stride_token", 100, "INVALID_ARGUMENT"),
+    ("block_table_stride", 50, "INVALID_ARGUMENT"),
+    ("batch", -1, "INVALID_ARGUMENT"),
+])
+def test_chunk_plan_rejects(gq, field, value, status):
+    d = baseline_chunk_desc(gq)
+    setattr(d, field, value)
+    got = gq.lib().gqap_chunk_plan(ctypes.byref(d), ctypes.byref(gq.ChunkPlan()))
+    assert gq.STATUS_NAMES[got] == status, gq.gqap_last_error()
+
+
+def test_chunk_validate_host(gq):
+    import numpy as np
+    d = baseline_chunk_desc(gq)
+    d.batch, d.total_q_tokens = 2, 600
+    p = gq.gqap_chunk_plan(d)
+    bt = np.full((2, 104), -1, np.int32)
+    bt[0, :3] = [5, 6, 7]        # 150 keys
+    bt[1, :9] = np.arange(9)     # 513 keys
+    cu = np.array([0, 100, 600], np.int32)
+    kv = np.array([150, 513], np.int32)
+    gq.gqap_chunk_validate_host(p, bt, cu, kv)
+    for bad_cu, bad_kv, what in (([0, 100, 700], [150, 513], "passes T"),
+                                 ([0, 100, 600], [90, 513], "fewer keys than chunk tokens"),
+                                 ([0, 100, 99], [150, 513], "decreasing"),
+                                 ([1, 100, 600], [150, 513], "not starting at 0"),
+                                 ([0, 100, 600], [150, 6657], "past max_kv_len")):
+        with pytest.raises(gq.GqapError):
+            gq.gqap_chunk_validate_host(p, bt, np.array(bad_cu, np.int32), np.array(bad_kv, np.int32))
+    bt[1, 8] = 464               # outside the pool
+    with pytest.raises(gq.GqapError, match="outside the pool"):
+        gq.gqap_chunk_validate_host(p, bt, cu, kv)
+
+
+def test_chunk_calls_reject_bad_arguments_without_a_gpu(gq):
+    p = gq.gqap_chunk_plan(baseline_chunk_desc(gq))
+    st = gq.lib().gqap_chunk_prefill(ctypes.byref(p), None, None, None, None, None, None, 1.0, None, None,
+                                     None, 0, None)
+    assert gq.STATUS_NAMES[st] == "INVALID_ARGUMENT"
+    st = gq.lib().gqap_append_kv(ctypes.byref(p), None, None, None, None, None, None, None, None)
+    assert gq.STATUS_NAMES[st] == "INVALID_ARGUMENT"
+    st = gq.lib().gqap_chunk_prefill(ctypes.byref(gq.ChunkPlan()), 16, 16, 16, 16, 16, 16, 1.0, 16, None,
+                                     None, 0, None)
+    assert gq.STATUS_NAMES[st] == "INVALID_ARGUMENT"      # unplanned (magic 0)

@@ -386,10 +386,125 @@ def prefill_blocksparse_bf16(seed: int = 1005, P: int = 8192, B: int = 2) -> Pre
                              Hq=32, Hk=8, D_qk=128, D_rope=0, D_v=128, mask_density=0.25)
 
 
+# ---------------------------------------------------------------------------
+# Chunked prefill against a paged KV cache
+# ---------------------------------------------------------------------------
+
+@dataclass
+class ChunkCase:
+    name: str
+    kv_lens: np.ndarray       # [B] int32: keys after the chunk is appended
+    cu_seqlens_q: np.ndarray  # [B+1] int32: the chunks packed back to back
+    Hq: int
+    Hk: int
+    D: int
+    q: np.ndarray             # [T, Hq, D] bf16 bits
+    k_new: np.ndarray         # [T, Hk, D] bf16 bits: the chunk's keys
+    v_new: np.ndarray         # [T, Hk, D]
+    k_pool: np.ndarray        # [NB, Hk, 64, D] bf16 bits: prefix rows filled, the rest NaN
+    v_pool: np.ndarray
+    block_table: np.ndarray   # [B, Nblk] int32 (-1 past ceil(kv_len / 64))
+    scale: float
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def B(self) -> int:
+        return int(self.kv_lens.shape[0])
+
+    @property
+    def T(self) -> int:
+        return int(self.cu_seqlens_q[-1])
+
+    @property
+    def q_lens(self) -> np.ndarray:
+        return np.diff(self.cu_seqlens_q).astype(np.int32)
+
+    def visible_pairs(self) -> int:
+        """(query, key) pairs the bottom-right aligned causal rule lets through."""
+        n = 0
+        for Lk, ql in zip(self.kv_lens.tolist(), self.q_lens.tolist()):
+            off = Lk - ql
+            # query i sees min(Lk, off + i + 1) keys (off >= 0 in every generated case)
+            n += sum(min(Lk, off + i + 1) for i in range(ql))
+        return n
+
+    def flops(self) -> int:
+        return 2 * self.Hq * (self.D + self.D) * self.visible_pairs()
+
+
+def make_chunk_case(
+    *,
+    name: str,
+    seed: int,
+    prefix_lens: Sequence[int],
+    q_lens: Sequence[int],
+    Hq: int,
+    Hk: int,
+    D: int = 128,
+    spare_blocks: int = 2,
+    scale: Optional[float] = None,
+) -> ChunkCase:
+    """Draw a chunked-prefill problem: sequence b already holds prefix_lens[b]
+    keys in a paged bf16 cache and appends a chunk of q_lens[b] tokens.
+
+    Draw order: block_table permutation -> q -> k_new -> v_new -> k_pool -> v_pool.
+    The pool has sum(ceil(kv_len / 64)) + spare_blocks blocks; the logical blocks
+    (b, j) in row-major order take a seeded permutation of the pool ids.  Pool
+    rows at or past each prefix (where the chunk will be appended), the rows past
+    kv_len and the spare blocks are NaN.
+    """
+    ss = np.random.SeedSequence(seed)
+    s_tab, s_q, s_kn, s_vn, s_k, s_v = ss.spawn(6)
+    prefix = np.asarray(prefix_lens, dtype=np.int32)
+    ql = np.asarray(q_lens, dtype=np.int32)
+    B = prefix.shape[0]
+    kv_lens = (prefix + ql).astype(np.int32)
+    need = _blocks_needed(kv_lens)
+    nblk = max(1, int(need.max()) if B else 1)
+    NB = int(need.sum()) + spare_blocks
+    perm = np.random.Generator(np.random.PCG64(s_tab)).permutation(NB)
+    block_table = np.full((B, nblk), -1, np.int32)
+    k = 0
+    for b in range(B):
+        for j in range(int(need[b])):
+            block_table[b, j] = perm[k]
+            k += 1
+    cu = np.zeros(B + 1, np.int32)
+    cu[1:] = np.cumsum(ql)
+    T = int(cu[-1])
+    q = to_bf16_bits(normal_f32(s_q, T * Hq * D).reshape(T, Hq, D))
+    k_new = to_bf16_bits(normal_f32(s_kn, T * Hk * D).reshape(T, Hk, D))
+    v_new = to_bf16_bits(normal_f32(s_vn, T * Hk * D).reshape(T, Hk, D))
+    pools = []
+    for s_x in (s_k, s_v):
+        x = to_bf16_bits(normal_f32(s_x, NB * Hk * BLOCK * D).reshape(NB, Hk, BLOCK, D))
+        keep = np.zeros((NB, BLOCK), bool)
+        for b in range(B):
+            for t in range(int(prefix[b])):
+                keep[block_table[b, t // BLOCK], t % BLOCK] = True
+        x.transpose(0, 2, 1, 3)[~keep] = BF16_NAN
+        pools.append(x)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    return ChunkCase(name=name, kv_lens=kv_lens, cu_seqlens_q=cu, Hq=Hq, Hk=Hk, D=D, q=q, k_new=k_new,
+                     v_new=v_new, k_pool=pools[0], v_pool=pools[1], block_table=block_table,
+                     scale=float(scale), meta={"seed": seed, "prefix_lens": prefix})
+
+
+def prefill_chunk_bf16(seed: int = 1006, B: int = 8, prefix_range=(1024, 6144), q_len: int = 512) -> ChunkCase:
+    """Chunked prefill: B=8 sequences with cached prefixes ~ U{1024..6144}
+    appending 512-token chunks; Hq=32, Hk=8, D=128, bf16, paged 64-row cache."""
+    lo, hi = prefix_range
+    prefix = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed).spawn(1)[0])).integers(lo, hi + 1, size=B)
+    return make_chunk_case(name="prefill_chunk_bf16", seed=seed + 1, prefix_lens=prefix.tolist(),
+                           q_lens=[q_len] * B, Hq=32, Hk=8, D=128)
+
+
 CONFIGS = {
     "decode_tiny_f32": decode_tiny_fp32,
     "decode_gqa_bf16": decode_gqa_bf16,
     "prefill_mla_bf16": prefill_mla_bf16,
     "decode_long_fp8": decode_long_fp8,
     "prefill_blocksparse_bf16": prefill_blocksparse_bf16,
+    "prefill_chunk_bf16": prefill_chunk_bf16,
 }
