@@ -78,8 +78,9 @@ DOMINANT_KERNEL = {
     "decode_gqa_bf16": "decode_worker_mfma<128, false>",
     "decode_long_fp8": "decode_worker_mfma<128, true>",
     "decode_tiny_fp32": "decode_worker_f32",
-    "prefill_mla_bf16": "prefill_fwd<64>",
-    "prefill_blocksparse_bf16": "prefill_fwd<0>",
+    "prefill_mla_bf16": "prefill_fwd<64, false>",
+    "prefill_blocksparse_bf16": "prefill_fwd<0, false>",
+    "prefill_chunk_bf16": "prefill_fwd<0, true>",
 }
 COPY_KERNEL = "neg_kernel"   # torch.neg(out=) over float32: reads and writes each byte once
 
@@ -239,6 +240,36 @@ def bench_prefill(case, steps, warmup, torch, gq, gu, check=True):
     }
 
 
+def bench_chunk(case, steps, warmup, torch, gq, gu, check=True):
+    """A step of chunked prefill: append the chunk into the paged cache, then
+    attend (both launches; the append rewrites the same rows every step)."""
+    dc = gu.DeviceChunk(case)
+
+    def run(i):
+        dc.append()
+        dc.run()
+
+    ms_step, ms_ev, evs = _timed_loop(run, steps, warmup, torch)
+    err = None
+    if check:
+        from oracle import attention as O
+        import numpy as np
+        out, _ = dc.results()
+        kp, vp = O.append_kv(case.k_new, case.v_new, case.k_pool, case.v_pool, case.block_table,
+                             case.cu_seqlens_q, case.kv_lens)
+        rows = np.linspace(0, case.T - 1, 48).astype(np.int64)
+        ref, _ = O.chunk_prefill(case.q, kp, vp, case.block_table, case.cu_seqlens_q, case.kv_lens, case.scale,
+                                 dtype="bf16", rows=rows)
+        err = float(abs(out[rows] - ref).max())
+    flops = case.flops()
+    return {
+        "workload": case.name, "flops": flops, "ms_per_step": ms_step, "ms_kernel": ms_ev,
+        "ms_kernel_p10": evs[len(evs) // 10], "ms_kernel_p90": evs[(9 * len(evs)) // 10],
+        "tflops_step": flops / (ms_step * 1e-3) / 1e12, "tflops_kernel": flops / (ms_ev * 1e-3) / 1e12,
+        "max_abs_err_sample": err,
+    }
+
+
 def cpu_baseline_decode(case, budget_s: float = 12.0):
     """The oracle, as it is, on the host: whole decode passes over the same
     workload until about `budget_s` seconds have run (at least one)."""
@@ -300,7 +331,8 @@ def main(argv=None) -> int:
     if args.only:
         mk = gen.CONFIGS[args.only]
         c = mk()
-        fn = bench_prefill if isinstance(c, gen.PrefillCase) else bench_decode
+        fn = (bench_prefill if isinstance(c, gen.PrefillCase) else
+              bench_chunk if isinstance(c, gen.ChunkCase) else bench_decode)
         print(json.dumps(fn(c, args.steps, args.warmup, torch, gq, gu)), flush=True)
         if args.copy_calibration_bytes:
             n = args.copy_calibration_bytes // 4
@@ -331,6 +363,14 @@ def main(argv=None) -> int:
                                   "traffic": _traffic(pc.name)}
                 secondary.append(rp)
                 del pc
+        if hasattr(gu, "DeviceChunk"):
+            cc = gen.prefill_chunk_bf16()
+            rc = bench_chunk(cc, args.steps, args.warmup, torch, gq, gu)
+            rc["roofline"] = {"bound": "mfma", "achieved": rc["tflops_kernel"], "peak": BF16_MFMA_PEAK_TFLOPS,
+                              "unit": "TFLOP/s", "frac": rc["tflops_kernel"] / BF16_MFMA_PEAK_TFLOPS,
+                              "traffic": _traffic(cc.name)}
+            secondary.append(rc)
+            del cc
 
     cpu = None if args.no_cpu_baseline else cpu_baseline_decode(case)
     line = {

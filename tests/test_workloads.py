@@ -70,3 +70,23 @@ def test_ragged_prefill_offsets():
     p = gen.prefill_mla_bf16()
     assert p.q.shape == (6584, 16, 192) and p.k.shape == (6584, 16, 128)
     assert p.k_rope.shape == (6584, 1, 64) and p.v.shape == (6584, 16, 128)
+
+
+def test_chunk_case_structure():
+    """Prefix rows filled, every other pool row NaN; kv_len = prefix + chunk;
+    the table covers ceil(kv_len / 64) distinct blocks; deterministic."""
+    c = gen.make_chunk_case(name="t", seed=7, prefix_lens=[0, 63, 130], q_lens=[5, 1, 64], Hq=4, Hk=2)
+    assert c.kv_lens.tolist() == [5, 64, 194] and c.cu_seqlens_q.tolist() == [0, 5, 6, 70]
+    assert c.k_pool.shape == (1 + 1 + 4 + 2, 2, 64, 128)
+    used = [int(x) for row, L in zip(c.block_table, c.kv_lens) for x in row[: (L + 63) // 64]]
+    assert len(set(used)) == len(used) == 6 and all(x == -1 for x in c.block_table[0, 1:])
+    finite = np.zeros(c.k_pool.shape[:1] + (64,), bool)
+    for b, p in enumerate([0, 63, 130]):
+        for t in range(p):
+            finite[c.block_table[b, t // 64], t % 64] = True
+    rows = c.k_pool.transpose(0, 2, 1, 3)                      # [NB, 64, Hk, D]
+    assert np.all(rows[~finite] == gen.BF16_NAN) and not np.any(rows[finite] == gen.BF16_NAN)
+    c2 = gen.make_chunk_case(name="t", seed=7, prefix_lens=[0, 63, 130], q_lens=[5, 1, 64], Hq=4, Hk=2)
+    assert np.array_equal(c.q, c2.q) and np.array_equal(c.k_pool, c2.k_pool)
+    # visible pairs: query i of chunk b sees prefix_b + i + 1 keys
+    assert c.visible_pairs() == sum(p * q + q * (q + 1) // 2 for p, q in ((0, 5), (63, 1), (130, 64)))
