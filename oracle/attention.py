@@ -284,6 +284,9 @@ def append_kv(
     block_table: np.ndarray,
     cu_seqlens_q: np.ndarray,
     kv_lens: np.ndarray,
+    *,
+    kr_new: Optional[np.ndarray] = None,
+    kr_pool: Optional[np.ndarray] = None,
 ):
     """Write a chunk's keys and values into the paged cache (storage bits, exact).
 
@@ -292,9 +295,13 @@ def append_kv(
     its kv_lens[b] keys, so its token i goes to logical position
     p = kv_lens[b] - q_len_b + i: row p % 64 of pool block block_table[b, p // 64]
     (FlashMLA tensor-shape reference, section 4, "Prefill to Cache Mapping").
-    Returns new pools; the inputs are not modified."""
+    With an MLA rope cache, kr_new [T, 1, Dr] goes to kr_pool [NB, 1, 64, Dr]
+    by the same rule (flare_mla_prefill, overload A: the rope keys live in a
+    paged cache too).  Returns new pools ((k, v) or (k, v, kr)); the inputs
+    are not modified."""
     kp = np.array(k_pool, copy=True)
     vp = np.array(v_pool, copy=True)
+    rp = np.array(kr_pool, copy=True) if kr_pool is not None else None
     cu = np.asarray(cu_seqlens_q, dtype=np.int64)
     for b in range(cu.shape[0] - 1):
         ql = int(cu[b + 1] - cu[b])
@@ -306,7 +313,9 @@ def append_kv(
             blk = int(block_table[b, p // BLOCK])
             kp[blk, :, p % BLOCK] = k_new[cu[b] + i]
             vp[blk, :, p % BLOCK] = v_new[cu[b] + i]
-    return kp, vp
+            if rp is not None:
+                rp[blk, :, p % BLOCK] = kr_new[cu[b] + i]
+    return (kp, vp) if rp is None else (kp, vp, rp)
 
 
 def chunk_prefill(
@@ -321,6 +330,7 @@ def chunk_prefill(
     dtype: str = "f64",
     rows: Optional[Sequence[int]] = None,
     row_chunk: int = 256,
+    kr_pool: Optional[np.ndarray] = None,
 ):
     """Causal attention of a chunk of new queries to a paged KV cache.
 
@@ -330,20 +340,28 @@ def chunk_prefill(
     cu[b+1] - cu[b] and offset o_b = kv_lens[b] - q_len_b (the chunk aligned to
     the end of the keys), query i sees logical key j iff j < kv_lens[b] and
     j <= o_b + i.  Keys are gathered from the pool exactly as in decode.
+    With kr_pool [NB, 1, 64, Dr] (MLA), q is [T, Hq, Dn + Dr] and the score of key
+    j adds q[i, h, Dn:] . kr[j], the rope key of token j from the same pages,
+    shared by every head (flare_mla_prefill: the K head lacks the rope part,
+    which comes from the rope cache for all heads).
     ``rows``: optional global query indices to evaluate (default all).
     Returns (out [n, Hq, D], lse [n, Hq]) in float64."""
     Q = widen(q, dtype)
-    T, Hq, D = Q.shape
-    Hk = k_pool.shape[1]
+    T, Hq, Dqk = Q.shape
+    Hk, Dn = k_pool.shape[1], k_pool.shape[3]
+    Dr = 0 if kr_pool is None else kr_pool.shape[3]
+    if Dn + Dr != Dqk:
+        raise ValueError("query width must equal K width plus rope width")
     if Hq % Hk:
         raise ValueError("Hq must be a multiple of Hk")
     r = Hq // Hk
+    Dv = v_pool.shape[3]
     cu = np.asarray(cu_seqlens_q, dtype=np.int64)
     B = cu.shape[0] - 1
     if rows is None:
         rows = np.arange(T)
     rows = np.asarray(rows, dtype=np.int64)
-    out = np.zeros((rows.shape[0], Hq, D), np.float64)
+    out = np.zeros((rows.shape[0], Hq, Dv), np.float64)
     lse = np.full((rows.shape[0], Hq), -np.inf, np.float64)
     seq_of_row = np.searchsorted(cu, rows, side="right") - 1
     for b in range(B):
@@ -353,6 +371,7 @@ def chunk_prefill(
             continue
         off = Lk - int(cu[b + 1] - cu[b])
         j = np.arange(Lk)
+        KR = widen(gather_kv_rows(kr_pool, block_table, b, 0, Lk), dtype) if Dr else None
         for g in range(Hk):
             K = widen(gather_kv_rows(k_pool, block_table, b, g, Lk), dtype)
             V = widen(gather_kv_rows(v_pool, block_table, b, g, Lk), dtype)
@@ -361,7 +380,11 @@ def chunk_prefill(
                 idx = sel[s0:s0 + row_chunk]
                 i = rows[idx] - cu[b]                      # local query index in the chunk
                 vis = j[None, :] <= (off + i)[:, None]     # bottom-right aligned causal bound
-                s = scale * (Q[rows[idx], heads, :] @ K.T)  # [n, r, Lk]
+                Qc = Q[rows[idx], heads, :]                # [n, r, Dqk]
+                s = Qc[:, :, :Dn] @ K.T                     # [n, r, Lk]
+                if Dr:
+                    s = s + Qc[:, :, Dn:] @ KR.T
+                s = scale * s
                 s = np.where(vis[:, None, :], s, -np.inf)
                 o, ls = _softmax_attend(s, V)
                 out[idx, heads] = o

@@ -81,10 +81,12 @@ def prefill(q, k, v, seq_lens, scale, *, k_rope=None, block_mask: Optional[objec
     return outs, lses
 
 
-def chunk_prefill(q, k, v, offsets, scale):
-    """Per-sequence lists: q[b] [n_b, Hq, D] (the chunk's queries), k[b], v[b]
-    [Lk_b, Hk, D] (every logical key of the sequence), offsets[b] = Lk_b - n_b.
-    Query i sees key j iff j < Lk_b and j <= offsets[b] + i."""
+def chunk_prefill(q, k, v, offsets, scale, k_rope=None):
+    """Per-sequence lists: q[b] [n_b, Hq, Dn + Dr] (the chunk's queries), k[b]
+    [Lk_b, Hk, Dn], v[b] [Lk_b, Hk, Dv] (every logical key of the sequence),
+    offsets[b] = Lk_b - n_b, k_rope[b] [Lk_b, Dr] or None.  Query i sees key j
+    iff j < Lk_b and j <= offsets[b] + i; the rope part of the query pairs with
+    the one shared rope key row."""
     outs, lses = [], []
     for b in range(len(q)):
         qb, kb, vb = q[b], k[b], v[b]
@@ -98,7 +100,10 @@ def chunk_prefill(q, k, v, offsets, scale):
                 keys, vals = [], []
                 for jj in range(Lk):
                     if jj <= offsets[b] + i:
-                        keys.append([float(x) for x in kb[jj, g]])
+                        key = [float(x) for x in kb[jj, g]]
+                        if k_rope is not None:
+                            key = key + [float(x) for x in k_rope[b][jj]]
+                        keys.append(key)
                         vals.append([float(x) for x in vb[jj, g]])
                 if not keys:
                     ob[i][h], lb[i][h] = [0.0] * vb.shape[2], -math.inf

@@ -197,3 +197,73 @@ def test_append_then_chunk_prefill_equals_prefill_of_the_whole_sequence():
     ro, rl = O.ragged_prefill(q, k, v, O.cu_seqlens_from_lengths([L]), 0.3)
     np.testing.assert_allclose(o, ro[c:], rtol=0, atol=1e-12)
     np.testing.assert_allclose(l, rl[c:], rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- MLA: the rope key from the paged cache
+
+def _mla_pool_case(seed, kv_lens, q_lens, Hq, Hk, Dn=8, Dr=4, Dv=6):
+    """As _pool_case, plus a one-head rope cache [NB, 1, 64, Dr] on the same pages
+    and queries of width Dn + Dr."""
+    rng = np.random.default_rng(seed)
+    B = len(kv_lens)
+    nblk = max(1, max((L + 63) // 64 for L in kv_lens))
+    NB = B * nblk + 2
+    table = rng.permutation(NB)[: B * nblk].reshape(B, nblk).astype(np.int32)
+    K = [rng.standard_normal((L, Hk, Dn)) for L in kv_lens]
+    V = [rng.standard_normal((L, Hk, Dv)) for L in kv_lens]
+    R = [rng.standard_normal((L, Dr)) for L in kv_lens]
+    kp = np.full((NB, Hk, 64, Dn), np.nan)
+    vp = np.full((NB, Hk, 64, Dv), np.nan)
+    rp = np.full((NB, 1, 64, Dr), np.nan)
+    for b, L in enumerate(kv_lens):
+        for t in range(L):
+            kp[table[b][t // 64], :, t % 64] = K[b][t]
+            vp[table[b][t // 64], :, t % 64] = V[b][t]
+            rp[table[b][t // 64], 0, t % 64] = R[b][t]
+    cu = O.cu_seqlens_from_lengths(q_lens)
+    q = rng.standard_normal((int(cu[-1]), Hq, Dn + Dr))
+    return q, K, V, R, kp, vp, rp, table, cu, np.asarray(kv_lens, np.int32)
+
+
+def test_mla_chunk_prefill_matches_bruteforce():
+    kv_lens, q_lens = [70, 5, 130], [6, 5, 64]
+    q, K, V, R, kp, vp, rp, table, cu, kvl = _mla_pool_case(71, kv_lens, q_lens, 4, 2)
+    out, lse = O.chunk_prefill(q, kp, vp, table, cu, kvl, 0.3, kr_pool=rp)
+    qs = [q[cu[b]:cu[b + 1]] for b in range(3)]
+    bo, bl = BF.chunk_prefill(qs, K, V, [kv_lens[b] - q_lens[b] for b in range(3)], 0.3, k_rope=R)
+    np.testing.assert_allclose(out, _cat(bo), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, _cat(bl), rtol=0, atol=1e-12)
+
+
+def test_mla_chunk_with_empty_prefix_equals_mla_ragged_prefill():
+    """No prefix: the MLA ragged prefill (rope rows given token-major) of the
+    same logical tensors."""
+    lens = [1, 64, 100]
+    q, K, V, R, kp, vp, rp, table, cu, kvl = _mla_pool_case(72, lens, lens, 4, 4)
+    out, lse = O.chunk_prefill(q, kp, vp, table, cu, kvl, 0.25, kr_pool=rp)
+    ro, rl = O.ragged_prefill(q, np.concatenate(K), np.concatenate(V), cu, 0.25,
+                              k_rope=np.concatenate(R)[:, None, :])
+    np.testing.assert_allclose(out, ro, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, rl, rtol=0, atol=1e-12)
+
+
+def test_mla_chunk_zero_rope_query_reduces_to_plain_chunk():
+    """Zeroing the rope part of the queries removes the rope term exactly."""
+    q, K, V, R, kp, vp, rp, table, cu, kvl = _mla_pool_case(73, [150, 20], [40, 20], 4, 2)
+    q[:, :, 8:] = 0.0
+    out, lse = O.chunk_prefill(q, kp, vp, table, cu, kvl, 0.3, kr_pool=rp)
+    po, pl = O.chunk_prefill(q[:, :, :8], kp, vp, table, cu, kvl, 0.3)
+    np.testing.assert_allclose(out, po, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lse, pl, rtol=0, atol=1e-14)
+
+
+def test_mla_append_writes_the_rope_rows_on_the_same_pages():
+    q, K, V, R, kp, vp, rp, table, cu, kvl = _mla_pool_case(74, [130, 64], [64, 1], 4, 2)
+    T = int(cu[-1])
+    rng = np.random.default_rng(75)
+    kn, vn, rn = rng.standard_normal((T, 2, 8)), rng.standard_normal((T, 2, 6)), rng.standard_normal((T, 1, 4))
+    kp2, vp2, rp2 = O.append_kv(kn, vn, kp, vp, table, cu, kvl, kr_new=rn, kr_pool=rp)
+    for b, (L, n) in enumerate(((130, 64), (64, 1))):
+        got = O.gather_kv_rows(rp2, table, b, 0, L)
+        np.testing.assert_array_equal(got[: L - n], R[b][: L - n])
+        np.testing.assert_array_equal(got[L - n:], rn[cu[b]:cu[b + 1], 0])
