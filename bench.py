@@ -81,6 +81,7 @@ DOMINANT_KERNEL = {
     "prefill_mla_bf16": "prefill_fwd<64, false>",
     "prefill_blocksparse_bf16": "prefill_fwd<0, false>",
     "prefill_chunk_bf16": "prefill_fwd<0, true>",
+    "prefill_chunk_mla_bf16": "prefill_fwd<64, true>",
 }
 COPY_KERNEL = "neg_kernel"   # torch.neg(out=) over float32: reads and writes each byte once
 
@@ -255,11 +256,11 @@ def bench_chunk(case, steps, warmup, torch, gq, gu, check=True):
         from oracle import attention as O
         import numpy as np
         out, _ = dc.results()
-        kp, vp = O.append_kv(case.k_new, case.v_new, case.k_pool, case.v_pool, case.block_table,
-                             case.cu_seqlens_q, case.kv_lens)
+        pools = O.append_kv(case.k_new, case.v_new, case.k_pool, case.v_pool, case.block_table,
+                            case.cu_seqlens_q, case.kv_lens, kr_new=case.kr_new, kr_pool=case.kr_pool)
         rows = np.linspace(0, case.T - 1, 48).astype(np.int64)
-        ref, _ = O.chunk_prefill(case.q, kp, vp, case.block_table, case.cu_seqlens_q, case.kv_lens, case.scale,
-                                 dtype="bf16", rows=rows)
+        ref, _ = O.chunk_prefill(case.q, pools[0], pools[1], case.block_table, case.cu_seqlens_q, case.kv_lens,
+                                 case.scale, dtype="bf16", rows=rows, kr_pool=pools[2] if len(pools) == 3 else None)
         err = float(abs(out[rows] - ref).max())
     flops = case.flops()
     return {
@@ -364,13 +365,14 @@ def main(argv=None) -> int:
                 secondary.append(rp)
                 del pc
         if hasattr(gu, "DeviceChunk"):
-            cc = gen.prefill_chunk_bf16()
-            rc = bench_chunk(cc, args.steps, args.warmup, torch, gq, gu)
-            rc["roofline"] = {"bound": "mfma", "achieved": rc["tflops_kernel"], "peak": BF16_MFMA_PEAK_TFLOPS,
-                              "unit": "TFLOP/s", "frac": rc["tflops_kernel"] / BF16_MFMA_PEAK_TFLOPS,
-                              "traffic": _traffic(cc.name)}
-            secondary.append(rc)
-            del cc
+            for mk in (gen.prefill_chunk_bf16, gen.prefill_chunk_mla_bf16):
+                cc = mk()
+                rc = bench_chunk(cc, args.steps, args.warmup, torch, gq, gu)
+                rc["roofline"] = {"bound": "mfma", "achieved": rc["tflops_kernel"], "peak": BF16_MFMA_PEAK_TFLOPS,
+                                  "unit": "TFLOP/s", "frac": rc["tflops_kernel"] / BF16_MFMA_PEAK_TFLOPS,
+                                  "traffic": _traffic(cc.name)}
+                secondary.append(rc)
+                del cc
 
     cpu = None if args.no_cpu_baseline else cpu_baseline_decode(case)
     line = {

@@ -89,12 +89,13 @@ class ChunkDesc(ctypes.Structure):
         ("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
         ("head_dim", ctypes.c_int32), ("block_size", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
         ("num_pool_blocks", ctypes.c_int32), ("total_q_tokens", ctypes.c_int32), ("max_q_len", ctypes.c_int32),
-        ("max_kv_len", ctypes.c_int32), ("dtype", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+        ("max_kv_len", ctypes.c_int32), ("dtype", ctypes.c_int32), ("head_dim_rope", ctypes.c_int32),
         ("q_stride_token", ctypes.c_int64), ("q_stride_head", ctypes.c_int64),
         ("new_stride_token", ctypes.c_int64), ("new_stride_head", ctypes.c_int64),
         ("out_stride_token", ctypes.c_int64), ("out_stride_head", ctypes.c_int64),
         ("kv_stride_block", ctypes.c_int64), ("kv_stride_head", ctypes.c_int64),
         ("block_table_stride", ctypes.c_int64),
+        ("kr_new_stride_token", ctypes.c_int64), ("kr_stride_block", ctypes.c_int64),
     ]
 
 
@@ -129,9 +130,10 @@ def _load() -> ctypes.CDLL:
     lib.gqap_chunk_plan.restype = st
     lib.gqap_chunk_validate_host.argtypes = [ctypes.POINTER(ChunkPlan), vp, vp, vp]
     lib.gqap_chunk_validate_host.restype = st
-    lib.gqap_append_kv.argtypes = [ctypes.POINTER(ChunkPlan), vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.gqap_append_kv.argtypes = [ctypes.POINTER(ChunkPlan), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.gqap_append_kv.restype = st
-    lib.gqap_chunk_prefill.argtypes = [ctypes.POINTER(ChunkPlan), vp, vp, vp, vp, vp, vp, f32, vp, vp, vp, u64, vp]
+    lib.gqap_chunk_prefill.argtypes = [ctypes.POINTER(ChunkPlan), vp, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp, u64,
+                                       vp]
     lib.gqap_chunk_prefill.restype = st
     lib.gqap_last_error.argtypes = []
     lib.gqap_last_error.restype = ctypes.c_char_p
@@ -240,19 +242,21 @@ def gqap_chunk_validate_host(plan: ChunkPlan, block_table_host, cu_seqlens_q_hos
     _check(_lib.gqap_chunk_validate_host(ctypes.byref(plan), bt.ctypes.data, cu.ctypes.data, kl.ctypes.data))
 
 
-def gqap_append_kv(plan: ChunkPlan, k_new, v_new, k_pool, v_pool, block_table, cu_seqlens_q, kv_lens,
-                   stream=None) -> None:
-    _check(_lib.gqap_append_kv(ctypes.byref(plan), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool),
-                               _ptr(block_table), _ptr(cu_seqlens_q), _ptr(kv_lens), _stream(stream)))
+def gqap_append_kv(plan: ChunkPlan, k_new, v_new, k_rope_new, k_pool, v_pool, kr_pool, block_table,
+                   cu_seqlens_q, kv_lens, stream=None) -> None:
+    _check(_lib.gqap_append_kv(ctypes.byref(plan), _ptr(k_new), _ptr(v_new), _ptr(k_rope_new), _ptr(k_pool),
+                               _ptr(v_pool), _ptr(kr_pool), _ptr(block_table), _ptr(cu_seqlens_q), _ptr(kv_lens),
+                               _stream(stream)))
 
 
-def gqap_chunk_prefill(plan: ChunkPlan, q, k_pool, v_pool, block_table, cu_seqlens_q, kv_lens, scale: float,
-                       out, lse=None, workspace=None, workspace_bytes: Optional[int] = None, stream=None) -> None:
+def gqap_chunk_prefill(plan: ChunkPlan, q, k_pool, v_pool, kr_pool, block_table, cu_seqlens_q, kv_lens,
+                       scale: float, out, lse=None, workspace=None, workspace_bytes: Optional[int] = None,
+                       stream=None) -> None:
     if workspace_bytes is None:
         workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(_lib.gqap_chunk_prefill(ctypes.byref(plan), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
-                                   _ptr(cu_seqlens_q), _ptr(kv_lens), scale, _ptr(out), _ptr(lse),
-                                   _ptr(workspace), workspace_bytes, _stream(stream)))
+    _check(_lib.gqap_chunk_prefill(ctypes.byref(plan), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(kr_pool),
+                                   _ptr(block_table), _ptr(cu_seqlens_q), _ptr(kv_lens), scale, _ptr(out),
+                                   _ptr(lse), _ptr(workspace), workspace_bytes, _stream(stream)))
 
 
 # ------------------------------------------------------------------ descriptors from tensors
@@ -318,11 +322,11 @@ def prefill_desc(q, k, v, k_rope, batch: int, max_seq_len: int, block_mask=None,
 
 
 def chunk_desc(q, k_new, k_pool, block_table, batch: int, max_q_len: int, max_kv_len: int,
-               out=None) -> ChunkDesc:
-    """Descriptor for q [T, Hq, D], k_new / v_new [T, Hk, D], pool [NB, Hk, 64, D],
-    block_table [B, Nblk]."""
-    T, Hq, D = q.shape
-    NB, Hk, blk, _ = k_pool.shape
+               out=None, k_rope_new=None, kr_pool=None) -> ChunkDesc:
+    """Descriptor for q [T, Hq, D + Dr], k_new / v_new [T, Hk, D], pool [NB, Hk, 64, D],
+    block_table [B, Nblk]; MLA: k_rope_new [T, 1, Dr], kr_pool [NB, 1, 64, Dr]."""
+    T, Hq, _ = q.shape
+    NB, Hk, blk, D = k_pool.shape
     out = q if out is None else out
     d = ChunkDesc()
     d.batch, d.num_q_heads, d.num_kv_heads, d.head_dim = batch, Hq, Hk, D
@@ -338,4 +342,8 @@ def chunk_desc(q, k_new, k_pool, block_table, batch: int, max_q_len: int, max_kv
     d.out_stride_token, d.out_stride_head = out.stride(0), out.stride(1)
     d.kv_stride_block, d.kv_stride_head = k_pool.stride(0), k_pool.stride(1)
     d.block_table_stride = block_table.stride(0)
+    if kr_pool is not None:
+        d.head_dim_rope = kr_pool.shape[3]
+        d.kr_new_stride_token = k_rope_new.stride(0)
+        d.kr_stride_block = kr_pool.stride(0)
     return d

@@ -230,9 +230,15 @@ extern "C" gqap_status gqap_chunk_plan(const gqap_chunk_desc_t* desc, gqap_chunk
   if (d.max_q_len > d.max_kv_len)
     return fail(GQAP_ERR_INVALID_ARGUMENT, "max_q_len %d exceeds max_kv_len %d (a chunk's tokens are among its keys)",
                 d.max_q_len, d.max_kv_len);
-  const int64_t D = d.head_dim, Hq = d.num_q_heads, Hk = d.num_kv_heads;
-  if (d.q_stride_head < D || d.q_stride_token < d.q_stride_head * Hq)
+  if (d.head_dim_rope != 0 && d.head_dim_rope != 64)
+    return fail(GQAP_ERR_UNSUPPORTED, "head_dim_rope must be 0 or 64 (got %d)", d.head_dim_rope);
+  const int64_t D = d.head_dim, Dr = d.head_dim_rope, Hq = d.num_q_heads, Hk = d.num_kv_heads;
+  if (d.q_stride_head < D + Dr || d.q_stride_token < d.q_stride_head * Hq)
     return fail(GQAP_ERR_INVALID_ARGUMENT, "q strides overlap");
+  if (Dr && (d.kr_new_stride_token < Dr || d.kr_stride_block < Dr * kBlock || !aligned16(d.kr_new_stride_token, 2) ||
+             !aligned16(d.kr_stride_block, 2)))
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "rope strides (new %lld, block %lld) overlap or break 16-byte alignment",
+                (long long)d.kr_new_stride_token, (long long)d.kr_stride_block);
   if (d.new_stride_head < D || d.new_stride_token < d.new_stride_head * Hk)
     return fail(GQAP_ERR_INVALID_ARGUMENT, "k_new/v_new strides overlap");
   if (d.out_stride_head < D || d.out_stride_token < d.out_stride_head * Hq)
@@ -258,7 +264,7 @@ extern "C" gqap_status gqap_chunk_plan(const gqap_chunk_desc_t* desc, gqap_chunk
   if ((int64_t)d.num_q_heads * d.batch * plan->q_tiles >= ((int64_t)1 << 24))
     return fail(GQAP_ERR_UNSUPPORTED, "Hq * batch * ceil(max_q_len/128) = %lld workgroups exceeds 2^24",
                 (long long)d.num_q_heads * d.batch * plan->q_tiles);
-  plan->kernel = 1;
+  plan->kernel = Dr ? 2 : 1;
   plan->workspace_bytes = 0;
   plan->magic = GQAP_PLAN_MAGIC;
   return GQAP_OK;

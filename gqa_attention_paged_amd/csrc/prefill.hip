@@ -50,6 +50,7 @@ struct PrefillArgs {
   int64_t bt_st;      // block_table row stride (int32 elements)
   int64_t kv_sb;      // elements between pool blocks
   int64_t kv_sh;      // elements between heads of a block
+  int64_t kr_sb;      // elements between rope-cache blocks
   int32_t max_kv;     // capacity: keys per sequence
 };
 
@@ -270,6 +271,14 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
     else
       return vg + (int64_t)kt * 64 * vstr;
   };
+  // The rope keys: one 64 x Dr slab per page with PAGED (one head, shared by
+  // every query head), else rows of the token-major rope tensor.
+  auto tile_r = [&](int kt) -> const unsigned char* {
+    if constexpr (PAGED)
+      return (const unsigned char*)a.kr + (int64_t)page_of(kt) * a.kr_sb * 2;
+    else
+      return rg + (int64_t)kt * 64 * rstr;
+  };
   // Rows past the last key read row Lk-1 instead: every key past Lk is
   // causally hidden from every query of the sequence, so its score is
   // replaced by -inf and its probability is exactly 0.
@@ -281,7 +290,7 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
     const int key0 = kt * 64;
     const unsigned char* kt_k = tile_k(kt);
     const unsigned char* kt_v = tile_v(kt);
-    const unsigned char* kt_r = DR ? rg + key0 * rstr : nullptr;
+    const unsigned char* kt_r = DR ? tile_r(kt) : nullptr;
     if (key0 + 64 <= Lk) {  // whole tile inside the keys
 #pragma unroll
       for (int i = 0; i < KLD; ++i) dma(kt_k + 16 * i * kstr + koff, kd + 4096 * i + wseg);
@@ -355,7 +364,7 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
     constexpr int NLD = KLD + RLD + VLD;
     const unsigned char* kt_k = WL ? tile_k(kn) : nullptr;
     const unsigned char* kt_v = WL ? tile_v(kn) : nullptr;
-    const unsigned char* kt_r = DR ? rg + kn * 64 * rstr : nullptr;
+    const unsigned char* kt_r = DR && WL ? tile_r(kn) : nullptr;
     auto issue_load = [&](int i) {
       if (i < KLD)
         dma(kt_k + 16 * i * kstr + koff, kd + 4096 * i + wseg);
@@ -552,7 +561,9 @@ struct AppendArgs {
   const int32_t* bt;
   const int32_t* cu;
   const int32_t* kvlens;
-  int64_t new_st, new_sh, kv_sb, kv_sh, bt_st;
+  const uint16_t* kr_new;  // MLA: [T, 1, 64] rope keys, or null
+  uint16_t* kr_pool;       // MLA: [NB, 1, 64, 64], or null
+  int64_t new_st, new_sh, kv_sb, kv_sh, bt_st, kr_new_st, kr_sb;
   int64_t rows;     // T * Hk
   int32_t B, Hk, max_kv;
 };
@@ -578,6 +589,9 @@ __global__ __launch_bounds__(256) void append_kv(AppendArgs a) {
   const int64_t src = (int64_t)t * a.new_st + (int64_t)g * a.new_sh + 8 * piece;
   dev::store16(a.k_pool + dst, dev::load16(a.k_new + src));
   dev::store16(a.v_pool + dst, dev::load16(a.v_new + src));
+  if (a.kr_pool && g == 0 && piece < 8)  // the 128-byte rope row, once per token
+    dev::store16(a.kr_pool + page * a.kr_sb + (int64_t)(p & 63) * 64 + 8 * piece,
+                 dev::load16(a.kr_new + (int64_t)t * a.kr_new_st + 8 * piece));
 }
 
 static bool misaligned16(const void* p) { return ((uintptr_t)p) & 15; }
@@ -641,15 +655,21 @@ extern "C" gqap_status gqap_prefill(const gqap_prefill_plan_t* plan, const void*
 }
 
 extern "C" gqap_status gqap_append_kv(const gqap_chunk_plan_t* plan, const void* k_new, const void* v_new,
-                                      void* k_pool, void* v_pool, const int32_t* block_table,
-                                      const int32_t* cu_seqlens_q, const int32_t* kv_lens, void* stream) {
+                                      const void* k_rope_new, void* k_pool, void* v_pool, void* kr_pool,
+                                      const int32_t* block_table, const int32_t* cu_seqlens_q,
+                                      const int32_t* kv_lens, void* stream) {
   if (!plan || plan->magic != GQAP_PLAN_MAGIC) return fail(GQAP_ERR_INVALID_ARGUMENT, "invalid chunk plan");
   const gqap_chunk_desc_t& d = plan->desc;
   if (d.batch == 0 || d.total_q_tokens == 0) return GQAP_OK;
   if (!k_new || !v_new || !k_pool || !v_pool || !block_table || !cu_seqlens_q || !kv_lens)
     return fail(GQAP_ERR_INVALID_ARGUMENT, "null device pointer");
+  if (d.head_dim_rope && (!k_rope_new || !kr_pool))
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "k_rope_new and kr_pool are required when head_dim_rope > 0");
+  if (!d.head_dim_rope && (k_rope_new || kr_pool))
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "rope tensors given but head_dim_rope == 0");
   if (misaligned16(k_new) || misaligned16(v_new) || misaligned16(k_pool) || misaligned16(v_pool) ||
-      ((uintptr_t)block_table & 3) || ((uintptr_t)cu_seqlens_q & 3) || ((uintptr_t)kv_lens & 3))
+      (kr_pool && (misaligned16(kr_pool) || misaligned16(k_rope_new))) || ((uintptr_t)block_table & 3) ||
+      ((uintptr_t)cu_seqlens_q & 3) || ((uintptr_t)kv_lens & 3))
     return fail(GQAP_ERR_INVALID_ARGUMENT, "device pointers must be 16-byte aligned (index arrays 4-byte)");
   AppendArgs a{};
   a.k_new = (const uint16_t*)k_new;
@@ -659,6 +679,10 @@ extern "C" gqap_status gqap_append_kv(const gqap_chunk_plan_t* plan, const void*
   a.bt = block_table;
   a.cu = cu_seqlens_q;
   a.kvlens = kv_lens;
+  a.kr_new = (const uint16_t*)k_rope_new;
+  a.kr_pool = (uint16_t*)kr_pool;
+  a.kr_new_st = d.kr_new_stride_token;
+  a.kr_sb = d.kr_stride_block;
   a.new_st = d.new_stride_token;
   a.new_sh = d.new_stride_head;
   a.kv_sb = d.kv_stride_block;
@@ -677,7 +701,7 @@ extern "C" gqap_status gqap_append_kv(const gqap_chunk_plan_t* plan, const void*
 }
 
 extern "C" gqap_status gqap_chunk_prefill(const gqap_chunk_plan_t* plan, const void* q, const void* k_pool,
-                                          const void* v_pool, const int32_t* block_table,
+                                          const void* v_pool, const void* kr_pool, const int32_t* block_table,
                                           const int32_t* cu_seqlens_q, const int32_t* kv_lens, float scale,
                                           void* out, float* lse, void* workspace, uint64_t workspace_bytes,
                                           void* stream) {
@@ -688,7 +712,10 @@ extern "C" gqap_status gqap_chunk_prefill(const gqap_chunk_plan_t* plan, const v
   if (d.batch == 0 || plan->q_tiles == 0) return GQAP_OK;
   if (!q || !k_pool || !v_pool || !block_table || !cu_seqlens_q || !kv_lens || !out)
     return fail(GQAP_ERR_INVALID_ARGUMENT, "null device pointer");
+  if (d.head_dim_rope && !kr_pool) return fail(GQAP_ERR_INVALID_ARGUMENT, "kr_pool is required when head_dim_rope > 0");
+  if (!d.head_dim_rope && kr_pool) return fail(GQAP_ERR_INVALID_ARGUMENT, "kr_pool given but head_dim_rope == 0");
   if (misaligned16(q) || misaligned16(k_pool) || misaligned16(v_pool) || misaligned16(out) ||
+      (kr_pool && misaligned16(kr_pool)) ||
       ((uintptr_t)block_table & 3) || ((uintptr_t)cu_seqlens_q & 3) || ((uintptr_t)kv_lens & 3) ||
       (lse && ((uintptr_t)lse & 3)))
     return fail(GQAP_ERR_INVALID_ARGUMENT, "device pointers must be 16-byte aligned (index arrays, lse 4-byte)");
@@ -697,7 +724,7 @@ extern "C" gqap_status gqap_chunk_prefill(const gqap_chunk_plan_t* plan, const v
   a.q = (const uint16_t*)q;
   a.k = (const uint16_t*)k_pool;
   a.v = (const uint16_t*)v_pool;
-  a.kr = nullptr;
+  a.kr = (const uint16_t*)kr_pool;
   a.cu = cu_seqlens_q;
   a.mask = nullptr;
   a.out = (uint16_t*)out;
@@ -708,7 +735,8 @@ extern "C" gqap_status gqap_chunk_prefill(const gqap_chunk_plan_t* plan, const v
   a.k_sh = 0;
   a.v_st = d.head_dim;
   a.v_sh = 0;
-  a.kr_st = 0;
+  a.kr_st = d.head_dim_rope;  // rows of a rope page slab are contiguous
+  a.kr_sb = d.kr_stride_block;
   a.o_st = d.out_stride_token;
   a.o_sh = d.out_stride_head;
   a.B = d.batch;
@@ -726,7 +754,10 @@ extern "C" gqap_status gqap_chunk_prefill(const gqap_chunk_plan_t* plan, const v
   a.kv_sh = d.kv_stride_head;
   a.max_kv = d.max_kv_len;
   const dim3 grid((unsigned)d.num_q_heads * (unsigned)d.batch * (unsigned)plan->q_tiles);
-  hipLaunchKernelGGL((prefill_fwd<0, true>), grid, dim3(256), 0, (hipStream_t)stream, a);
+  if (d.head_dim_rope == 64)
+    hipLaunchKernelGGL((prefill_fwd<64, true>), grid, dim3(256), 0, (hipStream_t)stream, a);
+  else
+    hipLaunchKernelGGL((prefill_fwd<0, true>), grid, dim3(256), 0, (hipStream_t)stream, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(GQAP_ERR_HIP, "chunk prefill launch: %s", hipGetErrorString(e));
   return GQAP_OK;

@@ -282,12 +282,18 @@ gqap_status gqap_prefill(const gqap_prefill_plan_t* plan,
  * uses the keys up to kv_len - q_len + i (MATE msa_interface,
  * _normalize_qo_offset and _resolve_seqused_k).
  *
- * Shapes (bf16 tensors, D = 128 contiguous):
- *   q             [T, Hq, D]       strides q_stride_token, q_stride_head
+ * Shapes (bf16 tensors, D = 128 contiguous, Dr = head_dim_rope):
+ *   q             [T, Hq, D + Dr]  strides q_stride_token, q_stride_head
  *   k_new, v_new  [T, Hk, D]       the chunk's keys and values; strides
  *                                  new_stride_token, new_stride_head
+ *   k_rope_new    [T, 1, Dr]       MLA only: the chunk's rope keys, token
+ *                                  stride kr_new_stride_token
  *   k_pool,v_pool [NB, Hk, 64, D]  strides kv_stride_block, kv_stride_head;
  *                                  each (block, head) 64 x D slab contiguous
+ *   kr_pool       [NB, 1, 64, Dr]  MLA only: the rope cache on the same pages,
+ *                                  block stride kr_stride_block, 64 x Dr slab
+ *                                  contiguous (flare_mla_prefill, overload A:
+ *                                  the rope keys come from a paged cache)
  *   block_table   [B, Nblk] int32  row stride block_table_stride; entries
  *                                  j < ceil(kv_lens[b] / 64) are used
  *   cu_seqlens_q  [B + 1] int32    chunk b is rows cu[b] .. cu[b+1]-1 of q,
@@ -298,7 +304,8 @@ gqap_status gqap_prefill(const gqap_prefill_plan_t* plan,
  *   out           [T, Hq, D]       strides out_stride_*
  *   lse           [T, Hq] float32  optional, contiguous, natural log
  * Query i of chunk b sees key j iff j <= kv_lens[b] - q_len_b + i; query head
- * h reads KV head h / (Hq / Hk).
+ * h reads KV head h / (Hq / Hk).  With Dr = 64 (MLA) the score adds
+ * q[i, h, D:] . kr[j], the one rope key row of token j shared by every head.
  */
 typedef struct gqap_chunk_desc_t {
   int32_t batch;               /* B >= 0 */
@@ -312,13 +319,15 @@ typedef struct gqap_chunk_desc_t {
   int32_t max_q_len;           /* capacity the grid is sized for */
   int32_t max_kv_len;          /* capacity; <= Nblk * 64 */
   int32_t dtype;               /* GQAP_BF16 */
-  int32_t reserved0;
+  int32_t head_dim_rope;       /* Dr: 0, or 64 for MLA */
   int64_t q_stride_token, q_stride_head;
   int64_t new_stride_token, new_stride_head;
   int64_t out_stride_token, out_stride_head;
   int64_t kv_stride_block;     /* elements between pool blocks */
   int64_t kv_stride_head;      /* elements between heads of a block, >= 64*D */
   int64_t block_table_stride;  /* int32 elements between rows, >= Nblk */
+  int64_t kr_new_stride_token; /* MLA: elements between rope rows of k_rope_new, >= Dr */
+  int64_t kr_stride_block;     /* MLA: elements between rope-cache blocks, >= 64*Dr */
 } gqap_chunk_desc_t;
 
 typedef struct gqap_chunk_plan_t {
@@ -336,8 +345,8 @@ typedef struct gqap_chunk_plan_t {
  * Validate a chunked-prefill request.  Pure host code.  Errors:
  * INVALID_ARGUMENT (sizes, strides that overlap or break 16-byte alignment,
  * Hq % Hk, max_kv_len > Nblk * 64, max_q_len > max_kv_len), DTYPE (not bf16),
- * UNSUPPORTED (block_size != 64, D != 128, Hq * batch * ceil(max_q_len / 128)
- * >= 2^24 workgroups).
+ * UNSUPPORTED (block_size != 64, D != 128, Dr not 0 or 64, Hq * batch *
+ * ceil(max_q_len / 128) >= 2^24 workgroups).
  */
 gqap_status gqap_chunk_plan(const gqap_chunk_desc_t* desc, gqap_chunk_plan_t* plan);
 
@@ -353,16 +362,19 @@ gqap_status gqap_chunk_validate_host(const gqap_chunk_plan_t* plan, const int32_
 /*
  * Write the chunk's keys and values into the paged cache: token i of chunk b
  * goes to logical position p = kv_lens[b] - q_len_b + i, i.e. row p % 64 of
- * pool block block_table[b, p / 64], for every KV head.  Nothing else in the
- * pools changes.  Asynchronous on `stream`; 16-byte aligned pointers.
+ * pool block block_table[b, p / 64], for every KV head, and with Dr = 64 its
+ * rope row to the same row of kr_pool (k_rope_new and kr_pool are NULL iff
+ * Dr == 0).  Nothing else in the pools changes.  Asynchronous on `stream`;
+ * 16-byte aligned pointers.
  */
 gqap_status gqap_append_kv(const gqap_chunk_plan_t* plan, const void* k_new, const void* v_new,
-                           void* k_pool, void* v_pool, const int32_t* block_table,
-                           const int32_t* cu_seqlens_q, const int32_t* kv_lens, void* stream);
+                           const void* k_rope_new, void* k_pool, void* v_pool, void* kr_pool,
+                           const int32_t* block_table, const int32_t* cu_seqlens_q, const int32_t* kv_lens,
+                           void* stream);
 
 /*
  * Attention of each chunk to its sequence's cached keys (the chunk's own
- * included, so gqap_append_kv runs first).  Only key rows j < kv_lens[b] are
+ * included, so gqap_append_kv runs first).  kr_pool is NULL iff Dr == 0.  Only key rows j < kv_lens[b] are
  * used; a key tile that runs past kv_lens[b] repeats row kv_lens[b] - 1,
  * whose probability is then exactly 0.  A query with no visible key gets
  * out = 0 and lse = -inf.  workspace may be NULL when plan->workspace_bytes
@@ -370,7 +382,7 @@ gqap_status gqap_append_kv(const gqap_chunk_plan_t* plan, const void* k_new, con
  * and kv_lens 4-byte).
  */
 gqap_status gqap_chunk_prefill(const gqap_chunk_plan_t* plan, const void* q, const void* k_pool,
-                               const void* v_pool, const int32_t* block_table,
+                               const void* v_pool, const void* kr_pool, const int32_t* block_table,
                                const int32_t* cu_seqlens_q, const int32_t* kv_lens, float scale,
                                void* out, float* lse, void* workspace, uint64_t workspace_bytes,
                                void* stream);

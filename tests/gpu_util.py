@@ -122,6 +122,8 @@ class DeviceChunk:
         self.v_new = bits_to_tensor(case.v_new, "bf16").to(device)
         self.k_pool = bits_to_tensor(case.k_pool, "bf16").to(device)
         self.v_pool = bits_to_tensor(case.v_pool, "bf16").to(device)
+        self.kr_new = bits_to_tensor(case.kr_new, "bf16").to(device) if case.kr_new is not None else None
+        self.kr_pool = bits_to_tensor(case.kr_pool, "bf16").to(device) if case.kr_pool is not None else None
         self.bt = torch.from_numpy(np.ascontiguousarray(case.block_table, dtype=np.int32)).to(device)
         self.cu = torch.from_numpy(np.ascontiguousarray(case.cu_seqlens_q, dtype=np.int32)).to(device)
         self.kvl = torch.from_numpy(np.ascontiguousarray(case.kv_lens, dtype=np.int32)).to(device)
@@ -131,17 +133,17 @@ class DeviceChunk:
         max_q = max(1, int(case.q_lens.max())) if case.B else 1
         max_kv = max(max_q, int(case.kv_lens.max())) if case.B else 1
         self.desc = gq.chunk_desc(self.q, self.k_new, self.k_pool, self.bt, batch=case.B, max_q_len=max_q,
-                                  max_kv_len=max_kv, out=self.out)
+                                  max_kv_len=max_kv, out=self.out, k_rope_new=self.kr_new, kr_pool=self.kr_pool)
         self.plan = gq.gqap_chunk_plan(self.desc)
         gq.gqap_chunk_validate_host(self.plan, case.block_table, case.cu_seqlens_q, case.kv_lens)
 
     def append(self, stream=None):
-        gq.gqap_append_kv(self.plan, self.k_new, self.v_new, self.k_pool, self.v_pool, self.bt, self.cu, self.kvl,
-                          stream=stream)
+        gq.gqap_append_kv(self.plan, self.k_new, self.v_new, self.kr_new, self.k_pool, self.v_pool, self.kr_pool,
+                          self.bt, self.cu, self.kvl, stream=stream)
 
     def run(self, stream=None):
-        gq.gqap_chunk_prefill(self.plan, self.q, self.k_pool, self.v_pool, self.bt, self.cu, self.kvl,
-                              self.case.scale, self.out, self.lse, stream=stream)
+        gq.gqap_chunk_prefill(self.plan, self.q, self.k_pool, self.v_pool, self.kr_pool, self.bt, self.cu,
+                              self.kvl, self.case.scale, self.out, self.lse, stream=stream)
         return self.out, self.lse
 
     def results(self):
@@ -149,6 +151,9 @@ class DeviceChunk:
         return tensor_to_f64(self.out), self.lse.detach().cpu().numpy().astype(np.float64)
 
     def pools_bits(self):
+        """(k, v) pools as bf16 bits, plus the rope pool for MLA cases."""
         torch.cuda.synchronize()
-        return (self.k_pool.detach().cpu().view(torch.int16).numpy().view(np.uint16),
-                self.v_pool.detach().cpu().view(torch.int16).numpy().view(np.uint16))
+        bits = lambda t: t.detach().cpu().view(torch.int16).numpy().view(np.uint16)
+        if self.kr_pool is None:
+            return bits(self.k_pool), bits(self.v_pool)
+        return bits(self.k_pool), bits(self.v_pool), bits(self.kr_pool)

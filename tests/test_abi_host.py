@@ -280,12 +280,26 @@ def test_chunk_plan_baseline(gq):
     ("new_stride_token", 100, "INVALID_ARGUMENT"),
     ("block_table_stride", 50, "INVALID_ARGUMENT"),
     ("batch", -1, "INVALID_ARGUMENT"),
+    ("head_dim_rope", 32, "UNSUPPORTED"),
+    ("head_dim_rope", 64, "INVALID_ARGUMENT"),          # no rope strides, and q rows too narrow
 ])
 def test_chunk_plan_rejects(gq, field, value, status):
     d = baseline_chunk_desc(gq)
     setattr(d, field, value)
     got = gq.lib().gqap_chunk_plan(ctypes.byref(d), ctypes.byref(gq.ChunkPlan()))
     assert gq.STATUS_NAMES[got] == status, gq.gqap_last_error()
+
+
+def test_chunk_plan_mla(gq):
+    d = baseline_chunk_desc(gq)
+    d.head_dim_rope = 64
+    d.q_stride_head, d.q_stride_token = 192, 192 * 32
+    d.kr_new_stride_token, d.kr_stride_block = 64, 64 * 64
+    p = gq.gqap_chunk_plan(d)
+    assert p.magic == gq.PLAN_MAGIC and p.kernel == 2
+    d.kr_stride_block = 64 * 63
+    with pytest.raises(gq.GqapError, match="rope strides"):
+        gq.gqap_chunk_plan(d)
 
 
 def test_chunk_validate_host(gq):
@@ -313,11 +327,14 @@ def test_chunk_validate_host(gq):
 
 def test_chunk_calls_reject_bad_arguments_without_a_gpu(gq):
     p = gq.gqap_chunk_plan(baseline_chunk_desc(gq))
-    st = gq.lib().gqap_chunk_prefill(ctypes.byref(p), None, None, None, None, None, None, 1.0, None, None,
-                                     None, 0, None)
+    st = gq.lib().gqap_chunk_prefill(ctypes.byref(p), None, None, None, None, None, None, None, 1.0, None,
+                                     None, None, 0, None)
     assert gq.STATUS_NAMES[st] == "INVALID_ARGUMENT"
-    st = gq.lib().gqap_append_kv(ctypes.byref(p), None, None, None, None, None, None, None, None)
+    st = gq.lib().gqap_append_kv(ctypes.byref(p), None, None, None, None, None, None, None, None, None, None)
     assert gq.STATUS_NAMES[st] == "INVALID_ARGUMENT"
-    st = gq.lib().gqap_chunk_prefill(ctypes.byref(gq.ChunkPlan()), 16, 16, 16, 16, 16, 16, 1.0, 16, None,
+    # a rope cache passed to a plan without rope
+    st = gq.lib().gqap_chunk_prefill(ctypes.byref(p), 16, 16, 16, 16, 16, 16, 16, 1.0, 16, None, None, 0, None)
+    assert gq.STATUS_NAMES[st] == "INVALID_ARGUMENT"
+    st = gq.lib().gqap_chunk_prefill(ctypes.byref(gq.ChunkPlan()), 16, 16, 16, None, 16, 16, 16, 1.0, 16, None,
                                      None, 0, None)
     assert gq.STATUS_NAMES[st] == "INVALID_ARGUMENT"      # unplanned (magic 0)

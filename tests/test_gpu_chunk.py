@@ -44,17 +44,19 @@ def _rows_sample(case, n_mid=48, seed=0):
 
 def _run(gu, case, rows=None, tol=TOL):
     gu.announce(f"chunk {case.name} kv_lens={case.kv_lens.tolist()[:8]} q_lens={case.q_lens.tolist()[:8]} "
-                f"Hq={case.Hq} Hk={case.Hk} seed={case.meta.get('seed')}")
+                f"Hq={case.Hq} Hk={case.Hk} Dr={case.D_rope} seed={case.meta.get('seed')}")
     dc = gu.DeviceChunk(case)
     dc.append()
-    kp, vp = O.append_kv(case.k_new, case.v_new, case.k_pool, case.v_pool, case.block_table, case.cu_seqlens_q,
-                         case.kv_lens)
-    gk, gv = dc.pools_bits()
-    assert np.array_equal(gk, kp) and np.array_equal(gv, vp), "appended pools differ from the oracle's"
+    pools = O.append_kv(case.k_new, case.v_new, case.k_pool, case.v_pool, case.block_table, case.cu_seqlens_q,
+                        case.kv_lens, kr_new=case.kr_new, kr_pool=case.kr_pool)
+    got = dc.pools_bits()
+    assert len(got) == len(pools) and all(np.array_equal(g, r) for g, r in zip(got, pools)), \
+        "appended pools differ from the oracle's"
+    kp, vp = pools[0], pools[1]
     dc.run()
     out, lse = dc.results()
     ref, ref_lse = O.chunk_prefill(case.q, kp, vp, case.block_table, case.cu_seqlens_q, case.kv_lens, case.scale,
-                                   dtype="bf16", rows=rows)
+                                   dtype="bf16", rows=rows, kr_pool=pools[2] if len(pools) == 3 else None)
     if rows is not None:
         out, lse = out[rows], lse[rows]
     e_out = gu.max_abs_err(out, ref)
@@ -89,7 +91,7 @@ def test_one_token_chunks_equal_decode(gu):
     case = gen.make_chunk_case(name="chunk_decode", seed=63, prefix_lens=[1023, 64, 5, 300],
                                q_lens=[1, 1, 1, 1], Hq=16, Hk=4)
     dc, out, lse = _run(gu, case)
-    kp, vp = dc.pools_bits()
+    kp, vp = dc.pools_bits()[:2]
     ref, ref_lse = O.paged_decode(case.q, kp, vp, case.block_table, case.kv_lens, case.scale, q_dtype="bf16",
                                   kv_dtype="bf16")
     assert gu.max_abs_err(out, ref) <= TOL and gu.lse_err(lse, ref_lse) <= TOL
@@ -136,4 +138,19 @@ def test_chunk_long_prefix_sampled(gu):
     """A 9000-key cache (more than 128 pages: two block-table words) and a
     600-token chunk."""
     case = gen.make_chunk_case(name="chunk_long", seed=67, prefix_lens=[8400, 40], q_lens=[600, 40], Hq=8, Hk=1)
+    _run(gu, case, rows=_rows_sample(case))
+
+
+@pytest.mark.parametrize("Hq,Hk", [(16, 16), (8, 2)])
+def test_mla_chunk_rope_from_cache(gu, Hq, Hk):
+    """MLA: Q 192 = 128 + 64 rope, the rope keys appended to and read from a
+    one-head rope cache on the same pages."""
+    case = gen.make_chunk_case(name="chunk_mla", seed=68, prefix_lens=[0, 63, 130, 700], q_lens=[5, 129, 64, 300],
+                               Hq=Hq, Hk=Hk, D_rope=64)
+    _run(gu, case)
+
+
+def test_mla_chunk_long_prefix_sampled(gu):
+    case = gen.make_chunk_case(name="chunk_mla_long", seed=69, prefix_lens=[5000, 1], q_lens=[512, 127], Hq=16,
+                               Hk=16, D_rope=64)
     _run(gu, case, rows=_rows_sample(case))

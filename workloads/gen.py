@@ -405,7 +405,13 @@ class ChunkCase:
     v_pool: np.ndarray
     block_table: np.ndarray   # [B, Nblk] int32 (-1 past ceil(kv_len / 64))
     scale: float
+    kr_new: Optional[np.ndarray] = None    # MLA: [T, 1, Dr] bf16 bits, the chunk's rope keys
+    kr_pool: Optional[np.ndarray] = None   # MLA: [NB, 1, 64, Dr] bf16 bits, rope cache on the same pages
     meta: dict = field(default_factory=dict)
+
+    @property
+    def D_rope(self) -> int:
+        return 0 if self.kr_pool is None else int(self.kr_pool.shape[3])
 
     @property
     def B(self) -> int:
@@ -429,7 +435,7 @@ class ChunkCase:
         return n
 
     def flops(self) -> int:
-        return 2 * self.Hq * (self.D + self.D) * self.visible_pairs()
+        return 2 * self.Hq * (self.D + self.D_rope + self.D) * self.visible_pairs()
 
 
 def make_chunk_case(
@@ -441,20 +447,23 @@ def make_chunk_case(
     Hq: int,
     Hk: int,
     D: int = 128,
+    D_rope: int = 0,
     spare_blocks: int = 2,
     scale: Optional[float] = None,
 ) -> ChunkCase:
     """Draw a chunked-prefill problem: sequence b already holds prefix_lens[b]
     keys in a paged bf16 cache and appends a chunk of q_lens[b] tokens.
 
-    Draw order: block_table permutation -> q -> k_new -> v_new -> k_pool -> v_pool.
+    Draw order: block_table permutation -> q -> k_new -> v_new -> k_pool -> v_pool
+    (-> kr_new -> kr_pool with a rope width D_rope: MLA, one rope head per token on
+    the same pages; q then has D + D_rope columns).
     The pool has sum(ceil(kv_len / 64)) + spare_blocks blocks; the logical blocks
     (b, j) in row-major order take a seeded permutation of the pool ids.  Pool
     rows at or past each prefix (where the chunk will be appended), the rows past
     kv_len and the spare blocks are NaN.
     """
     ss = np.random.SeedSequence(seed)
-    s_tab, s_q, s_kn, s_vn, s_k, s_v = ss.spawn(6)
+    s_tab, s_q, s_kn, s_vn, s_k, s_v, s_rn, s_r = ss.spawn(8)
     prefix = np.asarray(prefix_lens, dtype=np.int32)
     ql = np.asarray(q_lens, dtype=np.int32)
     B = prefix.shape[0]
@@ -472,23 +481,28 @@ def make_chunk_case(
     cu = np.zeros(B + 1, np.int32)
     cu[1:] = np.cumsum(ql)
     T = int(cu[-1])
-    q = to_bf16_bits(normal_f32(s_q, T * Hq * D).reshape(T, Hq, D))
+    q = to_bf16_bits(normal_f32(s_q, T * Hq * (D + D_rope)).reshape(T, Hq, D + D_rope))
     k_new = to_bf16_bits(normal_f32(s_kn, T * Hk * D).reshape(T, Hk, D))
     v_new = to_bf16_bits(normal_f32(s_vn, T * Hk * D).reshape(T, Hk, D))
+    keep = np.zeros((NB, BLOCK), bool)
+    for b in range(B):
+        for t in range(int(prefix[b])):
+            keep[block_table[b, t // BLOCK], t % BLOCK] = True
     pools = []
-    for s_x in (s_k, s_v):
-        x = to_bf16_bits(normal_f32(s_x, NB * Hk * BLOCK * D).reshape(NB, Hk, BLOCK, D))
-        keep = np.zeros((NB, BLOCK), bool)
-        for b in range(B):
-            for t in range(int(prefix[b])):
-                keep[block_table[b, t // BLOCK], t % BLOCK] = True
+    for s_x, heads, width in ((s_k, Hk, D), (s_v, Hk, D), (s_r, 1, D_rope)):
+        if width == 0:
+            pools.append(None)
+            continue
+        x = to_bf16_bits(normal_f32(s_x, NB * heads * BLOCK * width).reshape(NB, heads, BLOCK, width))
         x.transpose(0, 2, 1, 3)[~keep] = BF16_NAN
         pools.append(x)
+    kr_new = to_bf16_bits(normal_f32(s_rn, T * D_rope).reshape(T, 1, D_rope)) if D_rope else None
     if scale is None:
-        scale = 1.0 / math.sqrt(D)
+        scale = 1.0 / math.sqrt(D + D_rope)
     return ChunkCase(name=name, kv_lens=kv_lens, cu_seqlens_q=cu, Hq=Hq, Hk=Hk, D=D, q=q, k_new=k_new,
                      v_new=v_new, k_pool=pools[0], v_pool=pools[1], block_table=block_table,
-                     scale=float(scale), meta={"seed": seed, "prefix_lens": prefix})
+                     scale=float(scale), kr_new=kr_new, kr_pool=pools[2],
+                     meta={"seed": seed, "prefix_lens": prefix})
 
 
 def prefill_chunk_bf16(seed: int = 1006, B: int = 8, prefix_range=(1024, 6144), q_len: int = 512) -> ChunkCase:
@@ -500,6 +514,16 @@ def prefill_chunk_bf16(seed: int = 1006, B: int = 8, prefix_range=(1024, 6144), 
                            q_lens=[q_len] * B, Hq=32, Hk=8, D=128)
 
 
+def prefill_chunk_mla_bf16(seed: int = 1008, B: int = 4, prefix_range=(1024, 4096), q_len: int = 512) -> ChunkCase:
+    """MLA chunked prefill: 4 sequences with cached prefixes ~ U{1024..4096}
+    appending 512-token chunks; 16 heads, Q 192 = 128 + 64 rope, the rope keys
+    in a one-head paged rope cache, V / output 128, bf16."""
+    lo, hi = prefix_range
+    prefix = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed).spawn(1)[0])).integers(lo, hi + 1, size=B)
+    return make_chunk_case(name="prefill_chunk_mla_bf16", seed=seed + 1, prefix_lens=prefix.tolist(),
+                           q_lens=[q_len] * B, Hq=16, Hk=16, D=128, D_rope=64)
+
+
 CONFIGS = {
     "decode_tiny_f32": decode_tiny_fp32,
     "decode_gqa_bf16": decode_gqa_bf16,
@@ -507,4 +531,5 @@ CONFIGS = {
     "decode_long_fp8": decode_long_fp8,
     "prefill_blocksparse_bf16": prefill_blocksparse_bf16,
     "prefill_chunk_bf16": prefill_chunk_bf16,
+    "prefill_chunk_mla_bf16": prefill_chunk_mla_bf16,
 }
