@@ -7,6 +7,7 @@ package imports nothing from the device library.
 from .attention import (  # noqa: F401
     BLOCK,
     append_kv,
+    block_table_from_csr,
     chunk_prefill,
     bf16_to_f64,
     cu_seqlens_from_lengths,

@@ -390,3 +390,21 @@ def chunk_prefill(
                 out[idx, heads] = o
                 lse[idx, heads] = ls
     return out, lse
+
+
+# --------------------------------------------------------------------------
+# CSR page input
+# --------------------------------------------------------------------------
+
+def block_table_from_csr(kv_indices: np.ndarray, kv_page_indptr: np.ndarray, max_blocks: int) -> np.ndarray:
+    """Padded block table [B, max_blocks] from the flat page list of MATE
+    msa_interface (_build_page_table_from_flat_kv_indices): the pages of
+    sequence b are kv_indices[indptr[b] : indptr[b + 1]], in order; the rest of
+    each row is padding (-1).  Pages past max_blocks are not represented."""
+    ip = np.asarray(kv_page_indptr, dtype=np.int64)
+    B = ip.shape[0] - 1
+    table = np.full((B, max_blocks), -1, np.int32)
+    for b in range(B):
+        pages = np.asarray(kv_indices[ip[b]:ip[b + 1]], dtype=np.int32)[:max_blocks]
+        table[b, :pages.shape[0]] = pages
+    return table

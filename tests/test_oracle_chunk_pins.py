@@ -267,3 +267,38 @@ def test_mla_append_writes_the_rope_rows_on_the_same_pages():
         got = O.gather_kv_rows(rp2, table, b, 0, L)
         np.testing.assert_array_equal(got[: L - n], R[b][: L - n])
         np.testing.assert_array_equal(got[L - n:], rn[cu[b]:cu[b + 1], 0])
+
+
+# ---------------------------------------------------------------- CSR page input
+
+def test_csr_block_table_round_trip_and_decode_equivalence():
+    """A padded table written out as (kv_indices, kv_page_indptr) -- each
+    sequence's used pages in order, indptr the prefix of the page counts
+    ceil(L / 64) -- and read back gives the used entries of the original
+    table and -1 padding, so decode through it is unchanged."""
+    rng = np.random.default_rng(80)
+    B, Hq, Hk, D = 4, 4, 2, 8
+    lens = [130, 0, 64, 5]
+    nblk, NB = 3, 12
+    table = rng.permutation(NB)[: B * nblk].reshape(B, nblk).astype(np.int32)
+    counts = [(L + 63) // 64 for L in lens]
+    kv_indices = np.concatenate([table[b, :counts[b]] for b in range(B)]).astype(np.int32)
+    indptr = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    back = O.block_table_from_csr(kv_indices, indptr, nblk)
+    for b in range(B):
+        np.testing.assert_array_equal(back[b, :counts[b]], table[b, :counts[b]])
+        assert np.all(back[b, counts[b]:] == -1)
+    q = rng.standard_normal((B, Hq, D))
+    kp = rng.standard_normal((NB, Hk, 64, D))
+    vp = rng.standard_normal((NB, Hk, 64, D))
+    sl = np.array(lens, np.int32)
+    o1, l1 = O.paged_decode(q, kp, vp, table, sl, 0.3)
+    o2, l2 = O.paged_decode(q, kp, vp, back, sl, 0.3)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+
+
+def test_csr_block_table_follows_the_flat_index_order():
+    """Hand example: three sequences with 2, 0 and 3 pages."""
+    t = O.block_table_from_csr(np.array([7, 3, 9, 1, 4], np.int32), np.array([0, 2, 2, 5], np.int32), 4)
+    np.testing.assert_array_equal(t, [[7, 3, -1, -1], [-1, -1, -1, -1], [9, 1, 4, -1]])
