@@ -29,7 +29,7 @@ PLAN_MAGIC = 0x47514150
 C_FUNCTIONS = (
     "gqap_decode_plan", "gqap_decode_validate_host", "gqap_paged_decode", "gqap_debug_gather_kv",
     "gqap_prefill_plan", "gqap_prefill", "gqap_chunk_plan", "gqap_chunk_validate_host", "gqap_append_kv",
-    "gqap_chunk_prefill", "gqap_last_error", "gqap_version",
+    "gqap_chunk_prefill", "gqap_block_table_from_csr", "gqap_last_error", "gqap_version",
 )
 
 
@@ -135,6 +135,8 @@ def _load() -> ctypes.CDLL:
     lib.gqap_chunk_prefill.argtypes = [ctypes.POINTER(ChunkPlan), vp, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp, u64,
                                        vp]
     lib.gqap_chunk_prefill.restype = st
+    lib.gqap_block_table_from_csr.argtypes = [vp, vp, i32, i32, ctypes.c_int64, vp, vp]
+    lib.gqap_block_table_from_csr.restype = st
     lib.gqap_last_error.argtypes = []
     lib.gqap_last_error.restype = ctypes.c_char_p
     lib.gqap_version.argtypes = []
@@ -257,6 +259,14 @@ def gqap_chunk_prefill(plan: ChunkPlan, q, k_pool, v_pool, kr_pool, block_table,
     _check(_lib.gqap_chunk_prefill(ctypes.byref(plan), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(kr_pool),
                                    _ptr(block_table), _ptr(cu_seqlens_q), _ptr(kv_lens), scale, _ptr(out),
                                    _ptr(lse), _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def gqap_block_table_from_csr(kv_indices, kv_page_indptr, batch: int, max_blocks_per_seq: int, block_table,
+                              block_table_stride: Optional[int] = None, stream=None) -> None:
+    if block_table_stride is None:
+        block_table_stride = block_table.stride(0)
+    _check(_lib.gqap_block_table_from_csr(_ptr(kv_indices), _ptr(kv_page_indptr), batch, max_blocks_per_seq,
+                                          block_table_stride, _ptr(block_table), _stream(stream)))
 
 
 # ------------------------------------------------------------------ descriptors from tensors

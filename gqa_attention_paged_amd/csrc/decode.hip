@@ -692,6 +692,20 @@ __global__ __launch_bounds__(64) void decode_combine(DecodeArgs a) {
   if (a.lse && lane == 0) a.lse[bh] = nblk > 0 ? (M + log2f(den)) * kLn2 : -INFINITY;
 }
 
+// Padded block table from the flat CSR page list (MATE msa_interface,
+// _build_page_table_from_flat_kv_indices): row b holds the pages
+// kv_indices[indptr[b] .. indptr[b+1]) in order, then -1.  One thread per
+// table entry.
+__global__ __launch_bounds__(256) void block_table_from_csr(const int32_t* kv_indices, const int32_t* indptr,
+                                                           int32_t batch, int32_t width, int64_t stride,
+                                                           int32_t* table) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)batch * width) return;
+  const int b = (int)(i / width), j = (int)(i - (int64_t)b * width);
+  const int p0 = indptr[b], n = indptr[b + 1] - p0;
+  table[(int64_t)b * stride + j] = j < n ? kv_indices[(int64_t)p0 + j] : -1;
+}
+
 // Copy logical rows of one (sequence, KV head) out of the pool with the same
 // slab address function the decode kernels use.
 __global__ __launch_bounds__(256) void debug_gather_kv(const unsigned char* pool, const int32_t* block_table,
@@ -839,5 +853,26 @@ extern "C" gqap_status gqap_debug_gather_kv(const gqap_decode_plan_t* plan, cons
                      num_rows, (unsigned char*)dst);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(GQAP_ERR_HIP, "gather launch: %s", hipGetErrorString(e));
+  return GQAP_OK;
+}
+
+extern "C" gqap_status gqap_block_table_from_csr(const int32_t* kv_indices, const int32_t* kv_page_indptr,
+                                                 int32_t batch, int32_t max_blocks_per_seq,
+                                                 int64_t block_table_stride, int32_t* block_table, void* stream) {
+  if (batch < 0) return fail(GQAP_ERR_INVALID_ARGUMENT, "batch must be >= 0");
+  if (max_blocks_per_seq < 1) return fail(GQAP_ERR_INVALID_ARGUMENT, "max_blocks_per_seq must be positive");
+  if (block_table_stride < max_blocks_per_seq)
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "block_table_stride %lld < max_blocks_per_seq %d",
+                (long long)block_table_stride, max_blocks_per_seq);
+  if (batch == 0) return GQAP_OK;
+  if (!kv_indices || !kv_page_indptr || !block_table) return fail(GQAP_ERR_INVALID_ARGUMENT, "null device pointer");
+  if (misaligned(kv_indices, 4) || misaligned(kv_page_indptr, 4) || misaligned(block_table, 4))
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "index arrays must be 4-byte aligned");
+  const int64_t n = (int64_t)batch * max_blocks_per_seq;
+  if (n >= ((int64_t)1 << 39)) return fail(GQAP_ERR_UNSUPPORTED, "block table too large for one launch");
+  hipLaunchKernelGGL(block_table_from_csr, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, (hipStream_t)stream,
+                     kv_indices, kv_page_indptr, batch, max_blocks_per_seq, block_table_stride, block_table);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(GQAP_ERR_HIP, "block_table_from_csr launch: %s", hipGetErrorString(e));
   return GQAP_OK;
 }

@@ -388,6 +388,30 @@ gqap_status gqap_chunk_prefill(const gqap_chunk_plan_t* plan, const void* q, con
                                void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* CSR page input                                                            */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Padded block table from a flat page list (MATE msa_interface,
+ * _build_page_table_from_flat_kv_indices): the pages of sequence b are
+ * kv_indices[kv_page_indptr[b] .. kv_page_indptr[b+1]), in order.  Writes
+ * block_table[b, j] = kv_indices[kv_page_indptr[b] + j] for j < min(pages of b,
+ * max_blocks_per_seq) and -1 for the rest of the row up to max_blocks_per_seq
+ * (pages past the row width are not represented).  With it, every call that
+ * takes a block table also takes CSR page input.
+ *   kv_indices      [total pages] int32 device
+ *   kv_page_indptr  [batch + 1] int32 device, non-decreasing, starting at 0
+ *   block_table     [batch, >= max_blocks_per_seq] int32 device, row stride
+ *                   block_table_stride (elements), written
+ * Errors: INVALID_ARGUMENT (null pointer, batch < 0, max_blocks_per_seq < 1,
+ * block_table_stride < max_blocks_per_seq, misaligned pointer), HIP.
+ * Asynchronous on `stream`.
+ */
+gqap_status gqap_block_table_from_csr(const int32_t* kv_indices, const int32_t* kv_page_indptr, int32_t batch,
+                                      int32_t max_blocks_per_seq, int64_t block_table_stride,
+                                      int32_t* block_table, void* stream);
+
+/* ------------------------------------------------------------------------ */
 
 /* Message of the last non-OK status on this host thread ("" if none). */
 const char* gqap_last_error(void);

@@ -338,3 +338,13 @@ def test_chunk_calls_reject_bad_arguments_without_a_gpu(gq):
     st = gq.lib().gqap_chunk_prefill(ctypes.byref(gq.ChunkPlan()), 16, 16, 16, None, 16, 16, 16, 1.0, 16, None,
                                      None, 0, None)
     assert gq.STATUS_NAMES[st] == "INVALID_ARGUMENT"      # unplanned (magic 0)
+
+
+def test_csr_conversion_rejects_bad_arguments_without_a_gpu(gq):
+    lib = gq.lib()
+    assert gq.STATUS_NAMES[lib.gqap_block_table_from_csr(16, 16, -1, 4, 4, 16, None)] == "INVALID_ARGUMENT"
+    assert gq.STATUS_NAMES[lib.gqap_block_table_from_csr(16, 16, 2, 0, 4, 16, None)] == "INVALID_ARGUMENT"
+    assert gq.STATUS_NAMES[lib.gqap_block_table_from_csr(16, 16, 2, 4, 3, 16, None)] == "INVALID_ARGUMENT"
+    assert gq.STATUS_NAMES[lib.gqap_block_table_from_csr(None, 16, 2, 4, 4, 16, None)] == "INVALID_ARGUMENT"
+    assert gq.STATUS_NAMES[lib.gqap_block_table_from_csr(18, 16, 2, 4, 4, 16, None)] == "INVALID_ARGUMENT"
+    assert lib.gqap_block_table_from_csr(None, None, 0, 4, 4, None, None) == 0   # empty batch: nothing to do
