@@ -16,5 +16,6 @@ from .attention import (  # noqa: F401
     gather_kv_rows,
     paged_decode,
     ragged_prefill,
+    ragged_prefill_fp8,
     widen,
 )

@@ -7,6 +7,7 @@ import types
 import pytest
 
 from oracle import attention as O
+from tests import test_oracle_fp8_prefill_pins as P8
 from tests import test_oracle_pins as P
 
 SRC = inspect.getsource(O)
@@ -54,13 +55,25 @@ MUTANTS = {
     "lse_sign": ("m_safe + np.log(", "m_safe - np.log(", [P.test_decode_matches_torch_sdpa]),
     "gqa_ratio_inverted_prefill": ("Qc = Q[gi, heads, :]", "Qc = Q[gi, g:g + r, :]",
                                    [P.test_prefill_gqa_matches_sdpa]),
+    "fp8_q_scale_dropped": ('q = widen(q_nope, "e4m3fn") * float(q_scale)', 'q = widen(q_nope, "e4m3fn")',
+                            [P8.test_fp8_prefill_matches_bruteforce_on_torch_decoded_codes]),
+    "fp8_k_scale_dropped": ('kk = widen(k, "e4m3fn") * float(k_scale)', 'kk = widen(k, "e4m3fn")',
+                            [P8.test_fp8_prefill_gqa_without_rope_matches_sdpa]),
+    "fp8_scale_on_rope": ('np.concatenate([q, widen(q_rope, "bf16")], axis=2)',
+                          'np.concatenate([q, widen(q_rope, "bf16") * float(q_scale)], axis=2)',
+                          [P8.test_fp8_prefill_scales_leave_the_rope_part_alone]),
+    "fp8_rope_dropped": ('np.concatenate([q, widen(q_rope, "bf16")], axis=2)',
+                         'np.concatenate([q, 0 * widen(q_rope, "bf16")], axis=2)',
+                         [P8.test_fp8_prefill_matches_sdpa_with_concatenated_rope_key]),
 }
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_planted_mistake_is_caught(name, monkeypatch):
     old, new, catchers = MUTANTS[name]
-    monkeypatch.setattr(P, "O", _mutant(old, new))
+    mutant = _mutant(old, new)
+    monkeypatch.setattr(P, "O", mutant)
+    monkeypatch.setattr(P8, "O", mutant)
     caught = []
     for fn in catchers:
         try:

@@ -282,6 +282,12 @@ class PrefillCase:
     block_mask: Optional[np.ndarray]  # [B, nb, nb] uint8, or None
     scale: float
     dtype: str = "bf16"
+    # dtype 'e4m3fn': q holds the nope part only, [T, Hq, D_nope] e4m3fn codes,
+    # k [T, Hk, D_nope] e4m3fn codes, q_rope [T, Hq, D_rope] bf16 bits (None
+    # without rope); q_scale / k_scale are the two tensors' scales.
+    q_rope: Optional[np.ndarray] = None
+    q_scale: float = 1.0
+    k_scale: float = 1.0
     meta: dict = field(default_factory=dict)
 
     @property
@@ -372,6 +378,41 @@ def make_prefill_case(
                        block_mask=block_mask, scale=float(scale), meta={"seed": seed})
 
 
+def _bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).float().numpy()
+
+
+def make_prefill_fp8_case(
+    *,
+    name: str,
+    seed: int,
+    seq_lens: Sequence[int],
+    Hq: int,
+    Hk: int,
+    D_rope: int = 64,
+    mask_density: Optional[float] = None,
+    scale: Optional[float] = None,
+) -> PrefillCase:
+    """The bf16 prefill problem of make_prefill_case (same seed, same draws,
+    Dn = 128, Dv = 128), with the nope part of Q and all of K quantised to fp8
+    e4m3fn, each tensor with the per-tensor scale amax / 448 of the fp8 KV
+    recipe; the rope parts and V stay bf16.  scale defaults to 1/sqrt(128 + D_rope)."""
+    base = make_prefill_case(name=name, seed=seed, seq_lens=seq_lens, Hq=Hq, Hk=Hk, D_qk=128 + D_rope,
+                             D_rope=D_rope, D_v=128, mask_density=mask_density, scale=scale)
+    qf = _bf16_bits_to_f32(base.q[:, :, :128])
+    kf = _bf16_bits_to_f32(base.k)
+    scales = []
+    for x in (qf, kf):
+        amax = float(np.abs(x).max()) if x.size else 1.0
+        scales.append(float(np.float32(amax) / np.float32(E4M3FN_MAX)) if amax > 0 else 1.0)
+    base.q_rope = np.ascontiguousarray(base.q[:, :, 128:]) if D_rope else None
+    base.q = to_e4m3fn_bits(qf, scales[0])
+    base.k = to_e4m3fn_bits(kf, scales[1])
+    base.q_scale, base.k_scale = scales
+    base.dtype = "e4m3fn"
+    return base
+
+
 def prefill_mla_bf16(seed: int = 1003, seq_lens=(512, 1024, 2048, 3000)) -> PrefillCase:
     """Ragged MLA prefill: 16 heads, Q 192 = 128 nope + 64 rope, K_rope shared
     [T, 1, 64], V / output 128, causal, scale 1/sqrt(192)."""
@@ -384,6 +425,13 @@ def prefill_blocksparse_bf16(seed: int = 1005, P: int = 8192, B: int = 2) -> Pre
     mask with ~25% of the strictly-lower blocks on."""
     return make_prefill_case(name="prefill_blocksparse_bf16", seed=seed, seq_lens=[P] * B,
                              Hq=32, Hk=8, D_qk=128, D_rope=0, D_v=128, mask_density=0.25)
+
+
+def prefill_mla_fp8(seed: int = 1009, seq_lens=(512, 1024, 2048, 3000)) -> PrefillCase:
+    """The ragged MLA prefill shape (16 heads, Q 128 nope + 64 rope, shared
+    K_rope, V / output 128, causal, scale 1/sqrt(192)) with q_nope and K in fp8
+    e4m3fn, one scale each; q_rope, K_rope and V bf16."""
+    return make_prefill_fp8_case(name="prefill_mla_fp8", seed=seed, seq_lens=seq_lens, Hq=16, Hk=16, D_rope=64)
 
 
 # ---------------------------------------------------------------------------
@@ -532,4 +580,5 @@ CONFIGS = {
     "prefill_blocksparse_bf16": prefill_blocksparse_bf16,
     "prefill_chunk_bf16": prefill_chunk_bf16,
     "prefill_chunk_mla_bf16": prefill_chunk_mla_bf16,
+    "prefill_mla_fp8": prefill_mla_fp8,
 }
