@@ -9,7 +9,8 @@ V rows) divided by the measured time per step.  Inputs are resident in HBM
 before the timed region; consecutive steps read different copies of the KV
 pool, so no step is served from the 256 MB last-level cache by its
 predecessor.  The other workloads (fp8 KV decode, MLA prefill, block-sparse
-prefill) are measured the same way and reported under "secondary".
+prefill, fp8 MLA prefill, chunked prefill) are measured the same way and
+reported under "secondary".
 
 Prints ONE JSON line.
 """
@@ -29,6 +30,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores, TFLOP/s
+FP8_MFMA_PEAK_TFLOPS = 5000.0   # MI355X dense fp8 matrix cores, TFLOP/s
 METRIC = "paged decode KV-read GB/s (% HBM peak); MLA prefill TFLOP/s (% MFMA peak)"
 ROT_BYTES = 768 << 20          # keep the rotating copies larger than the last-level cache
 
@@ -78,11 +80,23 @@ DOMINANT_KERNEL = {
     "decode_gqa_bf16": "decode_worker_mfma<128, false>",
     "decode_long_fp8": "decode_worker_mfma<128, true>",
     "decode_tiny_fp32": "decode_worker_f32",
-    "prefill_mla_bf16": "prefill_fwd<64, false>",
-    "prefill_blocksparse_bf16": "prefill_fwd<0, false>",
-    "prefill_chunk_bf16": "prefill_fwd<0, true>",
-    "prefill_chunk_mla_bf16": "prefill_fwd<64, true>",
+    "prefill_mla_bf16": "prefill_fwd<64, false, false>",
+    "prefill_blocksparse_bf16": "prefill_fwd<0, false, false>",
+    "prefill_chunk_bf16": "prefill_fwd<0, true, false>",
+    "prefill_chunk_mla_bf16": "prefill_fwd<64, true, false>",
+    "prefill_mla_fp8": "prefill_fwd<64, false, true>",
 }
+
+
+def prefill_peak_tflops(case) -> float:
+    """The matrix-core peak for the prefill's mix of products: with fp8 inputs
+    the nope part of Q.K (Dn of the Dqk + Dv multiply-adds per visible pair
+    and head) runs at the fp8 rate and the rope part and P.V at the bf16 rate,
+    so the peak is the harmonic mix of the two; bf16 cases get the bf16 peak."""
+    if getattr(case, "dtype", "bf16") != "e4m3fn":
+        return BF16_MFMA_PEAK_TFLOPS
+    f8 = case.D_nope / (case.D_qk + case.D_v)
+    return 1.0 / (f8 / FP8_MFMA_PEAK_TFLOPS + (1.0 - f8) / BF16_MFMA_PEAK_TFLOPS)
 COPY_KERNEL = "neg_kernel"   # torch.neg(out=) over float32: reads and writes each byte once
 
 
@@ -229,8 +243,13 @@ def bench_prefill(case, steps, warmup, torch, gq, gu, check=True):
         import numpy as np
         out, _ = dp.results()
         rows = np.linspace(0, case.T - 1, 48).astype(np.int64)
-        ref, _ = O.ragged_prefill(case.q, case.k, case.v, case.cu_seqlens, case.scale, k_rope=case.k_rope,
-                                  block_mask=case.block_mask, dtype="bf16", rows=rows)
+        if case.dtype == "e4m3fn":
+            ref, _ = O.ragged_prefill_fp8(case.q, case.q_rope, case.k, case.v, case.k_rope, case.cu_seqlens,
+                                          case.scale, case.q_scale, case.k_scale, block_mask=case.block_mask,
+                                          rows=rows)
+        else:
+            ref, _ = O.ragged_prefill(case.q, case.k, case.v, case.cu_seqlens, case.scale, k_rope=case.k_rope,
+                                      block_mask=case.block_mask, dtype="bf16", rows=rows)
         err = float(abs(out[rows] - ref).max())
     flops = case.flops()
     return {
@@ -356,11 +375,12 @@ def main(argv=None) -> int:
         secondary.append(r4)
         del c4
         if hasattr(gu, "DevicePrefill"):
-            for mk in (gen.prefill_mla_bf16, gen.prefill_blocksparse_bf16):
+            for mk in (gen.prefill_mla_bf16, gen.prefill_blocksparse_bf16, gen.prefill_mla_fp8):
                 pc = mk()
                 rp = bench_prefill(pc, args.steps, args.warmup, torch, gq, gu)
-                rp["roofline"] = {"bound": "mfma", "achieved": rp["tflops_kernel"], "peak": BF16_MFMA_PEAK_TFLOPS,
-                                  "unit": "TFLOP/s", "frac": rp["tflops_kernel"] / BF16_MFMA_PEAK_TFLOPS,
+                peak = prefill_peak_tflops(pc)
+                rp["roofline"] = {"bound": "mfma", "achieved": rp["tflops_kernel"], "peak": round(peak, 1),
+                                  "unit": "TFLOP/s", "frac": rp["tflops_kernel"] / peak,
                                   "traffic": _traffic(pc.name)}
                 secondary.append(rp)
                 del pc

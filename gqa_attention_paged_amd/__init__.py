@@ -28,7 +28,8 @@ PLAN_MAGIC = 0x47514150
 
 C_FUNCTIONS = (
     "gqap_decode_plan", "gqap_decode_validate_host", "gqap_paged_decode", "gqap_debug_gather_kv",
-    "gqap_prefill_plan", "gqap_prefill", "gqap_chunk_plan", "gqap_chunk_validate_host", "gqap_append_kv",
+    "gqap_prefill_plan", "gqap_prefill", "gqap_prefill_fp8", "gqap_chunk_plan", "gqap_chunk_validate_host",
+    "gqap_append_kv",
     "gqap_chunk_prefill", "gqap_block_table_from_csr", "gqap_last_error", "gqap_version",
 )
 
@@ -73,6 +74,7 @@ class PrefillDesc(ctypes.Structure):
         ("kr_stride_token", ctypes.c_int64),
         ("out_stride_token", ctypes.c_int64), ("out_stride_head", ctypes.c_int64),
         ("num_cus", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("qr_stride_token", ctypes.c_int64), ("qr_stride_head", ctypes.c_int64),
     ]
 
 
@@ -126,6 +128,9 @@ def _load() -> ctypes.CDLL:
     lib.gqap_prefill_plan.restype = st
     lib.gqap_prefill.argtypes = [ctypes.POINTER(PrefillPlan), vp, vp, vp, vp, vp, vp, f32, vp, vp, vp, u64, vp]
     lib.gqap_prefill.restype = st
+    lib.gqap_prefill_fp8.argtypes = [ctypes.POINTER(PrefillPlan), vp, vp, vp, vp, vp, vp, vp, f32, f32, f32, vp, vp,
+                                     vp, u64, vp]
+    lib.gqap_prefill_fp8.restype = st
     lib.gqap_chunk_plan.argtypes = [ctypes.POINTER(ChunkDesc), ctypes.POINTER(ChunkPlan)]
     lib.gqap_chunk_plan.restype = st
     lib.gqap_chunk_validate_host.argtypes = [ctypes.POINTER(ChunkPlan), vp, vp, vp]
@@ -229,6 +234,16 @@ def gqap_prefill(plan: PrefillPlan, q, k, v, k_rope, cu_seqlens, block_mask, sca
                              _stream(stream)))
 
 
+def gqap_prefill_fp8(plan: PrefillPlan, q_nope, q_rope, k, v, k_rope, cu_seqlens, block_mask, scale: float,
+                     q_scale: float, k_scale: float, out, lse=None, workspace=None,
+                     workspace_bytes: Optional[int] = None, stream=None) -> None:
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.gqap_prefill_fp8(ctypes.byref(plan), _ptr(q_nope), _ptr(q_rope), _ptr(k), _ptr(v), _ptr(k_rope),
+                                 _ptr(cu_seqlens), _ptr(block_mask), scale, q_scale, k_scale, _ptr(out), _ptr(lse),
+                                 _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
 def gqap_chunk_plan(desc: ChunkDesc) -> ChunkPlan:
     plan = ChunkPlan()
     _check(_lib.gqap_chunk_plan(ctypes.byref(desc), ctypes.byref(plan)))
@@ -306,9 +321,12 @@ def decode_desc(q, k_pool, block_table, max_seq_len: int, out=None, num_workers:
 
 
 def prefill_desc(q, k, v, k_rope, batch: int, max_seq_len: int, block_mask=None, out=None,
-                 num_cus: int = 0) -> PrefillDesc:
-    """Descriptor for ragged q [T, Hq, Dqk], k [T, Hk, Dn], v [T, Hk, Dv], k_rope [T, 1, Dr] or None."""
+                 num_cus: int = 0, q_rope=None) -> PrefillDesc:
+    """Descriptor for ragged q [T, Hq, Dqk], k [T, Hk, Dn], v [T, Hk, Dv], k_rope [T, 1, Dr] or None.
+    fp8: q is q_nope [T, Hq, Dn] (codes) and q_rope [T, Hq, Dr] the bf16 rope part, or None."""
     T, Hq, Dqk = q.shape
+    if q_rope is not None:
+        Dqk += q_rope.shape[2]
     Hk = k.shape[1]
     out = out if out is not None else v.new_empty((T, Hq, v.shape[2]))
     d = PrefillDesc()
@@ -328,6 +346,8 @@ def prefill_desc(q, k, v, k_rope, batch: int, max_seq_len: int, block_mask=None,
     d.kr_stride_token = 0 if k_rope is None else k_rope.stride(0)
     d.out_stride_token, d.out_stride_head = out.stride(0), out.stride(1)
     d.num_cus = num_cus
+    if q_rope is not None:
+        d.qr_stride_token, d.qr_stride_head = q_rope.stride(0), q_rope.stride(1)
     return d
 
 

@@ -154,7 +154,9 @@ extern "C" gqap_status gqap_prefill_plan(const gqap_prefill_desc_t* desc, gqap_p
                 d.num_kv_heads);
   if (d.num_q_heads % d.num_kv_heads)
     return fail(GQAP_ERR_INVALID_ARGUMENT, "Hq (%d) must be a multiple of Hk (%d)", d.num_q_heads, d.num_kv_heads);
-  if (d.dtype != GQAP_BF16) return fail(GQAP_ERR_DTYPE, "prefill takes bf16 q/k/v (got dtype %d)", d.dtype);
+  if (d.dtype != GQAP_BF16 && d.dtype != GQAP_FP8_E4M3FN)
+    return fail(GQAP_ERR_DTYPE, "prefill takes bf16, or fp8 q_nope/k (got dtype %d)", d.dtype);
+  const bool f8 = d.dtype == GQAP_FP8_E4M3FN;
   if (d.causal != 1) return fail(GQAP_ERR_UNSUPPORTED, "only causal prefill is implemented");
   const bool mla = d.head_dim_qk == 192 && d.head_dim_rope == 64;
   const bool plain = d.head_dim_qk == 128 && d.head_dim_rope == 0;
@@ -167,8 +169,12 @@ extern "C" gqap_status gqap_prefill_plan(const gqap_prefill_desc_t* desc, gqap_p
   if (d.max_seq_len > d.total_tokens && d.batch > 0)
     return fail(GQAP_ERR_INVALID_ARGUMENT, "max_seq_len %d exceeds total_tokens %d", d.max_seq_len, d.total_tokens);
   const int64_t Dn = d.head_dim_qk - d.head_dim_rope;
-  if (d.q_stride_head < d.head_dim_qk || d.q_stride_token < d.q_stride_head * d.num_q_heads)
+  // fp8: q holds the nope part only, the rope part is the bf16 tensor q_rope.
+  if (d.q_stride_head < (f8 ? Dn : d.head_dim_qk) || d.q_stride_token < d.q_stride_head * d.num_q_heads)
     return fail(GQAP_ERR_INVALID_ARGUMENT, "q strides overlap");
+  if (f8 && d.head_dim_rope &&
+      (d.qr_stride_head < d.head_dim_rope || d.qr_stride_token < d.qr_stride_head * d.num_q_heads))
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "q_rope strides overlap");
   if (d.k_stride_head < Dn || d.k_stride_token < d.k_stride_head * d.num_kv_heads)
     return fail(GQAP_ERR_INVALID_ARGUMENT, "k strides overlap");
   if (d.v_stride_head < d.head_dim_v || d.v_stride_token < d.v_stride_head * d.num_kv_heads)
@@ -177,11 +183,14 @@ extern "C" gqap_status gqap_prefill_plan(const gqap_prefill_desc_t* desc, gqap_p
     return fail(GQAP_ERR_INVALID_ARGUMENT, "out strides overlap");
   if (d.head_dim_rope && d.kr_stride_token < d.head_dim_rope)
     return fail(GQAP_ERR_INVALID_ARGUMENT, "k_rope token stride < rope width");
-  const int64_t strides[] = {d.q_stride_token, d.q_stride_head, d.k_stride_token, d.k_stride_head,
-                             d.v_stride_token, d.v_stride_head, d.out_stride_token, d.out_stride_head,
-                             d.head_dim_rope ? d.kr_stride_token : 8};
-  for (int64_t s : strides)
-    if (!aligned16(s, 2)) return fail(GQAP_ERR_INVALID_ARGUMENT, "strides must keep rows 16-byte aligned");
+  const int64_t strides[] = {d.v_stride_token, d.v_stride_head, d.out_stride_token, d.out_stride_head,
+                             d.head_dim_rope ? d.kr_stride_token : 8,
+                             f8 && d.head_dim_rope ? d.qr_stride_token : 8, f8 && d.head_dim_rope ? d.qr_stride_head : 8};
+  const int64_t qk_strides[] = {d.q_stride_token, d.q_stride_head, d.k_stride_token, d.k_stride_head};
+  bool ok = true;
+  for (int64_t s : strides) ok = ok && aligned16(s, 2);
+  for (int64_t s : qk_strides) ok = ok && aligned16(s, f8 ? 1 : 2);
+  if (!ok) return fail(GQAP_ERR_INVALID_ARGUMENT, "strides must keep rows 16-byte aligned");
   if (d.has_block_mask != 0 && d.has_block_mask != 1)
     return fail(GQAP_ERR_INVALID_ARGUMENT, "has_block_mask must be 0 or 1");
   if (d.has_block_mask && (int64_t)d.mask_blocks < ceil_div(d.max_seq_len, kBlock))
@@ -196,7 +205,7 @@ extern "C" gqap_status gqap_prefill_plan(const gqap_prefill_desc_t* desc, gqap_p
   if ((int64_t)d.num_q_heads * d.batch * plan->q_tiles >= ((int64_t)1 << 24))
     return fail(GQAP_ERR_UNSUPPORTED, "Hq * batch * ceil(max_seq_len/128) = %lld workgroups exceeds 2^24",
                 (long long)d.num_q_heads * d.batch * plan->q_tiles);
-  plan->kernel = mla ? 2 : 1;
+  plan->kernel = (mla ? 2 : 1) + (f8 ? 2 : 0);
   plan->workspace_bytes = 0;
   plan->magic = GQAP_PLAN_MAGIC;
   return GQAP_OK;

@@ -52,14 +52,30 @@ struct PrefillArgs {
   int64_t kv_sh;      // elements between heads of a block
   int64_t kr_sb;      // elements between rope-cache blocks
   int32_t max_kv;     // capacity: keys per sequence
+  // fp8 prefill: q and k hold e4m3fn codes of the nope parts (strides in
+  // bytes), the rope part of the query is the bf16 tensor qr, and the nope
+  // term of a score is multiplied by qk = q_scale * k_scale.
+  const uint16_t* qr;
+  int64_t qr_st, qr_sh;
+  float qk;
 };
 
 namespace dev {
 
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
 
 __device__ __forceinline__ f32x16_t mfma32x32x16(bf16x8 a, bf16x8 b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// D += A B on fp8 e4m3fn operands (format code 0 for both), 64-deep: each lane
+// brings 32 codes.  Zero scale operands select the unscaled instruction
+// v_mfma_f32_32x32x64_f8f6f4.  The products of two e4m3fn values are exact in
+// fp32.  The output layout is that of the bf16 32x32 step, and a k order that
+// is the same for both operands gives the plain dot product.
+__device__ __forceinline__ f32x16_t mfma32x32x64_fp8(i32x8 a, i32x8 b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
 // 16-byte chunk c of row `row` of a tile with RC chunks per row, XOR-swizzled
@@ -87,13 +103,18 @@ __device__ __forceinline__ int vswz256(int row, int c) {
 
 using namespace dev;
 
-template <int DR, bool PAGED>
+// F8: the nope parts of Q and K are fp8 e4m3fn codes (K tiles of 64 rows x
+// 128 bytes, staged like the rope tile) and their products run on the fp8
+// matrix cores; the rope parts and V stay bf16.
+template <int DR, bool PAGED, bool F8>
 __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
+  static_assert(!(F8 && PAGED), "the fp8 path reads token-major K");
   constexpr int DN = 128;                     // per-head key width
   constexpr int DV = 128;                     // value / output width
-  constexpr int KSN = DN / 16;                // k-steps over the nope part
+  constexpr int KSN = DN / 16;                // k-steps over the nope part (bf16)
   constexpr int KSR = DR / 16;                // k-steps over the rope part
-  constexpr int KB = 64 * DN * 2;             // K tile bytes
+  constexpr int KE = F8 ? 1 : 2;              // bytes per K element
+  constexpr int KB = 64 * DN * KE;            // K tile bytes
   constexpr int RB = DR ? 64 * DR * 2 : 0;    // rope tile bytes
   constexpr int VB = 64 * DV * 2;             // V tile bytes
   constexpr int KLD = KB / 1024 / 4;          // 1 KB loads-to-LDS per wave and tile: K
@@ -165,14 +186,37 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
 
   // The wave's queries as the B operand: lane (query l32, half hh) holds
   // d = 16 s + 8 hh .. +7 for k-step s (s < KSN: nope part, then rope).
-  bf16x8 qop[KSN + KSR];
+  // With F8 the nope part is instead two 32-byte operands of the fp8 step,
+  // lane (l32, hh) holding codes 64 s + 32 hh .. +31 for step s, and qop
+  // holds only the bf16 rope part, read from its own tensor.
+  constexpr int NQ = F8 ? KSR : KSN + KSR;
+  bf16x8 qop[NQ > 0 ? NQ : 1];
+  i32x8 q8[2];
   {
     const bool ok = qrow < L;
-    const uint16_t* qp = a.q + (int64_t)(c0 + (ok ? qrow : 0)) * a.q_st + (int64_t)h * a.q_sh + 8 * hh;
+    const int64_t tok = c0 + (ok ? qrow : 0);
+    if constexpr (F8) {
+      const unsigned char* qp = (const unsigned char*)a.q + tok * a.q_st + (int64_t)h * a.q_sh + 32 * hh;
 #pragma unroll
-    for (int s = 0; s < KSN + KSR; ++s) {
-      const i32x4 v = load16(qp + 16 * s);
-      qop[s] = __builtin_bit_cast(bf16x8, ok ? v : i32x4{0, 0, 0, 0});
+      for (int s = 0; s < 2; ++s) {
+        const i32x4 lo = load16(qp + 64 * s), hi = load16(qp + 64 * s + 16);
+        q8[s] = ok ? __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7) : i32x8{};
+      }
+      if constexpr (DR > 0) {
+        const uint16_t* rp = a.qr + tok * a.qr_st + (int64_t)h * a.qr_sh + 8 * hh;
+#pragma unroll
+        for (int s = 0; s < KSR; ++s) {
+          const i32x4 v = load16(rp + 16 * s);
+          qop[s] = __builtin_bit_cast(bf16x8, ok ? v : i32x4{0, 0, 0, 0});
+        }
+      }
+    } else {
+      const uint16_t* qp = a.q + tok * a.q_st + (int64_t)h * a.q_sh + 8 * hh;
+#pragma unroll
+      for (int s = 0; s < KSN + KSR; ++s) {
+        const i32x4 v = load16(qp + 16 * s);
+        qop[s] = __builtin_bit_cast(bf16x8, ok ? v : i32x4{0, 0, 0, 0});
+      }
     }
   }
 
@@ -223,21 +267,25 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
   // Tile loads go straight to LDS (global_load_lds_dwordx4): wave w's i-th
   // load fills the 1 KB LDS segment 4 i + w, lane l the 16 bytes at 16 l of
   // it.  For K and V a segment is rows 16 i + tid/16 (4 rows of 256 bytes),
-  // for the rope part rows 32 i + tid/8 (8 rows of 128 bytes).  The LDS
-  // swizzle is applied on the global side: the lane that fills LDS chunk c'
-  // of a row fetches the chunk that the read swizzle expects there.
+  // for the rope part and an fp8 K tile rows 32 i + tid/8 (8 rows of 128
+  // bytes).  The LDS swizzle is applied on the global side: the lane that
+  // fills LDS chunk c' of a row fetches the chunk that the read swizzle
+  // expects there.
   const int row0 = tid >> 4, ch = tid & 15;
   const int row0r = tid >> 3, chr = tid & 7;
-  const int kch = ch ^ (row0 & 15);                                    // K: c' = c ^ (row & 15)
-  const int vch = (((ch >> 1) ^ vmask(row0)) << 1) | (ch & 1);         // V: 32-byte pieces ^ vmask(row)
   const int rch = chr ^ ((row0r >> 1) & 7);                            // rope: c' = c ^ ((row >> 1) & 7)
+  const int vch = (((ch >> 1) ^ vmask(row0)) << 1) | (ch & 1);         // V: 32-byte pieces ^ vmask(row)
+  constexpr int KRS = F8 ? 32 : 16;                                    // K rows per load round
+  const int krow = F8 ? row0r : row0;
+  const int kch = F8 ? rch : ch ^ (row0 & 15);                         // K: c' = c ^ (row & 15)
   // Tile bases are uniform (scalar) pointers; each lane adds one fixed 32-bit
   // byte offset, so the loads use the scalar-base addressing form.
-  const int64_t kstr = a.k_st * 2, vstr = a.v_st * 2, rstr = a.kr_st * 2;  // row strides in bytes
-  const unsigned char* kg = (const unsigned char*)(a.k + (int64_t)c0 * a.k_st + (int64_t)g * a.k_sh);
+  const int64_t kstr = a.k_st * KE, vstr = a.v_st * 2, rstr = a.kr_st * 2;  // row strides in bytes
+  const unsigned char* kg =
+      (const unsigned char*)a.k + ((int64_t)c0 * a.k_st + (int64_t)g * a.k_sh) * KE;
   const unsigned char* vg = (const unsigned char*)(a.v + (int64_t)c0 * a.v_st + (int64_t)g * a.v_sh);
   const unsigned char* rg = DR ? (const unsigned char*)(a.kr + (int64_t)c0 * a.kr_st) : nullptr;
-  const uint32_t koff = (uint32_t)(row0 * kstr) + 16u * kch;
+  const uint32_t koff = (uint32_t)(krow * kstr) + 16u * kch;
   const uint32_t voff = (uint32_t)(row0 * vstr) + 16u * vch;
   const uint32_t roff = DR ? (uint32_t)(row0r * rstr) + 16u * rch : 0u;
   const int wseg = __builtin_amdgcn_readfirstlane(wv) * 1024;
@@ -293,7 +341,7 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
     const unsigned char* kt_r = DR ? tile_r(kt) : nullptr;
     if (key0 + 64 <= Lk) {  // whole tile inside the keys
 #pragma unroll
-      for (int i = 0; i < KLD; ++i) dma(kt_k + 16 * i * kstr + koff, kd + 4096 * i + wseg);
+      for (int i = 0; i < KLD; ++i) dma(kt_k + KRS * i * kstr + koff, kd + 4096 * i + wseg);
 #pragma unroll
       for (int i = 0; i < RLD; ++i) dma(kt_r + 32 * i * rstr + roff, rd + 4096 * i + wseg);
 #pragma unroll
@@ -301,7 +349,7 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
     } else {
 #pragma unroll
       for (int i = 0; i < KLD; ++i)
-        dma(kt_k + (int64_t)min(row0 + 16 * i, Lk - 1 - key0) * kstr + 16 * kch, kd + 4096 * i + wseg);
+        dma(kt_k + (int64_t)min(krow + KRS * i, Lk - 1 - key0) * kstr + 16 * kch, kd + 4096 * i + wseg);
 #pragma unroll
       for (int i = 0; i < RLD; ++i)
         dma(kt_r + (int64_t)min(row0r + 32 * i, Lk - 1 - key0) * rstr + 16 * rch, rd + 4096 * i + wseg);
@@ -318,8 +366,14 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
 
   // Per-lane LDS read offsets; the tile half t, k-step and buffer parts are
   // immediates.  K: chunk (2s + hh) ^ (row & 15) = 2 (s ^ m) + ((hh ^ row) & 1).
-  int kra[KSN];
-  {
+  // fp8 K: 16-byte read u = 2 s + e of fp8 step s is chunk 4 s + 2 hh + e,
+  // stored at chunk ^ ((row >> 1) & 7).
+  int kra[F8 ? 4 : KSN];
+  if constexpr (F8) {
+    const int m = (l32 >> 1) & 7;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) kra[u] = l32 * 128 + (((4 * (u >> 1) + 2 * hh + (u & 1)) ^ m) << 4);
+  } else {
     const int m = (l32 & 15) >> 1;
     const int lo = ((hh ^ l32) & 1) << 4;
 #pragma unroll
@@ -367,39 +421,94 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
     const unsigned char* kt_r = DR && WL ? tile_r(kn) : nullptr;
     auto issue_load = [&](int i) {
       if (i < KLD)
-        dma(kt_k + 16 * i * kstr + koff, kd + 4096 * i + wseg);
+        dma(kt_k + KRS * i * kstr + koff, kd + 4096 * i + wseg);
       else if (i < KLD + RLD)
         dma(kt_r + 32 * (i - KLD) * rstr + roff, rd + 4096 * (i - KLD) + wseg);
       else
         dma(kt_v + 16 * (i - KLD - RLD) * vstr + voff, vd + 4096 * (i - KLD - RLD) + wseg);
     };
-    // S^T tile t (keys 32t .. 32t+31 of the tile) x 32 queries: 2 NS MFMAs
-    // whose K operands are read from LDS PF steps ahead.
-    constexpr int NS = KSN + KSR;
-    constexpr int PF = 8;
-    auto kfrag = [&](int idx) {
-      const int t = idx / NS, ss = idx % NS;
-      return ss < KSN ? load16(kb + t * 8192 + kra[ss]) : load16(rb + t * 4096 + rra[ss - KSN]);
-    };
     f32x16_t s[2] = {f32x16_t{}, f32x16_t{}};
-    i32x4 kf[PF];
+    if constexpr (!F8) {
+      // S^T tile t (keys 32t .. 32t+31 of the tile) x 32 queries: 2 NS MFMAs
+      // whose K operands are read from LDS PF steps ahead.
+      constexpr int NS = KSN + KSR;
+      constexpr int PF = 8;
+      auto kfrag = [&](int idx) {
+        const int t = idx / NS, ss = idx % NS;
+        return ss < KSN ? load16(kb + t * 8192 + kra[ss]) : load16(rb + t * 4096 + rra[ss - KSN]);
+      };
+      i32x4 kf[PF];
 #pragma unroll
-    for (int i = 0; i < PF; ++i) kf[i] = kfrag(i);
+      for (int i = 0; i < PF; ++i) kf[i] = kfrag(i);
 #pragma unroll
-    for (int idx = 0; idx < 2 * NS; ++idx) {
-      const i32x4 cur = kf[idx % PF];
-      if (idx + PF < 2 * NS) kf[idx % PF] = kfrag(idx + PF);
-      s[idx / NS] = mfma32x32x16(__builtin_bit_cast(bf16x8, cur), qop[idx % NS], s[idx / NS]);
-      if (WL && idx < NLD) issue_load(idx);
-    }
-    // Issue order: PF reads, then per MFMA one read (and one tile load
-    // while any is left).
-    __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
+      for (int idx = 0; idx < 2 * NS; ++idx) {
+        const i32x4 cur = kf[idx % PF];
+        if (idx + PF < 2 * NS) kf[idx % PF] = kfrag(idx + PF);
+        s[idx / NS] = mfma32x32x16(__builtin_bit_cast(bf16x8, cur), qop[idx % NS], s[idx / NS]);
+        if (WL && idx < NLD) issue_load(idx);
+      }
+      // Issue order: PF reads, then per MFMA one read (and one tile load
+      // while any is left).
+      __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
 #pragma unroll
-    for (int idx = 0; idx < 2 * NS; ++idx) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (idx + PF < 2 * NS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      if (WL && idx < NLD) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      for (int idx = 0; idx < 2 * NS; ++idx) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (idx + PF < 2 * NS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (WL && idx < NLD) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
+    } else {
+      // fp8 nope part: per tile half t two 64-deep fp8 steps, each K operand
+      // two 16-byte LDS reads (units 0..7); then the bf16 rope steps (units
+      // 8..), after the nope sum of the half has been multiplied by
+      // q_scale * k_scale.  Order nope t0, nope t1, rope t0, rope t1, so each
+      // multiply waits on a step issued two steps before it.  The tile loads
+      // are spread over the NM steps.
+      constexpr int NU = 8 + 2 * KSR;
+      constexpr int NM = 4 + 2 * KSR;
+      constexpr int PF = 8;
+      auto unit = [&](int u) -> i32x4 {
+        if (u < 8) return load16(kb + (u >> 2) * 4096 + kra[u & 3]);
+        if constexpr (KSR > 0) {
+          const int r = u - 8;
+          return load16(rb + (r / KSR) * 4096 + rra[r % KSR]);
+        } else {
+          return i32x4{};
+        }
+      };
+      i32x4 uf[NU];
+#pragma unroll
+      for (int u = 0; u < PF; ++u) uf[u] = unit(u);
+#pragma unroll
+      for (int i = 0; i < NM; ++i) {
+        if (i < 4) {
+          const int t = i >> 1, st = i & 1;
+          const i32x8 ka = __builtin_shufflevector(uf[4 * t + 2 * st], uf[4 * t + 2 * st + 1], 0, 1, 2, 3, 4, 5, 6,
+                                                   7);
+#pragma unroll
+          for (int e = 0; e < 2; ++e)
+            if (PF + 2 * i + e < NU) uf[PF + 2 * i + e] = unit(PF + 2 * i + e);
+          s[t] = mfma32x32x64_fp8(ka, q8[st], s[t]);
+        } else if constexpr (KSR > 0) {
+          const int r = i - 4, t = r / KSR;
+          if (r % KSR == 0) s[t] *= a.qk;
+          s[t] = mfma32x32x16(__builtin_bit_cast(bf16x8, uf[8 + r]), qop[r % KSR], s[t]);
+        }
+        if (WL)
+#pragma unroll
+          for (int j = i * NLD / NM; j < (i + 1) * NLD / NM; ++j) issue_load(j);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
+#pragma unroll
+      for (int i = 0; i < NM; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i < 4) {
+          if (PF + 2 * i < NU) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          if (PF + 2 * i + 1 < NU) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        if (WL)
+#pragma unroll
+          for (int j = i * NLD / NM; j < (i + 1) * NLD / NM; ++j) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
     }
     // Causal mask by select (only on tiles reaching past the wave's first row).
     if (kt * 64 + 63 > off + r0) {
@@ -600,28 +709,11 @@ static bool misaligned16(const void* p) { return ((uintptr_t)p) & 15; }
 
 using namespace gqap;
 
-extern "C" gqap_status gqap_prefill(const gqap_prefill_plan_t* plan, const void* q, const void* k, const void* v,
-                                    const void* k_rope, const int32_t* cu_seqlens, const uint8_t* block_mask,
-                                    float scale, void* out, float* lse, void* workspace, uint64_t workspace_bytes,
-                                    void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
-  if (!plan || plan->magic != GQAP_PLAN_MAGIC) return fail(GQAP_ERR_INVALID_ARGUMENT, "invalid prefill plan");
+// Fields shared by the bf16 and fp8 ragged launches.
+static PrefillArgs ragged_args(const gqap_prefill_plan_t* plan, const int32_t* cu_seqlens,
+                               const uint8_t* block_mask, void* out, float* lse) {
   const gqap_prefill_desc_t& d = plan->desc;
-  if (d.batch == 0 || plan->q_tiles == 0) return GQAP_OK;
-  if (!q || !k || !v || !cu_seqlens || !out) return fail(GQAP_ERR_INVALID_ARGUMENT, "null device pointer");
-  if (d.head_dim_rope && !k_rope) return fail(GQAP_ERR_INVALID_ARGUMENT, "k_rope is required when head_dim_rope > 0");
-  if (!d.head_dim_rope && k_rope) return fail(GQAP_ERR_INVALID_ARGUMENT, "k_rope given but head_dim_rope == 0");
-  if (d.has_block_mask && !block_mask) return fail(GQAP_ERR_INVALID_ARGUMENT, "block mask declared but null");
-  if (misaligned16(q) || misaligned16(k) || misaligned16(v) || misaligned16(out) ||
-      (k_rope && misaligned16(k_rope)) || ((uintptr_t)cu_seqlens & 3) || (lse && ((uintptr_t)lse & 3)))
-    return fail(GQAP_ERR_INVALID_ARGUMENT, "device pointers must be 16-byte aligned (cu_seqlens, lse 4-byte)");
-  if (!std::isfinite(scale)) return fail(GQAP_ERR_INVALID_ARGUMENT, "scale must be finite");
   PrefillArgs a{};
-  a.q = (const uint16_t*)q;
-  a.k = (const uint16_t*)k;
-  a.v = (const uint16_t*)v;
-  a.kr = (const uint16_t*)k_rope;
   a.cu = cu_seqlens;
   a.mask = d.has_block_mask ? block_mask : nullptr;
   a.out = (uint16_t*)out;
@@ -642,15 +734,88 @@ extern "C" gqap_status gqap_prefill(const gqap_prefill_plan_t* plan, const void*
   a.q_tiles = plan->q_tiles;
   a.mask_nb = d.mask_blocks;
   a.max_len = d.max_seq_len;
+  return a;
+}
+
+extern "C" gqap_status gqap_prefill(const gqap_prefill_plan_t* plan, const void* q, const void* k, const void* v,
+                                    const void* k_rope, const int32_t* cu_seqlens, const uint8_t* block_mask,
+                                    float scale, void* out, float* lse, void* workspace, uint64_t workspace_bytes,
+                                    void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  if (!plan || plan->magic != GQAP_PLAN_MAGIC) return fail(GQAP_ERR_INVALID_ARGUMENT, "invalid prefill plan");
+  const gqap_prefill_desc_t& d = plan->desc;
+  if (d.dtype != GQAP_BF16) return fail(GQAP_ERR_DTYPE, "gqap_prefill takes a bf16 plan (fp8: gqap_prefill_fp8)");
+  if (d.batch == 0 || plan->q_tiles == 0) return GQAP_OK;
+  if (!q || !k || !v || !cu_seqlens || !out) return fail(GQAP_ERR_INVALID_ARGUMENT, "null device pointer");
+  if (d.head_dim_rope && !k_rope) return fail(GQAP_ERR_INVALID_ARGUMENT, "k_rope is required when head_dim_rope > 0");
+  if (!d.head_dim_rope && k_rope) return fail(GQAP_ERR_INVALID_ARGUMENT, "k_rope given but head_dim_rope == 0");
+  if (d.has_block_mask && !block_mask) return fail(GQAP_ERR_INVALID_ARGUMENT, "block mask declared but null");
+  if (misaligned16(q) || misaligned16(k) || misaligned16(v) || misaligned16(out) ||
+      (k_rope && misaligned16(k_rope)) || ((uintptr_t)cu_seqlens & 3) || (lse && ((uintptr_t)lse & 3)))
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "device pointers must be 16-byte aligned (cu_seqlens, lse 4-byte)");
+  if (!std::isfinite(scale)) return fail(GQAP_ERR_INVALID_ARGUMENT, "scale must be finite");
+  PrefillArgs a = ragged_args(plan, cu_seqlens, block_mask, out, lse);
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k;
+  a.v = (const uint16_t*)v;
+  a.kr = (const uint16_t*)k_rope;
   a.scale_log2 = scale * dev::kLog2e;
   const dim3 grid((unsigned)d.num_q_heads * (unsigned)d.batch * (unsigned)plan->q_tiles);
   hipStream_t st = (hipStream_t)stream;
   if (d.head_dim_rope == 64)
-    hipLaunchKernelGGL((prefill_fwd<64, false>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((prefill_fwd<64, false, false>), grid, dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL((prefill_fwd<0, false>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((prefill_fwd<0, false, false>), grid, dim3(256), 0, st, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(GQAP_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
+  return GQAP_OK;
+}
+
+extern "C" gqap_status gqap_prefill_fp8(const gqap_prefill_plan_t* plan, const void* q_nope, const void* q_rope,
+                                        const void* k, const void* v, const void* k_rope,
+                                        const int32_t* cu_seqlens, const uint8_t* block_mask, float scale,
+                                        float q_scale, float k_scale, void* out, float* lse, void* workspace,
+                                        uint64_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  if (!plan || plan->magic != GQAP_PLAN_MAGIC) return fail(GQAP_ERR_INVALID_ARGUMENT, "invalid prefill plan");
+  const gqap_prefill_desc_t& d = plan->desc;
+  if (d.dtype != GQAP_FP8_E4M3FN)
+    return fail(GQAP_ERR_DTYPE, "gqap_prefill_fp8 takes a plan with dtype GQAP_FP8_E4M3FN");
+  if (!std::isfinite(scale) || !std::isfinite(q_scale) || !std::isfinite(k_scale))
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "scale, q_scale and k_scale must be finite");
+  if (d.batch == 0 || plan->q_tiles == 0) return GQAP_OK;
+  if (!q_nope || !k || !v || !cu_seqlens || !out) return fail(GQAP_ERR_INVALID_ARGUMENT, "null device pointer");
+  if (d.head_dim_rope && (!k_rope || !q_rope))
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "q_rope and k_rope are required when head_dim_rope > 0");
+  if (!d.head_dim_rope && (k_rope || q_rope))
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "rope tensors given but head_dim_rope == 0");
+  if (d.has_block_mask && !block_mask) return fail(GQAP_ERR_INVALID_ARGUMENT, "block mask declared but null");
+  if (misaligned16(q_nope) || misaligned16(k) || misaligned16(v) || misaligned16(out) ||
+      (k_rope && misaligned16(k_rope)) || (q_rope && misaligned16(q_rope)) || ((uintptr_t)cu_seqlens & 3) ||
+      (lse && ((uintptr_t)lse & 3)))
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "device pointers must be 16-byte aligned (cu_seqlens, lse 4-byte)");
+  PrefillArgs a = ragged_args(plan, cu_seqlens, block_mask, out, lse);
+  a.q = (const uint16_t*)q_nope;
+  a.k = (const uint16_t*)k;
+  a.v = (const uint16_t*)v;
+  a.kr = (const uint16_t*)k_rope;
+  a.qr = (const uint16_t*)q_rope;
+  a.qr_st = d.qr_stride_token;
+  a.qr_sh = d.qr_stride_head;
+  // With the rope part the nope sum is scaled inside the kernel; without it
+  // the whole score is the nope sum and the scales join the softmax constant.
+  a.qk = q_scale * k_scale;
+  a.scale_log2 = d.head_dim_rope ? scale * dev::kLog2e : scale * a.qk * dev::kLog2e;
+  const dim3 grid((unsigned)d.num_q_heads * (unsigned)d.batch * (unsigned)plan->q_tiles);
+  hipStream_t st = (hipStream_t)stream;
+  if (d.head_dim_rope == 64)
+    hipLaunchKernelGGL((prefill_fwd<64, false, true>), grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((prefill_fwd<0, false, true>), grid, dim3(256), 0, st, a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(GQAP_ERR_HIP, "fp8 prefill launch: %s", hipGetErrorString(e));
   return GQAP_OK;
 }
 
@@ -755,9 +920,9 @@ extern "C" gqap_status gqap_chunk_prefill(const gqap_chunk_plan_t* plan, const v
   a.max_kv = d.max_kv_len;
   const dim3 grid((unsigned)d.num_q_heads * (unsigned)d.batch * (unsigned)plan->q_tiles);
   if (d.head_dim_rope == 64)
-    hipLaunchKernelGGL((prefill_fwd<64, true>), grid, dim3(256), 0, (hipStream_t)stream, a);
+    hipLaunchKernelGGL((prefill_fwd<64, true, false>), grid, dim3(256), 0, (hipStream_t)stream, a);
   else
-    hipLaunchKernelGGL((prefill_fwd<0, true>), grid, dim3(256), 0, (hipStream_t)stream, a);
+    hipLaunchKernelGGL((prefill_fwd<0, true, false>), grid, dim3(256), 0, (hipStream_t)stream, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(GQAP_ERR_HIP, "chunk prefill launch: %s", hipGetErrorString(e));
   return GQAP_OK;

@@ -8,6 +8,11 @@
  *   - ragged causal prefill on bf16 matrix cores, with the MLA split head
  *     (a 128-wide per-head key part plus a 64-wide rope key shared by all
  *     heads) and an optional 64x64 block-sparse mask;
+ *   - the same prefill with the nope parts of Q and K in fp8 e4m3fn, one
+ *     scale per tensor, on the fp8 matrix cores;
+ *   - chunked prefill against the paged cache (append the chunk's keys and
+ *     values, then attend to the cached prefix and the chunk);
+ *   - the padded block table built from a CSR page list;
  *   - plan / validation calls that run on the host only;
  *   - a debug gather that exposes the decode kernels' page addressing.
  *
@@ -232,6 +237,8 @@ typedef struct gqap_prefill_desc_t {
   int64_t out_stride_token, out_stride_head;
   int32_t num_cus;             /* 0 = 256 */
   int32_t reserved;
+  int64_t qr_stride_token;     /* fp8 only: q_rope strides (bf16 elements) */
+  int64_t qr_stride_head;
 } gqap_prefill_desc_t;
 
 typedef struct gqap_prefill_plan_t {
@@ -246,8 +253,15 @@ typedef struct gqap_prefill_plan_t {
 } gqap_prefill_plan_t;
 
 /*
+ * dtype GQAP_FP8_E4M3FN plans the fp8 prefill (gqap_prefill_fp8): q holds
+ * only the nope part [T, Hq, Dn] and k [T, Hk, Dn], both e4m3fn codes with
+ * strides in bytes (multiples of 16); the rope part of the query is a
+ * separate bf16 tensor q_rope [T, Hq, Dr] with strides qr_stride_token,
+ * qr_stride_head; v, k_rope and out are bf16 as above.  head_dim_qk still
+ * counts Dn + Dr.
+ *
  * Validate a prefill request.  Pure host code.  Errors: INVALID_ARGUMENT
- * (sizes, strides, Hq % Hk, mask_blocks too small), DTYPE (not bf16),
+ * (sizes, strides, Hq % Hk, mask_blocks too small), DTYPE (not bf16 or fp8),
  * UNSUPPORTED (causal == 0, head widths other than 128/192 with rope 0/64,
  * Dv != 128, or Hq * batch * ceil(max_seq_len/128) >= 2^24 workgroups).
  */
@@ -267,6 +281,24 @@ gqap_status gqap_prefill(const gqap_prefill_plan_t* plan,
                          const int32_t* cu_seqlens, const uint8_t* block_mask,
                          float scale, void* out, float* lse,
                          void* workspace, uint64_t workspace_bytes, void* stream);
+
+/*
+ * Ragged causal prefill with the per-head (nope) parts of Q and K in fp8
+ * (Modular flare_mla_prefill, the overload that takes q_nope, q_rope, q_scale
+ * and k_scales).  The plan must have dtype GQAP_FP8_E4M3FN (layout above).
+ * The value of a code c is e4m3fn(c) * q_scale (query) or e4m3fn(c) * k_scale
+ * (key), one scale per tensor, host floats; the score is
+ *   scale * (q_scale * k_scale * (q_nope codes . k codes) + q_rope . k_rope).
+ * q_rope and k_rope are both NULL iff head_dim_rope == 0.  Masking, ragged
+ * rows, lse and the rows past a sequence's end behave as in gqap_prefill.
+ * Errors: INVALID_ARGUMENT (null or misaligned pointers, non-finite scales,
+ * rope tensors that do not match the plan), DTYPE (a bf16 plan), HIP.
+ */
+gqap_status gqap_prefill_fp8(const gqap_prefill_plan_t* plan,
+                             const void* q_nope, const void* q_rope, const void* k, const void* v,
+                             const void* k_rope, const int32_t* cu_seqlens, const uint8_t* block_mask,
+                             float scale, float q_scale, float k_scale, void* out, float* lse,
+                             void* workspace, uint64_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Chunked prefill against a paged KV cache                                  */

@@ -86,8 +86,10 @@ class DevicePrefill:
 
     def __init__(self, case, device: str = "cuda"):
         self.case = case
-        self.q = bits_to_tensor(case.q, "bf16").to(device)
-        self.k = bits_to_tensor(case.k, "bf16").to(device)
+        self.fp8 = case.dtype == "e4m3fn"   # q holds the nope codes, q_rope the bf16 rope part
+        self.q = bits_to_tensor(case.q, case.dtype).to(device)
+        self.qr = bits_to_tensor(case.q_rope, "bf16").to(device) if case.q_rope is not None else None
+        self.k = bits_to_tensor(case.k, case.dtype).to(device)
         self.v = bits_to_tensor(case.v, "bf16").to(device)
         self.kr = bits_to_tensor(case.k_rope, "bf16").to(device) if case.k_rope is not None else None
         self.cu = torch.from_numpy(np.ascontiguousarray(case.cu_seqlens, dtype=np.int32)).to(device)
@@ -98,12 +100,17 @@ class DevicePrefill:
         self.lse = torch.empty((T, case.Hq), dtype=torch.float32, device=device)
         max_len = max(1, int(case.seq_lens.max())) if case.B else 1
         self.desc = gq.prefill_desc(self.q, self.k, self.v, self.kr, batch=case.B, max_seq_len=max_len,
-                                    block_mask=self.mask, out=self.out)
+                                    block_mask=self.mask, out=self.out, q_rope=self.qr)
         self.plan = gq.gqap_prefill_plan(self.desc)
 
     def run(self, stream=None):
-        gq.gqap_prefill(self.plan, self.q, self.k, self.v, self.kr, self.cu, self.mask, self.case.scale, self.out,
-                        self.lse, stream=stream)
+        if self.fp8:
+            gq.gqap_prefill_fp8(self.plan, self.q, self.qr, self.k, self.v, self.kr, self.cu, self.mask,
+                                self.case.scale, self.case.q_scale, self.case.k_scale, self.out, self.lse,
+                                stream=stream)
+        else:
+            gq.gqap_prefill(self.plan, self.q, self.k, self.v, self.kr, self.cu, self.mask, self.case.scale,
+                            self.out, self.lse, stream=stream)
         return self.out, self.lse
 
     def results(self):

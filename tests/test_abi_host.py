@@ -247,6 +247,65 @@ def test_prefill_plan_block_mask_extent(gq):
     assert gq.gqap_prefill_plan(d).magic == gq.PLAN_MAGIC
 
 
+def baseline_fp8_prefill_desc(gq, mla=True):
+    """The bf16 baseline with fp8 q_nope [T, 16, 128] and k codes, q_rope [T, 16, 64] bf16."""
+    d = baseline_prefill_desc(gq, mla)
+    d.dtype = gq.FP8_E4M3FN
+    d.q_stride_head, d.q_stride_token = 128, 128 * d.num_q_heads
+    if mla:
+        d.qr_stride_head, d.qr_stride_token = 64, 64 * d.num_q_heads
+    return d
+
+
+def test_fp8_prefill_plan_baseline(gq):
+    p = gq.gqap_prefill_plan(baseline_fp8_prefill_desc(gq))
+    assert p.magic == gq.PLAN_MAGIC and p.kernel == 4 and p.q_tiles == 24
+    assert gq.gqap_prefill_plan(baseline_fp8_prefill_desc(gq, mla=False)).kernel == 3
+
+
+@pytest.mark.parametrize("field,value", [
+    ("q_stride_head", 120),        # q_nope narrower than 128 codes
+    ("q_stride_head", 136),        # 136-byte rows are not 16-byte aligned
+    ("k_stride_token", 16 * 128 + 8),
+    ("qr_stride_head", 32),        # q_rope narrower than the rope width
+    ("qr_stride_token", 64 * 15),  # q_rope heads overlap
+    ("qr_stride_head", 68),        # 136-byte bf16 rows
+])
+def test_fp8_prefill_plan_rejects(gq, field, value):
+    d = baseline_fp8_prefill_desc(gq)
+    setattr(d, field, value)
+    got = gq.lib().gqap_prefill_plan(ctypes.byref(d), ctypes.byref(gq.PrefillPlan()))
+    assert gq.STATUS_NAMES[got] == "INVALID_ARGUMENT", gq.gqap_last_error()
+
+
+def test_prefill_entry_points_reject_the_other_dtype(gq):
+    """gqap_prefill refuses an fp8 plan and gqap_prefill_fp8 a bf16 plan, before
+    any device work (the pointers are never looked at)."""
+    p8 = gq.gqap_prefill_plan(baseline_fp8_prefill_desc(gq))
+    pb = gq.gqap_prefill_plan(baseline_prefill_desc(gq))
+    st = gq.lib().gqap_prefill(ctypes.byref(p8), None, None, None, None, None, None, 1.0, None, None, None, 0, None)
+    assert gq.STATUS_NAMES[st] == "DTYPE"
+    st = gq.lib().gqap_prefill_fp8(ctypes.byref(pb), None, None, None, None, None, None, None, 1.0, 1.0, 1.0, None,
+                                   None, None, 0, None)
+    assert gq.STATUS_NAMES[st] == "DTYPE"
+
+
+@pytest.mark.parametrize("scales", [(float("nan"), 1.0, 1.0), (1.0, float("inf"), 1.0), (1.0, 1.0, float("nan"))])
+def test_fp8_prefill_rejects_non_finite_scales(gq, scales):
+    p8 = gq.gqap_prefill_plan(baseline_fp8_prefill_desc(gq))
+    st = gq.lib().gqap_prefill_fp8(ctypes.byref(p8), None, None, None, None, None, None, None, *scales, None, None,
+                                   None, 0, None)
+    assert gq.STATUS_NAMES[st] == "INVALID_ARGUMENT"
+
+
+def test_fp8_prefill_rejects_missing_rope_tensors(gq):
+    p8 = gq.gqap_prefill_plan(baseline_fp8_prefill_desc(gq))
+    fake = 1 << 20  # never dereferenced: validation fails first
+    st = gq.lib().gqap_prefill_fp8(ctypes.byref(p8), fake, None, fake, fake, fake, fake, None, 1.0, 1.0, 1.0, fake,
+                                   None, None, 0, None)
+    assert gq.STATUS_NAMES[st] == "INVALID_ARGUMENT" and "q_rope" in gq.gqap_last_error()
+
+
 # ---------------------------------------------------------------- chunked prefill planning
 
 def baseline_chunk_desc(gq):

@@ -1,0 +1,109 @@
+"""fp8 ragged prefill on the GPU through the C ABI (gqap_prefill_fp8), against
+the fp64 oracle run on the same fp8 codes and bf16 values.
+
+The nope parts of Q and K are e4m3fn codes with one scale per tensor; the rope
+parts and V are bf16.  Bar: max-abs-err of out and lse within 6e-2, the
+tolerance for fp8 inputs."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as O
+from workloads import gen
+
+pytestmark = pytest.mark.gpu
+
+TOL = 6e-2
+
+
+@pytest.fixture(scope="module")
+def gu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    from tests import gpu_util  # imports the HIP library; fails loudly if it is missing
+    return gpu_util
+
+
+def _rows_sample(case, n_mid=64, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = set()
+    for b in range(case.B):
+        c0, c1 = int(case.cu_seqlens[b]), int(case.cu_seqlens[b + 1])
+        if c1 == c0:
+            continue
+        for r in (0, 1, 31, 32, 63, 64, 65, 127, 128, 129):
+            if c0 + r < c1:
+                rows.add(c0 + r)
+        rows.update({c1 - 1, c1 - 2, c1 - 64} & set(range(c0, c1)))
+        rows.update(rng.integers(c0, c1, size=min(n_mid, c1 - c0)).tolist())
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+def _check(gu, case, rows=None, tol=TOL):
+    gu.announce(f"fp8 prefill {case.name} lens={list(case.seq_lens)[:8]} Hq={case.Hq} Hk={case.Hk} "
+                f"Dr={case.D_rope} mask={case.block_mask is not None} qs={case.q_scale:.3g} ks={case.k_scale:.3g} "
+                f"seed={case.meta.get('seed')}")
+    dp = gu.DevicePrefill(case)
+    dp.run()
+    out, lse = dp.results()
+    ref, ref_lse = O.ragged_prefill_fp8(case.q, case.q_rope, case.k, case.v, case.k_rope, case.cu_seqlens,
+                                        case.scale, case.q_scale, case.k_scale, block_mask=case.block_mask, rows=rows)
+    if rows is not None:
+        out, lse = out[rows], lse[rows]
+    e_out = gu.max_abs_err(out, ref)
+    e_lse = gu.lse_err(lse, ref_lse)
+    gu.announce(f"  max-abs-err out {e_out:.3e} lse {e_lse:.3e} (tol {tol:g}) rows={'all' if rows is None else len(rows)}")
+    assert e_out <= tol and e_lse <= tol, (e_out, e_lse)
+    return dp, out, lse
+
+
+def test_fp8_mla_config_full_size_sampled(gu):
+    case = gen.prefill_mla_fp8()
+    _check(gu, case, rows=_rows_sample(case))
+
+
+@pytest.mark.parametrize("Hq,Hk", [(16, 16), (8, 2)])
+def test_fp8_mla_small_ragged(gu, Hq, Hk):
+    """Lengths inside one tile, on tile and 128-row boundaries, and past them."""
+    case = gen.make_prefill_fp8_case(name="fp8_mla_small", seed=81, seq_lens=[1, 63, 64, 65, 130, 300], Hq=Hq,
+                                     Hk=Hk, D_rope=64)
+    _check(gu, case)
+
+
+@pytest.mark.parametrize("Hq,Hk", [(8, 8), (16, 2)])
+def test_fp8_without_rope(gu, Hq, Hk):
+    """Plain GQA prefill with fp8 Q and K (the scales join the softmax constant)."""
+    case = gen.make_prefill_fp8_case(name="fp8_gqa", seed=82, seq_lens=[5, 128, 257, 700], Hq=Hq, Hk=Hk, D_rope=0)
+    _check(gu, case)
+
+
+def test_fp8_block_mask(gu):
+    case = gen.make_prefill_fp8_case(name="fp8_mask", seed=83, seq_lens=[900, 333], Hq=8, Hk=2, D_rope=64,
+                                     mask_density=0.3)
+    _check(gu, case)
+
+
+def test_fp8_empty_and_single_token_sequences(gu):
+    case = gen.make_prefill_fp8_case(name="fp8_edges", seed=84, seq_lens=[0, 1, 0, 2, 129], Hq=4, Hk=4, D_rope=64)
+    _check(gu, case)
+
+
+def test_fp8_zero_nope_codes_leave_rope_attention(gu):
+    """All q_nope codes zero: the nope term vanishes, so the kernel must give
+    rope-only attention whatever the two scales are (a scale applied to the
+    whole score would change it)."""
+    case = gen.make_prefill_fp8_case(name="fp8_zero_nope", seed=85, seq_lens=[200, 70], Hq=4, Hk=4, D_rope=64)
+    case.q = np.zeros_like(case.q)
+    case.q_scale, case.k_scale = 3.0, 5.0
+    dp, out, lse = _check(gu, case)
+    case.q_scale, case.k_scale = 0.01, 0.02
+    dp2 = gu.DevicePrefill(case)
+    dp2.run()
+    out2, lse2 = dp2.results()
+    np.testing.assert_array_equal(out, out2)
+    np.testing.assert_array_equal(lse, lse2)
+
+
+def test_fp8_long_sequence_sampled(gu):
+    case = gen.make_prefill_fp8_case(name="fp8_long", seed=86, seq_lens=[8192], Hq=8, Hk=1, D_rope=64)
+    _check(gu, case, rows=_rows_sample(case))
