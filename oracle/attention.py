@@ -51,9 +51,10 @@ Readings where the pages are silent (each also listed in the design notes):
     mask[b, i // 64, j // 64] != 0 (a diagonal block that is off hides it);
   * a row with no visible key has out = 0 and lse = -inf;
   * fp8 values are e4m3fn(byte) * scale, with the pool's per-tensor scale;
-  * fp8 prefill: q_nope and K carry one scale per tensor (the page leaves
-    the layout of q_scale and k_scales open; per tensor is the plainest one);
-    the rope parts and V are bf16 and unscaled;
+  * fp8 prefill: q_nope and K carry one scale per tensor, or one per row of
+    a head (a 1 x 128 block: q_scale [T, Hq], k_scale [T, Hk]); the page leaves
+    the layout of q_scale and k_scales open and these are the two plainest
+    ones; the rope parts and V are bf16 and unscaled;
   * chunked prefill: a sequence holds kv_len keys in the paged cache, the last
     q_len of which are the chunk's own tokens (appended at logical positions
     kv_len - q_len + i); query i sees key j iff j <= kv_len - q_len + i.
@@ -425,28 +426,34 @@ def ragged_prefill_fp8(
     k_rope: Optional[np.ndarray],
     cu_seqlens: np.ndarray,
     scale: float,
-    q_scale: float,
-    k_scale: float,
+    q_scale,
+    k_scale,
     *,
     block_mask: Optional[np.ndarray] = None,
     rows: Optional[Sequence[int]] = None,
 ):
     """Ragged causal prefill with the per-head (nope) parts of Q and K in fp8
     (Modular flare_mla_prefill, the overload taking q_nope, q_rope, q_scale and
-    k_scales): q_nope [T, Hq, Dn] and k [T, Hk, Dn] hold e4m3fn codes, each
-    tensor with one scale; q_rope [T, Hq, Dr], k_rope [T, 1, Dr] and v [T, Hk, Dv]
-    are bf16 (q_rope and k_rope both None for a model without the rope part).
-    The value of a code c is e4m3fn(c) times its tensor's scale, the query is
-    those values followed by q_rope, and the rest is ragged_prefill on them:
-        score = scale * (q_scale * k_scale * (codes of q_nope . codes of k)
-                         + q_rope . k_rope)
+    k_scales): q_nope [T, Hq, Dn] and k [T, Hk, Dn] hold e4m3fn codes;
+    q_rope [T, Hq, Dr], k_rope [T, 1, Dr] and v [T, Hk, Dv] are bf16 (q_rope and
+    k_rope both None for a model without the rope part).
+
+    Scales: q_scale is one float for the whole tensor or an array [T, Hq] with
+    one scale per row of a head (a 1 x Dn block); k_scale likewise, a float or
+    [T, Hk].  The value of a code is e4m3fn(code) times the scale of its block,
+    the query is those values followed by q_rope, and the rest is
+    ragged_prefill on them:
+        score = scale * (q_scale[i,h] * k_scale[j,g] * (codes of q_nope[i,h] . codes of k[j,g])
+                         + q_rope[i,h] . k_rope[j])
     Returns (out [n, Hq, Dv], lse [n, Hq]) in float64."""
     if (q_rope is None) != (k_rope is None):
         raise ValueError("q_rope and k_rope go together")
-    q = widen(q_nope, "e4m3fn") * float(q_scale)
+    qs = np.asarray(q_scale, dtype=np.float64)
+    ks = np.asarray(k_scale, dtype=np.float64)
+    q = widen(q_nope, "e4m3fn") * (qs[..., None] if qs.ndim else qs)
     if q_rope is not None:
         q = np.concatenate([q, widen(q_rope, "bf16")], axis=2)
-    kk = widen(k, "e4m3fn") * float(k_scale)
+    kk = widen(k, "e4m3fn") * (ks[..., None] if ks.ndim else ks)
     kr = None if k_rope is None else widen(k_rope, "bf16")
     return ragged_prefill(q, kk, widen(v, "bf16"), cu_seqlens, scale, k_rope=kr, block_mask=block_mask,
                           dtype="f64", rows=rows)

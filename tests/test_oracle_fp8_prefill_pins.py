@@ -1,5 +1,5 @@
 """Pins for the oracle's fp8 prefill (q_nope and K as e4m3fn codes with one
-scale per tensor, rope parts and V in bf16).  CPU only.
+scale per tensor or one per row of a head, rope parts and V in bf16).  CPU only.
 
 Each pin decodes the codes with torch's own float8_e4m3fn and bfloat16 types
 (not the oracle's tables) and checks the oracle against plain-Python brute
@@ -154,3 +154,59 @@ def test_fp8_prefill_generator_recipe():
         assert not np.any((codes & 0x7F) == 0x7F)
         err = np.abs(_t8(codes) * sc - x)
         assert np.all(err <= np.abs(x) * 2.0 ** -4 + sc * 2.0 ** -10)
+
+
+# ---------------------------------------------------------------- blockwise scales (one per row of a head)
+
+def test_fp8_blockwise_matches_bruteforce_on_torch_decoded_codes():
+    lens = [3, 70, 130]
+    T = sum(lens)
+    rng = np.random.default_rng(78)
+    qs = rng.uniform(0.005, 0.05, size=(T, 4)).astype(np.float32)
+    ks = rng.uniform(0.005, 0.05, size=(T, 2)).astype(np.float32)
+    qn, qr, k, v, kr, cu = _case(79, lens, 4, 2, 8, 4, 6)
+    out, lse = O.ragged_prefill_fp8(qn, qr, k, v, kr, cu, 0.29, qs, ks)
+    q = np.concatenate([_t8(qn) * qs.astype(np.float64)[:, :, None], _tb(qr)], axis=2)
+    kv = _t8(k) * ks.astype(np.float64)[:, :, None]
+    bo, bl = BF.prefill(_split(q, cu), _split(kv, cu), _split(_tb(v), cu), lens, 0.29,
+                        k_rope=[x[:, 0, :] for x in _split(_tb(kr), cu)])
+    np.testing.assert_allclose(out, np.concatenate([np.array(x) for x in bo]), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, np.concatenate([np.array(x) for x in bl]), rtol=0, atol=1e-12)
+
+
+def test_fp8_blockwise_with_equal_scales_is_the_per_tensor_result():
+    lens = [90, 40]
+    qn, qr, k, v, kr, cu = _case(80, lens, 4, 2, 16, 8, 8)
+    a = O.ragged_prefill_fp8(qn, qr, k, v, kr, cu, 0.2, 0.03, 0.07)
+    b = O.ragged_prefill_fp8(qn, qr, k, v, kr, cu, 0.2, np.full((130, 4), 0.03), np.full((130, 2), 0.07))
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
+
+
+def test_fp8_blockwise_key_scale_zero_removes_the_nope_term_of_that_key():
+    """k_scale[j] = 0 leaves key j only its rope score: the result equals the
+    oracle with that key's codes zeroed (a different input, same definition)."""
+    lens = [40]
+    qn, qr, k, v, kr, cu = _case(81, lens, 2, 1, 16, 8, 8)
+    ks = np.full((40, 1), 0.04)
+    ks[[3, 17, 39]] = 0.0
+    a = O.ragged_prefill_fp8(qn, qr, k, v, kr, cu, 0.3, 0.02, ks)
+    k0 = k.copy()
+    k0[[3, 17, 39]] = 0
+    b = O.ragged_prefill_fp8(qn, qr, k0, v, kr, cu, 0.3, 0.02, 0.04)
+    np.testing.assert_allclose(a[0], b[0], rtol=0, atol=1e-14)
+
+
+def test_fp8_blockwise_generator_recipe():
+    lens = [70, 200]
+    c8 = gen.make_prefill_fp8_case(name="t", seed=6, seq_lens=lens, Hq=4, Hk=2, D_rope=64, blockwise=True)
+    cb = gen.make_prefill_case(name="t", seed=6, seq_lens=lens, Hq=4, Hk=2, D_qk=192, D_rope=64, D_v=128)
+    assert c8.q_scale.shape == (270, 4) and c8.k_scale.shape == (270, 2)
+    assert c8.q_scale.dtype == np.float32 and c8.k_scale.dtype == np.float32
+    for codes, bits, sc in ((c8.q, cb.q[:, :, :128], c8.q_scale), (c8.k, cb.k, c8.k_scale)):
+        x = _tb(np.ascontiguousarray(bits))
+        np.testing.assert_allclose(sc, np.abs(x).max(axis=2) / 448, rtol=1e-6)
+        err = np.abs(_t8(codes) * sc.astype(np.float64)[:, :, None] - x)
+        assert np.all(err <= np.abs(x) * 2.0 ** -4 + sc[:, :, None] * 2.0 ** -10)
+        # every row uses its full range: its largest code is +-448
+        assert np.all(np.abs(_t8(codes)).max(axis=2) == 448)

@@ -55,13 +55,20 @@ MUTANTS = {
     "lse_sign": ("m_safe + np.log(", "m_safe - np.log(", [P.test_decode_matches_torch_sdpa]),
     "gqa_ratio_inverted_prefill": ("Qc = Q[gi, heads, :]", "Qc = Q[gi, g:g + r, :]",
                                    [P.test_prefill_gqa_matches_sdpa]),
-    "fp8_q_scale_dropped": ('q = widen(q_nope, "e4m3fn") * float(q_scale)', 'q = widen(q_nope, "e4m3fn")',
+    "fp8_q_scale_dropped": ('q = widen(q_nope, "e4m3fn") * (qs[..., None] if qs.ndim else qs)',
+                            'q = widen(q_nope, "e4m3fn")',
                             [P8.test_fp8_prefill_matches_bruteforce_on_torch_decoded_codes]),
-    "fp8_k_scale_dropped": ('kk = widen(k, "e4m3fn") * float(k_scale)', 'kk = widen(k, "e4m3fn")',
+    "fp8_k_scale_dropped": ('kk = widen(k, "e4m3fn") * (ks[..., None] if ks.ndim else ks)',
+                            'kk = widen(k, "e4m3fn")',
                             [P8.test_fp8_prefill_gqa_without_rope_matches_sdpa]),
     "fp8_scale_on_rope": ('np.concatenate([q, widen(q_rope, "bf16")], axis=2)',
                           'np.concatenate([q, widen(q_rope, "bf16") * float(q_scale)], axis=2)',
                           [P8.test_fp8_prefill_scales_leave_the_rope_part_alone]),
+    "fp8_blockwise_key_scale_mean": ("(ks[..., None] if ks.ndim else ks)", "(ks.mean() if ks.ndim else ks)",
+                                     [P8.test_fp8_blockwise_matches_bruteforce_on_torch_decoded_codes]),
+    "fp8_blockwise_query_scale_flipped": ("(qs[..., None] if qs.ndim else qs)",
+                                          "(qs[::-1, :, None] if qs.ndim else qs)",
+                                          [P8.test_fp8_blockwise_matches_bruteforce_on_torch_decoded_codes]),
     "fp8_rope_dropped": ('np.concatenate([q, widen(q_rope, "bf16")], axis=2)',
                          'np.concatenate([q, 0 * widen(q_rope, "bf16")], axis=2)',
                          [P8.test_fp8_prefill_matches_sdpa_with_concatenated_rope_key]),

@@ -76,12 +76,16 @@ def to_bf16_bits(x: np.ndarray) -> np.ndarray:
 
 
 def to_e4m3fn_bits(x: np.ndarray, scale: float) -> np.ndarray:
-    """Quantise x / scale to OCP fp8 e4m3fn bytes with saturation to +-448.
+    """Quantise x / scale to OCP fp8 e4m3fn bytes with saturation to +-448
+    (scale a float, or an array that broadcasts against x).
 
     torch's cast rounds to nearest even but does not saturate (values >= 480
     become NaN), hence the clamp first."""
     t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
-    t = (t / np.float32(scale)).clamp_(-E4M3FN_MAX, E4M3FN_MAX)
+    if np.ndim(scale):  # one scale per block, broadcast against x
+        t = (t / torch.from_numpy(np.ascontiguousarray(scale, dtype=np.float32))).clamp_(-E4M3FN_MAX, E4M3FN_MAX)
+    else:
+        t = (t / np.float32(scale)).clamp_(-E4M3FN_MAX, E4M3FN_MAX)
     return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
 
 
@@ -284,10 +288,11 @@ class PrefillCase:
     dtype: str = "bf16"
     # dtype 'e4m3fn': q holds the nope part only, [T, Hq, D_nope] e4m3fn codes,
     # k [T, Hk, D_nope] e4m3fn codes, q_rope [T, Hq, D_rope] bf16 bits (None
-    # without rope); q_scale / k_scale are the two tensors' scales.
+    # without rope); q_scale / k_scale are the two tensors' scales (per tensor
+    # or per row of a head).
     q_rope: Optional[np.ndarray] = None
-    q_scale: float = 1.0
-    k_scale: float = 1.0
+    q_scale: object = 1.0     # float, or float32 [T, Hq] with blockwise scales
+    k_scale: object = 1.0     # float, or float32 [T, Hk]
     meta: dict = field(default_factory=dict)
 
     @property
@@ -392,22 +397,32 @@ def make_prefill_fp8_case(
     D_rope: int = 64,
     mask_density: Optional[float] = None,
     scale: Optional[float] = None,
+    blockwise: bool = False,
 ) -> PrefillCase:
     """The bf16 prefill problem of make_prefill_case (same seed, same draws,
     Dn = 128, Dv = 128), with the nope part of Q and all of K quantised to fp8
-    e4m3fn, each tensor with the per-tensor scale amax / 448 of the fp8 KV
-    recipe; the rope parts and V stay bf16.  scale defaults to 1/sqrt(128 + D_rope)."""
+    e4m3fn with scale amax / 448 (the fp8 KV recipe): per tensor, or with
+    ``blockwise`` per row of a head (a 1 x 128 block), giving float32 scale
+    arrays [T, Hq] and [T, Hk] (an all-zero row gets scale 1).  The rope parts
+    and V stay bf16.  scale defaults to 1/sqrt(128 + D_rope)."""
     base = make_prefill_case(name=name, seed=seed, seq_lens=seq_lens, Hq=Hq, Hk=Hk, D_qk=128 + D_rope,
                              D_rope=D_rope, D_v=128, mask_density=mask_density, scale=scale)
     qf = _bf16_bits_to_f32(base.q[:, :, :128])
     kf = _bf16_bits_to_f32(base.k)
-    scales = []
+    scales, codes = [], []
     for x in (qf, kf):
-        amax = float(np.abs(x).max()) if x.size else 1.0
-        scales.append(float(np.float32(amax) / np.float32(E4M3FN_MAX)) if amax > 0 else 1.0)
+        if blockwise:
+            amax = np.abs(x).max(axis=2) if x.size else np.ones(x.shape[:2], np.float32)
+            sc = np.where(amax > 0, amax.astype(np.float32) / np.float32(E4M3FN_MAX), np.float32(1.0))
+            sc = sc.astype(np.float32)
+            codes.append(to_e4m3fn_bits(x, sc[..., None]))
+        else:
+            amax = float(np.abs(x).max()) if x.size else 1.0
+            sc = float(np.float32(amax) / np.float32(E4M3FN_MAX)) if amax > 0 else 1.0
+            codes.append(to_e4m3fn_bits(x, sc))
+        scales.append(sc)
     base.q_rope = np.ascontiguousarray(base.q[:, :, 128:]) if D_rope else None
-    base.q = to_e4m3fn_bits(qf, scales[0])
-    base.k = to_e4m3fn_bits(kf, scales[1])
+    base.q, base.k = codes
     base.q_scale, base.k_scale = scales
     base.dtype = "e4m3fn"
     return base
