@@ -9,8 +9,8 @@ V rows) divided by the measured time per step.  Inputs are resident in HBM
 before the timed region; consecutive steps read different copies of the KV
 pool, so no step is served from the 256 MB last-level cache by its
 predecessor.  The other workloads (fp8 KV decode, MLA prefill, block-sparse
-prefill, fp8 MLA prefill, chunked prefill) are measured the same way and
-reported under "secondary".
+prefill, fp8 MLA prefill with per-tensor and blockwise scales, chunked
+prefill) are measured the same way and reported under "secondary".
 
 Prints ONE JSON line.
 """
@@ -80,11 +80,12 @@ DOMINANT_KERNEL = {
     "decode_gqa_bf16": "decode_worker_mfma<128, false>",
     "decode_long_fp8": "decode_worker_mfma<128, true>",
     "decode_tiny_fp32": "decode_worker_f32",
-    "prefill_mla_bf16": "prefill_fwd<64, false, false>",
-    "prefill_blocksparse_bf16": "prefill_fwd<0, false, false>",
-    "prefill_chunk_bf16": "prefill_fwd<0, true, false>",
-    "prefill_chunk_mla_bf16": "prefill_fwd<64, true, false>",
-    "prefill_mla_fp8": "prefill_fwd<64, false, true>",
+    "prefill_mla_bf16": "prefill_fwd<64, false, 0>",
+    "prefill_blocksparse_bf16": "prefill_fwd<0, false, 0>",
+    "prefill_chunk_bf16": "prefill_fwd<0, true, 0>",
+    "prefill_chunk_mla_bf16": "prefill_fwd<64, true, 0>",
+    "prefill_mla_fp8": "prefill_fwd<64, false, 1>",
+    "prefill_mla_fp8_blockwise": "prefill_fwd<64, false, 2>",
 }
 
 
@@ -375,7 +376,8 @@ def main(argv=None) -> int:
         secondary.append(r4)
         del c4
         if hasattr(gu, "DevicePrefill"):
-            for mk in (gen.prefill_mla_bf16, gen.prefill_blocksparse_bf16, gen.prefill_mla_fp8):
+            for mk in (gen.prefill_mla_bf16, gen.prefill_blocksparse_bf16, gen.prefill_mla_fp8,
+                       gen.prefill_mla_fp8_blockwise):
                 pc = mk()
                 rp = bench_prefill(pc, args.steps, args.warmup, torch, gq, gu)
                 peak = prefill_peak_tflops(pc)

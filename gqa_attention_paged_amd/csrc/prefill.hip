@@ -58,6 +58,10 @@ struct PrefillArgs {
   const uint16_t* qr;
   int64_t qr_st, qr_sh;
   float qk;
+  // fp8 prefill with blockwise scales: one float per row of a head,
+  // q_scale [T, Hq] and k_scale [T, Hk], both contiguous.
+  const float* qsc;
+  const float* ksc;
 };
 
 namespace dev {
@@ -103,10 +107,12 @@ __device__ __forceinline__ int vswz256(int row, int c) {
 
 using namespace dev;
 
-// F8: the nope parts of Q and K are fp8 e4m3fn codes (K tiles of 64 rows x
-// 128 bytes, staged like the rope tile) and their products run on the fp8
-// matrix cores; the rope parts and V stay bf16.
-template <int DR, bool PAGED, bool F8>
+// F8 = 1 or 2: the nope parts of Q and K are fp8 e4m3fn codes (K tiles of 64
+// rows x 128 bytes, staged like the rope tile) and their products run on the
+// fp8 matrix cores; the rope parts and V stay bf16.  F8 = 1 has one scale per
+// tensor, F8 = 2 one per row of a head (the key scales of a tile are staged in
+// LDS next to it).
+template <int DR, bool PAGED, int F8>
 __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
   static_assert(!(F8 && PAGED), "the fp8 path reads token-major K");
   constexpr int DN = 128;                     // per-head key width
@@ -125,6 +131,8 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
   __shared__ __attribute__((aligned(1024))) unsigned char kbuf0[KB], kbuf1[KB];
   __shared__ __attribute__((aligned(1024))) unsigned char rbuf0[RB ? RB : 16], rbuf1[RB ? RB : 16];
   __shared__ __attribute__((aligned(1024))) unsigned char vbuf0[VB], vbuf1[VB];
+  // Blockwise key scales of a tile: one 64-float copy per wave.
+  __shared__ __attribute__((aligned(1024))) float sbuf0[F8 == 2 ? 256 : 4], sbuf1[F8 == 2 ? 256 : 4];
 
   // Work item.  The grid is one-dimensional, Hq workgroups per (query tile,
   // sequence) pair; pairs are ranked deepest query tile first, then by
@@ -183,6 +191,11 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
   const bool wave_rows = r0 < L;
   const int rlast = min(L, r0 + 32) - 1;     // last valid row of the wave
   const int klast = off + rlast;             // last key visible to the wave
+  // Factor of the fp8 nope sum that belongs to this lane's query row: its
+  // blockwise scale (the key's comes per score), or q_scale * k_scale.
+  float qsl = 0.f;
+  if constexpr (F8 == 2) qsl = qrow < L ? a.qsc[(int64_t)(c0 + qrow) * a.Hq + h] : 0.f;
+  if constexpr (F8 == 1) qsl = a.qk;
 
   // The wave's queries as the B operand: lane (query l32, half hh) holds
   // d = 16 s + 8 hh .. +7 for k-step s (s < KSN: nope part, then rope).
@@ -292,6 +305,12 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
   auto dma = [&](const unsigned char* gp, unsigned char* lp) {
     __builtin_amdgcn_global_load_lds((const void*)gp, (GQAP_LDS void*)lp, 16, 0, 0);
   };
+  // Blockwise key scales: lane l of every wave fetches the scale of key l of
+  // the tile into the wave's own 256-byte copy.
+  auto dma4 = [&](const float* gp, float* lp) {
+    __builtin_amdgcn_global_load_lds((const void*)gp, (GQAP_LDS void*)((unsigned char*)lp + (wseg >> 2)), 4, 0, 0);
+  };
+  const float* ksg = F8 == 2 ? a.ksc + (int64_t)c0 * a.Hk + g : nullptr;
   // First byte of key tile kt of K / V.  With PAGED a tile is one page: the
   // 64 x D slab of pool block block_table[b, kt] for KV head g (FlashMLA
   // tensor-shape reference, section 1: tokens 64j .. 64j+63 live in
@@ -335,6 +354,8 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
     unsigned char* kd = BUF ? kbuf1 : kbuf0;
     unsigned char* rd = BUF ? rbuf1 : rbuf0;
     unsigned char* vd = BUF ? vbuf1 : vbuf0;
+    if constexpr (F8 == 2)
+      dma4(ksg + (int64_t)(kt * 64 + min(lane, Lk - 1 - kt * 64)) * a.Hk, BUF ? sbuf1 : sbuf0);
     const int key0 = kt * 64;
     const unsigned char* kt_k = tile_k(kt);
     const unsigned char* kt_v = tile_v(kt);
@@ -415,7 +436,9 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
     unsigned char* kd = BUF ? kbuf0 : kbuf1;
     unsigned char* rd = BUF ? rbuf0 : rbuf1;
     unsigned char* vd = BUF ? vbuf0 : vbuf1;
-    constexpr int NLD = KLD + RLD + VLD;
+    const float* sb = BUF ? sbuf1 : sbuf0;
+    float* sd = BUF ? sbuf0 : sbuf1;
+    constexpr int NLD = KLD + RLD + VLD + (F8 == 2 ? 1 : 0);
     const unsigned char* kt_k = WL ? tile_k(kn) : nullptr;
     const unsigned char* kt_v = WL ? tile_v(kn) : nullptr;
     const unsigned char* kt_r = DR && WL ? tile_r(kn) : nullptr;
@@ -424,8 +447,10 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
         dma(kt_k + KRS * i * kstr + koff, kd + 4096 * i + wseg);
       else if (i < KLD + RLD)
         dma(kt_r + 32 * (i - KLD) * rstr + roff, rd + 4096 * (i - KLD) + wseg);
-      else
+      else if (i < KLD + RLD + VLD)
         dma(kt_v + 16 * (i - KLD - RLD) * vstr + voff, vd + 4096 * (i - KLD - RLD) + wseg);
+      else if constexpr (F8 == 2)
+        dma4(ksg + (int64_t)(kn * 64 + lane) * a.Hk, sd);
     };
     f32x16_t s[2] = {f32x16_t{}, f32x16_t{}};
     if constexpr (!F8) {
@@ -466,6 +491,21 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
       constexpr int NU = 8 + 2 * KSR;
       constexpr int NM = 4 + 2 * KSR;
       constexpr int PF = 8;
+      // The nope sum of half t times its scales: per lane (query) and, with
+      // blockwise scales, per key (register j holds key 32t + 8(j/4) + 4hh + j%4).
+      auto scale_half = [&](int t) {
+        if constexpr (F8 == 2) {
+          const float* sp = sb + (wseg >> 4) + 32 * t + 4 * hh;
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const f32x4 w = *(const f32x4*)(sp + 8 * m);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s[t][4 * m + e] *= qsl * w[e];
+          }
+        } else {
+          s[t] *= qsl;
+        }
+      };
       auto unit = [&](int u) -> i32x4 {
         if (u < 8) return load16(kb + (u >> 2) * 4096 + kra[u & 3]);
         if constexpr (KSR > 0) {
@@ -490,12 +530,17 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
           s[t] = mfma32x32x64_fp8(ka, q8[st], s[t]);
         } else if constexpr (KSR > 0) {
           const int r = i - 4, t = r / KSR;
-          if (r % KSR == 0) s[t] *= a.qk;
+          if (r % KSR == 0) scale_half(t);
           s[t] = mfma32x32x16(__builtin_bit_cast(bf16x8, uf[8 + r]), qop[r % KSR], s[t]);
         }
         if (WL)
 #pragma unroll
           for (int j = i * NLD / NM; j < (i + 1) * NLD / NM; ++j) issue_load(j);
+      }
+      // Without rope the per-tensor scales are part of the softmax constant.
+      if constexpr (KSR == 0 && F8 == 2) {
+        scale_half(0);
+        scale_half(1);
       }
       __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
 #pragma unroll
@@ -764,27 +809,23 @@ extern "C" gqap_status gqap_prefill(const gqap_prefill_plan_t* plan, const void*
   const dim3 grid((unsigned)d.num_q_heads * (unsigned)d.batch * (unsigned)plan->q_tiles);
   hipStream_t st = (hipStream_t)stream;
   if (d.head_dim_rope == 64)
-    hipLaunchKernelGGL((prefill_fwd<64, false, false>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((prefill_fwd<64, false, 0>), grid, dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL((prefill_fwd<0, false, false>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((prefill_fwd<0, false, 0>), grid, dim3(256), 0, st, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(GQAP_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
   return GQAP_OK;
 }
 
-extern "C" gqap_status gqap_prefill_fp8(const gqap_prefill_plan_t* plan, const void* q_nope, const void* q_rope,
-                                        const void* k, const void* v, const void* k_rope,
-                                        const int32_t* cu_seqlens, const uint8_t* block_mask, float scale,
-                                        float q_scale, float k_scale, void* out, float* lse, void* workspace,
-                                        uint64_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
+// Checks and argument set-up shared by the two fp8 entry points.
+static gqap_status fp8_args(const gqap_prefill_plan_t* plan, const void* q_nope, const void* q_rope, const void* k,
+                            const void* v, const void* k_rope, const int32_t* cu_seqlens, const uint8_t* block_mask,
+                            float scale, void* out, float* lse, PrefillArgs* a) {
   if (!plan || plan->magic != GQAP_PLAN_MAGIC) return fail(GQAP_ERR_INVALID_ARGUMENT, "invalid prefill plan");
   const gqap_prefill_desc_t& d = plan->desc;
   if (d.dtype != GQAP_FP8_E4M3FN)
-    return fail(GQAP_ERR_DTYPE, "gqap_prefill_fp8 takes a plan with dtype GQAP_FP8_E4M3FN");
-  if (!std::isfinite(scale) || !std::isfinite(q_scale) || !std::isfinite(k_scale))
-    return fail(GQAP_ERR_INVALID_ARGUMENT, "scale, q_scale and k_scale must be finite");
+    return fail(GQAP_ERR_DTYPE, "the fp8 prefill takes a plan with dtype GQAP_FP8_E4M3FN");
+  if (!std::isfinite(scale)) return fail(GQAP_ERR_INVALID_ARGUMENT, "scale must be finite");
   if (d.batch == 0 || plan->q_tiles == 0) return GQAP_OK;
   if (!q_nope || !k || !v || !cu_seqlens || !out) return fail(GQAP_ERR_INVALID_ARGUMENT, "null device pointer");
   if (d.head_dim_rope && (!k_rope || !q_rope))
@@ -796,27 +837,68 @@ extern "C" gqap_status gqap_prefill_fp8(const gqap_prefill_plan_t* plan, const v
       (k_rope && misaligned16(k_rope)) || (q_rope && misaligned16(q_rope)) || ((uintptr_t)cu_seqlens & 3) ||
       (lse && ((uintptr_t)lse & 3)))
     return fail(GQAP_ERR_INVALID_ARGUMENT, "device pointers must be 16-byte aligned (cu_seqlens, lse 4-byte)");
-  PrefillArgs a = ragged_args(plan, cu_seqlens, block_mask, out, lse);
-  a.q = (const uint16_t*)q_nope;
-  a.k = (const uint16_t*)k;
-  a.v = (const uint16_t*)v;
-  a.kr = (const uint16_t*)k_rope;
-  a.qr = (const uint16_t*)q_rope;
-  a.qr_st = d.qr_stride_token;
-  a.qr_sh = d.qr_stride_head;
-  // With the rope part the nope sum is scaled inside the kernel; without it
-  // the whole score is the nope sum and the scales join the softmax constant.
-  a.qk = q_scale * k_scale;
-  a.scale_log2 = d.head_dim_rope ? scale * dev::kLog2e : scale * a.qk * dev::kLog2e;
+  *a = ragged_args(plan, cu_seqlens, block_mask, out, lse);
+  a->q = (const uint16_t*)q_nope;
+  a->k = (const uint16_t*)k;
+  a->v = (const uint16_t*)v;
+  a->kr = (const uint16_t*)k_rope;
+  a->qr = (const uint16_t*)q_rope;
+  a->qr_st = d.qr_stride_token;
+  a->qr_sh = d.qr_stride_head;
+  a->scale_log2 = scale * dev::kLog2e;
+  return GQAP_OK;
+}
+
+template <int F8>
+static gqap_status launch_fp8(const gqap_prefill_plan_t* plan, const PrefillArgs& a, void* stream) {
+  const gqap_prefill_desc_t& d = plan->desc;
   const dim3 grid((unsigned)d.num_q_heads * (unsigned)d.batch * (unsigned)plan->q_tiles);
   hipStream_t st = (hipStream_t)stream;
   if (d.head_dim_rope == 64)
-    hipLaunchKernelGGL((prefill_fwd<64, false, true>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((prefill_fwd<64, false, F8>), grid, dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL((prefill_fwd<0, false, true>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((prefill_fwd<0, false, F8>), grid, dim3(256), 0, st, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(GQAP_ERR_HIP, "fp8 prefill launch: %s", hipGetErrorString(e));
   return GQAP_OK;
+}
+
+extern "C" gqap_status gqap_prefill_fp8(const gqap_prefill_plan_t* plan, const void* q_nope, const void* q_rope,
+                                        const void* k, const void* v, const void* k_rope,
+                                        const int32_t* cu_seqlens, const uint8_t* block_mask, float scale,
+                                        float q_scale, float k_scale, void* out, float* lse, void* workspace,
+                                        uint64_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  if (!std::isfinite(q_scale) || !std::isfinite(k_scale))
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "scale, q_scale and k_scale must be finite");
+  PrefillArgs a{};
+  const gqap_status s = fp8_args(plan, q_nope, q_rope, k, v, k_rope, cu_seqlens, block_mask, scale, out, lse, &a);
+  if (s != GQAP_OK || plan->desc.batch == 0 || plan->q_tiles == 0) return s;
+  // With the rope part the nope sum is scaled inside the kernel; without it
+  // the whole score is the nope sum and the scales join the softmax constant.
+  a.qk = q_scale * k_scale;
+  if (!plan->desc.head_dim_rope) a.scale_log2 *= a.qk;
+  return launch_fp8<1>(plan, a, stream);
+}
+
+extern "C" gqap_status gqap_prefill_fp8_blockwise(const gqap_prefill_plan_t* plan, const void* q_nope,
+                                                  const void* q_rope, const void* k, const void* v,
+                                                  const void* k_rope, const int32_t* cu_seqlens,
+                                                  const uint8_t* block_mask, float scale, const float* q_scales,
+                                                  const float* k_scales, void* out, float* lse, void* workspace,
+                                                  uint64_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  PrefillArgs a{};
+  const gqap_status s = fp8_args(plan, q_nope, q_rope, k, v, k_rope, cu_seqlens, block_mask, scale, out, lse, &a);
+  if (s != GQAP_OK || plan->desc.batch == 0 || plan->q_tiles == 0) return s;
+  if (!q_scales || !k_scales) return fail(GQAP_ERR_INVALID_ARGUMENT, "q_scales and k_scales are required");
+  if (((uintptr_t)q_scales & 3) || ((uintptr_t)k_scales & 3))
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "q_scales and k_scales must be 4-byte aligned");
+  a.qsc = q_scales;
+  a.ksc = k_scales;
+  return launch_fp8<2>(plan, a, stream);
 }
 
 extern "C" gqap_status gqap_append_kv(const gqap_chunk_plan_t* plan, const void* k_new, const void* v_new,
@@ -920,9 +1002,9 @@ extern "C" gqap_status gqap_chunk_prefill(const gqap_chunk_plan_t* plan, const v
   a.max_kv = d.max_kv_len;
   const dim3 grid((unsigned)d.num_q_heads * (unsigned)d.batch * (unsigned)plan->q_tiles);
   if (d.head_dim_rope == 64)
-    hipLaunchKernelGGL((prefill_fwd<64, true, false>), grid, dim3(256), 0, (hipStream_t)stream, a);
+    hipLaunchKernelGGL((prefill_fwd<64, true, 0>), grid, dim3(256), 0, (hipStream_t)stream, a);
   else
-    hipLaunchKernelGGL((prefill_fwd<0, true, false>), grid, dim3(256), 0, (hipStream_t)stream, a);
+    hipLaunchKernelGGL((prefill_fwd<0, true, 0>), grid, dim3(256), 0, (hipStream_t)stream, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(GQAP_ERR_HIP, "chunk prefill launch: %s", hipGetErrorString(e));
   return GQAP_OK;

@@ -9,7 +9,7 @@
  *     (a 128-wide per-head key part plus a 64-wide rope key shared by all
  *     heads) and an optional 64x64 block-sparse mask;
  *   - the same prefill with the nope parts of Q and K in fp8 e4m3fn, one
- *     scale per tensor, on the fp8 matrix cores;
+ *     scale per tensor or one per row of a head, on the fp8 matrix cores;
  *   - chunked prefill against the paged cache (append the chunk's keys and
  *     values, then attend to the cached prefix and the chunk);
  *   - the padded block table built from a CSR page list;
@@ -299,6 +299,24 @@ gqap_status gqap_prefill_fp8(const gqap_prefill_plan_t* plan,
                              const void* k_rope, const int32_t* cu_seqlens, const uint8_t* block_mask,
                              float scale, float q_scale, float k_scale, void* out, float* lse,
                              void* workspace, uint64_t workspace_bytes, void* stream);
+
+/*
+ * The fp8 prefill with blockwise scales: one fp32 scale per row of a head,
+ * i.e. per 1 x Dn block of q_nope and of k (the page leaves the layout of
+ * q_scale and k_scales open; this is the finest one that keeps a row in a
+ * single scale).  q_scales [T, Hq] and k_scales [T, Hk] are contiguous fp32
+ * device arrays (4-byte aligned); the score is
+ *   scale * (q_scales[i,h] * k_scales[j,g] * (q_nope[i,h] codes . k[j,g] codes)
+ *            + q_rope[i,h] . k_rope[j]).
+ * Everything else as gqap_prefill_fp8.  Errors: those of gqap_prefill_fp8,
+ * and INVALID_ARGUMENT for a null or misaligned scale array.
+ */
+gqap_status gqap_prefill_fp8_blockwise(const gqap_prefill_plan_t* plan,
+                                       const void* q_nope, const void* q_rope, const void* k, const void* v,
+                                       const void* k_rope, const int32_t* cu_seqlens, const uint8_t* block_mask,
+                                       float scale, const float* q_scales, const float* k_scales,
+                                       void* out, float* lse, void* workspace, uint64_t workspace_bytes,
+                                       void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Chunked prefill against a paged KV cache                                  */

@@ -92,6 +92,11 @@ class DevicePrefill:
         self.k = bits_to_tensor(case.k, case.dtype).to(device)
         self.v = bits_to_tensor(case.v, "bf16").to(device)
         self.kr = bits_to_tensor(case.k_rope, "bf16").to(device) if case.k_rope is not None else None
+        # fp8 with one scale per row of a head: [T, Hq] and [T, Hk] float32 arrays on the device
+        self.blockwise = self.fp8 and np.ndim(case.q_scale) > 0
+        if self.blockwise:
+            self.qsc = torch.from_numpy(np.ascontiguousarray(case.q_scale, dtype=np.float32)).to(device)
+            self.ksc = torch.from_numpy(np.ascontiguousarray(case.k_scale, dtype=np.float32)).to(device)
         self.cu = torch.from_numpy(np.ascontiguousarray(case.cu_seqlens, dtype=np.int32)).to(device)
         self.mask = (torch.from_numpy(np.ascontiguousarray(case.block_mask, dtype=np.uint8)).to(device)
                      if case.block_mask is not None else None)
@@ -104,7 +109,10 @@ class DevicePrefill:
         self.plan = gq.gqap_prefill_plan(self.desc)
 
     def run(self, stream=None):
-        if self.fp8:
+        if self.blockwise:
+            gq.gqap_prefill_fp8_blockwise(self.plan, self.q, self.qr, self.k, self.v, self.kr, self.cu, self.mask,
+                                          self.case.scale, self.qsc, self.ksc, self.out, self.lse, stream=stream)
+        elif self.fp8:
             gq.gqap_prefill_fp8(self.plan, self.q, self.qr, self.k, self.v, self.kr, self.cu, self.mask,
                                 self.case.scale, self.case.q_scale, self.case.k_scale, self.out, self.lse,
                                 stream=stream)

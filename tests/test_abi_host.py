@@ -298,6 +298,23 @@ def test_fp8_prefill_rejects_non_finite_scales(gq, scales):
     assert gq.STATUS_NAMES[st] == "INVALID_ARGUMENT"
 
 
+def test_fp8_blockwise_prefill_rejects(gq):
+    p8 = gq.gqap_prefill_plan(baseline_fp8_prefill_desc(gq))
+    pb = gq.gqap_prefill_plan(baseline_prefill_desc(gq))
+    fake = 1 << 20  # never dereferenced: validation fails first
+    call = gq.lib().gqap_prefill_fp8_blockwise
+    st = call(ctypes.byref(pb), fake, fake, fake, fake, fake, fake, None, 1.0, fake, fake, fake, None, None, 0, None)
+    assert gq.STATUS_NAMES[st] == "DTYPE"
+    st = call(ctypes.byref(p8), fake, fake, fake, fake, fake, fake, None, 1.0, None, fake, fake, None, None, 0, None)
+    assert gq.STATUS_NAMES[st] == "INVALID_ARGUMENT" and "scales" in gq.gqap_last_error()
+    st = call(ctypes.byref(p8), fake, fake, fake, fake, fake, fake, None, 1.0, fake + 2, fake, fake, None, None, 0,
+              None)
+    assert gq.STATUS_NAMES[st] == "INVALID_ARGUMENT" and "aligned" in gq.gqap_last_error()
+    st = call(ctypes.byref(p8), fake, fake, fake, fake, fake, fake, None, float("nan"), fake, fake, fake, None, None,
+              0, None)
+    assert gq.STATUS_NAMES[st] == "INVALID_ARGUMENT"
+
+
 def test_fp8_prefill_rejects_missing_rope_tensors(gq):
     p8 = gq.gqap_prefill_plan(baseline_fp8_prefill_desc(gq))
     fake = 1 << 20  # never dereferenced: validation fails first

@@ -1,9 +1,10 @@
-"""fp8 ragged prefill on the GPU through the C ABI (gqap_prefill_fp8), against
-the fp64 oracle run on the same fp8 codes and bf16 values.
+"""fp8 ragged prefill on the GPU through the C ABI (gqap_prefill_fp8 and
+gqap_prefill_fp8_blockwise), against the fp64 oracle run on the same fp8 codes
+and bf16 values.
 
-The nope parts of Q and K are e4m3fn codes with one scale per tensor; the rope
-parts and V are bf16.  Bar: max-abs-err of out and lse within 6e-2, the
-tolerance for fp8 inputs."""
+The nope parts of Q and K are e4m3fn codes with one scale per tensor, or one
+per row of a head; the rope parts and V are bf16.  Bar: max-abs-err of out and
+lse within 6e-2, the tolerance for fp8 inputs."""
 import numpy as np
 import pytest
 import torch
@@ -39,9 +40,13 @@ def _rows_sample(case, n_mid=64, seed=0):
     return np.array(sorted(rows), dtype=np.int64)
 
 
+def _sc(x):
+    return f"per-row {np.shape(x)}" if np.ndim(x) else f"{x:.3g}"
+
+
 def _check(gu, case, rows=None, tol=TOL):
     gu.announce(f"fp8 prefill {case.name} lens={list(case.seq_lens)[:8]} Hq={case.Hq} Hk={case.Hk} "
-                f"Dr={case.D_rope} mask={case.block_mask is not None} qs={case.q_scale:.3g} ks={case.k_scale:.3g} "
+                f"Dr={case.D_rope} mask={case.block_mask is not None} qs={_sc(case.q_scale)} ks={_sc(case.k_scale)} "
                 f"seed={case.meta.get('seed')}")
     dp = gu.DevicePrefill(case)
     dp.run()
@@ -107,3 +112,45 @@ def test_fp8_zero_nope_codes_leave_rope_attention(gu):
 def test_fp8_long_sequence_sampled(gu):
     case = gen.make_prefill_fp8_case(name="fp8_long", seed=86, seq_lens=[8192], Hq=8, Hk=1, D_rope=64)
     _check(gu, case, rows=_rows_sample(case))
+
+
+# ---------------------------------------------------------------- blockwise scales (gqap_prefill_fp8_blockwise)
+
+def test_fp8_blockwise_mla_config_full_size_sampled(gu):
+    case = gen.prefill_mla_fp8_blockwise()
+    _check(gu, case, rows=_rows_sample(case))
+
+
+@pytest.mark.parametrize("Hq,Hk,Dr", [(16, 16, 64), (8, 2, 64), (8, 2, 0), (4, 1, 0)])
+def test_fp8_blockwise_small_ragged(gu, Hq, Hk, Dr):
+    case = gen.make_prefill_fp8_case(name="fp8_bw_small", seed=87, seq_lens=[1, 63, 64, 65, 130, 300], Hq=Hq,
+                                     Hk=Hk, D_rope=Dr, blockwise=True)
+    _check(gu, case)
+
+
+def test_fp8_blockwise_spread_scales_and_mask(gu):
+    """Row scales spread over three decades (codes unchanged), so a scale taken
+    from the wrong key, row or head shows; with a block mask and a ragged end."""
+    case = gen.make_prefill_fp8_case(name="fp8_bw_spread", seed=88, seq_lens=[700, 333], Hq=8, Hk=2, D_rope=64,
+                                     mask_density=0.4, blockwise=True)
+    rng = np.random.default_rng(5)
+    case.q_scale = (case.q_scale * 10.0 ** rng.uniform(-1.5, 1.0, size=case.q_scale.shape)).astype(np.float32)
+    case.k_scale = (case.k_scale * 10.0 ** rng.uniform(-1.5, 1.0, size=case.k_scale.shape)).astype(np.float32)
+    _check(gu, case)
+
+
+def test_fp8_blockwise_equal_scales_match_per_tensor(gu):
+    """Blockwise arrays that hold one value everywhere give the per-tensor
+    kernel's result to within rounding of the order of the two multiplies."""
+    case = gen.make_prefill_fp8_case(name="fp8_bw_eq", seed=89, seq_lens=[300, 129], Hq=8, Hk=2, D_rope=64)
+    dp = gu.DevicePrefill(case)
+    dp.run()
+    out_t, lse_t = dp.results()
+    T = case.T
+    case.q_scale = np.full((T, case.Hq), case.q_scale, np.float32)
+    case.k_scale = np.full((T, case.Hk), case.k_scale, np.float32)
+    dpb = gu.DevicePrefill(case)
+    assert dpb.blockwise
+    dpb.run()
+    out_b, lse_b = dpb.results()
+    assert gu.max_abs_err(out_b, out_t) <= 1e-2 and gu.lse_err(lse_b, lse_t) <= 1e-4

@@ -449,6 +449,13 @@ def prefill_mla_fp8(seed: int = 1009, seq_lens=(512, 1024, 2048, 3000)) -> Prefi
     return make_prefill_fp8_case(name="prefill_mla_fp8", seed=seed, seq_lens=seq_lens, Hq=16, Hk=16, D_rope=64)
 
 
+def prefill_mla_fp8_blockwise(seed: int = 1010, seq_lens=(512, 1024, 2048, 3000)) -> PrefillCase:
+    """prefill_mla_fp8 with one scale per row of a head (1 x 128 blocks of
+    q_nope and K) instead of one per tensor."""
+    return make_prefill_fp8_case(name="prefill_mla_fp8_blockwise", seed=seed, seq_lens=seq_lens, Hq=16, Hk=16,
+                                 D_rope=64, blockwise=True)
+
+
 # ---------------------------------------------------------------------------
 # Chunked prefill against a paged KV cache
 # ---------------------------------------------------------------------------
@@ -596,4 +603,5 @@ CONFIGS = {
     "prefill_chunk_bf16": prefill_chunk_bf16,
     "prefill_chunk_mla_bf16": prefill_chunk_mla_bf16,
     "prefill_mla_fp8": prefill_mla_fp8,
+    "prefill_mla_fp8_blockwise": prefill_mla_fp8_blockwise,
 }
