@@ -196,3 +196,23 @@ def test_decode_runs_on_a_side_stream(gu):
     out, lse = dd.results()
     ref_out, ref_lse = _oracle(case)
     assert gu.max_abs_err(out, ref_out) <= TOL["bf16"]
+
+
+def test_decode_very_long_sequence(gu):
+    """One 131072-token sequence (2048 pages: block-table reads far past the
+    first words, long prefix sums, many pieces per head) next to a 3-token one."""
+    case = gen.make_decode_case(name="very_long", seed=95, B=2, Hq=8, Hk=1, D=128, q_dtype="bf16",
+                                kv_dtype="bf16", seq_lens=[131072, 3])
+    _check(gu, case)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "e4m3fn"])
+def test_decode_many_short_sequences(gu, kv):
+    """1000 sequences of 0..200 tokens: far more sequences than a wave has lanes,
+    many of them inside one page, some empty."""
+    rng = np.random.default_rng(96)
+    lens = rng.integers(0, 201, size=1000)
+    lens[::97] = 0
+    case = gen.make_decode_case(name=f"many_{kv}", seed=96, B=1000, Hq=16, Hk=4, D=128, q_dtype="bf16",
+                                kv_dtype=kv, seq_lens=lens.tolist())
+    _check(gu, case)

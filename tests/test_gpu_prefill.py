@@ -163,3 +163,17 @@ def test_prefill_empty_sequences_in_the_batch(gu):
 def test_prefill_single_long_sequence_sampled(gu):
     case = gen.make_prefill_case(name="long1", seed=263, seq_lens=[5000], Hq=2, Hk=1, D_qk=192, D_rope=64, D_v=128)
     _check(gu, case, rows=_rows_sample(case, n_mid=96))
+
+
+def test_prefill_32k_sequence_sampled(gu):
+    """A 32768-token MLA sequence: 256 query tiles, 512 key tiles (eight 64-tile
+    schedule words), sampled rows checked one by one against the oracle."""
+    case = gen.make_prefill_case(name="long32k", seed=264, seq_lens=[32768, 77], Hq=2, Hk=1, D_qk=192, D_rope=64,
+                                 D_v=128)
+    _check(gu, case, rows=_rows_sample(case, n_mid=48))
+
+
+def test_prefill_32k_block_sparse_sampled(gu):
+    case = gen.make_prefill_case(name="long32k_mask", seed=265, seq_lens=[32768], Hq=2, Hk=2, D_qk=128, D_rope=0,
+                                 D_v=128, mask_density=0.1)
+    _check(gu, case, rows=_rows_sample(case, n_mid=48))
