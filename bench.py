@@ -10,7 +10,8 @@ before the timed region; consecutive steps read different copies of the KV
 pool, so no step is served from the 256 MB last-level cache by its
 predecessor.  The other workloads (fp8 KV decode, MLA prefill, block-sparse
 prefill, fp8 MLA prefill with per-tensor and blockwise scales, chunked
-prefill) are measured the same way and reported under "secondary".
+prefill, and a long-context chunk whose few query tiles are split along the
+keys) are measured the same way and reported under "secondary".
 
 Prints ONE JSON line.
 """
@@ -86,6 +87,7 @@ DOMINANT_KERNEL = {
     "prefill_chunk_mla_bf16": "prefill_fwd<64, true, 0>",
     "prefill_mla_fp8": "prefill_fwd<64, false, 1>",
     "prefill_mla_fp8_blockwise": "prefill_fwd<64, false, 2>",
+    "prefill_chunk_long_mla_bf16": "prefill_fwd<64, true, 0>",
 }
 
 
@@ -387,7 +389,7 @@ def main(argv=None) -> int:
                 secondary.append(rp)
                 del pc
         if hasattr(gu, "DeviceChunk"):
-            for mk in (gen.prefill_chunk_bf16, gen.prefill_chunk_mla_bf16):
+            for mk in (gen.prefill_chunk_bf16, gen.prefill_chunk_mla_bf16, gen.prefill_chunk_long_mla_bf16):
                 cc = mk()
                 rc = bench_chunk(cc, args.steps, args.warmup, torch, gq, gu)
                 rc["roofline"] = {"bound": "mfma", "achieved": rc["tflops_kernel"], "peak": BF16_MFMA_PEAK_TFLOPS,

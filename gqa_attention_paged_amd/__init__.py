@@ -72,7 +72,7 @@ class PrefillDesc(ctypes.Structure):
         ("v_stride_token", ctypes.c_int64), ("v_stride_head", ctypes.c_int64),
         ("kr_stride_token", ctypes.c_int64),
         ("out_stride_token", ctypes.c_int64), ("out_stride_head", ctypes.c_int64),
-        ("num_cus", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("num_cus", ctypes.c_int32), ("num_splits", ctypes.c_int32),
         ("qr_stride_token", ctypes.c_int64), ("qr_stride_head", ctypes.c_int64),
     ]
 
@@ -81,7 +81,7 @@ class PrefillPlan(ctypes.Structure):
     _fields_ = [
         ("desc", PrefillDesc), ("ratio", ctypes.c_int32), ("q_tiles", ctypes.c_int32),
         ("q_tile_rows", ctypes.c_int32), ("kernel", ctypes.c_int32), ("workspace_bytes", ctypes.c_uint64),
-        ("magic", ctypes.c_uint32), ("reserved", ctypes.c_uint32),
+        ("magic", ctypes.c_uint32), ("num_splits", ctypes.c_uint32),
     ]
 
 
@@ -97,6 +97,7 @@ class ChunkDesc(ctypes.Structure):
         ("kv_stride_block", ctypes.c_int64), ("kv_stride_head", ctypes.c_int64),
         ("block_table_stride", ctypes.c_int64),
         ("kr_new_stride_token", ctypes.c_int64), ("kr_stride_block", ctypes.c_int64),
+        ("num_splits", ctypes.c_int32), ("reserved", ctypes.c_int32),
     ]
 
 
@@ -104,7 +105,7 @@ class ChunkPlan(ctypes.Structure):
     _fields_ = [
         ("desc", ChunkDesc), ("ratio", ctypes.c_int32), ("q_tiles", ctypes.c_int32),
         ("q_tile_rows", ctypes.c_int32), ("kernel", ctypes.c_int32), ("workspace_bytes", ctypes.c_uint64),
-        ("magic", ctypes.c_uint32), ("reserved", ctypes.c_uint32),
+        ("magic", ctypes.c_uint32), ("num_splits", ctypes.c_uint32),
     ]
 
 
@@ -334,7 +335,7 @@ def decode_desc(q, k_pool, block_table, max_seq_len: int, out=None, num_workers:
 
 
 def prefill_desc(q, k, v, k_rope, batch: int, max_seq_len: int, block_mask=None, out=None,
-                 num_cus: int = 0, q_rope=None) -> PrefillDesc:
+                 num_cus: int = 0, q_rope=None, num_splits: int = 0) -> PrefillDesc:
     """Descriptor for ragged q [T, Hq, Dqk], k [T, Hk, Dn], v [T, Hk, Dv], k_rope [T, 1, Dr] or None.
     fp8: q is q_nope [T, Hq, Dn] (codes) and q_rope [T, Hq, Dr] the bf16 rope part, or None."""
     T, Hq, Dqk = q.shape
@@ -359,13 +360,14 @@ def prefill_desc(q, k, v, k_rope, batch: int, max_seq_len: int, block_mask=None,
     d.kr_stride_token = 0 if k_rope is None else k_rope.stride(0)
     d.out_stride_token, d.out_stride_head = out.stride(0), out.stride(1)
     d.num_cus = num_cus
+    d.num_splits = num_splits
     if q_rope is not None:
         d.qr_stride_token, d.qr_stride_head = q_rope.stride(0), q_rope.stride(1)
     return d
 
 
 def chunk_desc(q, k_new, k_pool, block_table, batch: int, max_q_len: int, max_kv_len: int,
-               out=None, k_rope_new=None, kr_pool=None) -> ChunkDesc:
+               out=None, k_rope_new=None, kr_pool=None, num_splits: int = 0) -> ChunkDesc:
     """Descriptor for q [T, Hq, D + Dr], k_new / v_new [T, Hk, D], pool [NB, Hk, 64, D],
     block_table [B, Nblk]; MLA: k_rope_new [T, 1, Dr], kr_pool [NB, 1, 64, Dr]."""
     T, Hq, _ = q.shape
@@ -389,4 +391,5 @@ def chunk_desc(q, k_new, k_pool, block_table, batch: int, max_q_len: int, max_kv
         d.head_dim_rope = kr_pool.shape[3]
         d.kr_new_stride_token = k_rope_new.stride(0)
         d.kr_stride_block = kr_pool.stride(0)
+    d.num_splits = num_splits
     return d

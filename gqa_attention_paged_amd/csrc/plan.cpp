@@ -144,6 +144,28 @@ extern "C" gqap_status gqap_decode_validate_host(const gqap_decode_plan_t* plan,
   return GQAP_OK;
 }
 
+// Key-axis splits of a prefill grid of `grid` workgroups (one per query tile
+// and head).  Only a grid that leaves more than a quarter of the compute
+// units without a workgroup is split: there the idle units are the loss.  A
+// grid of one workgroup per unit or more is left alone, because the partial
+// outputs a split writes and merges (fp32, 129 words per row and head) cost
+// about what the second workgroup slot of a unit would gain.  The count
+// fills the two slots of every unit, at most 4, and at most a quarter of the
+// key tiles of the longest sequence (so every split keeps a few tiles to
+// amortise its partial).  A positive request is taken as is.
+static int32_t key_splits(int32_t requested, int64_t grid, int64_t max_keys, int32_t num_cus) {
+  if (requested > 0) return requested;
+  const int64_t cus = num_cus > 0 ? num_cus : 256;
+  if (grid <= 0 || grid * 4 >= cus * 3) return 1;
+  int64_t ns = std::min<int64_t>(4, ceil_div(2 * cus, grid));
+  ns = std::min<int64_t>(ns, std::max<int64_t>(1, ceil_div(max_keys, kBlock) / 4));
+  return (int32_t)std::max<int64_t>(1, ns);
+}
+
+static uint64_t split_workspace(int32_t ns, int64_t T, int64_t Hq) {
+  return ns > 1 ? (uint64_t)ns * (uint64_t)T * (uint64_t)Hq * 129u * 4u : 0u;
+}
+
 extern "C" gqap_status gqap_prefill_plan(const gqap_prefill_desc_t* desc, gqap_prefill_plan_t* plan) {
   if (!desc || !plan) return fail(GQAP_ERR_INVALID_ARGUMENT, "null desc or plan");
   std::memset(plan, 0, sizeof(*plan));
@@ -196,17 +218,23 @@ extern "C" gqap_status gqap_prefill_plan(const gqap_prefill_desc_t* desc, gqap_p
   if (d.has_block_mask && (int64_t)d.mask_blocks < ceil_div(d.max_seq_len, kBlock))
     return fail(GQAP_ERR_INVALID_ARGUMENT, "mask_blocks %d < ceil(max_seq_len/64)", d.mask_blocks);
   if (d.num_cus < 0) return fail(GQAP_ERR_INVALID_ARGUMENT, "num_cus must be >= 0");
+  if (d.num_splits < 0 || d.num_splits > 16)
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "num_splits must be 0 (automatic) or 1..16 (got %d)", d.num_splits);
   plan->desc = d;
   plan->ratio = d.num_q_heads / d.num_kv_heads;
   plan->q_tile_rows = 128;
   plan->q_tiles = (int32_t)ceil_div(d.max_seq_len, plan->q_tile_rows);
-  // One workgroup of 256 work-items per (head, sequence, query tile) slot;
-  // the launch must stay under 2^32 work-items.
-  if ((int64_t)d.num_q_heads * d.batch * plan->q_tiles >= ((int64_t)1 << 24))
-    return fail(GQAP_ERR_UNSUPPORTED, "Hq * batch * ceil(max_seq_len/128) = %lld workgroups exceeds 2^24",
-                (long long)d.num_q_heads * d.batch * plan->q_tiles);
+  const int64_t grid = (int64_t)d.num_q_heads * d.batch * plan->q_tiles;
+  const int32_t ns = key_splits(d.num_splits, grid, d.max_seq_len, d.num_cus);
+  // One workgroup of 256 work-items per (head, sequence, query tile, split)
+  // slot; the launch must stay under 2^32 work-items.
+  if (grid * ns >= ((int64_t)1 << 24))
+    return fail(GQAP_ERR_UNSUPPORTED,
+                "Hq * batch * ceil(max_seq_len/128) * num_splits = %lld workgroups exceeds 2^24",
+                (long long)(grid * ns));
   plan->kernel = (mla ? 2 : 1) + (f8 ? 2 : 0);
-  plan->workspace_bytes = 0;
+  plan->num_splits = (uint32_t)ns;
+  plan->workspace_bytes = split_workspace(ns, d.total_tokens, d.num_q_heads);
   plan->magic = GQAP_PLAN_MAGIC;
   return GQAP_OK;
 }
@@ -268,13 +296,18 @@ extern "C" gqap_status gqap_chunk_plan(const gqap_chunk_desc_t* desc, gqap_chunk
   plan->ratio = d.num_q_heads / d.num_kv_heads;
   plan->q_tile_rows = 128;
   plan->q_tiles = (int32_t)ceil_div(d.max_q_len, plan->q_tile_rows);
+  if (d.num_splits < 0 || d.num_splits > 16)
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "num_splits must be 0 (automatic) or 1..16 (got %d)", d.num_splits);
+  const int64_t grid = (int64_t)d.num_q_heads * d.batch * plan->q_tiles;
+  const int32_t ns = key_splits(d.num_splits, grid, d.max_kv_len, 0);
   // One workgroup of 256 work-items per (head, sequence, query tile) slot;
   // the launch must stay under 2^32 work-items.
-  if ((int64_t)d.num_q_heads * d.batch * plan->q_tiles >= ((int64_t)1 << 24))
-    return fail(GQAP_ERR_UNSUPPORTED, "Hq * batch * ceil(max_q_len/128) = %lld workgroups exceeds 2^24",
-                (long long)d.num_q_heads * d.batch * plan->q_tiles);
+  if (grid * ns >= ((int64_t)1 << 24))
+    return fail(GQAP_ERR_UNSUPPORTED, "Hq * batch * ceil(max_q_len/128) * num_splits = %lld workgroups exceeds 2^24",
+                (long long)(grid * ns));
   plan->kernel = Dr ? 2 : 1;
-  plan->workspace_bytes = 0;
+  plan->num_splits = (uint32_t)ns;
+  plan->workspace_bytes = split_workspace(ns, d.total_q_tokens, d.num_q_heads);
   plan->magic = GQAP_PLAN_MAGIC;
   return GQAP_OK;
 }

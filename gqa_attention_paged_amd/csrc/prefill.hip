@@ -62,6 +62,14 @@ struct PrefillArgs {
   // q_scale [T, Hq] and k_scale [T, Hk], both contiguous.
   const float* qsc;
   const float* ksc;
+  // Split over the key axis: with nsplit > 1 each query tile is processed by
+  // nsplit workgroups, one contiguous range of its key tiles each, and they
+  // write normalised fp32 partials (ws_o [nsplit][T][Hq][128], ws_lse
+  // [nsplit][T][Hq], natural log) that prefill_merge combines.
+  int32_t nsplit;
+  int32_t T;
+  float* ws_o;
+  float* ws_lse;
 };
 
 namespace dev {
@@ -143,7 +151,8 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int x = blockIdx.x % a.Hq;
-  const int pair = blockIdx.x / a.Hq;
+  const int sp = (blockIdx.x / a.Hq) % a.nsplit;   // key-axis split
+  const int pair = blockIdx.x / a.Hq / a.nsplit;
   const int hpx = a.Hq >> 3;
   const int h = (a.Hq & 7) ? x : (x & 7) * hpx + (x >> 3);
   int b, qt;
@@ -235,6 +244,9 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
 
   // Key tiles this workgroup must visit: keys < min(Lk, off + q0 + 128).
   const int nkt = max(0, min(Lk, off + q0 + 128) + 63) >> 6;
+  // This workgroup's share of them: tiles [kt_begin, kt_end).
+  const int kt_begin = (int)((int64_t)nkt * sp / a.nsplit);
+  const int kt_end = (int)((int64_t)nkt * (sp + 1) / a.nsplit);
   const int qb0 = q0 >> 6;                   // the workgroup's two query blocks
   const int qb1 = min(qb0 + 1, (L - 1) >> 6);
   const int wqb = r0 >> 6;                   // this wave's query block
@@ -641,8 +653,8 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
 
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
-  int kt = a.mask ? first_needed(0) : 0;
-  if (kt < nkt) load_tile(kt, B0{});
+  int kt = a.mask ? first_needed(kt_begin) : kt_begin;
+  if (kt < kt_end) load_tile(kt, B0{});
   loads_done();
   __syncthreads();
   using WL0 = std::integral_constant<bool, false>;
@@ -651,7 +663,7 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
   // interleaved with this tile's matrix work when this wave computes and kn
   // lies wholly inside the sequence, else up front.
   auto step = [&](int kt, bool sees, int kn, auto bufc, auto nbufc) {
-    const bool more = kn < nkt;
+    const bool more = kn < kt_end;
     const bool inside = more && kn * 64 + 64 <= Lk;
     if (sees && inside) {
       compute_tile(kt, bufc, WL1{}, kn);
@@ -665,12 +677,12 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
   // Two tiles per trip so the LDS buffer index is static.  wave_sees(kt) is
   // read before next_tile() may move the bit words on to the next 64 tiles.
   // A buffer is refilled only after the barrier that ends the reads of it.
-  while (kt < nkt) {
+  while (kt < kt_end) {
     bool sees = wave_sees(kt);
     int kn = next_tile(kt);
     step(kt, sees, kn, B0{}, B1{});
     kt = kn;
-    if (kt >= nkt) break;
+    if (kt >= kt_end) break;
     sees = wave_sees(kt);
     kn = next_tile(kt);
     step(kt, sees, kn, B1{}, B0{});
@@ -686,6 +698,21 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
   }
   if (qrow >= L) return;
   const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+  if (a.nsplit > 1) {  // partial of this key range; prefill_merge writes the output
+    const int64_t prow = ((int64_t)sp * a.T + c0 + qrow) * a.Hq + h;
+    float* wp = a.ws_o + prow * DV;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int J = 0; J < 4; ++J) {
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = o[dt][4 * J + e] * inv;
+        *(f32x4*)(wp + 32 * dt + 8 * J + 4 * hh) = v;
+      }
+    if (hh == 0) a.ws_lse[prow] = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
+    return;
+  }
   uint16_t* op = a.out + (int64_t)(c0 + qrow) * a.o_st + (int64_t)h * a.o_sh;
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
@@ -700,6 +727,56 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
     }
   if (a.lse && hh == 0)
     a.lse[(int64_t)(c0 + qrow) * a.Hq + h] = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
+}
+
+
+// Merge of the key-axis splits of one (row, head): with w_s = exp(lse_s -
+// max lse), out = sum_s w_s o_s / sum_s w_s and lse = max + log(sum_s w_s);
+// a row that no split saw any key for gets 0 / -inf.  One wave per (row,
+// head), two output columns per lane.  Rows that are not outputs (past
+// cu[B], or past the planned length of their sequence) are skipped, as the
+// attention kernel skips them.
+struct MergeArgs {
+  const float* ws_o;
+  const float* ws_lse;
+  const int32_t* cu;
+  uint16_t* out;
+  float* lse;
+  int64_t o_st, o_sh;
+  int32_t T, Hq, B, nsplit, max_len;
+};
+
+__global__ __launch_bounds__(256) void prefill_merge(MergeArgs a) {
+  const int64_t rh = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (rh >= (int64_t)a.T * a.Hq) return;
+  const int row = (int)(rh / a.Hq);
+  const int h = (int)(rh - (int64_t)row * a.Hq);
+  if (row >= a.cu[a.B]) return;
+  int lo = 0, hi = a.B;  // the sequence b with cu[b] <= row < cu[b + 1]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (a.cu[mid] <= row) lo = mid; else hi = mid;
+  }
+  if (row - a.cu[lo] >= a.max_len) return;
+  const int64_t sstride = (int64_t)a.T * a.Hq;
+  float M = -INFINITY;
+  for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, a.ws_lse[s * sstride + rh]);
+  float den = 0.f, acc0 = 0.f, acc1 = 0.f;
+  if (M > -INFINITY) {
+    for (int s = 0; s < a.nsplit; ++s) {
+      const float ls = a.ws_lse[s * sstride + rh];
+      if (ls == -INFINITY) continue;
+      const float wgt = expf(ls - M);
+      const f32x2 v = *(const f32x2*)(a.ws_o + (s * sstride + rh) * 128 + 2 * lane);
+      den += wgt;
+      acc0 += wgt * v[0];
+      acc1 += wgt * v[1];
+    }
+  }
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+  *(uint32_t*)(a.out + (int64_t)row * a.o_st + (int64_t)h * a.o_sh + 2 * lane) = pack_bf16x2_hw(acc0 * inv, acc1 * inv);
+  if (a.lse && lane == 0) a.lse[rh] = den > 0.f ? M + logf(den) : -INFINITY;
 }
 
 // Append a chunk's keys and values to the paged cache (FlashMLA tensor-shape
@@ -750,6 +827,45 @@ __global__ __launch_bounds__(256) void append_kv(AppendArgs a) {
 
 static bool misaligned16(const void* p) { return ((uintptr_t)p) & 15; }
 
+// Key-axis splits: the workspace holds the partial outputs [nsplit][T][Hq][128]
+// fp32, then the partial LSEs [nsplit][T][Hq].
+static gqap_status split_setup(int32_t nsplit, int32_t T, int32_t Hq, uint64_t need, void* workspace,
+                               uint64_t workspace_bytes, PrefillArgs* a) {
+  a->nsplit = nsplit > 1 ? nsplit : 1;
+  a->T = T;
+  if (a->nsplit == 1) return GQAP_OK;
+  if (!workspace || workspace_bytes < need)
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "this plan splits the key axis %d ways and needs a workspace of %llu bytes",
+                nsplit, (unsigned long long)need);
+  if (misaligned16(workspace)) return fail(GQAP_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+  a->ws_o = (float*)workspace;
+  a->ws_lse = (float*)((unsigned char*)workspace + (uint64_t)nsplit * (uint64_t)T * (uint64_t)Hq * 128u * 4u);
+  return GQAP_OK;
+}
+
+static gqap_status launch_merge(const PrefillArgs& a, int32_t max_len, hipStream_t st) {
+  if (a.nsplit <= 1) return GQAP_OK;
+  MergeArgs m{};
+  m.ws_o = a.ws_o;
+  m.ws_lse = a.ws_lse;
+  m.cu = a.cu;
+  m.out = a.out;
+  m.lse = a.lse;
+  m.o_st = a.o_st;
+  m.o_sh = a.o_sh;
+  m.T = a.T;
+  m.Hq = a.Hq;
+  m.B = a.B;
+  m.nsplit = a.nsplit;
+  m.max_len = max_len;
+  const int64_t blocks = ((int64_t)a.T * a.Hq + 3) / 4;
+  if (blocks == 0) return GQAP_OK;
+  hipLaunchKernelGGL(prefill_merge, dim3((unsigned)blocks), dim3(256), 0, st, m);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(GQAP_ERR_HIP, "split merge launch: %s", hipGetErrorString(e));
+  return GQAP_OK;
+}
+
 }  // namespace gqap
 
 using namespace gqap;
@@ -786,8 +902,6 @@ extern "C" gqap_status gqap_prefill(const gqap_prefill_plan_t* plan, const void*
                                     const void* k_rope, const int32_t* cu_seqlens, const uint8_t* block_mask,
                                     float scale, void* out, float* lse, void* workspace, uint64_t workspace_bytes,
                                     void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   if (!plan || plan->magic != GQAP_PLAN_MAGIC) return fail(GQAP_ERR_INVALID_ARGUMENT, "invalid prefill plan");
   const gqap_prefill_desc_t& d = plan->desc;
   if (d.dtype != GQAP_BF16) return fail(GQAP_ERR_DTYPE, "gqap_prefill takes a bf16 plan (fp8: gqap_prefill_fp8)");
@@ -801,12 +915,16 @@ extern "C" gqap_status gqap_prefill(const gqap_prefill_plan_t* plan, const void*
     return fail(GQAP_ERR_INVALID_ARGUMENT, "device pointers must be 16-byte aligned (cu_seqlens, lse 4-byte)");
   if (!std::isfinite(scale)) return fail(GQAP_ERR_INVALID_ARGUMENT, "scale must be finite");
   PrefillArgs a = ragged_args(plan, cu_seqlens, block_mask, out, lse);
+  const gqap_status ss =
+      split_setup((int32_t)plan->num_splits, d.total_tokens, d.num_q_heads, plan->workspace_bytes, workspace,
+                  workspace_bytes, &a);
+  if (ss != GQAP_OK) return ss;
   a.q = (const uint16_t*)q;
   a.k = (const uint16_t*)k;
   a.v = (const uint16_t*)v;
   a.kr = (const uint16_t*)k_rope;
   a.scale_log2 = scale * dev::kLog2e;
-  const dim3 grid((unsigned)d.num_q_heads * (unsigned)d.batch * (unsigned)plan->q_tiles);
+  const dim3 grid((unsigned)d.num_q_heads * (unsigned)d.batch * (unsigned)plan->q_tiles * (unsigned)a.nsplit);
   hipStream_t st = (hipStream_t)stream;
   if (d.head_dim_rope == 64)
     hipLaunchKernelGGL((prefill_fwd<64, false, 0>), grid, dim3(256), 0, st, a);
@@ -814,7 +932,7 @@ extern "C" gqap_status gqap_prefill(const gqap_prefill_plan_t* plan, const void*
     hipLaunchKernelGGL((prefill_fwd<0, false, 0>), grid, dim3(256), 0, st, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(GQAP_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
-  return GQAP_OK;
+  return launch_merge(a, d.max_seq_len, st);
 }
 
 // Checks and argument set-up shared by the two fp8 entry points.
@@ -850,9 +968,13 @@ static gqap_status fp8_args(const gqap_prefill_plan_t* plan, const void* q_nope,
 }
 
 template <int F8>
-static gqap_status launch_fp8(const gqap_prefill_plan_t* plan, const PrefillArgs& a, void* stream) {
+static gqap_status launch_fp8(const gqap_prefill_plan_t* plan, PrefillArgs& a, void* workspace,
+                              uint64_t workspace_bytes, void* stream) {
   const gqap_prefill_desc_t& d = plan->desc;
-  const dim3 grid((unsigned)d.num_q_heads * (unsigned)d.batch * (unsigned)plan->q_tiles);
+  const gqap_status ss = split_setup((int32_t)plan->num_splits, d.total_tokens, d.num_q_heads, plan->workspace_bytes,
+                                     workspace, workspace_bytes, &a);
+  if (ss != GQAP_OK) return ss;
+  const dim3 grid((unsigned)d.num_q_heads * (unsigned)d.batch * (unsigned)plan->q_tiles * (unsigned)a.nsplit);
   hipStream_t st = (hipStream_t)stream;
   if (d.head_dim_rope == 64)
     hipLaunchKernelGGL((prefill_fwd<64, false, F8>), grid, dim3(256), 0, st, a);
@@ -860,7 +982,7 @@ static gqap_status launch_fp8(const gqap_prefill_plan_t* plan, const PrefillArgs
     hipLaunchKernelGGL((prefill_fwd<0, false, F8>), grid, dim3(256), 0, st, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(GQAP_ERR_HIP, "fp8 prefill launch: %s", hipGetErrorString(e));
-  return GQAP_OK;
+  return launch_merge(a, d.max_seq_len, st);
 }
 
 extern "C" gqap_status gqap_prefill_fp8(const gqap_prefill_plan_t* plan, const void* q_nope, const void* q_rope,
@@ -868,8 +990,6 @@ extern "C" gqap_status gqap_prefill_fp8(const gqap_prefill_plan_t* plan, const v
                                         const int32_t* cu_seqlens, const uint8_t* block_mask, float scale,
                                         float q_scale, float k_scale, void* out, float* lse, void* workspace,
                                         uint64_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   if (!std::isfinite(q_scale) || !std::isfinite(k_scale))
     return fail(GQAP_ERR_INVALID_ARGUMENT, "scale, q_scale and k_scale must be finite");
   PrefillArgs a{};
@@ -879,7 +999,7 @@ extern "C" gqap_status gqap_prefill_fp8(const gqap_prefill_plan_t* plan, const v
   // the whole score is the nope sum and the scales join the softmax constant.
   a.qk = q_scale * k_scale;
   if (!plan->desc.head_dim_rope) a.scale_log2 *= a.qk;
-  return launch_fp8<1>(plan, a, stream);
+  return launch_fp8<1>(plan, a, workspace, workspace_bytes, stream);
 }
 
 extern "C" gqap_status gqap_prefill_fp8_blockwise(const gqap_prefill_plan_t* plan, const void* q_nope,
@@ -888,8 +1008,6 @@ extern "C" gqap_status gqap_prefill_fp8_blockwise(const gqap_prefill_plan_t* pla
                                                   const uint8_t* block_mask, float scale, const float* q_scales,
                                                   const float* k_scales, void* out, float* lse, void* workspace,
                                                   uint64_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   PrefillArgs a{};
   const gqap_status s = fp8_args(plan, q_nope, q_rope, k, v, k_rope, cu_seqlens, block_mask, scale, out, lse, &a);
   if (s != GQAP_OK || plan->desc.batch == 0 || plan->q_tiles == 0) return s;
@@ -898,7 +1016,7 @@ extern "C" gqap_status gqap_prefill_fp8_blockwise(const gqap_prefill_plan_t* pla
     return fail(GQAP_ERR_INVALID_ARGUMENT, "q_scales and k_scales must be 4-byte aligned");
   a.qsc = q_scales;
   a.ksc = k_scales;
-  return launch_fp8<2>(plan, a, stream);
+  return launch_fp8<2>(plan, a, workspace, workspace_bytes, stream);
 }
 
 extern "C" gqap_status gqap_append_kv(const gqap_chunk_plan_t* plan, const void* k_new, const void* v_new,
@@ -952,8 +1070,6 @@ extern "C" gqap_status gqap_chunk_prefill(const gqap_chunk_plan_t* plan, const v
                                           const int32_t* cu_seqlens_q, const int32_t* kv_lens, float scale,
                                           void* out, float* lse, void* workspace, uint64_t workspace_bytes,
                                           void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   if (!plan || plan->magic != GQAP_PLAN_MAGIC) return fail(GQAP_ERR_INVALID_ARGUMENT, "invalid chunk plan");
   const gqap_chunk_desc_t& d = plan->desc;
   if (d.batch == 0 || plan->q_tiles == 0) return GQAP_OK;
@@ -1000,12 +1116,15 @@ extern "C" gqap_status gqap_chunk_prefill(const gqap_chunk_plan_t* plan, const v
   a.kv_sb = d.kv_stride_block;
   a.kv_sh = d.kv_stride_head;
   a.max_kv = d.max_kv_len;
-  const dim3 grid((unsigned)d.num_q_heads * (unsigned)d.batch * (unsigned)plan->q_tiles);
+  const gqap_status ss = split_setup((int32_t)plan->num_splits, d.total_q_tokens, d.num_q_heads,
+                                     plan->workspace_bytes, workspace, workspace_bytes, &a);
+  if (ss != GQAP_OK) return ss;
+  const dim3 grid((unsigned)d.num_q_heads * (unsigned)d.batch * (unsigned)plan->q_tiles * (unsigned)a.nsplit);
   if (d.head_dim_rope == 64)
     hipLaunchKernelGGL((prefill_fwd<64, true, 0>), grid, dim3(256), 0, (hipStream_t)stream, a);
   else
     hipLaunchKernelGGL((prefill_fwd<0, true, 0>), grid, dim3(256), 0, (hipStream_t)stream, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(GQAP_ERR_HIP, "chunk prefill launch: %s", hipGetErrorString(e));
-  return GQAP_OK;
+  return launch_merge(a, d.max_q_len, (hipStream_t)stream);
 }

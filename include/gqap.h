@@ -236,7 +236,7 @@ typedef struct gqap_prefill_desc_t {
   int64_t kr_stride_token;
   int64_t out_stride_token, out_stride_head;
   int32_t num_cus;             /* 0 = 256 */
-  int32_t reserved;
+  int32_t num_splits;          /* key-axis splits: 0 = chosen by the plan, 1..16 forced */
   int64_t qr_stride_token;     /* fp8 only: q_rope strides (bf16 elements) */
   int64_t qr_stride_head;
 } gqap_prefill_desc_t;
@@ -247,12 +247,26 @@ typedef struct gqap_prefill_plan_t {
   int32_t q_tiles;             /* ceil(max_seq_len / q_tile_rows) */
   int32_t q_tile_rows;
   int32_t kernel;
-  uint64_t workspace_bytes;    /* 0 in this version */
+  uint64_t workspace_bytes;    /* 0 unless num_splits > 1 */
   uint32_t magic;
-  uint32_t reserved;
+  uint32_t num_splits;         /* key-axis splits the calls will use */
 } gqap_prefill_plan_t;
 
 /*
+ * Key-axis splits (prefill and chunked prefill).  When the grid (one
+ * workgroup per 128-row query tile and head) would leave more than a quarter
+ * of the compute units idle, the plan gives each query tile num_splits
+ * workgroups, each taking one contiguous range of the tile's key tiles, so
+ * the GPU is filled.  They write normalised fp32 partial outputs and their
+ * LSEs into the caller's workspace, and a merge pass combines them with
+ * weights exp(lse_s - max):  out = sum_s w_s o_s / sum_s w_s.  This is the
+ * split-KV scheme of split decoding applied to query tiles (MATE msa:
+ * num_splits).  Auto choice, for grid < 3/4 * num_cus: ceil(2 * num_cus /
+ * grid), at most 4, and at most a quarter of the key tiles of the longest
+ * sequence; otherwise 1.  num_splits > 0 in the descriptor forces a count.  workspace_bytes = num_splits * T * Hq * 129 * 4
+ * when num_splits > 1; the workspace must then be 16-byte aligned and at
+ * least that large.  Results equal the unsplit ones up to fp32 rounding.
+ *
  * dtype GQAP_FP8_E4M3FN plans the fp8 prefill (gqap_prefill_fp8): q holds
  * only the nope part [T, Hq, Dn] and k [T, Hk, Dn], both e4m3fn codes with
  * strides in bytes (multiples of 16); the rope part of the query is a
@@ -263,7 +277,8 @@ typedef struct gqap_prefill_plan_t {
  * Validate a prefill request.  Pure host code.  Errors: INVALID_ARGUMENT
  * (sizes, strides, Hq % Hk, mask_blocks too small), DTYPE (not bf16 or fp8),
  * UNSUPPORTED (causal == 0, head widths other than 128/192 with rope 0/64,
- * Dv != 128, or Hq * batch * ceil(max_seq_len/128) >= 2^24 workgroups).
+ * Dv != 128, or Hq * batch * ceil(max_seq_len/128) * num_splits >= 2^24
+ * workgroups); INVALID_ARGUMENT also for num_splits outside 0..16.
  */
 gqap_status gqap_prefill_plan(const gqap_prefill_desc_t* desc, gqap_prefill_plan_t* plan);
 
@@ -378,6 +393,8 @@ typedef struct gqap_chunk_desc_t {
   int64_t block_table_stride;  /* int32 elements between rows, >= Nblk */
   int64_t kr_new_stride_token; /* MLA: elements between rope rows of k_rope_new, >= Dr */
   int64_t kr_stride_block;     /* MLA: elements between rope-cache blocks, >= 64*Dr */
+  int32_t num_splits;          /* key-axis splits: 0 = chosen by the plan, 1..16 forced */
+  int32_t reserved;
 } gqap_chunk_desc_t;
 
 typedef struct gqap_chunk_plan_t {
@@ -386,9 +403,9 @@ typedef struct gqap_chunk_plan_t {
   int32_t q_tiles;             /* ceil(max_q_len / q_tile_rows) */
   int32_t q_tile_rows;
   int32_t kernel;
-  uint64_t workspace_bytes;    /* 0 in this version */
+  uint64_t workspace_bytes;    /* 0 unless num_splits > 1 */
   uint32_t magic;
-  uint32_t reserved;
+  uint32_t num_splits;         /* key-axis splits the calls will use */
 } gqap_chunk_plan_t;
 
 /*
@@ -396,7 +413,8 @@ typedef struct gqap_chunk_plan_t {
  * INVALID_ARGUMENT (sizes, strides that overlap or break 16-byte alignment,
  * Hq % Hk, max_kv_len > Nblk * 64, max_q_len > max_kv_len), DTYPE (not bf16),
  * UNSUPPORTED (block_size != 64, D != 128, Dr not 0 or 64, Hq * batch *
- * ceil(max_q_len / 128) >= 2^24 workgroups).
+ * ceil(max_q_len / 128) * num_splits >= 2^24 workgroups); INVALID_ARGUMENT
+ * also for num_splits outside 0..16.  Key-axis splits as for the prefill.
  */
 gqap_status gqap_chunk_plan(const gqap_chunk_desc_t* desc, gqap_chunk_plan_t* plan);
 

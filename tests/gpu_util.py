@@ -82,9 +82,10 @@ def lse_err(gpu: np.ndarray, ref: np.ndarray) -> float:
 
 
 class DevicePrefill:
-    """A ragged prefill case resident on the device plus a plan for it."""
+    """A ragged prefill case resident on the device plus a plan for it (and
+    the workspace the plan asks for)."""
 
-    def __init__(self, case, device: str = "cuda"):
+    def __init__(self, case, device: str = "cuda", num_splits: int = 0):
         self.case = case
         self.fp8 = case.dtype == "e4m3fn"   # q holds the nope codes, q_rope the bf16 rope part
         self.q = bits_to_tensor(case.q, case.dtype).to(device)
@@ -105,20 +106,23 @@ class DevicePrefill:
         self.lse = torch.empty((T, case.Hq), dtype=torch.float32, device=device)
         max_len = max(1, int(case.seq_lens.max())) if case.B else 1
         self.desc = gq.prefill_desc(self.q, self.k, self.v, self.kr, batch=case.B, max_seq_len=max_len,
-                                    block_mask=self.mask, out=self.out, q_rope=self.qr)
+                                    block_mask=self.mask, out=self.out, q_rope=self.qr, num_splits=num_splits)
         self.plan = gq.gqap_prefill_plan(self.desc)
+        self.ws = torch.empty(max(256, self.plan.workspace_bytes), dtype=torch.uint8, device=device)
 
     def run(self, stream=None):
+        ws, wsb = self.ws, self.plan.workspace_bytes
         if self.blockwise:
             gq.gqap_prefill_fp8_blockwise(self.plan, self.q, self.qr, self.k, self.v, self.kr, self.cu, self.mask,
-                                          self.case.scale, self.qsc, self.ksc, self.out, self.lse, stream=stream)
+                                          self.case.scale, self.qsc, self.ksc, self.out, self.lse, ws, wsb,
+                                          stream=stream)
         elif self.fp8:
             gq.gqap_prefill_fp8(self.plan, self.q, self.qr, self.k, self.v, self.kr, self.cu, self.mask,
-                                self.case.scale, self.case.q_scale, self.case.k_scale, self.out, self.lse,
+                                self.case.scale, self.case.q_scale, self.case.k_scale, self.out, self.lse, ws, wsb,
                                 stream=stream)
         else:
             gq.gqap_prefill(self.plan, self.q, self.k, self.v, self.kr, self.cu, self.mask, self.case.scale,
-                            self.out, self.lse, stream=stream)
+                            self.out, self.lse, ws, wsb, stream=stream)
         return self.out, self.lse
 
     def results(self):
@@ -130,7 +134,7 @@ class DeviceChunk:
     """A chunked-prefill case on the device (cache with the prefixes filled)
     plus a plan for it."""
 
-    def __init__(self, case, device: str = "cuda"):
+    def __init__(self, case, device: str = "cuda", num_splits: int = 0):
         self.case = case
         self.q = bits_to_tensor(case.q, "bf16").to(device)
         self.k_new = bits_to_tensor(case.k_new, "bf16").to(device)
@@ -148,8 +152,10 @@ class DeviceChunk:
         max_q = max(1, int(case.q_lens.max())) if case.B else 1
         max_kv = max(max_q, int(case.kv_lens.max())) if case.B else 1
         self.desc = gq.chunk_desc(self.q, self.k_new, self.k_pool, self.bt, batch=case.B, max_q_len=max_q,
-                                  max_kv_len=max_kv, out=self.out, k_rope_new=self.kr_new, kr_pool=self.kr_pool)
+                                  max_kv_len=max_kv, out=self.out, k_rope_new=self.kr_new, kr_pool=self.kr_pool,
+                                  num_splits=num_splits)
         self.plan = gq.gqap_chunk_plan(self.desc)
+        self.ws = torch.empty(max(256, self.plan.workspace_bytes), dtype=torch.uint8, device=device)
         gq.gqap_chunk_validate_host(self.plan, case.block_table, case.cu_seqlens_q, case.kv_lens)
 
     def append(self, stream=None):
@@ -158,7 +164,8 @@ class DeviceChunk:
 
     def run(self, stream=None):
         gq.gqap_chunk_prefill(self.plan, self.q, self.k_pool, self.v_pool, self.kr_pool, self.bt, self.cu,
-                              self.kvl, self.case.scale, self.out, self.lse, stream=stream)
+                              self.kvl, self.case.scale, self.out, self.lse, self.ws, self.plan.workspace_bytes,
+                              stream=stream)
         return self.out, self.lse
 
     def results(self):

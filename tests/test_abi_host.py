@@ -424,3 +424,66 @@ def test_csr_conversion_rejects_bad_arguments_without_a_gpu(gq):
     assert gq.STATUS_NAMES[lib.gqap_block_table_from_csr(None, 16, 2, 4, 4, 16, None)] == "INVALID_ARGUMENT"
     assert gq.STATUS_NAMES[lib.gqap_block_table_from_csr(18, 16, 2, 4, 4, 16, None)] == "INVALID_ARGUMENT"
     assert lib.gqap_block_table_from_csr(None, None, 0, 4, 4, None, None) == 0   # empty batch: nothing to do
+
+
+# ---------------------------------------------------------------- key-axis splits
+
+def test_prefill_plans_split_small_grids_only(gq):
+    # 4 x 16 x 24 = 1536 workgroups fill the GPU: no split, no workspace
+    p = gq.gqap_prefill_plan(baseline_prefill_desc(gq))
+    assert p.num_splits == 1 and p.workspace_bytes == 0
+    # one 2048-token sequence, 16 heads: 256 workgroups, one per compute unit -> no split
+    d = baseline_prefill_desc(gq)
+    d.batch, d.total_tokens, d.max_seq_len = 1, 2048, 2048
+    assert gq.gqap_prefill_plan(d).num_splits == 1
+    # 8 heads: 128 workgroups leave half the units idle -> 4 splits
+    d.num_q_heads = d.num_kv_heads = 8
+    d.q_stride_token, d.k_stride_token = 192 * 8, 128 * 8
+    d.v_stride_token, d.out_stride_token = 128 * 8, 128 * 8
+    p = gq.gqap_prefill_plan(d)
+    assert p.num_splits == 4 and p.workspace_bytes == 4 * 2048 * 8 * 129 * 4
+    # a tiny grid is capped at 4 splits, and by a quarter of the key tiles
+    d.num_q_heads = d.num_kv_heads = 2
+    d.q_stride_token, d.k_stride_token = 192 * 2, 128 * 2
+    d.v_stride_token, d.out_stride_token = 128 * 2, 128 * 2
+    assert gq.gqap_prefill_plan(d).num_splits == 4
+    d.total_tokens = d.max_seq_len = 300          # 5 key tiles -> at most 1 split
+    assert gq.gqap_prefill_plan(d).num_splits == 1
+
+
+def test_prefill_plan_forced_splits(gq):
+    d = baseline_prefill_desc(gq)
+    d.num_splits = 3
+    p = gq.gqap_prefill_plan(d)
+    assert p.num_splits == 3 and p.workspace_bytes == 3 * 6584 * 16 * 129 * 4
+    for bad in (-1, 17):
+        d.num_splits = bad
+        st = gq.lib().gqap_prefill_plan(ctypes.byref(d), ctypes.byref(gq.PrefillPlan()))
+        assert gq.STATUS_NAMES[st] == "INVALID_ARGUMENT"
+
+
+def test_chunk_plan_splits(gq):
+    d = baseline_chunk_desc(gq)                    # 8 x 32 x 4 = 1024 workgroups
+    assert gq.gqap_chunk_plan(d).num_splits == 1
+    d.batch, d.num_q_heads, d.num_kv_heads = 4, 16, 16   # 4 x 16 x 4 = 256: one per unit -> 1
+    d.q_stride_token, d.out_stride_token = 128 * 16, 128 * 16
+    d.new_stride_token, d.kv_stride_block = 128 * 16, 16 * 64 * 128
+    assert gq.gqap_chunk_plan(d).num_splits == 1
+    d.batch = 1                                          # 1 x 16 x 4 = 64 -> 4 splits
+    p = gq.gqap_chunk_plan(d)
+    assert p.num_splits == 4 and p.workspace_bytes == 4 * 4096 * 16 * 129 * 4
+    d.num_splits = 5
+    assert gq.gqap_chunk_plan(d).num_splits == 5
+
+
+def test_split_calls_require_the_workspace(gq):
+    """A split plan refuses a missing, short or misaligned workspace before any
+    device work (the other pointers are never looked at)."""
+    d = baseline_prefill_desc(gq)
+    d.num_splits = 2
+    p = gq.gqap_prefill_plan(d)
+    fake = 1 << 20
+    call = gq.lib().gqap_prefill
+    for ws, wsb in ((None, 0), (fake, p.workspace_bytes - 16), (fake + 8, p.workspace_bytes)):
+        st = call(ctypes.byref(p), fake, fake, fake, fake, fake, None, 1.0, fake, None, ws, wsb, None)
+        assert gq.STATUS_NAMES[st] == "INVALID_ARGUMENT" and "workspace" in gq.gqap_last_error()

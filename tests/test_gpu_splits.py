@@ -1,0 +1,117 @@
+"""Key-axis splits of the prefill kernels on the GPU: with num_splits forced
+(and, for small grids, chosen by the plan) every prefill form matches the
+fp64 oracle, and the split result equals the unsplit one up to rounding.
+Cases include more splits than a short sequence has key tiles, so that some
+splits see no key at all and write an empty partial."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as O
+from workloads import gen
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 2e-2, "e4m3fn": 6e-2}
+
+
+@pytest.fixture(scope="module")
+def gu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    from tests import gpu_util  # imports the HIP library; fails loudly if it is missing
+    return gpu_util
+
+
+def _prefill_ref(case):
+    if case.dtype == "e4m3fn":
+        return O.ragged_prefill_fp8(case.q, case.q_rope, case.k, case.v, case.k_rope, case.cu_seqlens, case.scale,
+                                    case.q_scale, case.k_scale, block_mask=case.block_mask)
+    return O.ragged_prefill(case.q, case.k, case.v, case.cu_seqlens, case.scale, k_rope=case.k_rope,
+                            block_mask=case.block_mask, dtype="bf16")
+
+
+def _run_prefill(gu, case, ns):
+    dp = gu.DevicePrefill(case, num_splits=ns)
+    assert dp.plan.num_splits == ns
+    dp.run()
+    return dp.results()
+
+
+def _check_prefill(gu, case, splits):
+    ref, ref_lse = _prefill_ref(case)
+    tol = TOL[case.dtype]
+    base = None
+    for ns in splits:
+        gu.announce(f"split prefill {case.name} lens={list(case.seq_lens)[:6]} splits={ns}")
+        out, lse = _run_prefill(gu, case, ns)
+        e_out, e_lse = gu.max_abs_err(out, ref), gu.lse_err(lse, ref_lse)
+        gu.announce(f"  max-abs-err out {e_out:.3e} lse {e_lse:.3e} (tol {tol:g})")
+        assert e_out <= tol and e_lse <= tol, (ns, e_out, e_lse)
+        if base is None:
+            base = (out, lse)
+        else:  # against the first (unsplit) run
+            assert gu.max_abs_err(out, base[0]) <= 1e-2 and gu.lse_err(lse, base[1]) <= 1e-4
+
+
+def test_split_ragged_mla(gu):
+    case = gen.make_prefill_case(name="split_mla", seed=300, seq_lens=[1, 70, 700, 1500, 0, 129], Hq=8, Hk=8,
+                                 D_qk=192, D_rope=64, D_v=128)
+    _check_prefill(gu, case, (1, 2, 3, 4))
+
+
+def test_split_ragged_gqa_with_block_mask(gu):
+    case = gen.make_prefill_case(name="split_mask", seed=301, seq_lens=[1100, 333, 64], Hq=8, Hk=2, D_qk=128,
+                                 D_rope=0, D_v=128, mask_density=0.3)
+    _check_prefill(gu, case, (1, 3))
+
+
+@pytest.mark.parametrize("blockwise", [False, True])
+def test_split_fp8(gu, blockwise):
+    case = gen.make_prefill_fp8_case(name="split_fp8", seed=302, seq_lens=[900, 65, 300], Hq=8, Hk=2, D_rope=64,
+                                     blockwise=blockwise)
+    _check_prefill(gu, case, (1, 2))
+
+
+@pytest.mark.parametrize("Dr", [0, 64])
+def test_split_chunk(gu, Dr):
+    case = gen.make_chunk_case(name="split_chunk", seed=303 + Dr, prefix_lens=[3000, 10, 700], q_lens=[200, 64, 5],
+                               Hq=8, Hk=2 if Dr == 0 else 8, D_rope=Dr)
+    kp_ref = None
+    base = None
+    for ns in (1, 2, 4):
+        gu.announce(f"split chunk Dr={Dr} splits={ns}")
+        dc = gu.DeviceChunk(case, num_splits=ns)
+        assert dc.plan.num_splits == ns
+        dc.append()
+        dc.run()
+        out, lse = dc.results()
+        if kp_ref is None:
+            pools = dc.pools_bits()
+            kp_ref = pools
+            ref, ref_lse = O.chunk_prefill(case.q, pools[0], pools[1], case.block_table, case.cu_seqlens_q,
+                                           case.kv_lens, case.scale, dtype="bf16",
+                                           kr_pool=pools[2] if len(pools) == 3 else None)
+            base = (out, lse)
+        e_out, e_lse = gu.max_abs_err(out, ref), gu.lse_err(lse, ref_lse)
+        gu.announce(f"  max-abs-err out {e_out:.3e} lse {e_lse:.3e}")
+        assert e_out <= 2e-2 and e_lse <= 2e-2
+        assert gu.max_abs_err(out, base[0]) <= 1e-2 and gu.lse_err(lse, base[1]) <= 1e-4
+
+
+def test_split_chosen_by_the_plan_for_a_long_context_chunk(gu):
+    """The long-context MLA chunk workload (one sequence, 64 workgroups) gets
+    four splits from the plan; sampled rows match the oracle."""
+    case = gen.prefill_chunk_long_mla_bf16()
+    dc = gu.DeviceChunk(case)
+    assert dc.plan.num_splits == 4
+    dc.append()
+    dc.run()
+    out, lse = dc.results()
+    pools = dc.pools_bits()
+    rows = np.unique(np.linspace(0, case.T - 1, 97).astype(np.int64))
+    ref, ref_lse = O.chunk_prefill(case.q, pools[0], pools[1], case.block_table, case.cu_seqlens_q, case.kv_lens,
+                                   case.scale, dtype="bf16", rows=rows, kr_pool=pools[2])
+    e_out, e_lse = gu.max_abs_err(out[rows], ref), gu.lse_err(lse[rows], ref_lse)
+    gu.announce(f"long-context mla chunk, auto split: max-abs-err out {e_out:.3e} lse {e_lse:.3e}")
+    assert e_out <= 2e-2 and e_lse <= 2e-2

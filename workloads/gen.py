@@ -594,6 +594,14 @@ def prefill_chunk_mla_bf16(seed: int = 1008, B: int = 4, prefix_range=(1024, 409
                            q_lens=[q_len] * B, Hq=16, Hk=16, D=128, D_rope=64)
 
 
+def prefill_chunk_long_mla_bf16(seed: int = 1011, prefix: int = 15872, q_len: int = 512) -> ChunkCase:
+    """Long-context MLA chunked prefill: one sequence with a 15872-token cached
+    prefix appending a 512-token chunk (16384 keys); 16 heads, Q 192 = 128 + 64
+    rope, the rope keys in the paged rope cache, V / output 128, bf16."""
+    return make_chunk_case(name="prefill_chunk_long_mla_bf16", seed=seed, prefix_lens=[prefix], q_lens=[q_len],
+                           Hq=16, Hk=16, D=128, D_rope=64)
+
+
 CONFIGS = {
     "decode_tiny_f32": decode_tiny_fp32,
     "decode_gqa_bf16": decode_gqa_bf16,
@@ -604,4 +612,5 @@ CONFIGS = {
     "prefill_chunk_mla_bf16": prefill_chunk_mla_bf16,
     "prefill_mla_fp8": prefill_mla_fp8,
     "prefill_mla_fp8_blockwise": prefill_mla_fp8_blockwise,
+    "prefill_chunk_long_mla_bf16": prefill_chunk_long_mla_bf16,
 }
