@@ -760,18 +760,39 @@ __global__ __launch_bounds__(256) void prefill_merge(MergeArgs a) {
   }
   if (row - a.cu[lo] >= a.max_len) return;
   const int64_t sstride = (int64_t)a.T * a.Hq;
+  // Up to four splits (all the plan chooses by itself): every LSE and row is
+  // requested before the first is used, so the merge costs one memory round
+  // trip.  Forced counts above four take the remaining splits in a loop.
+  constexpr int NU = 4;
+  float ls[NU];
+  f32x2 v[NU];
+#pragma unroll
+  for (int s = 0; s < NU; ++s) {
+    const bool live = s < a.nsplit;
+    ls[s] = live ? a.ws_lse[s * sstride + rh] : -INFINITY;
+    v[s] = live ? *(const f32x2*)(a.ws_o + (s * sstride + rh) * 128 + 2 * lane) : f32x2{0.f, 0.f};
+  }
   float M = -INFINITY;
-  for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, a.ws_lse[s * sstride + rh]);
+#pragma unroll
+  for (int s = 0; s < NU; ++s) M = fmaxf(M, ls[s]);
+  for (int s = NU; s < a.nsplit; ++s) M = fmaxf(M, a.ws_lse[s * sstride + rh]);
   float den = 0.f, acc0 = 0.f, acc1 = 0.f;
   if (M > -INFINITY) {
-    for (int s = 0; s < a.nsplit; ++s) {
-      const float ls = a.ws_lse[s * sstride + rh];
-      if (ls == -INFINITY) continue;
-      const float wgt = expf(ls - M);
-      const f32x2 v = *(const f32x2*)(a.ws_o + (s * sstride + rh) * 128 + 2 * lane);
+#pragma unroll
+    for (int s = 0; s < NU; ++s) {
+      const float wgt = ls[s] == -INFINITY ? 0.f : expf(ls[s] - M);
       den += wgt;
-      acc0 += wgt * v[0];
-      acc1 += wgt * v[1];
+      acc0 += wgt * v[s][0];
+      acc1 += wgt * v[s][1];
+    }
+    for (int s = NU; s < a.nsplit; ++s) {
+      const float lsx = a.ws_lse[s * sstride + rh];
+      if (lsx == -INFINITY) continue;
+      const float wgt = expf(lsx - M);
+      const f32x2 vx = *(const f32x2*)(a.ws_o + (s * sstride + rh) * 128 + 2 * lane);
+      den += wgt;
+      acc0 += wgt * vx[0];
+      acc1 += wgt * vx[1];
     }
   }
   const float inv = den > 0.f ? 1.f / den : 0.f;
