@@ -15,6 +15,7 @@ from .attention import (  # noqa: F401
     e4m3fn_to_f64,
     gather_kv_rows,
     paged_decode,
+    quantize_e4m3fn,
     ragged_prefill,
     ragged_prefill_fp8,
     widen,

@@ -100,6 +100,33 @@ def e4m3fn_table() -> np.ndarray:
 _E4M3FN = e4m3fn_table()
 
 
+def quantize_e4m3fn(x: np.ndarray, scale: float) -> np.ndarray:
+    """Codes of x / scale in OCP fp8 E4M3FN (the writer's side of a per-tensor
+    scaled fp8 cache: the stored code c stands for e4m3fn(c) * scale).
+
+    The quotient is taken in float32 (x is float32; IEEE division, correctly
+    rounded).  Its code is the one whose value is nearest, ties going to the
+    code with an even last mantissa bit (round to nearest even); magnitudes
+    past the largest finite value 448 saturate to it (the format has no
+    infinities); the sign of zero is kept; NaN gives the NaN code with its
+    sign.  Returns uint8 codes."""
+    with np.errstate(over="ignore"):          # a quotient past float32 range saturates below
+        y = np.asarray(x, dtype=np.float32) / np.float32(scale)
+    a = np.abs(y).astype(np.float64)
+    pos = _E4M3FN[:0x7F]                       # values of codes 0x00 .. 0x7E, ascending
+    hi = np.clip(np.searchsorted(pos, a, side="left"), 0, 0x7E)   # first code with value >= a
+    lo = np.clip(hi - 1, 0, 0x7E)
+    d_hi = pos[hi] - a
+    d_lo = a - pos[lo]
+    pick_lo = (d_lo < d_hi) | ((d_lo == d_hi) & (lo % 2 == 0))
+    code = np.where(pick_lo, lo, hi)
+    code = np.where(a >= pos[0x7E], 0x7E, code)                     # saturate at 448
+    code = code.astype(np.uint8)
+    code |= np.where(np.signbit(y), np.uint8(0x80), np.uint8(0))
+    code = np.where(np.isnan(y), np.where(np.signbit(y), np.uint8(0xFF), np.uint8(0x7F)), code)
+    return code.astype(np.uint8)
+
+
 def e4m3fn_to_f64(bits: np.ndarray) -> np.ndarray:
     return _E4M3FN[np.asarray(bits, dtype=np.uint8)]
 
@@ -291,6 +318,9 @@ def append_kv(
     *,
     kr_new: Optional[np.ndarray] = None,
     kr_pool: Optional[np.ndarray] = None,
+    kv_dtype: str = "bf16",
+    k_scale: float = 1.0,
+    v_scale: float = 1.0,
 ):
     """Write a chunk's keys and values into the paged cache (storage bits, exact).
 
@@ -302,7 +332,17 @@ def append_kv(
     With an MLA rope cache, kr_new [T, 1, Dr] goes to kr_pool [NB, 1, 64, Dr]
     by the same rule (flare_mla_prefill, overload A: the rope keys live in a
     paged cache too).  Returns new pools ((k, v) or (k, v, kr)); the inputs
-    are not modified."""
+    are not modified.
+
+    With kv_dtype "e4m3fn" the pools hold fp8 codes with per-tensor scales
+    (the fp8 KV cache of decode): the chunk's bf16 keys and values are
+    written as quantize_e4m3fn(value, k_scale) and (value, v_scale); the
+    rope cache stays bf16."""
+    if kv_dtype == "e4m3fn":
+        k_new = quantize_e4m3fn(bf16_to_f64(k_new).astype(np.float32), k_scale)
+        v_new = quantize_e4m3fn(bf16_to_f64(v_new).astype(np.float32), v_scale)
+    elif kv_dtype != "bf16":
+        raise ValueError(f"unknown kv dtype {kv_dtype!r}")
     kp = np.array(k_pool, copy=True)
     vp = np.array(v_pool, copy=True)
     rp = np.array(kr_pool, copy=True) if kr_pool is not None else None
@@ -335,6 +375,9 @@ def chunk_prefill(
     rows: Optional[Sequence[int]] = None,
     row_chunk: int = 256,
     kr_pool: Optional[np.ndarray] = None,
+    kv_dtype: Optional[str] = None,
+    k_scale: float = 1.0,
+    v_scale: float = 1.0,
 ):
     """Causal attention of a chunk of new queries to a paged KV cache.
 
@@ -349,8 +392,12 @@ def chunk_prefill(
     shared by every head (flare_mla_prefill: the K head lacks the rope part,
     which comes from the rope cache for all heads).
     ``rows``: optional global query indices to evaluate (default all).
+    ``kv_dtype``: storage of the K/V pools when it differs from ``dtype``;
+    "e4m3fn" pools hold fp8 codes whose values are e4m3fn(code) * k_scale
+    (keys) and * v_scale (values), as for decode; the rope cache has ``dtype``.
     Returns (out [n, Hq, D], lse [n, Hq]) in float64."""
     Q = widen(q, dtype)
+    kvd = dtype if kv_dtype is None else kv_dtype
     T, Hq, Dqk = Q.shape
     Hk, Dn = k_pool.shape[1], k_pool.shape[3]
     Dr = 0 if kr_pool is None else kr_pool.shape[3]
@@ -377,8 +424,8 @@ def chunk_prefill(
         j = np.arange(Lk)
         KR = widen(gather_kv_rows(kr_pool, block_table, b, 0, Lk), dtype) if Dr else None
         for g in range(Hk):
-            K = widen(gather_kv_rows(k_pool, block_table, b, g, Lk), dtype)
-            V = widen(gather_kv_rows(v_pool, block_table, b, g, Lk), dtype)
+            K = widen(gather_kv_rows(k_pool, block_table, b, g, Lk), kvd) * float(k_scale)
+            V = widen(gather_kv_rows(v_pool, block_table, b, g, Lk), kvd) * float(v_scale)
             heads = slice(g * r, (g + 1) * r)
             for s0 in range(0, sel.size, row_chunk):
                 idx = sel[s0:s0 + row_chunk]

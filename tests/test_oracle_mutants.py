@@ -8,6 +8,7 @@ import pytest
 
 from oracle import attention as O
 from tests import test_oracle_fp8_prefill_pins as P8
+from tests import test_oracle_fp8kv_chunk_pins as PQ
 from tests import test_oracle_pins as P
 
 SRC = inspect.getsource(O)
@@ -69,6 +70,15 @@ MUTANTS = {
     "fp8_blockwise_query_scale_flipped": ("(qs[..., None] if qs.ndim else qs)",
                                           "(qs[::-1, :, None] if qs.ndim else qs)",
                                           [P8.test_fp8_blockwise_matches_bruteforce_on_torch_decoded_codes]),
+    "quantizer_ties_to_odd": ("((d_lo == d_hi) & (lo % 2 == 0))", "((d_lo == d_hi) & (lo % 2 == 1))",
+                              [PQ.test_quantizer_closed_form_points]),
+    "quantizer_top_code_missing": ("pos = _E4M3FN[:0x7F]", "pos = _E4M3FN[:0x7E]",
+                                   [PQ.test_quantizer_closed_form_points]),
+    "quantizer_rounds_down": ("pick_lo = (d_lo < d_hi)", "pick_lo = (d_lo <= 1e30)",
+                              [lambda: PQ.test_quantizer_matches_torch_cast_on_every_bf16_value(1.0)]),
+    "fp8kv_v_scale_dropped": ("V = widen(gather_kv_rows(v_pool, block_table, b, g, Lk), kvd) * float(v_scale)",
+                              "V = widen(gather_kv_rows(v_pool, block_table, b, g, Lk), kvd)",
+                              [PQ.test_fp8_chunk_prefill_matches_bruteforce_on_torch_decoded_pages]),
     "fp8_rope_dropped": ('np.concatenate([q, widen(q_rope, "bf16")], axis=2)',
                          'np.concatenate([q, 0 * widen(q_rope, "bf16")], axis=2)',
                          [P8.test_fp8_prefill_matches_sdpa_with_concatenated_rope_key]),
@@ -81,6 +91,7 @@ def test_planted_mistake_is_caught(name, monkeypatch):
     mutant = _mutant(old, new)
     monkeypatch.setattr(P, "O", mutant)
     monkeypatch.setattr(P8, "O", mutant)
+    monkeypatch.setattr(PQ, "O", mutant)
     caught = []
     for fn in catchers:
         try:

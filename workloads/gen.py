@@ -477,6 +477,9 @@ class ChunkCase:
     scale: float
     kr_new: Optional[np.ndarray] = None    # MLA: [T, 1, Dr] bf16 bits, the chunk's rope keys
     kr_pool: Optional[np.ndarray] = None   # MLA: [NB, 1, 64, Dr] bf16 bits, rope cache on the same pages
+    kv_dtype: str = "bf16"                 # 'e4m3fn': k_pool / v_pool hold fp8 codes (k_new / v_new stay bf16)
+    k_scale: float = 1.0                   # fp8 pools: the value of code c is e4m3fn(c) * scale
+    v_scale: float = 1.0
     meta: dict = field(default_factory=dict)
 
     @property
@@ -520,9 +523,14 @@ def make_chunk_case(
     D_rope: int = 0,
     spare_blocks: int = 2,
     scale: Optional[float] = None,
+    kv_dtype: str = "bf16",
 ) -> ChunkCase:
     """Draw a chunked-prefill problem: sequence b already holds prefix_lens[b]
     keys in a paged bf16 cache and appends a chunk of q_lens[b] tokens.
+    With kv_dtype 'e4m3fn' the K and V pools are an fp8 cache: the same draws,
+    quantised with the per-tensor scale amax / 448, the amax taken over the
+    pool's values and the chunk's new bf16 values together (so the append
+    does not saturate); unused rows hold the NaN code.
 
     Draw order: block_table permutation -> q -> k_new -> v_new -> k_pool -> v_pool
     (-> kr_new -> kr_pool with a rope width D_rope: MLA, one rope head per token on
@@ -559,20 +567,32 @@ def make_chunk_case(
         for t in range(int(prefix[b])):
             keep[block_table[b, t // BLOCK], t % BLOCK] = True
     pools = []
-    for s_x, heads, width in ((s_k, Hk, D), (s_v, Hk, D), (s_r, 1, D_rope)):
+    scales = [1.0, 1.0]
+    for i, (s_x, heads, width) in enumerate(((s_k, Hk, D), (s_v, Hk, D), (s_r, 1, D_rope))):
         if width == 0:
             pools.append(None)
             continue
-        x = to_bf16_bits(normal_f32(s_x, NB * heads * BLOCK * width).reshape(NB, heads, BLOCK, width))
-        x.transpose(0, 2, 1, 3)[~keep] = BF16_NAN
+        xf = normal_f32(s_x, NB * heads * BLOCK * width).reshape(NB, heads, BLOCK, width)
+        if kv_dtype == "e4m3fn" and i < 2:
+            new = _bf16_bits_to_f32(k_new if i == 0 else v_new)
+            amax = max(float(np.abs(xf).max()) if xf.size else 0.0, float(np.abs(new).max()) if new.size else 0.0)
+            sc = float(np.float32(amax) / np.float32(E4M3FN_MAX)) if amax > 0 else 1.0
+            x = to_e4m3fn_bits(xf, sc)
+            x.transpose(0, 2, 1, 3)[~keep] = E4M3FN_NAN
+            scales[i] = sc
+        elif kv_dtype in ("bf16", "e4m3fn"):
+            x = to_bf16_bits(xf)
+            x.transpose(0, 2, 1, 3)[~keep] = BF16_NAN
+        else:
+            raise ValueError(kv_dtype)
         pools.append(x)
     kr_new = to_bf16_bits(normal_f32(s_rn, T * D_rope).reshape(T, 1, D_rope)) if D_rope else None
     if scale is None:
         scale = 1.0 / math.sqrt(D + D_rope)
     return ChunkCase(name=name, kv_lens=kv_lens, cu_seqlens_q=cu, Hq=Hq, Hk=Hk, D=D, q=q, k_new=k_new,
                      v_new=v_new, k_pool=pools[0], v_pool=pools[1], block_table=block_table,
-                     scale=float(scale), kr_new=kr_new, kr_pool=pools[2],
-                     meta={"seed": seed, "prefix_lens": prefix})
+                     scale=float(scale), kr_new=kr_new, kr_pool=pools[2], kv_dtype=kv_dtype,
+                     k_scale=scales[0], v_scale=scales[1], meta={"seed": seed, "prefix_lens": prefix})
 
 
 def prefill_chunk_bf16(seed: int = 1006, B: int = 8, prefix_range=(1024, 6144), q_len: int = 512) -> ChunkCase:
