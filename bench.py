@@ -10,8 +10,9 @@ before the timed region; consecutive steps read different copies of the KV
 pool, so no step is served from the 256 MB last-level cache by its
 predecessor.  The other workloads (fp8 KV decode, MLA prefill, block-sparse
 prefill, fp8 MLA prefill with per-tensor and blockwise scales, chunked
-prefill, and a long-context chunk whose few query tiles are split along the
-keys) are measured the same way and reported under "secondary".
+prefill over a bf16 and over an fp8 e4m3fn cache, and a long-context chunk
+whose few query tiles are split along the keys) are measured the same way
+and reported under "secondary".
 
 Prints ONE JSON line.
 """
@@ -88,6 +89,7 @@ DOMINANT_KERNEL = {
     "prefill_mla_fp8": "prefill_fwd<64, false, 1>",
     "prefill_mla_fp8_blockwise": "prefill_fwd<64, false, 2>",
     "prefill_chunk_long_mla_bf16": "prefill_fwd<64, true, 0>",
+    "prefill_chunk_fp8kv": "prefill_fwd<0, true, 3>",
 }
 
 
@@ -278,11 +280,13 @@ def bench_chunk(case, steps, warmup, torch, gq, gu, check=True):
         from oracle import attention as O
         import numpy as np
         out, _ = dc.results()
+        fp8 = dict(kv_dtype=case.kv_dtype, k_scale=case.k_scale, v_scale=case.v_scale)
         pools = O.append_kv(case.k_new, case.v_new, case.k_pool, case.v_pool, case.block_table,
-                            case.cu_seqlens_q, case.kv_lens, kr_new=case.kr_new, kr_pool=case.kr_pool)
+                            case.cu_seqlens_q, case.kv_lens, kr_new=case.kr_new, kr_pool=case.kr_pool, **fp8)
         rows = np.linspace(0, case.T - 1, 48).astype(np.int64)
         ref, _ = O.chunk_prefill(case.q, pools[0], pools[1], case.block_table, case.cu_seqlens_q, case.kv_lens,
-                                 case.scale, dtype="bf16", rows=rows, kr_pool=pools[2] if len(pools) == 3 else None)
+                                 case.scale, dtype="bf16", rows=rows, kr_pool=pools[2] if len(pools) == 3 else None,
+                                 **fp8)
         err = float(abs(out[rows] - ref).max())
     flops = case.flops()
     return {
@@ -389,7 +393,10 @@ def main(argv=None) -> int:
                 secondary.append(rp)
                 del pc
         if hasattr(gu, "DeviceChunk"):
-            for mk in (gen.prefill_chunk_bf16, gen.prefill_chunk_mla_bf16, gen.prefill_chunk_long_mla_bf16):
+            # the fp8-cache chunk widens its codes to bf16 before the matrix
+            # cores, so every chunk workload is priced at the bf16 peak
+            for mk in (gen.prefill_chunk_bf16, gen.prefill_chunk_mla_bf16, gen.prefill_chunk_long_mla_bf16,
+                       gen.prefill_chunk_fp8kv):
                 cc = mk()
                 rc = bench_chunk(cc, args.steps, args.warmup, torch, gq, gu)
                 rc["roofline"] = {"bound": "mfma", "achieved": rc["tflops_kernel"], "peak": BF16_MFMA_PEAK_TFLOPS,

@@ -29,7 +29,8 @@ PLAN_MAGIC = 0x47514150
 C_FUNCTIONS = (
     "gqap_decode_plan", "gqap_decode_validate_host", "gqap_paged_decode", "gqap_debug_gather_kv",
     "gqap_prefill_plan", "gqap_prefill", "gqap_prefill_fp8", "gqap_prefill_fp8_blockwise", "gqap_chunk_plan",
-    "gqap_chunk_validate_host", "gqap_append_kv", "gqap_chunk_prefill", "gqap_block_table_from_csr", "gqap_last_error", "gqap_version",
+    "gqap_chunk_validate_host", "gqap_append_kv", "gqap_chunk_prefill", "gqap_append_kv_fp8",
+    "gqap_chunk_prefill_fp8kv", "gqap_block_table_from_csr", "gqap_last_error", "gqap_version",
 )
 
 
@@ -97,7 +98,7 @@ class ChunkDesc(ctypes.Structure):
         ("kv_stride_block", ctypes.c_int64), ("kv_stride_head", ctypes.c_int64),
         ("block_table_stride", ctypes.c_int64),
         ("kr_new_stride_token", ctypes.c_int64), ("kr_stride_block", ctypes.c_int64),
-        ("num_splits", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("num_splits", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
     ]
 
 
@@ -143,6 +144,11 @@ def _load() -> ctypes.CDLL:
     lib.gqap_chunk_prefill.argtypes = [ctypes.POINTER(ChunkPlan), vp, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp, u64,
                                        vp]
     lib.gqap_chunk_prefill.restype = st
+    lib.gqap_append_kv_fp8.argtypes = [ctypes.POINTER(ChunkPlan), vp, vp, vp, vp, vp, vp, vp, vp, vp, f32, f32, vp]
+    lib.gqap_append_kv_fp8.restype = st
+    lib.gqap_chunk_prefill_fp8kv.argtypes = [ctypes.POINTER(ChunkPlan), vp, vp, vp, vp, vp, vp, vp, f32, f32, f32, vp,
+                                             vp, vp, u64, vp]
+    lib.gqap_chunk_prefill_fp8kv.restype = st
     lib.gqap_block_table_from_csr.argtypes = [vp, vp, i32, i32, ctypes.c_int64, vp, vp]
     lib.gqap_block_table_from_csr.restype = st
     lib.gqap_last_error.argtypes = []
@@ -290,6 +296,24 @@ def gqap_chunk_prefill(plan: ChunkPlan, q, k_pool, v_pool, kr_pool, block_table,
                                    _ptr(lse), _ptr(workspace), workspace_bytes, _stream(stream)))
 
 
+def gqap_append_kv_fp8(plan: ChunkPlan, k_new, v_new, k_rope_new, k_pool, v_pool, kr_pool, block_table,
+                       cu_seqlens_q, kv_lens, k_scale: float, v_scale: float, stream=None) -> None:
+    _check(_lib.gqap_append_kv_fp8(ctypes.byref(plan), _ptr(k_new), _ptr(v_new), _ptr(k_rope_new), _ptr(k_pool),
+                                   _ptr(v_pool), _ptr(kr_pool), _ptr(block_table), _ptr(cu_seqlens_q),
+                                   _ptr(kv_lens), k_scale, v_scale, _stream(stream)))
+
+
+def gqap_chunk_prefill_fp8kv(plan: ChunkPlan, q, k_pool, v_pool, kr_pool, block_table, cu_seqlens_q, kv_lens,
+                             scale: float, k_scale: float, v_scale: float, out, lse=None, workspace=None,
+                             workspace_bytes: Optional[int] = None, stream=None) -> None:
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.gqap_chunk_prefill_fp8kv(ctypes.byref(plan), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(kr_pool),
+                                         _ptr(block_table), _ptr(cu_seqlens_q), _ptr(kv_lens), scale, k_scale,
+                                         v_scale, _ptr(out), _ptr(lse), _ptr(workspace), workspace_bytes,
+                                         _stream(stream)))
+
+
 def gqap_block_table_from_csr(kv_indices, kv_page_indptr, batch: int, max_blocks_per_seq: int, block_table,
                               block_table_stride: Optional[int] = None, stream=None) -> None:
     if block_table_stride is None:
@@ -369,7 +393,8 @@ def prefill_desc(q, k, v, k_rope, batch: int, max_seq_len: int, block_mask=None,
 def chunk_desc(q, k_new, k_pool, block_table, batch: int, max_q_len: int, max_kv_len: int,
                out=None, k_rope_new=None, kr_pool=None, num_splits: int = 0) -> ChunkDesc:
     """Descriptor for q [T, Hq, D + Dr], k_new / v_new [T, Hk, D], pool [NB, Hk, 64, D],
-    block_table [B, Nblk]; MLA: k_rope_new [T, 1, Dr], kr_pool [NB, 1, 64, Dr]."""
+    block_table [B, Nblk]; MLA: k_rope_new [T, 1, Dr], kr_pool [NB, 1, 64, Dr].
+    A float8_e4m3fn pool makes an fp8 cache (kv_dtype FP8_E4M3FN)."""
     T, Hq, _ = q.shape
     NB, Hk, blk, D = k_pool.shape
     out = q if out is None else out
@@ -386,6 +411,7 @@ def chunk_desc(q, k_new, k_pool, block_table, batch: int, max_q_len: int, max_kv
     d.new_stride_token, d.new_stride_head = k_new.stride(0), k_new.stride(1)
     d.out_stride_token, d.out_stride_head = out.stride(0), out.stride(1)
     d.kv_stride_block, d.kv_stride_head = k_pool.stride(0), k_pool.stride(1)
+    d.kv_dtype = dtype_tag(k_pool)
     d.block_table_stride = block_table.stride(0)
     if kr_pool is not None:
         d.head_dim_rope = kr_pool.shape[3]

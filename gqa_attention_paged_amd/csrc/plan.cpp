@@ -255,6 +255,11 @@ extern "C" gqap_status gqap_chunk_plan(const gqap_chunk_desc_t* desc, gqap_chunk
   if (d.block_size != kBlock) return fail(GQAP_ERR_UNSUPPORTED, "block_size must be %d (got %d)", kBlock, d.block_size);
   if (d.head_dim != 128) return fail(GQAP_ERR_UNSUPPORTED, "head_dim must be 128 (got %d)", d.head_dim);
   if (d.dtype != GQAP_BF16) return fail(GQAP_ERR_DTYPE, "chunked prefill takes bf16 tensors (got dtype %d)", d.dtype);
+  // The cache: bf16 like the chunk (kv_dtype 0 in a zero-filled descriptor),
+  // or fp8 e4m3fn codes with per-tensor scales.
+  if (d.kv_dtype != 0 && d.kv_dtype != GQAP_BF16 && d.kv_dtype != GQAP_FP8_E4M3FN)
+    return fail(GQAP_ERR_DTYPE, "kv_dtype must be 0, GQAP_BF16 or GQAP_FP8_E4M3FN (got %d)", d.kv_dtype);
+  const int kv_esz = d.kv_dtype == GQAP_FP8_E4M3FN ? 1 : 2;
   if (d.max_blocks_per_seq <= 0)
     return fail(GQAP_ERR_INVALID_ARGUMENT, "max_blocks_per_seq must be positive (got %d)", d.max_blocks_per_seq);
   if (d.num_pool_blocks <= 0)
@@ -289,9 +294,11 @@ extern "C" gqap_status gqap_chunk_plan(const gqap_chunk_desc_t* desc, gqap_chunk
     return fail(GQAP_ERR_INVALID_ARGUMENT, "block_table_stride %lld < Nblk %d", (long long)d.block_table_stride,
                 d.max_blocks_per_seq);
   const int64_t strides[] = {d.q_stride_token, d.q_stride_head, d.new_stride_token, d.new_stride_head,
-                             d.out_stride_token, d.out_stride_head, d.kv_stride_block, d.kv_stride_head};
+                             d.out_stride_token, d.out_stride_head};
   for (int64_t st : strides)
     if (!aligned16(st, 2)) return fail(GQAP_ERR_INVALID_ARGUMENT, "strides must keep rows 16-byte aligned");
+  if (!aligned16(d.kv_stride_block, kv_esz) || !aligned16(d.kv_stride_head, kv_esz))
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "pool strides must keep page slabs 16-byte aligned");
   plan->desc = d;
   plan->ratio = d.num_q_heads / d.num_kv_heads;
   plan->q_tile_rows = 128;
@@ -305,7 +312,7 @@ extern "C" gqap_status gqap_chunk_plan(const gqap_chunk_desc_t* desc, gqap_chunk
   if (grid * ns >= ((int64_t)1 << 24))
     return fail(GQAP_ERR_UNSUPPORTED, "Hq * batch * ceil(max_q_len/128) * num_splits = %lld workgroups exceeds 2^24",
                 (long long)(grid * ns));
-  plan->kernel = Dr ? 2 : 1;
+  plan->kernel = (Dr ? 2 : 1) + (kv_esz == 1 ? 2 : 0);
   plan->num_splits = (uint32_t)ns;
   plan->workspace_bytes = split_workspace(ns, d.total_q_tokens, d.num_q_heads);
   plan->magic = GQAP_PLAN_MAGIC;

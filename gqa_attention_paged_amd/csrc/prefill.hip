@@ -70,6 +70,10 @@ struct PrefillArgs {
   int32_t T;
   float* ws_o;
   float* ws_lse;
+  // fp8 KV pages: the value of a V code is e4m3fn(code) * v_scale; k_scale is
+  // folded into scale_log2 without a rope part, else held in qk and applied
+  // to the nope sum only (the rope cache is bf16 and unscaled).
+  float v_scale;
 };
 
 namespace dev {
@@ -120,20 +124,32 @@ using namespace dev;
 // fp8 matrix cores; the rope parts and V stay bf16.  F8 = 1 has one scale per
 // tensor, F8 = 2 one per row of a head (the key scales of a tile are staged in
 // LDS next to it).
+// F8 = 3 (paged only): the K and V pages hold fp8 e4m3fn codes with
+// per-tensor scales.  Each page is loaded into registers, widened exactly to
+// bf16 (every e4m3fn value is a bf16 value) and written to the LDS layouts of
+// a bf16 tile, so the math is that of the bf16 path; k_scale is part of the
+// softmax constant and v_scale multiplies the normalised output.
 template <int DR, bool PAGED, int F8>
 __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
-  static_assert(!(F8 && PAGED), "the fp8 path reads token-major K");
+  constexpr bool QK8 = F8 == 1 || F8 == 2;    // fp8 nope Q.K on the fp8 matrix cores
+  constexpr bool KV8 = F8 == 3;               // fp8 KV pages, widened to bf16 in LDS
+  static_assert(!(QK8 && PAGED), "the fp8 Q.K path reads token-major K");
+  static_assert(!KV8 || PAGED, "the fp8 KV path reads pages");
   constexpr int DN = 128;                     // per-head key width
   constexpr int DV = 128;                     // value / output width
   constexpr int KSN = DN / 16;                // k-steps over the nope part (bf16)
   constexpr int KSR = DR / 16;                // k-steps over the rope part
-  constexpr int KE = F8 ? 1 : 2;              // bytes per K element
+  constexpr int KE = QK8 ? 1 : 2;             // bytes per K element in LDS
+  constexpr int KGE = QK8 || KV8 ? 1 : 2;     // bytes per K element in memory
+  constexpr int VGE = KV8 ? 1 : 2;            // bytes per V element in memory
   constexpr int KB = 64 * DN * KE;            // K tile bytes
   constexpr int RB = DR ? 64 * DR * 2 : 0;    // rope tile bytes
   constexpr int VB = 64 * DV * 2;             // V tile bytes
-  constexpr int KLD = KB / 1024 / 4;          // 1 KB loads-to-LDS per wave and tile: K
-  constexpr int RLD = RB / 1024 / 4;          //   rope
-  constexpr int VLD = VB / 1024 / 4;          //   V
+  // Loads per lane and tile: 16-byte loads-to-LDS (1 KB per wave each), or
+  // with KV8 16-byte register loads of codes (two per lane for K, two for V).
+  constexpr int KLD = KV8 ? 2 : KB / 1024 / 4;  // K
+  constexpr int RLD = RB / 1024 / 4;            // rope
+  constexpr int VLD = KV8 ? 2 : VB / 1024 / 4;  // V
   // LDS: one array per tile buffer, so the compiler can tell the buffer being
   // filled by the direct-to-LDS loads from the one being read.
   __shared__ __attribute__((aligned(1024))) unsigned char kbuf0[KB], kbuf1[KB];
@@ -211,13 +227,13 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
   // With F8 the nope part is instead two 32-byte operands of the fp8 step,
   // lane (l32, hh) holding codes 64 s + 32 hh .. +31 for step s, and qop
   // holds only the bf16 rope part, read from its own tensor.
-  constexpr int NQ = F8 ? KSR : KSN + KSR;
+  constexpr int NQ = QK8 ? KSR : KSN + KSR;
   bf16x8 qop[NQ > 0 ? NQ : 1];
   i32x8 q8[2];
   {
     const bool ok = qrow < L;
     const int64_t tok = c0 + (ok ? qrow : 0);
-    if constexpr (F8) {
+    if constexpr (QK8) {
       const unsigned char* qp = (const unsigned char*)a.q + tok * a.q_st + (int64_t)h * a.q_sh + 32 * hh;
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
@@ -300,12 +316,12 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
   const int row0r = tid >> 3, chr = tid & 7;
   const int rch = chr ^ ((row0r >> 1) & 7);                            // rope: c' = c ^ ((row >> 1) & 7)
   const int vch = (((ch >> 1) ^ vmask(row0)) << 1) | (ch & 1);         // V: 32-byte pieces ^ vmask(row)
-  constexpr int KRS = F8 ? 32 : 16;                                    // K rows per load round
-  const int krow = F8 ? row0r : row0;
-  const int kch = F8 ? rch : ch ^ (row0 & 15);                         // K: c' = c ^ (row & 15)
+  constexpr int KRS = QK8 ? 32 : 16;                                   // K rows per load round
+  const int krow = QK8 ? row0r : row0;
+  const int kch = QK8 ? rch : ch ^ (row0 & 15);                        // K: c' = c ^ (row & 15)
   // Tile bases are uniform (scalar) pointers; each lane adds one fixed 32-bit
   // byte offset, so the loads use the scalar-base addressing form.
-  const int64_t kstr = a.k_st * KE, vstr = a.v_st * 2, rstr = a.kr_st * 2;  // row strides in bytes
+  const int64_t kstr = a.k_st * KGE, vstr = a.v_st * VGE, rstr = a.kr_st * 2;  // row strides in bytes
   const unsigned char* kg =
       (const unsigned char*)a.k + ((int64_t)c0 * a.k_st + (int64_t)g * a.k_sh) * KE;
   const unsigned char* vg = (const unsigned char*)(a.v + (int64_t)c0 * a.v_st + (int64_t)g * a.v_sh);
@@ -340,13 +356,13 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
   };
   auto tile_k = [&](int kt) -> const unsigned char* {
     if constexpr (PAGED)
-      return (const unsigned char*)a.k + ((int64_t)page_of(kt) * a.kv_sb + (int64_t)g * a.kv_sh) * 2;
+      return (const unsigned char*)a.k + ((int64_t)page_of(kt) * a.kv_sb + (int64_t)g * a.kv_sh) * KGE;
     else
       return kg + (int64_t)kt * 64 * kstr;
   };
   auto tile_v = [&](int kt) -> const unsigned char* {
     if constexpr (PAGED)
-      return (const unsigned char*)a.v + ((int64_t)page_of(kt) * a.kv_sb + (int64_t)g * a.kv_sh) * 2;
+      return (const unsigned char*)a.v + ((int64_t)page_of(kt) * a.kv_sb + (int64_t)g * a.kv_sh) * VGE;
     else
       return vg + (int64_t)kt * 64 * vstr;
   };
@@ -361,6 +377,13 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
   // Rows past the last key read row Lk-1 instead: every key past Lk is
   // causally hidden from every query of the sequence, so its score is
   // replaced by -inf and its probability is exactly 0.
+  // fp8 KV pages: lane tid loads the 16 codes at byte 16 c8 of rows row8 and
+  // row8 + 32 of the K and of the V page (rows of 128 bytes), into k8r / v8r;
+  // stage8 widens them and writes the bf16 tile.
+  const int row8 = tid >> 3, c8 = tid & 7;
+  const uint32_t koff8 = (uint32_t)(row8 * kstr) + 16u * c8;
+  const uint32_t voff8 = (uint32_t)(row8 * vstr) + 16u * c8;
+  i32x4 k8r[KV8 ? 2 : 1], v8r[KV8 ? 2 : 1];
   auto load_tile = [&](int kt, auto bufc) {
     constexpr int BUF = decltype(bufc)::value;
     unsigned char* kd = BUF ? kbuf1 : kbuf0;
@@ -372,7 +395,23 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
     const unsigned char* kt_k = tile_k(kt);
     const unsigned char* kt_v = tile_v(kt);
     const unsigned char* kt_r = DR ? tile_r(kt) : nullptr;
-    if (key0 + 64 <= Lk) {  // whole tile inside the keys
+    if constexpr (KV8) {
+      const bool whole = key0 + 64 <= Lk;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int64_t r = whole ? row8 + 32 * i : min(row8 + 32 * i, Lk - 1 - key0);
+        k8r[i] = load16(kt_k + r * kstr + 16 * c8);
+      }
+#pragma unroll
+      for (int i = 0; i < RLD; ++i)
+        dma(kt_r + (int64_t)(whole ? row0r + 32 * i : min(row0r + 32 * i, Lk - 1 - key0)) * rstr + 16 * rch,
+            rd + 4096 * i + wseg);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int64_t r = whole ? row8 + 32 * i : min(row8 + 32 * i, Lk - 1 - key0);
+        v8r[i] = load16(kt_v + r * vstr + 16 * c8);
+      }
+    } else if (key0 + 64 <= Lk) {  // whole tile inside the keys
 #pragma unroll
       for (int i = 0; i < KLD; ++i) dma(kt_k + KRS * i * kstr + koff, kd + 4096 * i + wseg);
 #pragma unroll
@@ -393,6 +432,31 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
     // Keep the loads at the top of the tile so they overlap its math.
     __builtin_amdgcn_sched_barrier(0);
   };
+  // fp8 KV pages: widen the codes in k8r / v8r to bf16 and write them where a
+  // bf16 tile's loads would have put them: K chunk c of a row (16 bytes) at
+  // chunk c ^ (row & 15), V 32-byte piece p at piece p ^ vmask(row).  The
+  // buffer written is not read during the current tile; the barrier that ends
+  // the tile publishes it.
+  auto stage8 = [&](auto bufc) {
+    if constexpr (KV8) {
+      constexpr int BUF = decltype(bufc)::value;
+      unsigned char* kd = BUF ? kbuf1 : kbuf0;
+      unsigned char* vd = BUF ? vbuf1 : vbuf0;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int row = row8 + 32 * i;
+        const bf16x8 k0 = fp8x8_to_bf16x8(i32x2{k8r[i][0], k8r[i][1]});
+        const bf16x8 k1 = fp8x8_to_bf16x8(i32x2{k8r[i][2], k8r[i][3]});
+        store16(kd + row * 256 + (((2 * c8) ^ (row & 15)) << 4), __builtin_bit_cast(i32x4, k0));
+        store16(kd + row * 256 + (((2 * c8 + 1) ^ (row & 15)) << 4), __builtin_bit_cast(i32x4, k1));
+        const bf16x8 w0 = fp8x8_to_bf16x8(i32x2{v8r[i][0], v8r[i][1]});
+        const bf16x8 w1 = fp8x8_to_bf16x8(i32x2{v8r[i][2], v8r[i][3]});
+        unsigned char* vp = vd + row * 256 + ((c8 ^ vmask(row)) << 5);
+        store16(vp, __builtin_bit_cast(i32x4, w0));
+        store16(vp + 16, __builtin_bit_cast(i32x4, w1));
+      }
+    }
+  };
   // Waits for this thread's tile loads; the barrier that follows publishes
   // every thread's.
   auto loads_done = [] { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
@@ -401,8 +465,8 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
   // immediates.  K: chunk (2s + hh) ^ (row & 15) = 2 (s ^ m) + ((hh ^ row) & 1).
   // fp8 K: 16-byte read u = 2 s + e of fp8 step s is chunk 4 s + 2 hh + e,
   // stored at chunk ^ ((row >> 1) & 7).
-  int kra[F8 ? 4 : KSN];
-  if constexpr (F8) {
+  int kra[QK8 ? 4 : KSN];
+  if constexpr (QK8) {
     const int m = (l32 >> 1) & 7;
 #pragma unroll
     for (int u = 0; u < 4; ++u) kra[u] = l32 * 128 + (((4 * (u >> 1) + 2 * hh + (u & 1)) ^ m) << 4);
@@ -455,6 +519,15 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
     const unsigned char* kt_v = WL ? tile_v(kn) : nullptr;
     const unsigned char* kt_r = DR && WL ? tile_r(kn) : nullptr;
     auto issue_load = [&](int i) {
+      if constexpr (KV8) {  // whole tile inside the keys: no row clamp
+        if (i < KLD)
+          k8r[i] = load16(kt_k + 32 * i * kstr + koff8);
+        else if (i < KLD + RLD)
+          dma(kt_r + 32 * (i - KLD) * rstr + roff, rd + 4096 * (i - KLD) + wseg);
+        else
+          v8r[i - KLD - RLD] = load16(kt_v + 32 * (i - KLD - RLD) * vstr + voff8);
+        return;
+      }
       if (i < KLD)
         dma(kt_k + KRS * i * kstr + koff, kd + 4096 * i + wseg);
       else if (i < KLD + RLD)
@@ -465,9 +538,11 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
         dma4(ksg + (int64_t)(kn * 64 + lane) * a.Hk, sd);
     };
     f32x16_t s[2] = {f32x16_t{}, f32x16_t{}};
-    if constexpr (!F8) {
+    if constexpr (!QK8) {
       // S^T tile t (keys 32t .. 32t+31 of the tile) x 32 queries: 2 NS MFMAs
-      // whose K operands are read from LDS PF steps ahead.
+      // whose K operands are read from LDS PF steps ahead.  With an fp8 cache
+      // and a rope part only the nope sum carries k_scale: it is applied
+      // before the first rope step of each half.
       constexpr int NS = KSN + KSR;
       constexpr int PF = 8;
       auto kfrag = [&](int idx) {
@@ -481,6 +556,7 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
       for (int idx = 0; idx < 2 * NS; ++idx) {
         const i32x4 cur = kf[idx % PF];
         if (idx + PF < 2 * NS) kf[idx % PF] = kfrag(idx + PF);
+        if (KV8 && KSR > 0 && idx % NS == KSN) s[idx / NS] *= a.qk;
         s[idx / NS] = mfma32x32x16(__builtin_bit_cast(bf16x8, cur), qop[idx % NS], s[idx / NS]);
         if (WL && idx < NLD) issue_load(idx);
       }
@@ -654,7 +730,10 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
   int kt = a.mask ? first_needed(kt_begin) : kt_begin;
-  if (kt < kt_end) load_tile(kt, B0{});
+  if (kt < kt_end) {
+    load_tile(kt, B0{});
+    stage8(B0{});
+  }
   loads_done();
   __syncthreads();
   using WL0 = std::integral_constant<bool, false>;
@@ -667,9 +746,11 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
     const bool inside = more && kn * 64 + 64 <= Lk;
     if (sees && inside) {
       compute_tile(kt, bufc, WL1{}, kn);
+      stage8(nbufc);
     } else {
       if (more) load_tile(kn, nbufc);
       if (sees) compute_tile(kt, bufc, WL0{}, kn);
+      if (more) stage8(nbufc);
     }
     loads_done();
     __syncthreads();
@@ -697,7 +778,7 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
     l_run = __builtin_bit_cast(float, (uint32_t)sw[0]) + __builtin_bit_cast(float, (uint32_t)sw[1]);
   }
   if (qrow >= L) return;
-  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+  const float inv = l_run > 0.f ? (KV8 ? a.v_scale : 1.f) / l_run : 0.f;
   if (a.nsplit > 1) {  // partial of this key range; prefill_merge writes the output
     const int64_t prow = ((int64_t)sp * a.T + c0 + qrow) * a.Hq + h;
     float* wp = a.ws_o + prow * DV;
@@ -818,8 +899,23 @@ struct AppendArgs {
   int64_t new_st, new_sh, kv_sb, kv_sh, bt_st, kr_new_st, kr_sb;
   int64_t rows;     // T * Hk
   int32_t B, Hk, max_kv;
+  float k_scale, v_scale;  // fp8 pools: a code c stands for e4m3fn(c) * scale
 };
 
+// Code of x / scale in OCP e4m3fn for two values at a time, into byte pair
+// HI of w.  The quotient is the correctly rounded float32 one; magnitudes
+// past the largest finite value 448 saturate to it (the format has no
+// infinity; NaN stays NaN and gives a NaN code), and the hardware conversion
+// rounds to the nearest value, ties to even.
+__device__ __forceinline__ float sat_e4m3(float y) { return fabsf(y) > 448.f ? copysignf(448.f, y) : y; }
+template <bool HI>
+__device__ __forceinline__ int quant_pair(uint32_t bf2, float scale, int w) {
+  const float x0 = dev::bf16_to_f32((uint16_t)(bf2 & 0xffffu));
+  const float x1 = dev::bf16_to_f32((uint16_t)(bf2 >> 16));
+  return __builtin_amdgcn_cvt_pk_fp8_f32(sat_e4m3(__fdiv_rn(x0, scale)), sat_e4m3(__fdiv_rn(x1, scale)), w, HI);
+}
+
+template <bool FP8>
 __global__ __launch_bounds__(256) void append_kv(AppendArgs a) {
   constexpr int D = 128;
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -839,8 +935,20 @@ __global__ __launch_bounds__(256) void append_kv(AppendArgs a) {
   const int64_t page = a.bt[(int64_t)b * a.bt_st + (p >> 6)];
   const int64_t dst = page * a.kv_sb + (int64_t)g * a.kv_sh + (int64_t)(p & 63) * D + 8 * piece;
   const int64_t src = (int64_t)t * a.new_st + (int64_t)g * a.new_sh + 8 * piece;
-  dev::store16(a.k_pool + dst, dev::load16(a.k_new + src));
-  dev::store16(a.v_pool + dst, dev::load16(a.v_new + src));
+  if constexpr (FP8) {  // 8 values -> 8 code bytes; dst counts bytes
+    const dev::i32x4 kx = dev::load16(a.k_new + src), vx = dev::load16(a.v_new + src);
+    dev::i32x2 kc, vc;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      kc[e] = quant_pair<true>((uint32_t)kx[2 * e + 1], a.k_scale, quant_pair<false>((uint32_t)kx[2 * e], a.k_scale, 0));
+      vc[e] = quant_pair<true>((uint32_t)vx[2 * e + 1], a.v_scale, quant_pair<false>((uint32_t)vx[2 * e], a.v_scale, 0));
+    }
+    *(dev::i32x2*)((unsigned char*)a.k_pool + dst) = kc;
+    *(dev::i32x2*)((unsigned char*)a.v_pool + dst) = vc;
+  } else {
+    dev::store16(a.k_pool + dst, dev::load16(a.k_new + src));
+    dev::store16(a.v_pool + dst, dev::load16(a.v_new + src));
+  }
   if (a.kr_pool && g == 0 && piece < 8)  // the 128-byte rope row, once per token
     dev::store16(a.kr_pool + page * a.kr_sb + (int64_t)(p & 63) * 64 + 8 * piece,
                  dev::load16(a.kr_new + (int64_t)t * a.kr_new_st + 8 * piece));
@@ -1040,12 +1148,20 @@ extern "C" gqap_status gqap_prefill_fp8_blockwise(const gqap_prefill_plan_t* pla
   return launch_fp8<2>(plan, a, workspace, workspace_bytes, stream);
 }
 
-extern "C" gqap_status gqap_append_kv(const gqap_chunk_plan_t* plan, const void* k_new, const void* v_new,
-                                      const void* k_rope_new, void* k_pool, void* v_pool, void* kr_pool,
-                                      const int32_t* block_table, const int32_t* cu_seqlens_q,
-                                      const int32_t* kv_lens, void* stream) {
+// The cache's storage: bf16 (kv_dtype 0 or GQAP_BF16) or fp8 e4m3fn codes.
+static bool chunk_fp8_cache(const gqap_chunk_desc_t& d) { return d.kv_dtype == GQAP_FP8_E4M3FN; }
+
+static gqap_status append_common(const gqap_chunk_plan_t* plan, const void* k_new, const void* v_new,
+                                 const void* k_rope_new, void* k_pool, void* v_pool, void* kr_pool,
+                                 const int32_t* block_table, const int32_t* cu_seqlens_q, const int32_t* kv_lens,
+                                 bool fp8, float k_scale, float v_scale, void* stream) {
   if (!plan || plan->magic != GQAP_PLAN_MAGIC) return fail(GQAP_ERR_INVALID_ARGUMENT, "invalid chunk plan");
   const gqap_chunk_desc_t& d = plan->desc;
+  if (chunk_fp8_cache(d) != fp8)
+    return fail(GQAP_ERR_DTYPE, fp8 ? "gqap_append_kv_fp8 needs a plan with kv_dtype GQAP_FP8_E4M3FN"
+                                    : "this plan has an fp8 cache: append with gqap_append_kv_fp8");
+  if (fp8 && !(std::isfinite(k_scale) && k_scale > 0.f && std::isfinite(v_scale) && v_scale > 0.f))
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "k_scale and v_scale must be finite and > 0");
   if (d.batch == 0 || d.total_q_tokens == 0) return GQAP_OK;
   if (!k_new || !v_new || !k_pool || !v_pool || !block_table || !cu_seqlens_q || !kv_lens)
     return fail(GQAP_ERR_INVALID_ARGUMENT, "null device pointer");
@@ -1078,21 +1194,48 @@ extern "C" gqap_status gqap_append_kv(const gqap_chunk_plan_t* plan, const void*
   a.B = d.batch;
   a.Hk = d.num_kv_heads;
   a.max_kv = d.max_kv_len;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
   const int64_t blocks = (a.rows * 16 + 255) / 256;
   if (blocks >= ((int64_t)1 << 31)) return fail(GQAP_ERR_UNSUPPORTED, "chunk too large for one append launch");
-  hipLaunchKernelGGL(append_kv, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, a);
+  if (fp8)
+    hipLaunchKernelGGL(append_kv<true>, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, a);
+  else
+    hipLaunchKernelGGL(append_kv<false>, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(GQAP_ERR_HIP, "append launch: %s", hipGetErrorString(e));
   return GQAP_OK;
 }
 
-extern "C" gqap_status gqap_chunk_prefill(const gqap_chunk_plan_t* plan, const void* q, const void* k_pool,
-                                          const void* v_pool, const void* kr_pool, const int32_t* block_table,
-                                          const int32_t* cu_seqlens_q, const int32_t* kv_lens, float scale,
-                                          void* out, float* lse, void* workspace, uint64_t workspace_bytes,
-                                          void* stream) {
+extern "C" gqap_status gqap_append_kv(const gqap_chunk_plan_t* plan, const void* k_new, const void* v_new,
+                                      const void* k_rope_new, void* k_pool, void* v_pool, void* kr_pool,
+                                      const int32_t* block_table, const int32_t* cu_seqlens_q,
+                                      const int32_t* kv_lens, void* stream) {
+  return append_common(plan, k_new, v_new, k_rope_new, k_pool, v_pool, kr_pool, block_table, cu_seqlens_q, kv_lens,
+                       false, 1.f, 1.f, stream);
+}
+
+extern "C" gqap_status gqap_append_kv_fp8(const gqap_chunk_plan_t* plan, const void* k_new, const void* v_new,
+                                          const void* k_rope_new, void* k_pool, void* v_pool, void* kr_pool,
+                                          const int32_t* block_table, const int32_t* cu_seqlens_q,
+                                          const int32_t* kv_lens, float k_scale, float v_scale, void* stream) {
+  return append_common(plan, k_new, v_new, k_rope_new, k_pool, v_pool, kr_pool, block_table, cu_seqlens_q, kv_lens,
+                       true, k_scale, v_scale, stream);
+}
+
+static gqap_status chunk_common(const gqap_chunk_plan_t* plan, const void* q, const void* k_pool,
+                                const void* v_pool, const void* kr_pool, const int32_t* block_table,
+                                const int32_t* cu_seqlens_q, const int32_t* kv_lens, float scale, bool fp8,
+                                float k_scale, float v_scale, void* out, float* lse, void* workspace,
+                                uint64_t workspace_bytes, void* stream) {
   if (!plan || plan->magic != GQAP_PLAN_MAGIC) return fail(GQAP_ERR_INVALID_ARGUMENT, "invalid chunk plan");
   const gqap_chunk_desc_t& d = plan->desc;
+  if (chunk_fp8_cache(d) != fp8)
+    return fail(GQAP_ERR_DTYPE, fp8 ? "gqap_chunk_prefill_fp8kv needs a plan with kv_dtype GQAP_FP8_E4M3FN"
+                                    : "this plan has an fp8 cache: use gqap_chunk_prefill_fp8kv");
+  if (!std::isfinite(scale)) return fail(GQAP_ERR_INVALID_ARGUMENT, "scale must be finite");
+  if (fp8 && !(std::isfinite(k_scale) && k_scale > 0.f && std::isfinite(v_scale) && v_scale > 0.f))
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "k_scale and v_scale must be finite and > 0");
   if (d.batch == 0 || plan->q_tiles == 0) return GQAP_OK;
   if (!q || !k_pool || !v_pool || !block_table || !cu_seqlens_q || !kv_lens || !out)
     return fail(GQAP_ERR_INVALID_ARGUMENT, "null device pointer");
@@ -1103,7 +1246,6 @@ extern "C" gqap_status gqap_chunk_prefill(const gqap_chunk_plan_t* plan, const v
       ((uintptr_t)block_table & 3) || ((uintptr_t)cu_seqlens_q & 3) || ((uintptr_t)kv_lens & 3) ||
       (lse && ((uintptr_t)lse & 3)))
     return fail(GQAP_ERR_INVALID_ARGUMENT, "device pointers must be 16-byte aligned (index arrays, lse 4-byte)");
-  if (!std::isfinite(scale)) return fail(GQAP_ERR_INVALID_ARGUMENT, "scale must be finite");
   PrefillArgs a{};
   a.q = (const uint16_t*)q;
   a.k = (const uint16_t*)k_pool;
@@ -1130,7 +1272,12 @@ extern "C" gqap_status gqap_chunk_prefill(const gqap_chunk_plan_t* plan, const v
   a.q_tiles = plan->q_tiles;
   a.mask_nb = 0;
   a.max_len = d.max_q_len;
-  a.scale_log2 = scale * dev::kLog2e;
+  // fp8 cache: the key scale joins the softmax constant when the score is the
+  // nope sum alone; with a rope part it multiplies the nope sum only.  The
+  // value scale multiplies the normalised output.
+  a.scale_log2 = scale * (fp8 && !d.head_dim_rope ? k_scale : 1.f) * dev::kLog2e;
+  a.qk = fp8 ? k_scale : 1.f;
+  a.v_scale = fp8 ? v_scale : 1.f;
   a.kvlens = kv_lens;
   a.bt = block_table;
   a.bt_st = d.block_table_stride;
@@ -1141,11 +1288,37 @@ extern "C" gqap_status gqap_chunk_prefill(const gqap_chunk_plan_t* plan, const v
                                      plan->workspace_bytes, workspace, workspace_bytes, &a);
   if (ss != GQAP_OK) return ss;
   const dim3 grid((unsigned)d.num_q_heads * (unsigned)d.batch * (unsigned)plan->q_tiles * (unsigned)a.nsplit);
-  if (d.head_dim_rope == 64)
-    hipLaunchKernelGGL((prefill_fwd<64, true, 0>), grid, dim3(256), 0, (hipStream_t)stream, a);
-  else
-    hipLaunchKernelGGL((prefill_fwd<0, true, 0>), grid, dim3(256), 0, (hipStream_t)stream, a);
+  hipStream_t st = (hipStream_t)stream;
+  if (d.head_dim_rope == 64) {
+    if (fp8)
+      hipLaunchKernelGGL((prefill_fwd<64, true, 3>), grid, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((prefill_fwd<64, true, 0>), grid, dim3(256), 0, st, a);
+  } else {
+    if (fp8)
+      hipLaunchKernelGGL((prefill_fwd<0, true, 3>), grid, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((prefill_fwd<0, true, 0>), grid, dim3(256), 0, st, a);
+  }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(GQAP_ERR_HIP, "chunk prefill launch: %s", hipGetErrorString(e));
-  return launch_merge(a, d.max_q_len, (hipStream_t)stream);
+  return launch_merge(a, d.max_q_len, st);
+}
+
+extern "C" gqap_status gqap_chunk_prefill(const gqap_chunk_plan_t* plan, const void* q, const void* k_pool,
+                                          const void* v_pool, const void* kr_pool, const int32_t* block_table,
+                                          const int32_t* cu_seqlens_q, const int32_t* kv_lens, float scale,
+                                          void* out, float* lse, void* workspace, uint64_t workspace_bytes,
+                                          void* stream) {
+  return chunk_common(plan, q, k_pool, v_pool, kr_pool, block_table, cu_seqlens_q, kv_lens, scale, false, 1.f, 1.f,
+                      out, lse, workspace, workspace_bytes, stream);
+}
+
+extern "C" gqap_status gqap_chunk_prefill_fp8kv(const gqap_chunk_plan_t* plan, const void* q, const void* k_pool,
+                                                const void* v_pool, const void* kr_pool, const int32_t* block_table,
+                                                const int32_t* cu_seqlens_q, const int32_t* kv_lens, float scale,
+                                                float k_scale, float v_scale, void* out, float* lse, void* workspace,
+                                                uint64_t workspace_bytes, void* stream) {
+  return chunk_common(plan, q, k_pool, v_pool, kr_pool, block_table, cu_seqlens_q, kv_lens, scale, true, k_scale,
+                      v_scale, out, lse, workspace, workspace_bytes, stream);
 }

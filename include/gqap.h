@@ -11,7 +11,8 @@
  *   - the same prefill with the nope parts of Q and K in fp8 e4m3fn, one
  *     scale per tensor or one per row of a head, on the fp8 matrix cores;
  *   - chunked prefill against the paged cache (append the chunk's keys and
- *     values, then attend to the cached prefix and the chunk);
+ *     values, then attend to the cached prefix and the chunk), with a bf16
+ *     cache or an fp8 e4m3fn cache with per-tensor scales;
  *   - the padded block table built from a CSR page list;
  *   - plan / validation calls that run on the host only;
  *   - a debug gather that exposes the decode kernels' page addressing.
@@ -394,7 +395,11 @@ typedef struct gqap_chunk_desc_t {
   int64_t kr_new_stride_token; /* MLA: elements between rope rows of k_rope_new, >= Dr */
   int64_t kr_stride_block;     /* MLA: elements between rope-cache blocks, >= 64*Dr */
   int32_t num_splits;          /* key-axis splits: 0 = chosen by the plan, 1..16 forced */
-  int32_t reserved;
+  int32_t kv_dtype;            /* storage of k_pool / v_pool: GQAP_BF16, or GQAP_FP8_E4M3FN
+                                  for an fp8 cache with per-tensor scales (the calls
+                                  gqap_append_kv_fp8 / gqap_chunk_prefill_fp8kv); 0, as a
+                                  zero-filled descriptor leaves it, means GQAP_BF16.  With
+                                  fp8 the kv_stride_* count bytes */
 } gqap_chunk_desc_t;
 
 typedef struct gqap_chunk_plan_t {
@@ -411,7 +416,8 @@ typedef struct gqap_chunk_plan_t {
 /*
  * Validate a chunked-prefill request.  Pure host code.  Errors:
  * INVALID_ARGUMENT (sizes, strides that overlap or break 16-byte alignment,
- * Hq % Hk, max_kv_len > Nblk * 64, max_q_len > max_kv_len), DTYPE (not bf16),
+ * Hq % Hk, max_kv_len > Nblk * 64, max_q_len > max_kv_len), DTYPE (dtype
+ * not bf16, kv_dtype not 0, bf16 or fp8 e4m3fn),
  * UNSUPPORTED (block_size != 64, D != 128, Dr not 0 or 64, Hq * batch *
  * ceil(max_q_len / 128) * num_splits >= 2^24 workgroups); INVALID_ARGUMENT
  * also for num_splits outside 0..16.  Key-axis splits as for the prefill.
@@ -454,6 +460,36 @@ gqap_status gqap_chunk_prefill(const gqap_chunk_plan_t* plan, const void* q, con
                                const int32_t* cu_seqlens_q, const int32_t* kv_lens, float scale,
                                void* out, float* lse, void* workspace, uint64_t workspace_bytes,
                                void* stream);
+
+/*
+ * The same two calls over an fp8 e4m3fn KV cache (plan kv_dtype
+ * GQAP_FP8_E4M3FN; the plain calls reject such a plan with DTYPE and these
+ * reject a bf16 one).  The cache is the per-tensor scaled fp8 cache that the
+ * paged decode reads (MATE msa_interface: k_scale / v_scale dequantisation
+ * scales; FlashMLA tensor-shape reference: FP8 caches): a stored code c
+ * stands for e4m3fn(c) * k_scale in k_pool and e4m3fn(c) * v_scale in v_pool.
+ * k_pool and v_pool are [NB, Hk, 64, D] bytes; q, k_new, v_new, the rope
+ * tensors, out and lse are as above (bf16 / float32), and the rope cache
+ * stays bf16.
+ *
+ * gqap_append_kv_fp8 writes the code of k_new / k_scale (v_new / v_scale),
+ * the quotient taken in float32, rounded to the nearest e4m3fn value with
+ * ties to the even code, magnitudes past 448 saturating to +-448 and NaN
+ * giving a NaN code; positions as gqap_append_kv.
+ * gqap_chunk_prefill_fp8kv computes the attention of gqap_chunk_prefill with
+ * the dequantised keys and values; queries stay bf16 and are never
+ * quantised.  k_scale and v_scale must be finite and > 0.
+ */
+gqap_status gqap_append_kv_fp8(const gqap_chunk_plan_t* plan, const void* k_new, const void* v_new,
+                               const void* k_rope_new, void* k_pool, void* v_pool, void* kr_pool,
+                               const int32_t* block_table, const int32_t* cu_seqlens_q, const int32_t* kv_lens,
+                               float k_scale, float v_scale, void* stream);
+
+gqap_status gqap_chunk_prefill_fp8kv(const gqap_chunk_plan_t* plan, const void* q, const void* k_pool,
+                                     const void* v_pool, const void* kr_pool, const int32_t* block_table,
+                                     const int32_t* cu_seqlens_q, const int32_t* kv_lens, float scale,
+                                     float k_scale, float v_scale, void* out, float* lse, void* workspace,
+                                     uint64_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* CSR page input                                                            */

@@ -139,8 +139,10 @@ class DeviceChunk:
         self.q = bits_to_tensor(case.q, "bf16").to(device)
         self.k_new = bits_to_tensor(case.k_new, "bf16").to(device)
         self.v_new = bits_to_tensor(case.v_new, "bf16").to(device)
-        self.k_pool = bits_to_tensor(case.k_pool, "bf16").to(device)
-        self.v_pool = bits_to_tensor(case.v_pool, "bf16").to(device)
+        self.fp8 = getattr(case, "kv_dtype", "bf16") == "e4m3fn"   # fp8 cache with per-tensor scales
+        pool_tag = "e4m3fn" if self.fp8 else "bf16"
+        self.k_pool = bits_to_tensor(case.k_pool, pool_tag).to(device)
+        self.v_pool = bits_to_tensor(case.v_pool, pool_tag).to(device)
         self.kr_new = bits_to_tensor(case.kr_new, "bf16").to(device) if case.kr_new is not None else None
         self.kr_pool = bits_to_tensor(case.kr_pool, "bf16").to(device) if case.kr_pool is not None else None
         self.bt = torch.from_numpy(np.ascontiguousarray(case.block_table, dtype=np.int32)).to(device)
@@ -159,10 +161,20 @@ class DeviceChunk:
         gq.gqap_chunk_validate_host(self.plan, case.block_table, case.cu_seqlens_q, case.kv_lens)
 
     def append(self, stream=None):
+        if self.fp8:
+            gq.gqap_append_kv_fp8(self.plan, self.k_new, self.v_new, self.kr_new, self.k_pool, self.v_pool,
+                                  self.kr_pool, self.bt, self.cu, self.kvl, self.case.k_scale, self.case.v_scale,
+                                  stream=stream)
+            return
         gq.gqap_append_kv(self.plan, self.k_new, self.v_new, self.kr_new, self.k_pool, self.v_pool, self.kr_pool,
                           self.bt, self.cu, self.kvl, stream=stream)
 
     def run(self, stream=None):
+        if self.fp8:
+            gq.gqap_chunk_prefill_fp8kv(self.plan, self.q, self.k_pool, self.v_pool, self.kr_pool, self.bt, self.cu,
+                                        self.kvl, self.case.scale, self.case.k_scale, self.case.v_scale, self.out,
+                                        self.lse, self.ws, self.plan.workspace_bytes, stream=stream)
+            return self.out, self.lse
         gq.gqap_chunk_prefill(self.plan, self.q, self.k_pool, self.v_pool, self.kr_pool, self.bt, self.cu,
                               self.kvl, self.case.scale, self.out, self.lse, self.ws, self.plan.workspace_bytes,
                               stream=stream)
@@ -173,9 +185,11 @@ class DeviceChunk:
         return tensor_to_f64(self.out), self.lse.detach().cpu().numpy().astype(np.float64)
 
     def pools_bits(self):
-        """(k, v) pools as bf16 bits, plus the rope pool for MLA cases."""
+        """(k, v) pools as bf16 bits (uint8 codes for an fp8 cache), plus the rope pool for MLA cases."""
         torch.cuda.synchronize()
         bits = lambda t: t.detach().cpu().view(torch.int16).numpy().view(np.uint16)
+        codes = lambda t: t.detach().cpu().view(torch.uint8).numpy()
+        kv = codes if self.fp8 else bits
         if self.kr_pool is None:
-            return bits(self.k_pool), bits(self.v_pool)
-        return bits(self.k_pool), bits(self.v_pool), bits(self.kr_pool)
+            return kv(self.k_pool), kv(self.v_pool)
+        return kv(self.k_pool), kv(self.v_pool), bits(self.kr_pool)

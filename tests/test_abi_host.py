@@ -416,6 +416,55 @@ def test_chunk_calls_reject_bad_arguments_without_a_gpu(gq):
     assert gq.STATUS_NAMES[st] == "INVALID_ARGUMENT"      # unplanned (magic 0)
 
 
+def test_chunk_plan_fp8_cache(gq):
+    """kv_dtype FP8_E4M3FN plans an fp8 cache (pool strides in bytes, which
+    must keep 16-byte slabs); 0 and BF16 plan a bf16 cache; other values are
+    DTYPE errors."""
+    d = baseline_chunk_desc(gq)
+    assert gq.gqap_chunk_plan(d).kernel == 1
+    d.kv_dtype = gq.BF16
+    assert gq.gqap_chunk_plan(d).kernel == 1
+    d.kv_dtype = gq.FP8_E4M3FN
+    assert gq.gqap_chunk_plan(d).kernel == 3
+    d.kv_stride_block = 8 * 64 * 128 + 8      # 8 bytes past a 16-byte boundary for fp8 pages
+    with pytest.raises(gq.GqapError, match="16-byte"):
+        gq.gqap_chunk_plan(d)
+    for bad in (gq.F16, 7):
+        d = baseline_chunk_desc(gq)
+        d.kv_dtype = bad
+        got = gq.lib().gqap_chunk_plan(ctypes.byref(d), ctypes.byref(gq.ChunkPlan()))
+        assert gq.STATUS_NAMES[got] == "DTYPE", gq.gqap_last_error()
+
+
+def test_chunk_calls_check_the_cache_dtype_without_a_gpu(gq):
+    """The bf16 calls refuse an fp8-cache plan and the fp8 calls a bf16 one,
+    before touching any pointer; the fp8 calls refuse scales that are not
+    finite and positive."""
+    lib = gq.lib()
+    p16 = gq.gqap_chunk_plan(baseline_chunk_desc(gq))
+    d8 = baseline_chunk_desc(gq)
+    d8.kv_dtype = gq.FP8_E4M3FN
+    p8 = gq.gqap_chunk_plan(d8)
+    st = lib.gqap_chunk_prefill(ctypes.byref(p8), 16, 16, 16, None, 16, 16, 16, 1.0, 16, None, None, 0, None)
+    assert gq.STATUS_NAMES[st] == "DTYPE"
+    st = lib.gqap_append_kv(ctypes.byref(p8), 16, 16, None, 16, 16, None, 16, 16, 16, None)
+    assert gq.STATUS_NAMES[st] == "DTYPE"
+    st = lib.gqap_chunk_prefill_fp8kv(ctypes.byref(p16), 16, 16, 16, None, 16, 16, 16, 1.0, 1.0, 1.0, 16, None,
+                                      None, 0, None)
+    assert gq.STATUS_NAMES[st] == "DTYPE"
+    st = lib.gqap_append_kv_fp8(ctypes.byref(p16), 16, 16, None, 16, 16, None, 16, 16, 16, 1.0, 1.0, None)
+    assert gq.STATUS_NAMES[st] == "DTYPE"
+    for ks, vs in ((0.0, 1.0), (1.0, -2.0), (float("inf"), 1.0), (1.0, float("nan"))):
+        st = lib.gqap_chunk_prefill_fp8kv(ctypes.byref(p8), 16, 16, 16, None, 16, 16, 16, 1.0, ks, vs, 16, None,
+                                          None, 0, None)
+        assert gq.STATUS_NAMES[st] == "INVALID_ARGUMENT", (ks, vs)
+        st = lib.gqap_append_kv_fp8(ctypes.byref(p8), 16, 16, None, 16, 16, None, 16, 16, 16, ks, vs, None)
+        assert gq.STATUS_NAMES[st] == "INVALID_ARGUMENT", (ks, vs)
+    st = lib.gqap_append_kv_fp8(ctypes.byref(p8), None, None, None, None, None, None, None, None, None, 1.0, 1.0,
+                                None)
+    assert gq.STATUS_NAMES[st] == "INVALID_ARGUMENT"
+
+
 def test_csr_conversion_rejects_bad_arguments_without_a_gpu(gq):
     lib = gq.lib()
     assert gq.STATUS_NAMES[lib.gqap_block_table_from_csr(16, 16, -1, 4, 4, 16, None)] == "INVALID_ARGUMENT"

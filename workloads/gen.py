@@ -622,6 +622,17 @@ def prefill_chunk_long_mla_bf16(seed: int = 1011, prefix: int = 15872, q_len: in
                            Hq=16, Hk=16, D=128, D_rope=64)
 
 
+def prefill_chunk_fp8kv(seed: int = 1006, B: int = 8, prefix_range=(1024, 6144), q_len: int = 512) -> ChunkCase:
+    """Chunked prefill over an fp8 e4m3fn KV cache: the shapes and draws of
+    prefill_chunk_bf16 (B=8, cached prefixes ~ U{1024..6144}, 512-token chunks,
+    Hq=32, Hk=8, D=128, bf16 queries), the K and V pools quantised with the
+    per-tensor scale amax / 448 as in the fp8 decode workload."""
+    lo, hi = prefix_range
+    prefix = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed).spawn(1)[0])).integers(lo, hi + 1, size=B)
+    return make_chunk_case(name="prefill_chunk_fp8kv", seed=seed + 1, prefix_lens=prefix.tolist(),
+                           q_lens=[q_len] * B, Hq=32, Hk=8, D=128, kv_dtype="e4m3fn")
+
+
 CONFIGS = {
     "decode_tiny_f32": decode_tiny_fp32,
     "decode_gqa_bf16": decode_gqa_bf16,
@@ -633,4 +644,5 @@ CONFIGS = {
     "prefill_mla_fp8": prefill_mla_fp8,
     "prefill_mla_fp8_blockwise": prefill_mla_fp8_blockwise,
     "prefill_chunk_long_mla_bf16": prefill_chunk_long_mla_bf16,
+    "prefill_chunk_fp8kv": prefill_chunk_fp8kv,
 }
