@@ -94,6 +94,19 @@ __device__ __forceinline__ f32x16_t mfma32x32x64_fp8(i32x8 a, i32x8 b, f32x16_t 
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
+// Eight OCP e4m3fn bytes (little-endian in w) -> eight bf16 values, two per
+// instruction with the gfx950 scaled conversion at scale 1 (exact: every
+// e4m3fn value is a bf16 value).
+__device__ __forceinline__ i32x4 fp8x8_to_bf16x8_pk(i32x2 w) {
+  typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+  i32x4 r;
+  r[0] = __builtin_bit_cast(int, (bf16x2)__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)w[0], 1.f, false));
+  r[1] = __builtin_bit_cast(int, (bf16x2)__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)w[0], 1.f, true));
+  r[2] = __builtin_bit_cast(int, (bf16x2)__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)w[1], 1.f, false));
+  r[3] = __builtin_bit_cast(int, (bf16x2)__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)w[1], 1.f, true));
+  return r;
+}
+
 // 16-byte chunk c of row `row` of a tile with RC chunks per row, XOR-swizzled
 // so that 16 consecutive rows read at one logical chunk hit distinct banks.
 template <int RC>
@@ -383,7 +396,7 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
   const int row8 = tid >> 3, c8 = tid & 7;
   const uint32_t koff8 = (uint32_t)(row8 * kstr) + 16u * c8;
   const uint32_t voff8 = (uint32_t)(row8 * vstr) + 16u * c8;
-  i32x4 k8r[KV8 ? 2 : 1], v8r[KV8 ? 2 : 1];
+  i32x4 k8r[KV8 ? 2 : 1] = {}, v8r[KV8 ? 2 : 1] = {};
   auto load_tile = [&](int kt, auto bufc) {
     constexpr int BUF = decltype(bufc)::value;
     unsigned char* kd = BUF ? kbuf1 : kbuf0;
@@ -436,7 +449,9 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
   // bf16 tile's loads would have put them: K chunk c of a row (16 bytes) at
   // chunk c ^ (row & 15), V 32-byte piece p at piece p ^ vmask(row).  The
   // buffer written is not read during the current tile; the barrier that ends
-  // the tile publishes it.
+  // the tile publishes it.  A wave that computes the tile does this during
+  // its P.V steps; when no tile follows, the registers hold stale codes and
+  // the buffer they land in is never read again.
   auto stage8 = [&](auto bufc) {
     if constexpr (KV8) {
       constexpr int BUF = decltype(bufc)::value;
@@ -445,15 +460,11 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int row = row8 + 32 * i;
-        const bf16x8 k0 = fp8x8_to_bf16x8(i32x2{k8r[i][0], k8r[i][1]});
-        const bf16x8 k1 = fp8x8_to_bf16x8(i32x2{k8r[i][2], k8r[i][3]});
-        store16(kd + row * 256 + (((2 * c8) ^ (row & 15)) << 4), __builtin_bit_cast(i32x4, k0));
-        store16(kd + row * 256 + (((2 * c8 + 1) ^ (row & 15)) << 4), __builtin_bit_cast(i32x4, k1));
-        const bf16x8 w0 = fp8x8_to_bf16x8(i32x2{v8r[i][0], v8r[i][1]});
-        const bf16x8 w1 = fp8x8_to_bf16x8(i32x2{v8r[i][2], v8r[i][3]});
+        store16(kd + row * 256 + (((2 * c8) ^ (row & 15)) << 4), fp8x8_to_bf16x8_pk(i32x2{k8r[i][0], k8r[i][1]}));
+        store16(kd + row * 256 + (((2 * c8 + 1) ^ (row & 15)) << 4), fp8x8_to_bf16x8_pk(i32x2{k8r[i][2], k8r[i][3]}));
         unsigned char* vp = vd + row * 256 + ((c8 ^ vmask(row)) << 5);
-        store16(vp, __builtin_bit_cast(i32x4, w0));
-        store16(vp + 16, __builtin_bit_cast(i32x4, w1));
+        store16(vp, fp8x8_to_bf16x8_pk(i32x2{v8r[i][0], v8r[i][1]}));
+        store16(vp + 16, fp8x8_to_bf16x8_pk(i32x2{v8r[i][2], v8r[i][3]}));
       }
     }
   };
@@ -712,6 +723,9 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
     i16x8 vf[PV];
 #pragma unroll
     for (int i = 0; i < PV; ++i) vf[i] = vfrag(i);
+    // fp8 pages: the next tile's codes are widened and written between these
+    // matrix steps (three conversions and at most one LDS write per step).
+    if constexpr (KV8) stage8(std::integral_constant<int, 1 - BUF>{});
 #pragma unroll
     for (int idx = 0; idx < 16; ++idx) {
       const i16x8 cur = vf[idx % PV];
@@ -723,6 +737,10 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
     for (int idx = 0; idx < 16 - PV; ++idx) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      if constexpr (KV8) {
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+        if (idx < 8) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+      }
     }
     __builtin_amdgcn_sched_group_barrier(0x008, PV, 0);
   };
@@ -745,12 +763,13 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
     const bool more = kn < kt_end;
     const bool inside = more && kn * 64 + 64 <= Lk;
     if (sees && inside) {
-      compute_tile(kt, bufc, WL1{}, kn);
-      stage8(nbufc);
+      compute_tile(kt, bufc, WL1{}, kn);  // with fp8 pages, stages kn during its P.V steps
     } else {
       if (more) load_tile(kn, nbufc);
-      if (sees) compute_tile(kt, bufc, WL0{}, kn);
-      if (more) stage8(nbufc);
+      if (sees)
+        compute_tile(kt, bufc, WL0{}, kn);
+      else if (more)
+        stage8(nbufc);
     }
     loads_done();
     __syncthreads();

@@ -178,3 +178,25 @@ def test_fp8kv_at_unit_scales_matches_bf16_cache_bits(gu, Dr):
     d16.run()
     out16, lse16 = d16.results()
     assert np.array_equal(out8, out16) and np.array_equal(lse8, lse16)
+
+
+def test_fp8_append_then_paged_decode_reads_the_same_cache(gu):
+    """One-token chunks appended into an fp8 cache, then the fp8 paged decode
+    over the same pools and scales: both paths share the cache format, and
+    both match the oracle's decode over the appended codes."""
+    case = gen.make_chunk_case(name="fp8kv_decode", seed=90, prefix_lens=[1023, 64, 5, 300, 0],
+                               q_lens=[1, 1, 1, 1, 1], Hq=16, Hk=4, kv_dtype="e4m3fn")
+    dc, out_c, lse_c = _run(gu, case)
+    kp, vp = dc.pools_bits()
+    ref, ref_lse = O.paged_decode(case.q, kp, vp, case.block_table, case.kv_lens, case.scale, q_dtype="bf16",
+                                  kv_dtype="e4m3fn", k_scale=case.k_scale, v_scale=case.v_scale)
+    dec = dataclasses.make_dataclass("DecodeView", ["q", "k_pool", "v_pool", "block_table", "seq_lens", "q_dtype",
+                                                     "kv_dtype", "scale", "k_scale", "v_scale", "B", "Hq"])
+    view = dec(q=case.q, k_pool=kp, v_pool=vp, block_table=case.block_table, seq_lens=case.kv_lens, q_dtype="bf16",
+               kv_dtype="e4m3fn", scale=case.scale, k_scale=case.k_scale, v_scale=case.v_scale, B=case.B, Hq=case.Hq)
+    gu.announce("fp8 paged decode over the appended cache")
+    dd = gu.DeviceDecode(view)
+    dd.run()
+    out_d, lse_d = dd.results()
+    for out, lse in ((out_c, lse_c), (out_d, lse_d)):
+        assert gu.max_abs_err(out, ref) <= TOL and gu.lse_err(lse, ref_lse) <= TOL

@@ -82,13 +82,14 @@ def test_prefill_bf16_and_fp8_in_a_graph(gu):
         _replays_match(gu, g, [dp.out, dp.lse], ref, lambda: scratch.add_(1.0))
 
 
-def test_chunk_step_in_a_graph(gu):
-    """A chunked-prefill step (append, then attention) captured together.  The
-    append writes the same bytes on every replay, so the cache and the output
-    must match the eager step exactly."""
+@pytest.mark.parametrize("kv_dtype", ["bf16", "e4m3fn"])
+def test_chunk_step_in_a_graph(gu, kv_dtype):
+    """A chunked-prefill step (append, then attention) captured together, over
+    a bf16 and over an fp8 cache.  The append writes the same bytes on every
+    replay, so the cache and the output must match the eager step exactly."""
     case = gen.make_chunk_case(name="graph_chunk", seed=98, prefix_lens=[100, 0, 640], q_lens=[28, 64, 129], Hq=8,
-                               Hk=2, D_rope=64)
-    gu.announce("graph chunk step")
+                               Hk=2, D_rope=64, kv_dtype=kv_dtype)
+    gu.announce(f"graph chunk step, {kv_dtype} cache")
     dc = gu.DeviceChunk(case)
 
     def step():
