@@ -200,3 +200,14 @@ def test_fp8_append_then_paged_decode_reads_the_same_cache(gu):
     out_d, lse_d = dd.results()
     for out, lse in ((out_c, lse_c), (out_d, lse_d)):
         assert gu.max_abs_err(out, ref) <= TOL and gu.lse_err(lse, ref_lse) <= TOL
+
+
+def test_fp8kv_long_context_mla_split_by_the_plan(gu):
+    """One sequence with a 15872-token fp8 cache and a 512-token MLA chunk:
+    64 workgroups, so the plan splits the key axis four ways; sampled rows
+    (first, last, tile edges) match the oracle."""
+    case = gen.make_chunk_case(name="fp8kv_long_mla", seed=91, prefix_lens=[15872], q_lens=[512], Hq=16, Hk=16,
+                               D_rope=64, kv_dtype="e4m3fn")
+    dc = gu.DeviceChunk(case)
+    assert dc.plan.num_splits == 4
+    _run(gu, case, rows=_rows_sample(case, n_mid=32))
