@@ -222,9 +222,15 @@ extern "C" gqap_status gqap_prefill_plan(const gqap_prefill_desc_t* desc, gqap_p
     return fail(GQAP_ERR_INVALID_ARGUMENT, "num_splits must be 0 (automatic) or 1..16 (got %d)", d.num_splits);
   plan->desc = d;
   plan->ratio = d.num_q_heads / d.num_kv_heads;
-  plan->q_tile_rows = 128;
+  // A workgroup takes 128 query rows of one head, or, with a block mask and
+  // heads of a KV group that pair up (Hq / Hk even), 64 rows of two heads of
+  // the group: its two 64-row query blocks would follow different mask rows,
+  // and half its waves would sit out every tile only one block needs, while
+  // the two heads of a pair follow the same row.  Without a mask the two
+  // blocks see nearly the same tiles and 128-row tiles measure faster.
+  plan->q_tile_rows = plan->ratio % 2 == 0 && d.has_block_mask ? 64 : 128;
   plan->q_tiles = (int32_t)ceil_div(d.max_seq_len, plan->q_tile_rows);
-  const int64_t grid = (int64_t)d.num_q_heads * d.batch * plan->q_tiles;
+  const int64_t grid = (int64_t)d.num_q_heads * d.batch * plan->q_tiles * plan->q_tile_rows / 128;
   const int32_t ns = key_splits(d.num_splits, grid, d.max_seq_len, d.num_cus);
   // One workgroup of 256 work-items per (head, sequence, query tile, split)
   // slot; the launch must stay under 2^32 work-items.
@@ -301,11 +307,11 @@ extern "C" gqap_status gqap_chunk_plan(const gqap_chunk_desc_t* desc, gqap_chunk
     return fail(GQAP_ERR_INVALID_ARGUMENT, "pool strides must keep page slabs 16-byte aligned");
   plan->desc = d;
   plan->ratio = d.num_q_heads / d.num_kv_heads;
-  plan->q_tile_rows = 128;
+  plan->q_tile_rows = 128;  // no block mask: one head per workgroup
   plan->q_tiles = (int32_t)ceil_div(d.max_q_len, plan->q_tile_rows);
   if (d.num_splits < 0 || d.num_splits > 16)
     return fail(GQAP_ERR_INVALID_ARGUMENT, "num_splits must be 0 (automatic) or 1..16 (got %d)", d.num_splits);
-  const int64_t grid = (int64_t)d.num_q_heads * d.batch * plan->q_tiles;
+  const int64_t grid = (int64_t)d.num_q_heads * d.batch * plan->q_tiles * plan->q_tile_rows / 128;
   const int32_t ns = key_splits(d.num_splits, grid, d.max_kv_len, 0);
   // One workgroup of 256 work-items per (head, sequence, query tile) slot;
   // the launch must stay under 2^32 work-items.

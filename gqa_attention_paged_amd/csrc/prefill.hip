@@ -10,7 +10,8 @@
 // output has the value width (128).
 //
 // Work split: one workgroup of four waves per (sequence, query head, 128-row
-// query tile); each wave owns 32 query rows.  Key tiles of 64 rows (K, the
+// query tile), or, when Hq / Hk is even, per (sequence, pair of heads of one
+// KV group, 64-row query tile); each wave owns 32 query rows of one head.  Key tiles of 64 rows (K, the
 // shared rope K and V) are staged into XOR-swizzled LDS through registers,
 // double-buffered so the next tile's loads are in flight during the current
 // tile's math.  Scores are formed transposed, S^T = K Q^T, on
@@ -42,6 +43,8 @@ struct PrefillArgs {
   float* lse;
   int64_t q_st, q_sh, k_st, k_sh, v_st, v_sh, kr_st, o_st, o_sh;
   int32_t B, Hq, Hk, ratio, q_tiles, mask_nb, max_len;
+  int32_t hpw;       // heads per workgroup: 1 (128 query rows of one head) or
+                     // 2 (64 rows of two heads of one KV group)
   float scale_log2;  // scale * log2(e)
   // Chunked prefill against the paged cache: k and v are the pools, the
   // query rows of sequence b are the last of its kvlens[b] keys.
@@ -179,15 +182,23 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
   // heads of one KV group share an XCD (workgroup i runs on XCD i % 8).
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int x = blockIdx.x % a.Hq;
-  const int sp = (blockIdx.x / a.Hq) % a.nsplit;   // key-axis split
-  const int pair = blockIdx.x / a.Hq / a.nsplit;
-  const int hpx = a.Hq >> 3;
-  const int h = (a.Hq & 7) ? x : (x & 7) * hpx + (x >> 3);
+  const int wv = tid >> 6;
+  // With hpw = 2 the workgroup's unit is a pair of heads of one KV group,
+  // waves 0-1 taking 64 query rows of the first head and waves 2-3 the same
+  // rows of the second, so that all four waves see the same key tiles.
+  const int NH = a.Hq / a.hpw;                     // workgroups per (query tile, sequence) pair
+  const int QT = 128 / a.hpw;                      // query rows per workgroup and head
+  const int x = blockIdx.x % NH;
+  const int sp = (blockIdx.x / NH) % a.nsplit;     // key-axis split
+  const int pair = blockIdx.x / NH / a.nsplit;
+  const int hpx = NH >> 3;
+  const int hx = (NH & 7) ? x : (x & 7) * hpx + (x >> 3);  // head, or head pair
+  const int h = a.hpw == 2 ? 2 * hx + (wv >> 1) : hx;      // this wave's head
+  const int wslot = a.hpw == 2 ? (wv & 1) : wv;            // this wave's 32-row slot
   int b, qt;
   if (a.B <= 64) {
     int nq = 0;  // query tiles of sequence `lane`
-    if (lane < a.B) nq = (min(a.cu[lane + 1] - a.cu[lane], a.max_len) + 127) >> 7;
+    if (lane < a.B) nq = (min(a.cu[lane + 1] - a.cu[lane], a.max_len) + QT - 1) / QT;
     b = -1;
     qt = -1;
     int before = 0;
@@ -217,14 +228,13 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
     Lk = min(a.kvlens[b], a.max_kv);
     off = Lk - L;
   }
-  const int q0 = qt * 128;
+  const int q0 = qt * QT;
   if (q0 >= L) return;
-  const int g = h / a.ratio;
+  const int g = a.hpw * hx / a.ratio;        // KV head: the same for both heads of a pair
 
-  const int wv = tid >> 6;
   const int l32 = lane & 31;
   const int hh = lane >> 5;
-  const int r0 = q0 + 32 * wv;               // first query row of this wave (local)
+  const int r0 = q0 + 32 * wslot;            // first query row of this wave (local)
   const int qrow = r0 + l32;                 // this lane's query row
   const bool wave_rows = r0 < L;
   const int rlast = min(L, r0 + 32) - 1;     // last valid row of the wave
@@ -271,13 +281,13 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
     }
   }
 
-  // Key tiles this workgroup must visit: keys < min(Lk, off + q0 + 128).
-  const int nkt = max(0, min(Lk, off + q0 + 128) + 63) >> 6;
+  // Key tiles this workgroup must visit: keys < min(Lk, off + q0 + QT).
+  const int nkt = max(0, min(Lk, off + q0 + QT) + 63) >> 6;
   // This workgroup's share of them: tiles [kt_begin, kt_end).
   const int kt_begin = (int)((int64_t)nkt * sp / a.nsplit);
   const int kt_end = (int)((int64_t)nkt * (sp + 1) / a.nsplit);
-  const int qb0 = q0 >> 6;                   // the workgroup's two query blocks
-  const int qb1 = min(qb0 + 1, (L - 1) >> 6);
+  const int qb0 = q0 >> 6;                   // the workgroup's query blocks (one with hpw = 2)
+  const int qb1 = min((q0 + QT - 1) >> 6, (L - 1) >> 6);
   const int wqb = r0 >> 6;                   // this wave's query block
   // Tile schedule as bit words: bit i of word w is key tile 64 w + i.  `need`
   // = loaded by the workgroup (either query block sees it), `see` = this
@@ -1041,6 +1051,7 @@ static PrefillArgs ragged_args(const gqap_prefill_plan_t* plan, const int32_t* c
   a.Hk = d.num_kv_heads;
   a.ratio = plan->ratio;
   a.q_tiles = plan->q_tiles;
+  a.hpw = 128 / plan->q_tile_rows;
   a.mask_nb = d.mask_blocks;
   a.max_len = d.max_seq_len;
   return a;
@@ -1072,7 +1083,7 @@ extern "C" gqap_status gqap_prefill(const gqap_prefill_plan_t* plan, const void*
   a.v = (const uint16_t*)v;
   a.kr = (const uint16_t*)k_rope;
   a.scale_log2 = scale * dev::kLog2e;
-  const dim3 grid((unsigned)d.num_q_heads * (unsigned)d.batch * (unsigned)plan->q_tiles * (unsigned)a.nsplit);
+  const dim3 grid((unsigned)(d.num_q_heads / a.hpw) * (unsigned)d.batch * (unsigned)plan->q_tiles * (unsigned)a.nsplit);
   hipStream_t st = (hipStream_t)stream;
   if (d.head_dim_rope == 64)
     hipLaunchKernelGGL((prefill_fwd<64, false, 0>), grid, dim3(256), 0, st, a);
@@ -1122,7 +1133,7 @@ static gqap_status launch_fp8(const gqap_prefill_plan_t* plan, PrefillArgs& a, v
   const gqap_status ss = split_setup((int32_t)plan->num_splits, d.total_tokens, d.num_q_heads, plan->workspace_bytes,
                                      workspace, workspace_bytes, &a);
   if (ss != GQAP_OK) return ss;
-  const dim3 grid((unsigned)d.num_q_heads * (unsigned)d.batch * (unsigned)plan->q_tiles * (unsigned)a.nsplit);
+  const dim3 grid((unsigned)(d.num_q_heads / a.hpw) * (unsigned)d.batch * (unsigned)plan->q_tiles * (unsigned)a.nsplit);
   hipStream_t st = (hipStream_t)stream;
   if (d.head_dim_rope == 64)
     hipLaunchKernelGGL((prefill_fwd<64, false, F8>), grid, dim3(256), 0, st, a);
@@ -1289,6 +1300,7 @@ static gqap_status chunk_common(const gqap_chunk_plan_t* plan, const void* q, co
   a.Hk = d.num_kv_heads;
   a.ratio = plan->ratio;
   a.q_tiles = plan->q_tiles;
+  a.hpw = 128 / plan->q_tile_rows;
   a.mask_nb = 0;
   a.max_len = d.max_q_len;
   // fp8 cache: the key scale joins the softmax constant when the score is the
@@ -1306,7 +1318,7 @@ static gqap_status chunk_common(const gqap_chunk_plan_t* plan, const void* q, co
   const gqap_status ss = split_setup((int32_t)plan->num_splits, d.total_q_tokens, d.num_q_heads,
                                      plan->workspace_bytes, workspace, workspace_bytes, &a);
   if (ss != GQAP_OK) return ss;
-  const dim3 grid((unsigned)d.num_q_heads * (unsigned)d.batch * (unsigned)plan->q_tiles * (unsigned)a.nsplit);
+  const dim3 grid((unsigned)(d.num_q_heads / a.hpw) * (unsigned)d.batch * (unsigned)plan->q_tiles * (unsigned)a.nsplit);
   hipStream_t st = (hipStream_t)stream;
   if (d.head_dim_rope == 64) {
     if (fp8)

@@ -216,8 +216,18 @@ def baseline_prefill_desc(gq, mla=True):
 def test_prefill_plan_baseline(gq):
     p = gq.gqap_prefill_plan(baseline_prefill_desc(gq))
     assert p.magic == gq.PLAN_MAGIC and p.q_tile_rows == 128 and p.q_tiles == 24 and p.workspace_bytes == 0
-    p = gq.gqap_prefill_plan(baseline_prefill_desc(gq, mla=False))
-    assert p.ratio == 2
+    d = baseline_prefill_desc(gq, mla=False)
+    p = gq.gqap_prefill_plan(d)
+    assert p.ratio == 2 and p.q_tile_rows == 128 and p.q_tiles == 24
+    # with a block mask an even head ratio pairs the heads of a KV group: 64-row query tiles,
+    # the same number of workgroups
+    d.has_block_mask, d.mask_blocks = 1, 47
+    p = gq.gqap_prefill_plan(d)
+    assert p.q_tile_rows == 64 and p.q_tiles == 47
+    d.num_kv_heads = 16                  # ratio 1: no pairs
+    d.k_stride_token, d.v_stride_token = 128 * 16, 128 * 16
+    p = gq.gqap_prefill_plan(d)
+    assert p.q_tile_rows == 128 and p.q_tiles == 24
 
 
 @pytest.mark.parametrize("field,value,status", [

@@ -72,6 +72,18 @@ def test_prefill_ragged_small(gu, rope):
     _check(gu, case)
 
 
+@pytest.mark.parametrize("Hq,Hk,rope", [(4, 2, 0), (16, 2, 0), (8, 4, 64)])
+def test_prefill_head_pairs_with_mask_ragged(gu, Hq, Hk, rope):
+    """A block mask with an even head ratio: each workgroup takes 64 rows of
+    two heads of one KV group.  Sequences shorter than one wave's 32 rows,
+    ends on and off the 32- and 64-row edges, and a mask of density 0.3."""
+    case = gen.make_prefill_case(name=f"pairs_{Hq}_{Hk}_r{rope}", seed=240 + Hq + rope,
+                                 seq_lens=[1, 2, 31, 33, 63, 64, 65, 97, 200, 513], Hq=Hq, Hk=Hk, D_qk=128 + rope,
+                                 D_rope=rope, D_v=128, mask_density=0.3)
+    dp, _, _ = _check(gu, case)
+    assert dp.plan.q_tile_rows == 64
+
+
 def test_prefill_gqa_ratios(gu):
     for Hq, Hk in ((8, 1), (16, 4), (4, 4)):
         case = gen.make_prefill_case(name=f"gqa_{Hq}_{Hk}", seed=210 + Hq, seq_lens=[200, 129], Hq=Hq, Hk=Hk,
