@@ -246,7 +246,10 @@ typedef struct gqap_prefill_plan_t {
   gqap_prefill_desc_t desc;
   int32_t ratio;               /* Hq / Hk */
   int32_t q_tiles;             /* ceil(max_seq_len / q_tile_rows) */
-  int32_t q_tile_rows;
+  int32_t q_tile_rows;         /* query rows per workgroup and head: 128, or 64 when a
+                                  block mask is given and Hq / Hk is even (a workgroup
+                                  then takes two heads of one KV group, so that all its
+                                  waves follow the same mask row) */
   int32_t kernel;
   uint64_t workspace_bytes;    /* 0 unless num_splits > 1 */
   uint32_t magic;
@@ -406,7 +409,7 @@ typedef struct gqap_chunk_plan_t {
   gqap_chunk_desc_t desc;
   int32_t ratio;               /* Hq / Hk */
   int32_t q_tiles;             /* ceil(max_q_len / q_tile_rows) */
-  int32_t q_tile_rows;
+  int32_t q_tile_rows;         /* query rows per workgroup and head: 128 */
   int32_t kernel;
   uint64_t workspace_bytes;    /* 0 unless num_splits > 1 */
   uint32_t magic;
