@@ -10,8 +10,9 @@
 // output has the value width (128).
 //
 // Work split: one workgroup of four waves per (sequence, query head, 128-row
-// query tile), or, when Hq / Hk is even, per (sequence, pair of heads of one
-// KV group, 64-row query tile); each wave owns 32 query rows of one head.  Key tiles of 64 rows (K, the
+// query tile), or, with a block mask and Hq / Hk even, per (sequence, pair of
+// heads of one KV group, 64-row query tile); each wave owns 32 query rows of
+// one head.  Key tiles of 64 rows (K, the
 // shared rope K and V) are staged into XOR-swizzled LDS through registers,
 // double-buffered so the next tile's loads are in flight during the current
 // tile's math.  Scores are formed transposed, S^T = K Q^T, on
@@ -174,23 +175,24 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
   // Blockwise key scales of a tile: one 64-float copy per wave.
   __shared__ __attribute__((aligned(1024))) float sbuf0[F8 == 2 ? 256 : 4], sbuf1[F8 == 2 ? 256 : 4];
 
-  // Work item.  The grid is one-dimensional, Hq workgroups per (query tile,
-  // sequence) pair; pairs are ranked deepest query tile first, then by
-  // sequence, and only pairs that exist (query tile inside its sequence) are
-  // ranked, so all real work precedes the empty tail of the grid and is
-  // spread evenly over the dispatcher's shader engines.  Within a pair the
-  // heads of one KV group share an XCD (workgroup i runs on XCD i % 8).
+  // Work item.  The grid is one-dimensional, Hq / hpw workgroups (times the
+  // key-axis splits) per (query tile, sequence) item; items are ranked
+  // deepest query tile first, then by sequence, and only items that exist
+  // (query tile inside its sequence) are ranked, so all real work precedes
+  // the empty tail of the grid and is spread evenly over the dispatcher's
+  // shader engines.  Within an item the heads of one KV group share an XCD
+  // (workgroup i runs on XCD i % 8).
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
   // With hpw = 2 the workgroup's unit is a pair of heads of one KV group,
   // waves 0-1 taking 64 query rows of the first head and waves 2-3 the same
   // rows of the second, so that all four waves see the same key tiles.
-  const int NH = a.Hq / a.hpw;                     // workgroups per (query tile, sequence) pair
+  const int NH = a.Hq / a.hpw;                     // workgroups per item and split
   const int QT = 128 / a.hpw;                      // query rows per workgroup and head
   const int x = blockIdx.x % NH;
   const int sp = (blockIdx.x / NH) % a.nsplit;     // key-axis split
-  const int pair = blockIdx.x / NH / a.nsplit;
+  const int item = blockIdx.x / NH / a.nsplit;
   const int hpx = NH >> 3;
   const int hx = (NH & 7) ? x : (x & 7) * hpx + (x >> 3);  // head, or head pair
   const int h = a.hpw == 2 ? 2 * hx + (wv >> 1) : hx;      // this wave's head
@@ -205,18 +207,18 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
     for (int t = a.q_tiles - 1; t >= 0; --t) {
       uint64_t m = __ballot(nq > t);
       const int cnt = __builtin_popcountll(m);
-      if (pair < before + cnt) {
-        for (int k = pair - before; k > 0; --k) m &= m - 1;  // drop the lower set bits
+      if (item < before + cnt) {
+        for (int k = item - before; k > 0; --k) m &= m - 1;  // drop the lower set bits
         b = __builtin_ctzll(m);
         qt = t;
         break;
       }
       before += cnt;
     }
-    if (qt < 0) return;  // past the last real pair
+    if (qt < 0) return;  // past the last real item
   } else {
-    b = pair % a.B;
-    qt = a.q_tiles - 1 - pair / a.B;
+    b = item % a.B;
+    qt = a.q_tiles - 1 - item / a.B;
   }
   const int c0 = a.cu[b];
   const int L = min(a.cu[b + 1] - c0, a.max_len);  // query rows (capacity from the plan)
