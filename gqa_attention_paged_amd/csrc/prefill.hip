@@ -249,9 +249,9 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
 
   // The wave's queries as the B operand: lane (query l32, half hh) holds
   // d = 16 s + 8 hh .. +7 for k-step s (s < KSN: nope part, then rope).
-  // With F8 the nope part is instead two 32-byte operands of the fp8 step,
-  // lane (l32, hh) holding codes 64 s + 32 hh .. +31 for step s, and qop
-  // holds only the bf16 rope part, read from its own tensor.
+  // With fp8 Q.K (F8 = 1, 2) the nope part is instead two 32-byte operands
+  // of the fp8 step, lane (l32, hh) holding codes 64 s + 32 hh .. +31 for
+  // step s, and qop holds only the bf16 rope part, read from its own tensor.
   constexpr int NQ = QK8 ? KSR : KSN + KSR;
   bf16x8 qop[NQ > 0 ? NQ : 1];
   i32x8 q8[2];
@@ -575,8 +575,9 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
       i32x4 kf[PF];
       // Without a rope part the matrix phases run at raised wave priority, so
       // that the SIMD's other wave does not delay a wave that feeds the matrix
-      // core (measured: the D = 128 chunked prefill 8 % faster, block-sparse
-      // 1 %; with the rope tile, neutral to 2 % slower, so left out there).
+      // core (measured: the D = 128 chunked prefill about 8 % faster,
+      // block-sparse 1-3 %; with the rope tile neutral to 2 % slower, so left
+      // out there).
       if constexpr (DR == 0) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int i = 0; i < PF; ++i) kf[i] = kfrag(i);
