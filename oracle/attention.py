@@ -272,24 +272,27 @@ def ragged_prefill(
         sel = np.nonzero(seq_of_row == b)[0]
         if sel.size == 0 or c1 == c0:
             continue
-        L = c1 - c0
-        j = np.arange(L)
         for s0 in range(0, sel.size, row_chunk):
             idx = sel[s0:s0 + row_chunk]
             gi = rows[idx]                    # global token ids of these queries
             i = gi - c0                       # local query positions
+            n = idx.size
+            # Keys past the last query of the chunk are causally hidden from
+            # every row of it, so only keys 0 .. max(i) are scored.
+            nk = int(i.max()) + 1
+            j = np.arange(nk)
             vis = j[None, :] <= i[:, None]    # causal: key j visible to query i iff j <= i
             if block_mask is not None:
                 vis &= block_mask[b][(i // BLOCK)[:, None], (j // BLOCK)[None, :]] != 0
             for g in range(Hk):
                 heads = slice(g * r, (g + 1) * r)
-                Qc = Q[gi, heads, :]                        # [n, r, Dqk]
-                s = Qc[:, :, :Dn] @ K[c0:c1, g, :].T        # [n, r, L]
+                Qc = Q[gi, heads, :].reshape(n * r, Dqk)    # the r query heads of KV head g, row-major
+                s = Qc[:, :Dn] @ K[c0:c0 + nk, g, :].T      # [n * r, nk]
                 if KR is not None:
-                    s = s + Qc[:, :, Dn:] @ KR[c0:c1, 0, :].T
-                s = scale * s
+                    s = s + Qc[:, Dn:] @ KR[c0:c0 + nk, 0, :].T
+                s = scale * s.reshape(n, r, nk)
                 s = np.where(vis[:, None, :], s, -np.inf)
-                o, ls = _softmax_attend(s, V[c0:c1, g, :])
+                o, ls = _softmax_attend(s, V[c0:c0 + nk, g, :])
                 out[idx, heads] = o
                 lse[idx, heads] = ls
     return out, lse
@@ -429,15 +432,18 @@ def chunk_prefill(
             heads = slice(g * r, (g + 1) * r)
             for s0 in range(0, sel.size, row_chunk):
                 idx = sel[s0:s0 + row_chunk]
+                n = idx.size
                 i = rows[idx] - cu[b]                      # local query index in the chunk
-                vis = j[None, :] <= (off + i)[:, None]     # bottom-right aligned causal bound
-                Qc = Q[rows[idx], heads, :]                # [n, r, Dqk]
-                s = Qc[:, :, :Dn] @ K.T                     # [n, r, Lk]
+                # keys past off + max(i) are hidden from every row of the chunk
+                nk = max(0, min(Lk, off + int(i.max()) + 1))
+                vis = j[None, :nk] <= (off + i)[:, None]   # bottom-right aligned causal bound
+                Qc = Q[rows[idx], heads, :].reshape(n * r, Dqk)
+                s = Qc[:, :Dn] @ K[:nk].T                  # [n * r, nk]
                 if Dr:
-                    s = s + Qc[:, :, Dn:] @ KR.T
-                s = scale * s
+                    s = s + Qc[:, Dn:] @ KR[:nk].T
+                s = scale * s.reshape(n, r, nk)
                 s = np.where(vis[:, None, :], s, -np.inf)
-                o, ls = _softmax_attend(s, V)
+                o, ls = _softmax_attend(s, V[:nk])
                 out[idx, heads] = o
                 lse[idx, heads] = ls
     return out, lse

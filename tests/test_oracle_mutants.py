@@ -7,6 +7,7 @@ import types
 import pytest
 
 from oracle import attention as O
+from tests import test_oracle_chunk_pins as PC
 from tests import test_oracle_fp8_prefill_pins as P8
 from tests import test_oracle_fp8kv_chunk_pins as PQ
 from tests import test_oracle_pins as P
@@ -31,9 +32,11 @@ MUTANTS = {
     "block_order_reversed": ("phys = np.asarray(block_table[b, :nb], dtype=np.int64)",
                              "phys = np.asarray(block_table[b, :nb][::-1], dtype=np.int64)",
                              [_bf, P.test_gather_follows_page_token_block_mapping]),
-    "rope_term_dropped": ("s = s + Qc[:, :, Dn:] @ KR[c0:c1, 0, :].T", "s = s",
+    "rope_term_dropped": ("s = s + Qc[:, Dn:] @ KR[c0:c0 + nk, 0, :].T", "s = s",
                           [P.test_prefill_mla_matches_sdpa_with_concatenated_rope_key,
                            P.test_prefill_matches_bruteforce_with_rope]),
+    "causal_key_range_short": ("nk = int(i.max()) + 1", "nk = int(i.max())",
+                               [P.test_prefill_gqa_matches_sdpa, P.test_prefill_first_row_returns_its_own_value_row]),
     "causal_strict": ("vis = j[None, :] <= i[:, None]", "vis = j[None, :] < i[:, None]",
                       [P.test_prefill_gqa_matches_sdpa, P.test_prefill_first_row_returns_its_own_value_row]),
     "block_mask_transposed": ("block_mask[b][(i // BLOCK)[:, None], (j // BLOCK)[None, :]]",
@@ -79,6 +82,9 @@ MUTANTS = {
     "fp8kv_v_scale_dropped": ("V = widen(gather_kv_rows(v_pool, block_table, b, g, Lk), kvd) * float(v_scale)",
                               "V = widen(gather_kv_rows(v_pool, block_table, b, g, Lk), kvd)",
                               [PQ.test_fp8_chunk_prefill_matches_bruteforce_on_torch_decoded_pages]),
+    "chunk_key_range_short": ("off + int(i.max()) + 1))", "off + int(i.max())))",
+                              [PC.test_chunk_prefill_matches_sdpa_with_offset_mask,
+                               PC.test_chunk_first_query_of_a_new_sequence_returns_its_value_row]),
     "fp8_rope_dropped": ('np.concatenate([q, widen(q_rope, "bf16")], axis=2)',
                          'np.concatenate([q, 0 * widen(q_rope, "bf16")], axis=2)',
                          [P8.test_fp8_prefill_matches_sdpa_with_concatenated_rope_key]),
@@ -92,6 +98,7 @@ def test_planted_mistake_is_caught(name, monkeypatch):
     monkeypatch.setattr(P, "O", mutant)
     monkeypatch.setattr(P8, "O", mutant)
     monkeypatch.setattr(PQ, "O", mutant)
+    monkeypatch.setattr(PC, "O", mutant)
     caught = []
     for fn in catchers:
         try:
