@@ -315,6 +315,49 @@ def cpu_baseline_decode(case, budget_s: float = 12.0):
             "sample": f"{reps} full fp64 decode pass(es) over the same {case.B}-sequence workload, {dt:.1f} s"}
 
 
+def cpu_baseline_full(case):
+    """One full evaluation of the oracle, as it is, on the host for a secondary
+    workload: every sequence (decode) or every row (prefill, chunked prefill:
+    the append and the attention), cut into pieces that run in worker threads
+    with one BLAS thread each.  Reported in the workload's own unit, from the
+    same numerator as the GPU figure."""
+    from oracle import attention as O
+    from oracle import parallel as OP
+    from workloads import gen
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    t0 = time.perf_counter()
+    if isinstance(case, gen.DecodeCase):
+        OP.all_batches(lambda bb: O.paged_decode(case.q, case.k_pool, case.v_pool, case.block_table, case.seq_lens,
+                                                 case.scale, q_dtype=case.q_dtype, kv_dtype=case.kv_dtype,
+                                                 k_scale=case.k_scale, v_scale=case.v_scale, batches=bb),
+                       case.B, workers=workers)
+        dt = time.perf_counter() - t0
+        return {"value": case.kv_bytes() / dt / 1e9, "unit": "GB/s", "cores": workers, "kind": "oracle",
+                "sample": f"one full fp64 decode of all {case.B} sequences, {dt:.1f} s"}
+    if isinstance(case, gen.ChunkCase):
+        fp8 = dict(kv_dtype=case.kv_dtype, k_scale=case.k_scale, v_scale=case.v_scale)
+        pools = O.append_kv(case.k_new, case.v_new, case.k_pool, case.v_pool, case.block_table,
+                            case.cu_seqlens_q, case.kv_lens, kr_new=case.kr_new, kr_pool=case.kr_pool, **fp8)
+        OP.all_rows(lambda rr: O.chunk_prefill(case.q, pools[0], pools[1], case.block_table, case.cu_seqlens_q,
+                                               case.kv_lens, case.scale, dtype="bf16", rows=rr,
+                                               kr_pool=pools[2] if len(pools) == 3 else None, **fp8),
+                    case.T, block=64, workers=workers)
+        what = f"one full fp64 append and chunked prefill of all {case.T} query rows"
+    elif case.dtype == "e4m3fn":
+        OP.all_rows(lambda rr: O.ragged_prefill_fp8(case.q, case.q_rope, case.k, case.v, case.k_rope,
+                                                    case.cu_seqlens, case.scale, case.q_scale, case.k_scale,
+                                                    block_mask=case.block_mask, rows=rr), case.T, workers=workers)
+        what = f"one full fp64 prefill of all {case.T} rows"
+    else:
+        OP.all_rows(lambda rr: O.ragged_prefill(case.q, case.k, case.v, case.cu_seqlens, case.scale,
+                                                k_rope=case.k_rope, block_mask=case.block_mask, dtype="bf16",
+                                                rows=rr), case.T, workers=workers)
+        what = f"one full fp64 prefill of all {case.T} rows"
+    dt = time.perf_counter() - t0
+    return {"value": case.flops() / dt / 1e12, "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
+            "sample": f"{what}, {dt:.1f} s"}
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -348,7 +391,7 @@ def main(argv=None) -> int:
 
     import torch
     import gqa_attention_paged_amd as gq
-    from tests import gpu_util as gu
+    from workloads import device as gu
     from workloads import gen
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
@@ -379,6 +422,7 @@ def main(argv=None) -> int:
         r4["roofline"] = {"bound": "hbm", "achieved": r4["gbs_kernel"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                           "frac": r4["gbs_kernel"] / HBM_PEAK_GBS,
                           "traffic": _traffic("decode_long_fp8")}
+        r4["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline_full(c4)
         secondary.append(r4)
         del c4
         if hasattr(gu, "DevicePrefill"):
@@ -390,6 +434,7 @@ def main(argv=None) -> int:
                 rp["roofline"] = {"bound": "mfma", "achieved": rp["tflops_kernel"], "peak": round(peak, 1),
                                   "unit": "TFLOP/s", "frac": rp["tflops_kernel"] / peak,
                                   "traffic": _traffic(pc.name)}
+                rp["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline_full(pc)
                 secondary.append(rp)
                 del pc
         if hasattr(gu, "DeviceChunk"):
@@ -402,6 +447,7 @@ def main(argv=None) -> int:
                 rc["roofline"] = {"bound": "mfma", "achieved": rc["tflops_kernel"], "peak": BF16_MFMA_PEAK_TFLOPS,
                                   "unit": "TFLOP/s", "frac": rc["tflops_kernel"] / BF16_MFMA_PEAK_TFLOPS,
                                   "traffic": _traffic(cc.name)}
+                rc["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline_full(cc)
                 secondary.append(rc)
                 del cc
 

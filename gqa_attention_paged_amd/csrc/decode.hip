@@ -50,7 +50,7 @@ struct DecodeArgs {
   int64_t q_sb, q_sh, o_sb, o_sh;
   int64_t kv_block_bytes, kv_head_bytes, bt_stride;
   int32_t B, Hq, Hk, ratio, head_chunks, hkhc, nworkers;
-  int32_t max_len;  // capacity from the plan; longer seq_lens are clamped to it
+  int32_t max_len;  // capacity from the plan; a longer (or negative) seq_len empties the sequence
   float score_scale_log2;  // scale * k_scale * log2(e)
   float score_scale;       // scale * k_scale
   float v_scale;
@@ -65,8 +65,12 @@ __device__ __forceinline__ int ld_const(const int32_t* p, int64_t i) {
   return ((const int32_t __attribute__((address_space(4)))*)p)[i];
 }
 
-__device__ __forceinline__ int clamp_len(const DecodeArgs& a, int b) {
-  return min(max(ld_const(a.seq_lens, b), 0), a.max_len);
+// Keys of sequence b.  A length outside [0, max_len] (the capacity the plan
+// was made for) is not truncated: the sequence is treated as empty, so its
+// rows come out as 0 with lse = -inf, the same whatever the length was.
+__device__ __forceinline__ int valid_len(const DecodeArgs& a, int b) {
+  const int L = ld_const(a.seq_lens, b);
+  return (L < 0 || L > a.max_len) ? 0 : L;
 }
 
 // Position of one work unit.
@@ -79,10 +83,10 @@ struct Unit {
   int phys;  // pool block holding block j
 };
 
-__device__ __forceinline__ int seq_blocks(const DecodeArgs& a, int b) { return (clamp_len(a, b) + 63) >> 6; }
+__device__ __forceinline__ int seq_blocks(const DecodeArgs& a, int b) { return (valid_len(a, b) + 63) >> 6; }
 
 __device__ __forceinline__ void unit_load_seq(const DecodeArgs& a, Unit& u) {
-  u.L = clamp_len(a, u.b);
+  u.L = valid_len(a, u.b);
   u.nblk = (u.L + 63) >> 6;
 }
 
@@ -869,7 +873,8 @@ extern "C" gqap_status gqap_block_table_from_csr(const int32_t* kv_indices, cons
   if (misaligned(kv_indices, 4) || misaligned(kv_page_indptr, 4) || misaligned(block_table, 4))
     return fail(GQAP_ERR_INVALID_ARGUMENT, "index arrays must be 4-byte aligned");
   const int64_t n = (int64_t)batch * max_blocks_per_seq;
-  if (n >= ((int64_t)1 << 39)) return fail(GQAP_ERR_UNSUPPORTED, "block table too large for one launch");
+  if (n > kMaxLaunchItems) return fail(GQAP_ERR_UNSUPPORTED, "block table of %lld entries too large for one launch",
+                                       (long long)n);
   hipLaunchKernelGGL(block_table_from_csr, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, (hipStream_t)stream,
                      kv_indices, kv_page_indptr, batch, max_blocks_per_seq, block_table_stride, block_table);
   const hipError_t e = hipGetLastError();

@@ -90,6 +90,11 @@ static gqap_status check_decode_desc(const gqap_decode_desc_t& d, int* q_esz, in
                 d.max_blocks_per_seq);
   if (d.num_workers < 0 || d.num_workers > (1 << 20))
     return fail(GQAP_ERR_INVALID_ARGUMENT, "num_workers must be in [0, 2^20]");
+  // The combine launches one 64-lane wave per (sequence, query head); a
+  // launch holds fewer than 2^32 work-items.
+  if ((int64_t)d.batch * d.num_q_heads * 64 > kMaxLaunchItems)
+    return fail(GQAP_ERR_UNSUPPORTED, "batch * Hq = %lld (sequence, head) pairs exceed one combine launch",
+                (long long)d.batch * d.num_q_heads);
   if (d.num_cus < 0) return fail(GQAP_ERR_INVALID_ARGUMENT, "num_cus must be >= 0");
   return GQAP_OK;
 }
@@ -229,7 +234,9 @@ extern "C" gqap_status gqap_prefill_plan(const gqap_prefill_desc_t* desc, gqap_p
   // the two heads of a pair follow the same row.  Without a mask the two
   // blocks see nearly the same tiles and 128-row tiles measure faster.
   plan->q_tile_rows = plan->ratio % 2 == 0 && d.has_block_mask ? 64 : 128;
-  plan->q_tiles = (int32_t)ceil_div(d.max_seq_len, plan->q_tile_rows);
+  // At least one query tile per sequence, so that a sequence longer than the
+  // capacity always has a workgroup to clear its rows past max_seq_len.
+  plan->q_tiles = (int32_t)std::max<int64_t>(d.batch > 0 ? 1 : 0, ceil_div(d.max_seq_len, plan->q_tile_rows));
   const int64_t grid = (int64_t)d.num_q_heads * d.batch * plan->q_tiles * plan->q_tile_rows / 128;
   const int32_t ns = key_splits(d.num_splits, grid, d.max_seq_len, d.num_cus);
   // One workgroup of 256 work-items per (head, sequence, query tile, split)
@@ -238,6 +245,10 @@ extern "C" gqap_status gqap_prefill_plan(const gqap_prefill_desc_t* desc, gqap_p
     return fail(GQAP_ERR_UNSUPPORTED,
                 "Hq * batch * ceil(max_seq_len/128) * num_splits = %lld workgroups exceeds 2^24",
                 (long long)(grid * ns));
+  // The split merge runs one 64-lane wave per (token, head).
+  if (ns > 1 && (int64_t)d.total_tokens * d.num_q_heads * 64 > kMaxLaunchItems)
+    return fail(GQAP_ERR_UNSUPPORTED, "T * Hq = %lld (token, head) pairs exceed one split-merge launch",
+                (long long)d.total_tokens * d.num_q_heads);
   plan->kernel = (mla ? 2 : 1) + (f8 ? 2 : 0);
   plan->num_splits = (uint32_t)ns;
   plan->workspace_bytes = split_workspace(ns, d.total_tokens, d.num_q_heads);
@@ -308,7 +319,8 @@ extern "C" gqap_status gqap_chunk_plan(const gqap_chunk_desc_t* desc, gqap_chunk
   plan->desc = d;
   plan->ratio = d.num_q_heads / d.num_kv_heads;
   plan->q_tile_rows = 128;  // no block mask: one head per workgroup
-  plan->q_tiles = (int32_t)ceil_div(d.max_q_len, plan->q_tile_rows);
+  // At least one query tile per sequence (see the prefill plan).
+  plan->q_tiles = (int32_t)std::max<int64_t>(d.batch > 0 ? 1 : 0, ceil_div(d.max_q_len, plan->q_tile_rows));
   if (d.num_splits < 0 || d.num_splits > 16)
     return fail(GQAP_ERR_INVALID_ARGUMENT, "num_splits must be 0 (automatic) or 1..16 (got %d)", d.num_splits);
   const int64_t grid = (int64_t)d.num_q_heads * d.batch * plan->q_tiles * plan->q_tile_rows / 128;
@@ -318,6 +330,13 @@ extern "C" gqap_status gqap_chunk_plan(const gqap_chunk_desc_t* desc, gqap_chunk
   if (grid * ns >= ((int64_t)1 << 24))
     return fail(GQAP_ERR_UNSUPPORTED, "Hq * batch * ceil(max_q_len/128) * num_splits = %lld workgroups exceeds 2^24",
                 (long long)(grid * ns));
+  if (ns > 1 && (int64_t)d.total_q_tokens * Hq * 64 > kMaxLaunchItems)
+    return fail(GQAP_ERR_UNSUPPORTED, "T * Hq = %lld (token, head) pairs exceed one split-merge launch",
+                (long long)d.total_q_tokens * Hq);
+  // The append runs one work-item per 16-byte piece of a (token, KV head) row.
+  if ((int64_t)d.total_q_tokens * Hk * (D / 8) > kMaxLaunchItems)
+    return fail(GQAP_ERR_UNSUPPORTED, "T * Hk = %lld (token, KV head) rows exceed one append launch",
+                (long long)d.total_q_tokens * Hk);
   plan->kernel = (Dr ? 2 : 1) + (kv_esz == 1 ? 2 : 0);
   plan->num_splits = (uint32_t)ns;
   plan->workspace_bytes = split_workspace(ns, d.total_q_tokens, d.num_q_heads);

@@ -197,10 +197,16 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
   const int hx = (NH & 7) ? x : (x & 7) * hpx + (x >> 3);  // head, or head pair
   const int h = a.hpw == 2 ? 2 * hx + (wv >> 1) : hx;      // this wave's head
   const int wslot = a.hpw == 2 ? (wv & 1) : wv;            // this wave's 32-row slot
+  // Query tiles of a sequence of Lq query rows: those of its first max_len
+  // rows, and all of the plan's tiles when it is longer (the last of them
+  // then also clears the rows past the capacity).
+  auto item_tiles = [&](int Lq) {
+    return Lq <= 0 ? 0 : Lq > a.max_len ? a.q_tiles : (Lq + QT - 1) / QT;
+  };
   int b, qt;
   if (a.B <= 64) {
     int nq = 0;  // query tiles of sequence `lane`
-    if (lane < a.B) nq = (min(a.cu[lane + 1] - a.cu[lane], a.max_len) + QT - 1) / QT;
+    if (lane < a.B) nq = item_tiles(a.cu[lane + 1] - a.cu[lane]);
     b = -1;
     qt = -1;
     int before = 0;
@@ -221,14 +227,31 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
     qt = a.q_tiles - 1 - item / a.B;
   }
   const int c0 = a.cu[b];
-  const int L = min(a.cu[b + 1] - c0, a.max_len);  // query rows (capacity from the plan)
+  const int Lq = a.cu[b + 1] - c0;             // query rows of the sequence
+  const int nqb = item_tiles(Lq);
+  if (qt >= nqb) return;
+  int L = min(Lq, a.max_len);                  // rows computed: those within the plan's capacity
   // Keys: the sequence itself, or with PAGED its Lk cached keys, the query
-  // rows being the last L of them (offset off = Lk - L), so query i sees key
-  // j iff j <= off + i.
+  // rows being the last Lq of them (offset off = Lk - Lq), so query i sees
+  // key j iff j <= off + i.  A chunk whose keys exceed the capacity, or that
+  // is longer than its keys, has no row computed.
   int Lk = L, off = 0;
   if constexpr (PAGED) {
-    Lk = min(a.kvlens[b], a.max_kv);
-    off = Lk - L;
+    Lk = a.kvlens[b];
+    if (Lk > a.max_kv || Lk < Lq) L = Lk = 0;
+    off = Lk - Lq;
+  }
+  // Rows that are not computed get out = 0 and lse = -inf, written once, by
+  // split 0 of the sequence's last query tile, for the workgroup's heads.
+  if (Lq > L && sp == 0 && qt == nqb - 1) {
+    const int64_t pieces = (int64_t)(Lq - L) * a.hpw * 16;  // 16-byte pieces of 256-byte rows
+    for (int64_t e = tid; e < pieces; e += 256) {
+      const int64_t rh = e >> 4;
+      const int row = L + (int)(rh / a.hpw);
+      const int hz = a.hpw * hx + (int)(rh % a.hpw);
+      store16(a.out + (int64_t)(c0 + row) * a.o_st + (int64_t)hz * a.o_sh + 8 * (e & 15), i32x4{0, 0, 0, 0});
+      if (a.lse && (e & 15) == 0) a.lse[(int64_t)(c0 + row) * a.Hq + hz] = -INFINITY;
+    }
   }
   const int q0 = qt * QT;
   if (q0 >= L) return;
@@ -306,7 +329,8 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
       const bool v0 = kt <= qb0 && mb[(int64_t)qb0 * a.mask_nb + kt];
       const bool v1 = kt <= qb1 && mb[(int64_t)qb1 * a.mask_nb + kt];
       need = v0 || v1;
-      see = kt <= wqb && mb[(int64_t)wqb * a.mask_nb + kt];
+      // (a wave whose rows all lie past the sequence end has no mask row)
+      see = wave_rows && kt <= wqb && mb[(int64_t)wqb * a.mask_nb + kt];
     }
     need_word = __ballot(need);
     see_word = __ballot(see);
@@ -861,10 +885,11 @@ struct MergeArgs {
   const float* ws_o;
   const float* ws_lse;
   const int32_t* cu;
+  const int32_t* kvlens;  // chunked prefill: keys per sequence, else null
   uint16_t* out;
   float* lse;
   int64_t o_st, o_sh;
-  int32_t T, Hq, B, nsplit, max_len;
+  int32_t T, Hq, B, nsplit, max_len, max_kv;
 };
 
 __global__ __launch_bounds__(256) void prefill_merge(MergeArgs a) {
@@ -880,6 +905,10 @@ __global__ __launch_bounds__(256) void prefill_merge(MergeArgs a) {
     if (a.cu[mid] <= row) lo = mid; else hi = mid;
   }
   if (row - a.cu[lo] >= a.max_len) return;
+  if (a.kvlens) {  // a chunk outside the capacity was cleared by the attention kernel
+    const int kl = a.kvlens[lo];
+    if (kl > a.max_kv || kl < a.cu[lo + 1] - a.cu[lo]) return;
+  }
   const int64_t sstride = (int64_t)a.T * a.Hq;
   // Up to four splits (all the plan chooses by itself): every LSE and row is
   // requested before the first is used, so the merge costs one memory round
@@ -970,8 +999,9 @@ __global__ __launch_bounds__(256) void append_kv(AppendArgs a) {
     if (a.cu[mid] <= t) lo = mid; else hi = mid;
   }
   const int b = lo;
-  const int p = a.kvlens[b] - (a.cu[b + 1] - a.cu[b]) + (t - a.cu[b]);
-  if (p < 0 || p >= a.max_kv) return;  // outside the keys the plan covers
+  const int kl = a.kvlens[b], ql = a.cu[b + 1] - a.cu[b];
+  if (kl > a.max_kv || kl < ql) return;  // a chunk outside the plan's capacity writes nothing
+  const int p = kl - ql + (t - a.cu[b]);
   const int64_t page = a.bt[(int64_t)b * a.bt_st + (p >> 6)];
   const int64_t dst = page * a.kv_sb + (int64_t)g * a.kv_sh + (int64_t)(p & 63) * D + 8 * piece;
   const int64_t src = (int64_t)t * a.new_st + (int64_t)g * a.new_sh + 8 * piece;
@@ -1027,6 +1057,8 @@ static gqap_status launch_merge(const PrefillArgs& a, int32_t max_len, hipStream
   m.B = a.B;
   m.nsplit = a.nsplit;
   m.max_len = max_len;
+  m.kvlens = a.kvlens;
+  m.max_kv = a.max_kv;
   const int64_t blocks = ((int64_t)a.T * a.Hq + 3) / 4;
   if (blocks == 0) return GQAP_OK;
   hipLaunchKernelGGL(prefill_merge, dim3((unsigned)blocks), dim3(256), 0, st, m);
@@ -1237,8 +1269,8 @@ static gqap_status append_common(const gqap_chunk_plan_t* plan, const void* k_ne
   a.max_kv = d.max_kv_len;
   a.k_scale = k_scale;
   a.v_scale = v_scale;
+  if (a.rows * 16 > kMaxLaunchItems) return fail(GQAP_ERR_UNSUPPORTED, "chunk too large for one append launch");
   const int64_t blocks = (a.rows * 16 + 255) / 256;
-  if (blocks >= ((int64_t)1 << 31)) return fail(GQAP_ERR_UNSUPPORTED, "chunk too large for one append launch");
   if (fp8)
     hipLaunchKernelGGL(append_kv<true>, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, a);
   else

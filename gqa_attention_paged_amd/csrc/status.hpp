@@ -25,6 +25,8 @@ inline gqap_status fail(gqap_status st, const char* fmt, ...) {
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 constexpr int kBlock = GQAP_BLOCK_SIZE;
+// Work-items one launch may hold (grid x workgroup size stays below 2^32).
+constexpr int64_t kMaxLaunchItems = ((int64_t)1 << 32) - 256;
 constexpr int kDefaultCUs = 256;
 
 // Kernel variants recorded in a decode plan.

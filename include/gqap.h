@@ -86,7 +86,10 @@ typedef enum gqap_dtype {
  *                                      [b, j] is the pool block holding logical
  *                                      tokens 64j .. 64j+63 of sequence b; only
  *                                      entries j < ceil(seq_lens[b] / 64) are read.
- *   seq_lens     [B] int32             0 <= seq_lens[b] <= min(Nblk*64, max_seq_len).
+ *   seq_lens     [B] int32             0 <= seq_lens[b] <= min(Nblk*64, max_seq_len);
+ *                                      a length outside [0, max_seq_len] is
+ *                                      not truncated: that sequence is treated
+ *                                      as empty (out = 0, lse = -inf).
  *   out          [B, Hq, D]            dtype q_dtype; strides out_stride_*.
  *   lse          [B, Hq] float32       optional, contiguous, natural log.
  * Query head h reads KV head h / (Hq / Hk).  The decode query is the newest
@@ -151,7 +154,7 @@ typedef struct gqap_decode_plan_t {
  * Errors: INVALID_ARGUMENT (non-positive sizes, Hq % Hk != 0, max_seq_len >
  * Nblk*64, strides that overlap or break 16-byte alignment, bad num_workers),
  * DTYPE (dtype pair not in the list above), UNSUPPORTED (block_size != 64,
- * head_dim not 64/128, F16).
+ * head_dim not 64/128, F16, batch * Hq * 64 >= 2^32: one combine launch).
  */
 gqap_status gqap_decode_plan(const gqap_decode_desc_t* desc, gqap_decode_plan_t* plan);
 
@@ -281,15 +284,20 @@ typedef struct gqap_prefill_plan_t {
  * Validate a prefill request.  Pure host code.  Errors: INVALID_ARGUMENT
  * (sizes, strides, Hq % Hk, mask_blocks too small), DTYPE (not bf16 or fp8),
  * UNSUPPORTED (causal == 0, head widths other than 128/192 with rope 0/64,
- * Dv != 128, or Hq * batch * ceil(max_seq_len/128) * num_splits >= 2^24
- * workgroups); INVALID_ARGUMENT also for num_splits outside 0..16.
+ * Dv != 128, Hq * batch * ceil(max_seq_len/128) * num_splits >= 2^24
+ * workgroups, or with splits T * Hq * 64 >= 2^32: one merge launch);
+ * INVALID_ARGUMENT also for num_splits outside 0..16.  A plan with batch > 0
+ * has q_tiles >= 1 (the last query tile of a sequence clears its rows past
+ * the capacity).
  */
 gqap_status gqap_prefill_plan(const gqap_prefill_desc_t* desc, gqap_prefill_plan_t* plan);
 
 /*
  * Ragged causal prefill.  All device pointers 16-byte aligned.  workspace may
  * be NULL when plan->workspace_bytes == 0.  Asynchronous on `stream`.
- * Sequences longer than the plan's max_seq_len are truncated to it.  Only
+ * Capacity: the rows of a sequence past the plan's max_seq_len are not
+ * computed; they get out = 0 and lse = -inf (the rows below it are exact,
+ * since a causal row never sees a later key).  Only
  * rows inside each sequence are read: a key tile that runs past the end
  * repeats the sequence's last row, whose probability is then exactly 0, so
  * K/V are expected to be finite (an infinite value in a sequence's last V
@@ -422,8 +430,15 @@ typedef struct gqap_chunk_plan_t {
  * Hq % Hk, max_kv_len > Nblk * 64, max_q_len > max_kv_len), DTYPE (dtype
  * not bf16, kv_dtype not 0, bf16 or fp8 e4m3fn),
  * UNSUPPORTED (block_size != 64, D != 128, Dr not 0 or 64, Hq * batch *
- * ceil(max_q_len / 128) * num_splits >= 2^24 workgroups); INVALID_ARGUMENT
+ * ceil(max_q_len / 128) * num_splits >= 2^24 workgroups, T * Hk * 16 >= 2^32
+ * (one append launch), with splits T * Hq * 64 >= 2^32); INVALID_ARGUMENT
  * also for num_splits outside 0..16.  Key-axis splits as for the prefill.
+ *
+ * Capacity (both calls below): a chunk whose kv_lens[b] exceeds max_kv_len,
+ * or is smaller than its own length q_len_b, is outside the plan: it is not
+ * appended and all its rows get out = 0 and lse = -inf.  A chunk longer than
+ * max_q_len keeps its causal offset kv_lens[b] - q_len_b; its first max_q_len
+ * rows are computed and the rest get out = 0 and lse = -inf.
  */
 gqap_status gqap_chunk_plan(const gqap_chunk_desc_t* desc, gqap_chunk_plan_t* plan);
 
@@ -504,14 +519,19 @@ gqap_status gqap_chunk_prefill_fp8kv(const gqap_chunk_plan_t* plan, const void* 
  * kv_indices[kv_page_indptr[b] .. kv_page_indptr[b+1]), in order.  Writes
  * block_table[b, j] = kv_indices[kv_page_indptr[b] + j] for j < min(pages of b,
  * max_blocks_per_seq) and -1 for the rest of the row up to max_blocks_per_seq
- * (pages past the row width are not represented).  With it, every call that
- * takes a block table also takes CSR page input.
+ * (pages past the row width are not represented).  The page's own builder
+ * pads with 0 into a table as wide as the longest page list; here the width
+ * is the caller's and the padding -1, which no valid page id equals, so a
+ * stray read of padding cannot alias block 0.  No attention call reads
+ * padding entries, so results do not depend on the choice.  With it, every
+ * call that takes a block table also takes CSR page input.
  *   kv_indices      [total pages] int32 device
  *   kv_page_indptr  [batch + 1] int32 device, non-decreasing, starting at 0
  *   block_table     [batch, >= max_blocks_per_seq] int32 device, row stride
  *                   block_table_stride (elements), written
  * Errors: INVALID_ARGUMENT (null pointer, batch < 0, max_blocks_per_seq < 1,
- * block_table_stride < max_blocks_per_seq, misaligned pointer), HIP.
+ * block_table_stride < max_blocks_per_seq, misaligned pointer), UNSUPPORTED
+ * (batch * max_blocks_per_seq >= 2^32 entries: one launch), HIP.
  * Asynchronous on `stream`.
  */
 gqap_status gqap_block_table_from_csr(const int32_t* kv_indices, const int32_t* kv_page_indptr, int32_t batch,

@@ -546,3 +546,55 @@ def test_split_calls_require_the_workspace(gq):
     for ws, wsb in ((None, 0), (fake, p.workspace_bytes - 16), (fake + 8, p.workspace_bytes)):
         st = call(ctypes.byref(p), fake, fake, fake, fake, fake, None, 1.0, fake, None, ws, wsb, None)
         assert gq.STATUS_NAMES[st] == "INVALID_ARGUMENT" and "workspace" in gq.gqap_last_error()
+
+
+# ---------------------------------------------------------------- launch-size limits
+
+def test_plans_reject_launches_past_2_to_the_32_work_items(gq):
+    """Every launch stays under 2^32 work-items: the decode combine (one wave
+    per sequence and query head), the split merge (one wave per token and
+    head) and the append (one work-item per 16 bytes of a token's K/V row)."""
+    lib = gq.lib()
+    d = baseline_decode_desc(gq)
+    d.batch, d.num_q_heads, d.num_kv_heads = 65535, 1025, 1
+    d.q_stride_batch = d.out_stride_batch = 1025 * 128
+    d.kv_stride_block = 64 * 128
+    st = lib.gqap_decode_plan(ctypes.byref(d), ctypes.byref(gq.DecodePlan()))
+    assert gq.STATUS_NAMES[st] == "UNSUPPORTED" and "combine" in gq.gqap_last_error()
+    d.num_q_heads = 1024                           # 65535 x 1024 x 64 < 2^32
+    d.q_stride_batch = d.out_stride_batch = 1024 * 128
+    assert gq.gqap_decode_plan(d).magic == gq.PLAN_MAGIC
+
+    p = baseline_prefill_desc(gq)                  # 16 heads
+    p.total_tokens = (1 << 22) + 1                 # T x 16 x 64 > 2^32 once the merge runs
+    p.num_splits = 2
+    st = lib.gqap_prefill_plan(ctypes.byref(p), ctypes.byref(gq.PrefillPlan()))
+    assert gq.STATUS_NAMES[st] == "UNSUPPORTED" and "merge" in gq.gqap_last_error()
+    p.num_splits = 1                               # no merge: accepted
+    assert gq.gqap_prefill_plan(p).magic == gq.PLAN_MAGIC
+
+    c = baseline_chunk_desc(gq)                    # Hk = 8: 16 work-items per (token, KV head)
+    c.total_q_tokens = (1 << 25)                   # 2^25 x 8 x 16 = 2^32
+    st = lib.gqap_chunk_plan(ctypes.byref(c), ctypes.byref(gq.ChunkPlan()))
+    assert gq.STATUS_NAMES[st] == "UNSUPPORTED" and "append" in gq.gqap_last_error()
+    c.total_q_tokens = (1 << 25) - 2
+    assert gq.gqap_chunk_plan(c).magic == gq.PLAN_MAGIC
+
+    # the CSR conversion: one work-item per table entry
+    st = lib.gqap_block_table_from_csr(16, 16, 65536, 65536, 65536, 16, None)
+    assert gq.STATUS_NAMES[st] == "UNSUPPORTED"
+
+
+def test_plans_keep_one_query_tile_for_rows_past_the_capacity(gq):
+    """A sequence longer than max_seq_len has its rows past the capacity
+    cleared by the last query tile's workgroup, so a plan with batch > 0
+    always has at least one query tile, even for max_seq_len = 0."""
+    d = baseline_prefill_desc(gq)
+    d.max_seq_len = 0
+    p = gq.gqap_prefill_plan(d)
+    assert p.q_tiles == 1 and p.num_splits == 1
+    d.batch = 0
+    assert gq.gqap_prefill_plan(d).q_tiles == 0
+    c = baseline_chunk_desc(gq)
+    c.max_q_len = 0
+    assert gq.gqap_chunk_plan(c).q_tiles == 1

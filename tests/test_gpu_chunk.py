@@ -12,11 +12,13 @@ import pytest
 import torch
 
 from oracle import attention as O
+from oracle import parallel as OR
 from workloads import gen
 
 pytestmark = pytest.mark.gpu
 
 TOL = 2e-2
+LSE_TOL = 1e-3   # the LSE is fp32 end to end; one dropped 64-key tile moves it by ~1e-2
 
 
 @pytest.fixture(scope="module")
@@ -55,20 +57,32 @@ def _run(gu, case, rows=None, tol=TOL):
     kp, vp = pools[0], pools[1]
     dc.run()
     out, lse = dc.results()
-    ref, ref_lse = O.chunk_prefill(case.q, kp, vp, case.block_table, case.cu_seqlens_q, case.kv_lens, case.scale,
-                                   dtype="bf16", rows=rows, kr_pool=pools[2] if len(pools) == 3 else None)
-    if rows is not None:
+    ref_fn = lambda rr: O.chunk_prefill(case.q, kp, vp, case.block_table, case.cu_seqlens_q,  # noqa: E731
+                                        case.kv_lens, case.scale, dtype="bf16", rows=rr,
+                                        kr_pool=pools[2] if len(pools) == 3 else None)
+    if rows is None:
+        ref, ref_lse = OR.all_rows(ref_fn, case.T, block=128)
+    else:
+        ref, ref_lse = ref_fn(rows)
         out, lse = out[rows], lse[rows]
     e_out = gu.max_abs_err(out, ref)
     e_lse = gu.lse_err(lse, ref_lse)
-    gu.announce(f"  max-abs-err out {e_out:.3e} lse {e_lse:.3e} (tol {tol:g}) rows={'all' if rows is None else len(rows)}")
-    assert e_out <= tol and e_lse <= tol, (e_out, e_lse)
+    gu.announce(f"  max-abs-err out {e_out:.3e} lse {e_lse:.3e} (tol {tol:g}, lse {LSE_TOL:g}) "
+                f"rows={'all' if rows is None else len(rows)}")
+    assert e_out <= tol and e_lse <= LSE_TOL, (e_out, e_lse)
     return dc, out, lse
 
 
-def test_chunk_config_full_size_sampled(gu):
-    case = gen.prefill_chunk_bf16()
-    _run(gu, case, rows=_rows_sample(case))
+def test_chunk_config_full_size(gu):
+    """Every row and head of the chunked-prefill workload (8 x 512-token chunks
+    over 1024..6144-token cached prefixes, 32 query heads)."""
+    _run(gu, gen.prefill_chunk_bf16())
+
+
+def test_mla_chunk_config_full_size(gu):
+    """Every row and head of the MLA chunked-prefill workload (rope keys from
+    the paged rope cache)."""
+    _run(gu, gen.prefill_chunk_mla_bf16())
 
 
 @pytest.mark.parametrize("Hq,Hk", [(8, 8), (8, 2), (16, 1)])
@@ -94,7 +108,7 @@ def test_one_token_chunks_equal_decode(gu):
     kp, vp = dc.pools_bits()[:2]
     ref, ref_lse = O.paged_decode(case.q, kp, vp, case.block_table, case.kv_lens, case.scale, q_dtype="bf16",
                                   kv_dtype="bf16")
-    assert gu.max_abs_err(out, ref) <= TOL and gu.lse_err(lse, ref_lse) <= TOL
+    assert gu.max_abs_err(out, ref) <= TOL and gu.lse_err(lse, ref_lse) <= LSE_TOL
 
 
 def test_two_chunks_equal_one_prefill(gu):
@@ -131,7 +145,7 @@ def test_two_chunks_equal_one_prefill(gu):
     lse = np.concatenate([p[1] for p in pieces])
     e_out, e_lse = gu.max_abs_err(out, ref_out), gu.lse_err(lse, ref_lse)
     gu.announce(f"  two chunks vs one prefill: out {e_out:.3e} lse {e_lse:.3e}")
-    assert e_out <= TOL and e_lse <= TOL
+    assert e_out <= TOL and e_lse <= LSE_TOL
 
 
 def test_chunk_long_prefix_sampled(gu):

@@ -7,11 +7,14 @@ import pytest
 import torch
 
 from oracle import attention as O
+from oracle import parallel as OR
 from workloads import gen
 
 pytestmark = pytest.mark.gpu
 
 TOL = {"f32": 1e-5, "bf16": 2e-2, "e4m3fn": 6e-2}
+# The LSE is fp32 from end to end: 1e-3 catches a dropped or repeated block.
+LSE_TOL = {"f32": 1e-5, "bf16": 1e-3, "e4m3fn": 1e-3}
 
 
 @pytest.fixture(scope="module")
@@ -23,6 +26,8 @@ def gu():
 
 
 def _oracle(case, batches=None):
+    if batches is None and case.B > 16:
+        return OR.all_batches(lambda bb: _oracle(case, bb), case.B)
     return O.paged_decode(case.q, case.k_pool, case.v_pool, case.block_table, case.seq_lens, case.scale,
                           q_dtype=case.q_dtype, kv_dtype=case.kv_dtype, k_scale=case.k_scale,
                           v_scale=case.v_scale, batches=batches)
@@ -41,7 +46,7 @@ def _check(gu, case, num_workers=0, batches=None, tol=None):
     e_out = gu.max_abs_err(out, ref_out)
     e_lse = gu.lse_err(lse, ref_lse)
     gu.announce(f"  max-abs-err out {e_out:.3e} lse {e_lse:.3e} (tol {tol:g}) workers={dd.plan.num_workers}")
-    assert e_out <= tol and e_lse <= tol, (e_out, e_lse)
+    assert e_out <= tol and e_lse <= min(tol, LSE_TOL[case.kv_dtype]), (e_out, e_lse)
     return dd, out, lse
 
 
@@ -53,11 +58,9 @@ def test_decode_gqa_bf16_config_full_size(gu):
     _check(gu, gen.decode_gqa_bf16())
 
 
-def test_decode_long_fp8_config_full_size_sampled(gu):
-    case = gen.decode_long_fp8()
-    rng = np.random.default_rng(0)
-    batches = sorted(rng.choice(case.B, size=12, replace=False).tolist())
-    _check(gu, case, batches=batches)
+def test_decode_long_fp8_config_full_size(gu):
+    """All 128 sequences and 64 heads of the long fp8 workload."""
+    _check(gu, gen.decode_long_fp8())
 
 
 @pytest.mark.parametrize("kv", ["f32", "bf16", "e4m3fn"])

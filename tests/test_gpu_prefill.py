@@ -1,17 +1,21 @@
 """Ragged causal prefill on the GPU through the C ABI, against the fp64 oracle.
 
-bf16 inputs: max-abs-err of out and lse against the oracle run on the same
-rounded inputs must stay within 2e-2."""
+bf16 inputs: max-abs-err of out against the oracle run on the same rounded
+inputs must stay within 2e-2.  The LSE is fp32 from end to end and is held to
+1e-3: one 64-key tile dropped from a row of a few thousand keys moves it by
+about 1e-2.  The two full-size workloads are compared on every row and head."""
 import numpy as np
 import pytest
 import torch
 
 from oracle import attention as O
+from oracle import parallel as OR
 from workloads import gen
 
 pytestmark = pytest.mark.gpu
 
 TOL = 2e-2
+LSE_TOL = 1e-3
 
 
 @pytest.fixture(scope="module")
@@ -44,25 +48,30 @@ def _check(gu, case, rows=None, tol=TOL):
     dp = gu.DevicePrefill(case)
     dp.run()
     out, lse = dp.results()
-    ref, ref_lse = O.ragged_prefill(case.q, case.k, case.v, case.cu_seqlens, case.scale, k_rope=case.k_rope,
-                                    block_mask=case.block_mask, dtype="bf16", rows=rows)
-    if rows is not None:
+    ref_fn = lambda rr: O.ragged_prefill(case.q, case.k, case.v, case.cu_seqlens, case.scale,  # noqa: E731
+                                         k_rope=case.k_rope, block_mask=case.block_mask, dtype="bf16", rows=rr)
+    if rows is None:
+        ref, ref_lse = OR.all_rows(ref_fn, case.T)
+    else:
+        ref, ref_lse = ref_fn(rows)
         out, lse = out[rows], lse[rows]
     e_out = gu.max_abs_err(out, ref)
     e_lse = gu.lse_err(lse, ref_lse)
-    gu.announce(f"  max-abs-err out {e_out:.3e} lse {e_lse:.3e} (tol {tol:g}) rows={'all' if rows is None else len(rows)}")
-    assert e_out <= tol and e_lse <= tol, (e_out, e_lse)
+    gu.announce(f"  max-abs-err out {e_out:.3e} lse {e_lse:.3e} (tol {tol:g}, lse {LSE_TOL:g}) "
+                f"rows={'all' if rows is None else len(rows)}")
+    assert e_out <= tol and e_lse <= LSE_TOL, (e_out, e_lse)
     return dp, out, lse
 
 
-def test_prefill_mla_config_full_size_sampled(gu):
-    case = gen.prefill_mla_bf16()
-    _check(gu, case, rows=_rows_sample(case))
+def test_prefill_mla_config_full_size(gu):
+    """Every row and head of the ragged MLA workload (6584 tokens, 16 heads)."""
+    _check(gu, gen.prefill_mla_bf16())
 
 
-def test_prefill_blocksparse_config_full_size_sampled(gu):
-    case = gen.prefill_blocksparse_bf16()
-    _check(gu, case, rows=_rows_sample(case, n_mid=48))
+def test_prefill_blocksparse_config_full_size(gu):
+    """Every row and head of the block-sparse workload (2 x 8192 tokens, 32
+    query heads): every query tile and head pair the grid ranks is checked."""
+    _check(gu, gen.prefill_blocksparse_bf16())
 
 
 @pytest.mark.parametrize("rope", [0, 64])

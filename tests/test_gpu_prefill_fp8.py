@@ -3,18 +3,21 @@ gqap_prefill_fp8_blockwise), against the fp64 oracle run on the same fp8 codes
 and bf16 values.
 
 The nope parts of Q and K are e4m3fn codes with one scale per tensor, or one
-per row of a head; the rope parts and V are bf16.  Bar: max-abs-err of out and
-lse within 6e-2, the tolerance for fp8 inputs."""
+per row of a head; the rope parts and V are bf16.  Bar: max-abs-err of out
+within 6e-2, the tolerance for fp8 inputs; the fp32 LSE within 1e-3.  The two
+full-size workloads are compared on every row and head."""
 import numpy as np
 import pytest
 import torch
 
 from oracle import attention as O
+from oracle import parallel as OR
 from workloads import gen
 
 pytestmark = pytest.mark.gpu
 
 TOL = 6e-2
+LSE_TOL = 1e-3
 
 
 @pytest.fixture(scope="module")
@@ -51,20 +54,24 @@ def _check(gu, case, rows=None, tol=TOL):
     dp = gu.DevicePrefill(case)
     dp.run()
     out, lse = dp.results()
-    ref, ref_lse = O.ragged_prefill_fp8(case.q, case.q_rope, case.k, case.v, case.k_rope, case.cu_seqlens,
-                                        case.scale, case.q_scale, case.k_scale, block_mask=case.block_mask, rows=rows)
-    if rows is not None:
+    ref_fn = lambda rr: O.ragged_prefill_fp8(case.q, case.q_rope, case.k, case.v, case.k_rope,  # noqa: E731
+                                             case.cu_seqlens, case.scale, case.q_scale, case.k_scale,
+                                             block_mask=case.block_mask, rows=rr)
+    if rows is None:
+        ref, ref_lse = OR.all_rows(ref_fn, case.T)
+    else:
+        ref, ref_lse = ref_fn(rows)
         out, lse = out[rows], lse[rows]
     e_out = gu.max_abs_err(out, ref)
     e_lse = gu.lse_err(lse, ref_lse)
-    gu.announce(f"  max-abs-err out {e_out:.3e} lse {e_lse:.3e} (tol {tol:g}) rows={'all' if rows is None else len(rows)}")
-    assert e_out <= tol and e_lse <= tol, (e_out, e_lse)
+    gu.announce(f"  max-abs-err out {e_out:.3e} lse {e_lse:.3e} (tol {tol:g}, lse {LSE_TOL:g}) "
+                f"rows={'all' if rows is None else len(rows)}")
+    assert e_out <= tol and e_lse <= LSE_TOL, (e_out, e_lse)
     return dp, out, lse
 
 
-def test_fp8_mla_config_full_size_sampled(gu):
-    case = gen.prefill_mla_fp8()
-    _check(gu, case, rows=_rows_sample(case))
+def test_fp8_mla_config_full_size(gu):
+    _check(gu, gen.prefill_mla_fp8())
 
 
 @pytest.mark.parametrize("Hq,Hk", [(16, 16), (8, 2)])
@@ -116,9 +123,8 @@ def test_fp8_long_sequence_sampled(gu):
 
 # ---------------------------------------------------------------- blockwise scales (gqap_prefill_fp8_blockwise)
 
-def test_fp8_blockwise_mla_config_full_size_sampled(gu):
-    case = gen.prefill_mla_fp8_blockwise()
-    _check(gu, case, rows=_rows_sample(case))
+def test_fp8_blockwise_mla_config_full_size(gu):
+    _check(gu, gen.prefill_mla_fp8_blockwise())
 
 
 @pytest.mark.parametrize("Hq,Hk,Dr", [(16, 16, 64), (8, 2, 64), (8, 2, 0), (4, 1, 0)])

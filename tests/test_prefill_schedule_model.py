@@ -1,48 +1,153 @@
-"""Host model of how the prefill kernel ranks its work items (no GPU).
+"""Host model of how the prefill kernel maps its grid to work (no GPU).
 
-Workgroup i of the one-dimensional grid serves query head i % Hq and the
-(i // Hq)-th existing (sequence, 128-row query tile) pair, pairs ranked
-deepest query tile first, then by sequence (for up to 64 sequences a wave
-ranks them with one ballot per depth).  This model restates that ranking and
-checks that every pair is served exactly once, that the grid covers them
-all, and that the tail past the last pair is empty."""
+Workgroup i of the one-dimensional grid takes head slot x = i % NH (NH = Hq /
+hpw workgroups per item: one head with hpw = 1, a pair of heads of one KV
+group with hpw = 2), key-axis split sp = (i // NH) % S, and the
+(i // NH // S)-th existing (sequence, query tile) item, items ranked deepest
+query tile first, then by sequence (for up to 64 sequences a wave ranks them
+with one ballot per depth; past 64 the order is plain).  A query tile has
+QT = 128 / hpw rows; split sp takes key tiles [nkt sp / S, nkt (sp+1) / S)
+of the nkt tiles the tile needs.  Rows of a sequence past the plan's
+capacity are cleared by split 0 of the sequence's last query tile.
+
+This model restates that mapping and checks, on random problems:
+  * every (sequence, head, query row) within the capacity is computed by
+    exactly one workgroup per split, and the splits' key ranges partition
+    the tile's key tiles;
+  * every row past the capacity is cleared exactly once, by a workgroup of
+    its own head, and never also computed;
+  * the block-mask reads stay inside the sequence's [nb, nb] slice;
+  * the real items precede the empty tail of the grid (ranked path), and
+  * the heads of one KV group share an XCD (workgroup i runs on XCD i % 8)
+    whenever the group fits in one XCD's share of the heads."""
 import numpy as np
 import pytest
 
 
-def kernel_rank(lens, max_len, pair):
-    """(b, qt) of grid pair `pair`, or None past the last real pair."""
+def item_tiles(Lq, max_len, q_tiles, QT):
+    return 0 if Lq <= 0 else q_tiles if Lq > max_len else -(-Lq // QT)
+
+
+def rank(lens, max_len, q_tiles, QT, item):
+    """(b, qt) of grid item `item`, or None (the workgroup returns at once)."""
     B = len(lens)
-    q_tiles = -(-max_len // 128)
     if B <= 64:
-        nq = [(min(L, max_len) + 127) // 128 for L in lens]
+        nq = [item_tiles(L, max_len, q_tiles, QT) for L in lens]
         before = 0
         for t in range(q_tiles - 1, -1, -1):
-            members = [b for b in range(B) if nq[b] > t]     # ballot(nq > t), lane order
-            if pair < before + len(members):
-                return members[pair - before], t
+            members = [b for b in range(B) if nq[b] > t]      # ballot(nq > t), lane order
+            if item < before + len(members):
+                return members[item - before], t
             before += len(members)
         return None
-    b, qt = pair % B, q_tiles - 1 - pair // B
-    return (b, qt) if qt * 128 < min(lens[b], max_len) else None
+    b, qt = item % B, q_tiles - 1 - item // B
+    return (b, qt) if qt < item_tiles(lens[b], max_len, q_tiles, QT) else None
 
 
-@pytest.mark.parametrize("seed", range(40))
-def test_every_query_tile_served_once(seed):
+def head_of(x, NH):
+    hpx = NH >> 3
+    return x if NH & 7 else (x & 7) * hpx + (x >> 3)
+
+
+def simulate(lens, max_len, Hq, Hk, hpw, S, nb=None):
+    QT = 128 // hpw
+    NH = Hq // hpw
+    ratio = Hq // Hk
+    q_tiles = max(1 if lens else 0, -(-max_len // QT))
+    grid = NH * len(lens) * q_tiles * S
+    computed = {}      # (b, h, row) -> list of (sp, key-tile range)
+    cleared = {}       # (b, h, row) -> count
+    mask_rows = []     # (b, mask row index) read
+    served_items = []
+    for i in range(grid):
+        x, sp, item = i % NH, (i // NH) % S, i // NH // S
+        r = rank(lens, max_len, q_tiles, QT, item)
+        if sp == 0 and x == 0:
+            served_items.append(r)
+        if r is None:
+            continue
+        b, qt = r
+        hx = head_of(x, NH)
+        heads = [hx] if hpw == 1 else [2 * hx, 2 * hx + 1]
+        assert len({h // ratio for h in heads}) == 1        # a pair shares its KV head
+        Lq = lens[b]
+        L = min(Lq, max_len)
+        nqb = item_tiles(Lq, max_len, q_tiles, QT)
+        if Lq > L and sp == 0 and qt == nqb - 1:
+            for h in heads:
+                for row in range(L, Lq):
+                    cleared[(b, h, row)] = cleared.get((b, h, row), 0) + 1
+        q0 = qt * QT
+        if q0 >= L:
+            continue
+        nkt = -(-min(L, q0 + QT) // 64)
+        kt0, kt1 = nkt * sp // S, nkt * (sp + 1) // S
+        for wv in range(4):
+            wslot = (wv & 1) if hpw == 2 else wv
+            h = 2 * hx + (wv >> 1) if hpw == 2 else hx
+            r0 = q0 + 32 * wslot
+            wave_rows = r0 < L
+            qb0, qb1, wqb = q0 >> 6, min((q0 + QT - 1) >> 6, (L - 1) >> 6), r0 >> 6
+            if nb is not None:                             # rows of the mask the wave reads
+                mask_rows += [(b, qb0), (b, qb1)] + ([(b, wqb)] if wave_rows else [])
+            for row in range(r0, min(r0 + 32, L)):
+                computed.setdefault((b, h, row), []).append((sp, kt0, kt1, nkt))
+    return computed, cleared, mask_rows, served_items
+
+
+CASES = []
+rng0 = np.random.default_rng(7)
+for k in range(36):
+    B = int(rng0.choice([1, 2, 5, 63, 64, 65, 90]))
+    hpw = int(rng0.choice([1, 2]))
+    Hk = int(rng0.choice([1, 2, 4]))
+    ratio = int(rng0.choice([2, 4])) if hpw == 2 else int(rng0.choice([1, 2, 4]))
+    CASES.append((k, B, hpw, Hk, Hk * ratio, int(rng0.choice([1, 2, 3, 4]))))
+
+
+@pytest.mark.parametrize("seed,B,hpw,Hk,Hq,S", CASES)
+def test_grid_covers_every_row_once(seed, B, hpw, Hk, Hq, S):
     rng = np.random.default_rng(seed)
-    B = int(rng.choice([1, 2, 7, 63, 64, 65, 100]))
-    lens = rng.integers(0, 3000, size=B).tolist()
-    if seed % 5 == 0:
+    lens = rng.integers(0, 700, size=B).tolist()
+    if seed % 4 == 0:
         lens[0] = 0
-    max_len = max(lens + [1])
-    q_tiles = -(-max_len // 128)
-    served = [kernel_rank(lens, max_len, p) for p in range(B * q_tiles)]
-    real = [s for s in served if s is not None]
-    want = {(b, t) for b, L in enumerate(lens) for t in range(-(-L // 128))}
-    assert len(real) == len(set(real)) == len(want) and set(real) == want
+    cap = int(rng.choice([max(lens + [1]), 256, 129, 64, 0]))   # capacities below the longest sequence too
+    nb = max(1, -(-cap // 64))
+    computed, cleared, mask_rows, served = simulate(lens, cap, Hq, Hk, hpw, S, nb=nb)
+    for b, Lq in enumerate(lens):
+        L = min(Lq, cap)
+        for h in range(Hq):
+            for row in range(max(Lq, 0)):
+                key = (b, h, row)
+                if row < L:
+                    parts = computed.get(key, [])
+                    assert sorted(p[0] for p in parts) == list(range(S)), key
+                    nkt = parts[0][3]
+                    tiles = sorted(t for _, a, e, _ in parts for t in range(a, e))
+                    assert tiles == list(range(nkt)) and nkt * 64 >= row + 1, key
+                    assert key not in cleared
+                else:
+                    assert cleared.get(key) == 1 and key not in computed, key
+    assert len(computed) == sum(min(L, cap) for L in lens) * Hq
+    assert all(0 <= r < nb for _, r in mask_rows)
     if B <= 64:
-        # dense: real pairs first, then only empty slots; deepest first
-        k = len(real)
+        k = sum(1 for s in served if s is not None)
         assert all(s is not None for s in served[:k]) and all(s is None for s in served[k:])
-        depths = [t for _, t in real]
+        depths = [t for _, t in served[:k]]
         assert depths == sorted(depths, reverse=True)
+
+
+@pytest.mark.parametrize("Hq,Hk,hpw", [(32, 8, 1), (32, 8, 2), (64, 8, 1), (16, 2, 2), (128, 16, 1)])
+def test_heads_of_one_kv_group_share_an_xcd(Hq, Hk, hpw):
+    """With NH a multiple of 8, workgroup i runs on XCD i % 8 = x % 8, and the
+    slots x with one x % 8 take NH / 8 consecutive heads (or head pairs)."""
+    NH = Hq // hpw
+    ratio = Hq // Hk
+    xcd_of_group = {}
+    for x in range(NH):
+        hx = head_of(x, NH)
+        heads = [hx] if hpw == 1 else [2 * hx, 2 * hx + 1]
+        for h in heads:
+            xcd_of_group.setdefault(h // ratio, set()).add(x % 8)
+    if (NH // 8) % max(1, ratio // hpw) == 0:
+        assert all(len(s) == 1 for s in xcd_of_group.values())
