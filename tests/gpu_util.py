@@ -6,6 +6,7 @@ import sys
 
 import numpy as np
 
+import gqa_attention_paged_amd as gq  # noqa: F401  (the library; fails loudly when it is not built)
 from workloads.device import (DeviceChunk, DeviceDecode, DevicePrefill, bits_to_tensor,  # noqa: F401
                               tensor_to_f64)
 
@@ -32,3 +33,13 @@ def lse_err(gpu: np.ndarray, ref: np.ndarray) -> float:
         return float("inf")
     fin = np.isfinite(ref)
     return float(np.abs(gpu[fin] - ref[fin]).max()) if fin.any() else 0.0
+
+
+def lse_within(gpu: np.ndarray, ref: np.ndarray, bound) -> bool:
+    """|gpu - ref| <= bound (a scalar or an array shaped like ref) on every
+    finite entry, the same -inf pattern, and no NaN."""
+    if np.isnan(gpu).any() or not np.array_equal(np.isneginf(gpu), np.isneginf(ref)):
+        return False
+    fin = np.isfinite(ref)
+    b = np.broadcast_to(np.asarray(bound, np.float64), ref.shape)
+    return bool(np.all(np.abs(gpu[fin] - ref[fin]) <= b[fin]))

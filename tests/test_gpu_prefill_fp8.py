@@ -4,8 +4,14 @@ and bf16 values.
 
 The nope parts of Q and K are e4m3fn codes with one scale per tensor, or one
 per row of a head; the rope parts and V are bf16.  Bar: max-abs-err of out
-within 6e-2, the tolerance for fp8 inputs; the fp32 LSE within 1e-3.  The two
-full-size workloads are compared on every row and head."""
+within 6e-2, the tolerance for fp8 inputs.  The fp32 LSE is held to 1e-3
+plus the fp32 summation bound of its scores: the LSE moves by at most the
+largest error of a score, and a score summed in fp32 from n exact products
+errs by at most n * 2^-24 * (the sum of the products' magnitudes).  With
+row scales spread over three decades the products of one score reach a few
+hundred in magnitude and cancel, so the bound there is a few 1e-3; at the
+workloads' scales it is about 1e-4, far below the 2e-2 shift of a dropped
+key tile.  The two full-size workloads are compared on every row and head."""
 import numpy as np
 import pytest
 import torch
@@ -18,6 +24,29 @@ pytestmark = pytest.mark.gpu
 
 TOL = 6e-2
 LSE_TOL = 1e-3
+
+
+def fp8_lse_bound(case) -> np.ndarray:
+    """[T, Hq]: 1e-3 plus (Dn + Dr) * 2^-24 * scale * max over the keys of
+    the sequence of sum_d |q_d k_d| (dequantised nope parts and rope parts),
+    the fp32 summation bound of the row's largest score error."""
+    qs, ks = np.asarray(case.q_scale, np.float64), np.asarray(case.k_scale, np.float64)
+    qa = np.abs(O.widen(case.q, "e4m3fn") * (qs[..., None] if qs.ndim else qs))
+    ka = np.abs(O.widen(case.k, "e4m3fn") * (ks[..., None] if ks.ndim else ks))
+    n = case.D_nope + case.D_rope
+    r = case.Hq // case.Hk
+    bound = np.full((case.T, case.Hq), LSE_TOL)
+    for b in range(case.B):
+        c0, c1 = int(case.cu_seqlens[b]), int(case.cu_seqlens[b + 1])
+        if c1 == c0:
+            continue
+        for h in range(case.Hq):
+            m = qa[c0:c1, h] @ ka[c0:c1, h // r].T
+            if case.D_rope:
+                m = m + np.abs(O.widen(case.q_rope[c0:c1, h], "bf16")) @ np.abs(O.widen(case.k_rope[c0:c1, 0],
+                                                                                        "bf16")).T
+            bound[c0:c1, h] += n * 2.0 ** -24 * case.scale * m.max(axis=1)
+    return bound
 
 
 @pytest.fixture(scope="module")
@@ -64,9 +93,12 @@ def _check(gu, case, rows=None, tol=TOL):
         out, lse = out[rows], lse[rows]
     e_out = gu.max_abs_err(out, ref)
     e_lse = gu.lse_err(lse, ref_lse)
-    gu.announce(f"  max-abs-err out {e_out:.3e} lse {e_lse:.3e} (tol {tol:g}, lse {LSE_TOL:g}) "
+    bound = fp8_lse_bound(case)
+    if rows is not None:
+        bound = bound[rows]
+    gu.announce(f"  max-abs-err out {e_out:.3e} lse {e_lse:.3e} (tol {tol:g}, lse bound {bound.max():.2e}) "
                 f"rows={'all' if rows is None else len(rows)}")
-    assert e_out <= tol and e_lse <= LSE_TOL, (e_out, e_lse)
+    assert e_out <= tol and gu.lse_within(lse, ref_lse, bound), (e_out, e_lse)
     return dp, out, lse
 
 
