@@ -24,10 +24,12 @@ STATUS_NAMES = {0: "OK", 1: "INVALID_ARGUMENT", 2: "DTYPE", 3: "UNSUPPORTED", 4:
 
 F32, BF16, FP8_E4M3FN, F16 = 0, 1, 2, 3
 BLOCK_SIZE = 64
+NOALLOC_SCRATCH_BYTES = 32 << 20   # GQAP_NOALLOC_SCRATCH_BYTES
 PLAN_MAGIC = 0x47514150
 
 C_FUNCTIONS = (
-    "gqap_decode_plan", "gqap_decode_validate_host", "gqap_paged_decode", "gqap_debug_gather_kv",
+    "gqap_decode_plan", "gqap_decode_validate_host", "gqap_paged_decode", "gqap_paged_decode_noalloc",
+    "gqap_debug_gather_kv",
     "gqap_prefill_plan", "gqap_prefill", "gqap_prefill_fp8", "gqap_prefill_fp8_blockwise", "gqap_chunk_plan",
     "gqap_chunk_validate_host", "gqap_append_kv", "gqap_chunk_prefill", "gqap_append_kv_fp8",
     "gqap_chunk_prefill_fp8kv", "gqap_block_table_from_csr", "gqap_last_error", "gqap_version",
@@ -123,6 +125,9 @@ def _load() -> ctypes.CDLL:
     lib.gqap_paged_decode.argtypes = [ctypes.POINTER(DecodePlan), vp, vp, vp, vp, vp, f32, f32, f32, vp, vp, vp,
                                       u64, vp]
     lib.gqap_paged_decode.restype = st
+    lib.gqap_paged_decode_noalloc.argtypes = [ctypes.POINTER(DecodePlan), vp, vp, vp, vp, vp, f32, f32, f32, vp, vp,
+                                              vp]
+    lib.gqap_paged_decode_noalloc.restype = st
     lib.gqap_debug_gather_kv.argtypes = [ctypes.POINTER(DecodePlan), vp, vp, vp, i32, i32, i32, vp, vp]
     lib.gqap_debug_gather_kv.restype = st
     lib.gqap_prefill_plan.argtypes = [ctypes.POINTER(PrefillDesc), ctypes.POINTER(PrefillPlan)]
@@ -220,6 +225,13 @@ def gqap_paged_decode(plan: DecodePlan, q, k_pool, v_pool, block_table, seq_lens
     _check(_lib.gqap_paged_decode(ctypes.byref(plan), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
                                   _ptr(seq_lens), scale, k_scale, v_scale, _ptr(out), _ptr(lse), _ptr(workspace),
                                   workspace_bytes, _stream(stream)))
+
+
+def gqap_paged_decode_noalloc(plan: DecodePlan, q, k_pool, v_pool, block_table, seq_lens, scale: float,
+                              k_scale: float, v_scale: float, out, lse=None, stream=None) -> None:
+    _check(_lib.gqap_paged_decode_noalloc(ctypes.byref(plan), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                                          _ptr(block_table), _ptr(seq_lens), scale, k_scale, v_scale, _ptr(out),
+                                          _ptr(lse), _stream(stream)))
 
 
 def gqap_debug_gather_kv(plan: DecodePlan, pool, block_table, seq_lens, b: int, kv_head: int, num_rows: int,

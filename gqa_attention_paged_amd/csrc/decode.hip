@@ -32,6 +32,7 @@
 #include "status.hpp"
 
 #include <cmath>
+#include <mutex>
 #include <type_traits>
 
 namespace gqap {
@@ -731,6 +732,40 @@ static int dtype_size(int32_t dt) { return dt == GQAP_F32 ? 4 : dt == GQAP_BF16 
 
 static bool misaligned(const void* p, uintptr_t a) { return ((uintptr_t)p) & (a - 1); }
 
+// Workspace of the decode variant that allocates nothing: one array per GPU,
+// held from the first call on that GPU until the process ends.  Host code
+// never uses its name as an address (on the host it is a stand-in): the
+// device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[GQAP_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+
+// Device address of `scratch` on the current device, looked up on the first
+// call made with that device current and kept.
+static gqap_status scratch_address(void** out) {
+  static std::mutex mu;
+  static void* ptr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(GQAP_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(GQAP_ERR_UNSUPPORTED, "device %d beyond the %d supported", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(GQAP_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    ptr[dev] = p;
+  }
+  *out = ptr[dev];
+  return GQAP_OK;
+}
+
+static gqap_status decode_launch(const gqap_decode_plan_t* plan, const void* q, const void* k_pool,
+                                 const void* v_pool, const int32_t* block_table, const int32_t* seq_lens,
+                                 float scale, float k_scale, float v_scale, void* out, float* lse, void* workspace,
+                                 uint64_t workspace_bytes, void* stream);
+
 }  // namespace gqap
 
 using namespace gqap;
@@ -739,6 +774,32 @@ extern "C" gqap_status gqap_paged_decode(const gqap_decode_plan_t* plan, const v
                                          const void* v_pool, const int32_t* block_table, const int32_t* seq_lens,
                                          float scale, float k_scale, float v_scale, void* out, float* lse,
                                          void* workspace, uint64_t workspace_bytes, void* stream) {
+  return decode_launch(plan, q, k_pool, v_pool, block_table, seq_lens, scale, k_scale, v_scale, out, lse, workspace,
+                       workspace_bytes, stream);
+}
+
+extern "C" gqap_status gqap_paged_decode_noalloc(const gqap_decode_plan_t* plan, const void* q, const void* k_pool,
+                                                 const void* v_pool, const int32_t* block_table,
+                                                 const int32_t* seq_lens, float scale, float k_scale, float v_scale,
+                                                 void* out, float* lse, void* stream) {
+  if (!plan || plan->magic != GQAP_PLAN_MAGIC) return fail(GQAP_ERR_INVALID_ARGUMENT, "invalid decode plan");
+  if (plan->workspace_bytes > (uint64_t)GQAP_NOALLOC_SCRATCH_BYTES)
+    return fail(GQAP_ERR_UNSUPPORTED,
+                "this plan needs %llu bytes of workspace; the allocation-free decode has %llu "
+                "(use gqap_paged_decode with a caller workspace, or fewer sequences, heads or workers)",
+                (unsigned long long)plan->workspace_bytes, (unsigned long long)GQAP_NOALLOC_SCRATCH_BYTES);
+  if (plan->desc.batch == 0) return GQAP_OK;
+  void* ws = nullptr;
+  const gqap_status s = scratch_address(&ws);
+  if (s != GQAP_OK) return s;
+  return decode_launch(plan, q, k_pool, v_pool, block_table, seq_lens, scale, k_scale, v_scale, out, lse, ws,
+                       (uint64_t)GQAP_NOALLOC_SCRATCH_BYTES, stream);
+}
+
+gqap_status gqap::decode_launch(const gqap_decode_plan_t* plan, const void* q, const void* k_pool,
+                                const void* v_pool, const int32_t* block_table, const int32_t* seq_lens,
+                                float scale, float k_scale, float v_scale, void* out, float* lse,
+                                void* workspace, uint64_t workspace_bytes, void* stream) {
   if (!plan || plan->magic != GQAP_PLAN_MAGIC) return fail(GQAP_ERR_INVALID_ARGUMENT, "invalid decode plan");
   const gqap_decode_desc_t& d = plan->desc;
   if (d.batch == 0) return GQAP_OK;

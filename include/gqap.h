@@ -187,6 +187,29 @@ gqap_status gqap_paged_decode(const gqap_decode_plan_t* plan,
                               void* stream);
 
 /*
+ * The decode of gqap_paged_decode without a caller workspace and without any
+ * allocation: for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).  The
+ * partial results live in a scratch array inside the library, one per GPU,
+ * GQAP_NOALLOC_SCRATCH_BYTES long and held from the first call on that GPU
+ * (whose address lookup is the call's only set-up) until the process ends.
+ * The caller still passes every input and output, as for gqap_paged_decode.
+ * Errors: those of gqap_paged_decode, and UNSUPPORTED when the plan's
+ * workspace_bytes exceeds GQAP_NOALLOC_SCRATCH_BYTES (checked first, before
+ * any device call).  Every call on one GPU shares that GPU's array: calls that
+ * overlap on one GPU (different streams, or threads without ordering) race
+ * and must not be issued; calls in one stream are ordered and safe.  Nothing
+ * in the array needs to start at zero.  Asynchronous on `stream`.
+ */
+#define GQAP_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+gqap_status gqap_paged_decode_noalloc(const gqap_decode_plan_t* plan,
+                                      const void* q, const void* k_pool, const void* v_pool,
+                                      const int32_t* block_table, const int32_t* seq_lens,
+                                      float scale, float k_scale, float v_scale,
+                                      void* out, float* lse, void* stream);
+
+/*
  * Copy logical rows [0, num_rows) of KV head `kv_head` of sequence `b` from a
  * paged pool into dst [num_rows, D] (same dtype as the pool, contiguous),
  * using the same address arithmetic as the decode kernels.  Rows at or past

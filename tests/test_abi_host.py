@@ -598,3 +598,20 @@ def test_plans_keep_one_query_tile_for_rows_past_the_capacity(gq):
     c = baseline_chunk_desc(gq)
     c.max_q_len = 0
     assert gq.gqap_chunk_plan(c).q_tiles == 1
+
+
+def test_noalloc_decode_rejects_a_plan_past_its_scratch_without_a_gpu(gq):
+    """The allocation-free decode checks the plan's workspace against its fixed
+    scratch before any device call."""
+    d = baseline_decode_desc(gq)
+    d.num_workers = 5000                         # 5000+ partial slots of 16 x 128 floats: past 32 MiB
+    p = gq.gqap_decode_plan(d)
+    assert p.workspace_bytes > gq.NOALLOC_SCRATCH_BYTES
+    st = gq.lib().gqap_paged_decode_noalloc(ctypes.byref(p), 16, 16, 16, 16, 16, 1.0, 1.0, 1.0, 16, None, None)
+    assert gq.STATUS_NAMES[st] == "UNSUPPORTED" and "workspace" in gq.gqap_last_error()
+    st = gq.lib().gqap_paged_decode_noalloc(ctypes.byref(gq.DecodePlan()), 16, 16, 16, 16, 16, 1.0, 1.0, 1.0, 16,
+                                            None, None)
+    assert gq.STATUS_NAMES[st] == "INVALID_ARGUMENT"
+    assert gq.NOALLOC_SCRATCH_BYTES == 32 << 20
+    text = open(HEADER).read()
+    assert "#define GQAP_NOALLOC_SCRATCH_BYTES (32u << 20)" in text
