@@ -18,5 +18,6 @@ from .attention import (  # noqa: F401
     quantize_e4m3fn,
     ragged_prefill,
     ragged_prefill_fp8,
+    ragged_prefill_rope_fp8,
     widen,
 )

@@ -58,6 +58,9 @@ Readings where the pages are silent (each also listed in the design notes):
   * chunked prefill: a sequence holds kv_len keys in the paged cache, the last
     q_len of which are the chunk's own tokens (appended at logical positions
     kv_len - q_len + i); query i sees key j iff j <= kv_len - q_len + i.
+  * quantised rope key: the shared rope key rows are e4m3fn codes with one
+    fp32 scale per row (token), the value of a code being e4m3fn(code) times
+    its row's scale; the query, the per-head keys and V stay bf16.
 """
 from __future__ import annotations
 
@@ -510,3 +513,36 @@ def ragged_prefill_fp8(
     kr = None if k_rope is None else widen(k_rope, "bf16")
     return ragged_prefill(q, kk, widen(v, "bf16"), cu_seqlens, scale, k_rope=kr, block_mask=block_mask,
                           dtype="f64", rows=rows)
+
+
+# --------------------------------------------------------------------------
+# MLA prefill with a quantised shared rope key
+# --------------------------------------------------------------------------
+
+def ragged_prefill_rope_fp8(
+    q: np.ndarray,
+    k: np.ndarray,
+    v: np.ndarray,
+    k_rope: np.ndarray,
+    k_rope_scale,
+    cu_seqlens: np.ndarray,
+    scale: float,
+    *,
+    block_mask: Optional[np.ndarray] = None,
+    rows: Optional[Sequence[int]] = None,
+):
+    """Ragged causal MLA prefill whose shared rope key is quantised (Modular
+    flare_mla_prefill, the overload that takes k_rope together with
+    k_rope_scales): q [T, Hq, Dn + Dr], k [T, Hk, Dn] and v [T, Hk, Dv] are bf16;
+    k_rope [T, 1, Dr] holds e4m3fn codes and k_rope_scale [T] one float32
+    scale per rope row.  The value of a rope code is e4m3fn(code) times its
+    row's scale (a per-tensor scale is the case of equal entries), and the
+    rest is ragged_prefill on those values:
+        score = scale * (q[i,h,:Dn] . k[j,g] + k_rope_scale[j] * (q[i,h,Dn:] . codes of k_rope[j]))
+    Returns (out [n, Hq, Dv], lse [n, Hq]) in float64."""
+    ks = np.asarray(k_rope_scale, dtype=np.float64)
+    if ks.shape != (k_rope.shape[0],):
+        raise ValueError("k_rope_scale holds one scale per rope row")
+    kr = widen(k_rope, "e4m3fn") * ks[:, None, None]
+    return ragged_prefill(widen(q, "bf16"), widen(k, "bf16"), widen(v, "bf16"), cu_seqlens, scale, k_rope=kr,
+                          block_mask=block_mask, dtype="f64", rows=rows)

@@ -11,6 +11,7 @@ from tests import test_oracle_chunk_pins as PC
 from tests import test_oracle_fp8_prefill_pins as P8
 from tests import test_oracle_fp8kv_chunk_pins as PQ
 from tests import test_oracle_pins as P
+from tests import test_oracle_rope_fp8_pins as PR
 
 SRC = inspect.getsource(O)
 
@@ -85,6 +86,16 @@ MUTANTS = {
     "chunk_key_range_short": ("off + int(i.max()) + 1))", "off + int(i.max())))",
                               [PC.test_chunk_prefill_matches_sdpa_with_offset_mask,
                                PC.test_chunk_first_query_of_a_new_sequence_returns_its_value_row]),
+    "rope_fp8_scale_on_the_nope_keys": ("kr = widen(k_rope, \"e4m3fn\") * ks[:, None, None]\n    return ragged_prefill(widen(q, \"bf16\"), widen(k, \"bf16\")",
+                                        "kr = widen(k_rope, \"e4m3fn\")\n    return ragged_prefill(widen(q, \"bf16\"), widen(k, \"bf16\") * ks[:, None, None]",
+                                        [PR.test_rope_fp8_scales_touch_only_the_rope_term,
+                                         PR.test_rope_fp8_prefill_matches_bruteforce_on_torch_decoded_codes]),
+    "rope_fp8_scale_rows_reversed": ("kr = widen(k_rope, \"e4m3fn\") * ks[:, None, None]",
+                                     "kr = widen(k_rope, \"e4m3fn\") * ks[::-1, None, None]",
+                                     [PR.test_rope_fp8_zero_scale_acts_as_zero_codes_row_by_row]),
+    "rope_fp8_scale_dropped": ("kr = widen(k_rope, \"e4m3fn\") * ks[:, None, None]",
+                               "kr = widen(k_rope, \"e4m3fn\")",
+                               [PR.test_rope_fp8_with_power_of_two_scales_is_a_bf16_rope_key]),
     "fp8_rope_dropped": ('np.concatenate([q, widen(q_rope, "bf16")], axis=2)',
                          'np.concatenate([q, 0 * widen(q_rope, "bf16")], axis=2)',
                          [P8.test_fp8_prefill_matches_sdpa_with_concatenated_rope_key]),
@@ -99,6 +110,7 @@ def test_planted_mistake_is_caught(name, monkeypatch):
     monkeypatch.setattr(P8, "O", mutant)
     monkeypatch.setattr(PQ, "O", mutant)
     monkeypatch.setattr(PC, "O", mutant)
+    monkeypatch.setattr(PR, "O", mutant)
     caught = []
     for fn in catchers:
         try:

@@ -293,6 +293,10 @@ class PrefillCase:
     q_rope: Optional[np.ndarray] = None
     q_scale: object = 1.0     # float, or float32 [T, Hq] with blockwise scales
     k_scale: object = 1.0     # float, or float32 [T, Hk]
+    # rope_dtype 'e4m3fn': k_rope holds e4m3fn codes [T, 1, D_rope] with one
+    # float32 scale per row in k_rope_scale [T]; q, k and v stay bf16.
+    rope_dtype: str = "bf16"
+    k_rope_scale: Optional[np.ndarray] = None
     meta: dict = field(default_factory=dict)
 
     @property
@@ -428,6 +432,33 @@ def make_prefill_fp8_case(
     return base
 
 
+def make_prefill_rope_fp8_case(
+    *,
+    name: str,
+    seed: int,
+    seq_lens: Sequence[int],
+    Hq: int,
+    Hk: int,
+    D_rope: int = 64,
+    mask_density: Optional[float] = None,
+    scale: Optional[float] = None,
+) -> PrefillCase:
+    """The bf16 MLA prefill problem of make_prefill_case (same seed, same
+    draws, Dn = 128, Dv = 128) with the shared rope key quantised to fp8
+    e4m3fn row by row: the scale of token t's rope row is amax over the row /
+    448 (1 for an all-zero row), the codes those of the row over its scale.
+    q, k and v stay bf16."""
+    base = make_prefill_case(name=name, seed=seed, seq_lens=seq_lens, Hq=Hq, Hk=Hk, D_qk=128 + D_rope,
+                             D_rope=D_rope, D_v=128, mask_density=mask_density, scale=scale)
+    x = _bf16_bits_to_f32(base.k_rope)                                     # [T, 1, Dr]
+    amax = np.abs(x).max(axis=(1, 2)) if x.size else np.ones(x.shape[0], np.float32)
+    sc = np.where(amax > 0, amax.astype(np.float32) / np.float32(E4M3FN_MAX), np.float32(1.0)).astype(np.float32)
+    base.k_rope = to_e4m3fn_bits(x, sc[:, None, None])
+    base.k_rope_scale = sc
+    base.rope_dtype = "e4m3fn"
+    return base
+
+
 def prefill_mla_bf16(seed: int = 1003, seq_lens=(512, 1024, 2048, 3000)) -> PrefillCase:
     """Ragged MLA prefill: 16 heads, Q 192 = 128 nope + 64 rope, K_rope shared
     [T, 1, 64], V / output 128, causal, scale 1/sqrt(192)."""
@@ -454,6 +485,13 @@ def prefill_mla_fp8_blockwise(seed: int = 1010, seq_lens=(512, 1024, 2048, 3000)
     q_nope and K) instead of one per tensor."""
     return make_prefill_fp8_case(name="prefill_mla_fp8_blockwise", seed=seed, seq_lens=seq_lens, Hq=16, Hk=16,
                                  D_rope=64, blockwise=True)
+
+
+def prefill_mla_rope_fp8(seed: int = 1012, seq_lens=(512, 1024, 2048, 3000)) -> PrefillCase:
+    """The ragged MLA prefill shape (16 heads, Q 128 nope + 64 rope, V /
+    output 128, causal, scale 1/sqrt(192)) with the shared rope key in fp8
+    e4m3fn, one scale per rope row; q, k and v bf16."""
+    return make_prefill_rope_fp8_case(name="prefill_mla_rope_fp8", seed=seed, seq_lens=seq_lens, Hq=16, Hk=16)
 
 
 # ---------------------------------------------------------------------------
@@ -645,4 +683,5 @@ CONFIGS = {
     "prefill_mla_fp8_blockwise": prefill_mla_fp8_blockwise,
     "prefill_chunk_long_mla_bf16": prefill_chunk_long_mla_bf16,
     "prefill_chunk_fp8kv": prefill_chunk_fp8kv,
+    "prefill_mla_rope_fp8": prefill_mla_rope_fp8,
 }
