@@ -9,7 +9,8 @@ V rows) divided by the measured time per step.  Inputs are resident in HBM
 before the timed region; consecutive steps read different copies of the KV
 pool, so no step is served from the 256 MB last-level cache by its
 predecessor.  The other workloads (fp8 KV decode, MLA prefill, block-sparse
-prefill, fp8 MLA prefill with per-tensor and blockwise scales, chunked
+prefill, fp8 MLA prefill with per-tensor and blockwise scales, MLA prefill
+with an fp8 rope key, chunked
 prefill over a bf16 and over an fp8 e4m3fn cache, and a long-context chunk
 whose few query tiles are split along the keys) are measured the same way
 and reported under "secondary".
@@ -90,6 +91,7 @@ DOMINANT_KERNEL = {
     "prefill_mla_fp8_blockwise": "prefill_fwd<64, false, 2>",
     "prefill_chunk_long_mla_bf16": "prefill_fwd<64, true, 0>",
     "prefill_chunk_fp8kv": "prefill_fwd<0, true, 3>",
+    "prefill_mla_rope_fp8": "prefill_fwd<64, false, 4>",
 }
 
 
@@ -248,7 +250,10 @@ def bench_prefill(case, steps, warmup, torch, gq, gu, check=True):
         import numpy as np
         out, _ = dp.results()
         rows = np.linspace(0, case.T - 1, 48).astype(np.int64)
-        if case.dtype == "e4m3fn":
+        if getattr(case, "rope_dtype", "bf16") == "e4m3fn":
+            ref, _ = O.ragged_prefill_rope_fp8(case.q, case.k, case.v, case.k_rope, case.k_rope_scale,
+                                               case.cu_seqlens, case.scale, block_mask=case.block_mask, rows=rows)
+        elif case.dtype == "e4m3fn":
             ref, _ = O.ragged_prefill_fp8(case.q, case.q_rope, case.k, case.v, case.k_rope, case.cu_seqlens,
                                           case.scale, case.q_scale, case.k_scale, block_mask=case.block_mask,
                                           rows=rows)
@@ -343,6 +348,11 @@ def cpu_baseline_full(case):
                                                kr_pool=pools[2] if len(pools) == 3 else None, **fp8),
                     case.T, block=64, workers=workers)
         what = f"one full fp64 append and chunked prefill of all {case.T} query rows"
+    elif getattr(case, "rope_dtype", "bf16") == "e4m3fn":
+        OP.all_rows(lambda rr: O.ragged_prefill_rope_fp8(case.q, case.k, case.v, case.k_rope, case.k_rope_scale,
+                                                         case.cu_seqlens, case.scale, block_mask=case.block_mask,
+                                                         rows=rr), case.T, workers=workers)
+        what = f"one full fp64 prefill of all {case.T} rows"
     elif case.dtype == "e4m3fn":
         OP.all_rows(lambda rr: O.ragged_prefill_fp8(case.q, case.q_rope, case.k, case.v, case.k_rope,
                                                     case.cu_seqlens, case.scale, case.q_scale, case.k_scale,
@@ -427,7 +437,7 @@ def main(argv=None) -> int:
         del c4
         if hasattr(gu, "DevicePrefill"):
             for mk in (gen.prefill_mla_bf16, gen.prefill_blocksparse_bf16, gen.prefill_mla_fp8,
-                       gen.prefill_mla_fp8_blockwise):
+                       gen.prefill_mla_fp8_blockwise, gen.prefill_mla_rope_fp8):
                 pc = mk()
                 rp = bench_prefill(pc, args.steps, args.warmup, torch, gq, gu)
                 peak = prefill_peak_tflops(pc)

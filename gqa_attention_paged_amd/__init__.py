@@ -30,7 +30,8 @@ PLAN_MAGIC = 0x47514150
 C_FUNCTIONS = (
     "gqap_decode_plan", "gqap_decode_validate_host", "gqap_paged_decode", "gqap_paged_decode_noalloc",
     "gqap_debug_gather_kv",
-    "gqap_prefill_plan", "gqap_prefill", "gqap_prefill_fp8", "gqap_prefill_fp8_blockwise", "gqap_chunk_plan",
+    "gqap_prefill_plan", "gqap_prefill", "gqap_prefill_fp8", "gqap_prefill_fp8_blockwise",
+    "gqap_prefill_rope_fp8", "gqap_chunk_plan",
     "gqap_chunk_validate_host", "gqap_append_kv", "gqap_chunk_prefill", "gqap_append_kv_fp8",
     "gqap_chunk_prefill_fp8kv", "gqap_block_table_from_csr", "gqap_last_error", "gqap_version",
 )
@@ -140,6 +141,9 @@ def _load() -> ctypes.CDLL:
     lib.gqap_prefill_fp8_blockwise.argtypes = [ctypes.POINTER(PrefillPlan), vp, vp, vp, vp, vp, vp, vp, f32, vp, vp,
                                                vp, vp, vp, u64, vp]
     lib.gqap_prefill_fp8_blockwise.restype = st
+    lib.gqap_prefill_rope_fp8.argtypes = [ctypes.POINTER(PrefillPlan), vp, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp,
+                                          u64, vp]
+    lib.gqap_prefill_rope_fp8.restype = st
     lib.gqap_chunk_plan.argtypes = [ctypes.POINTER(ChunkDesc), ctypes.POINTER(ChunkPlan)]
     lib.gqap_chunk_plan.restype = st
     lib.gqap_chunk_validate_host.argtypes = [ctypes.POINTER(ChunkPlan), vp, vp, vp]
@@ -274,6 +278,15 @@ def gqap_prefill_fp8_blockwise(plan: PrefillPlan, q_nope, q_rope, k, v, k_rope, 
                                            _ptr(k_rope), _ptr(cu_seqlens), _ptr(block_mask), scale, _ptr(q_scales),
                                            _ptr(k_scales), _ptr(out), _ptr(lse), _ptr(workspace), workspace_bytes,
                                            _stream(stream)))
+
+
+def gqap_prefill_rope_fp8(plan: PrefillPlan, q, k, v, k_rope, k_rope_scales, cu_seqlens, block_mask, scale: float,
+                          out, lse=None, workspace=None, workspace_bytes: Optional[int] = None, stream=None) -> None:
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.gqap_prefill_rope_fp8(ctypes.byref(plan), _ptr(q), _ptr(k), _ptr(v), _ptr(k_rope),
+                                      _ptr(k_rope_scales), _ptr(cu_seqlens), _ptr(block_mask), scale, _ptr(out),
+                                      _ptr(lse), _ptr(workspace), workspace_bytes, _stream(stream)))
 
 
 def gqap_chunk_plan(desc: ChunkDesc) -> ChunkPlan:

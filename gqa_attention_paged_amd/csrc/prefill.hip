@@ -28,6 +28,7 @@
 #include "dev.hpp"
 #include "status.hpp"
 
+#include <algorithm>
 #include <cmath>
 #include <type_traits>
 
@@ -146,12 +147,20 @@ using namespace dev;
 // bf16 (every e4m3fn value is a bf16 value) and written to the LDS layouts of
 // a bf16 tile, so the math is that of the bf16 path; k_scale is part of the
 // softmax constant and v_scale multiplies the normalised output.
+// F8 = 4 (ragged MLA only): the shared rope keys are fp8 e4m3fn codes with
+// one scale per row (token).  The rope tile is staged as 64-byte code rows
+// with its 64 scales; a rope operand is widened exactly to bf16 when it is
+// read, each half tile runs its rope steps first, multiplies that sum by the
+// keys' scales, then accumulates the bf16 per-head steps.
 template <int DR, bool PAGED, int F8>
 __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
   constexpr bool QK8 = F8 == 1 || F8 == 2;    // fp8 nope Q.K on the fp8 matrix cores
   constexpr bool KV8 = F8 == 3;               // fp8 KV pages, widened to bf16 in LDS
+  constexpr bool RK8 = F8 == 4;               // fp8 rope keys with per-row scales
+  constexpr bool KSC = F8 == 2 || RK8;        // per-key scales staged in LDS with each tile
   static_assert(!(QK8 && PAGED), "the fp8 Q.K path reads token-major K");
   static_assert(!KV8 || PAGED, "the fp8 KV path reads pages");
+  static_assert(!RK8 || (DR == 64 && !PAGED), "fp8 rope keys: ragged MLA prefill");
   constexpr int DN = 128;                     // per-head key width
   constexpr int DV = 128;                     // value / output width
   constexpr int KSN = DN / 16;                // k-steps over the nope part (bf16)
@@ -160,7 +169,7 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
   constexpr int KGE = QK8 || KV8 ? 1 : 2;     // bytes per K element in memory
   constexpr int VGE = KV8 ? 1 : 2;            // bytes per V element in memory
   constexpr int KB = 64 * DN * KE;            // K tile bytes
-  constexpr int RB = DR ? 64 * DR * 2 : 0;    // rope tile bytes
+  constexpr int RB = DR ? 64 * DR * (RK8 ? 1 : 2) : 0;  // rope tile bytes
   constexpr int VB = 64 * DV * 2;             // V tile bytes
   // Loads per lane and tile: 16-byte loads-to-LDS (1 KB per wave each), or
   // with KV8 16-byte register loads of codes (two per lane for K, two for V).
@@ -173,7 +182,7 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
   __shared__ __attribute__((aligned(1024))) unsigned char rbuf0[RB ? RB : 16], rbuf1[RB ? RB : 16];
   __shared__ __attribute__((aligned(1024))) unsigned char vbuf0[VB], vbuf1[VB];
   // Blockwise key scales of a tile: one 64-float copy per wave.
-  __shared__ __attribute__((aligned(1024))) float sbuf0[F8 == 2 ? 256 : 4], sbuf1[F8 == 2 ? 256 : 4];
+  __shared__ __attribute__((aligned(1024))) float sbuf0[KSC ? 256 : 4], sbuf1[KSC ? 256 : 4];
 
   // Work item.  The grid is one-dimensional, Hq / hpw workgroups (times the
   // key-axis splits) per (query tile, sequence) item; items are ranked
@@ -362,19 +371,24 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
   // fills LDS chunk c' of a row fetches the chunk that the read swizzle
   // expects there.
   const int row0 = tid >> 4, ch = tid & 15;
-  const int row0r = tid >> 3, chr = tid & 7;
-  const int rch = chr ^ ((row0r >> 1) & 7);                            // rope: c' = c ^ ((row >> 1) & 7)
+  // Rope rows: 128 bytes (bf16; 8 rows per 1 KB segment, 32 per load round)
+  // or 64 bytes (fp8 codes; 16 rows per segment, the whole tile in one round).
+  constexpr int RRS = RK8 ? 64 : 32;                                   // rope rows per load round
+  const int row0r = RK8 ? tid >> 2 : tid >> 3;
+  const int chr = RK8 ? tid & 3 : tid & 7;
+  const int rch = RK8 ? chr ^ ((row0r >> 2) & 3)                       // fp8 rope: c' = c ^ ((row >> 2) & 3)
+                      : chr ^ ((row0r >> 1) & 7);                      // rope: c' = c ^ ((row >> 1) & 7)
   const int vch = (((ch >> 1) ^ vmask(row0)) << 1) | (ch & 1);         // V: 32-byte pieces ^ vmask(row)
   constexpr int KRS = QK8 ? 32 : 16;                                   // K rows per load round
   const int krow = QK8 ? row0r : row0;
   const int kch = QK8 ? rch : ch ^ (row0 & 15);                        // K: c' = c ^ (row & 15)
   // Tile bases are uniform (scalar) pointers; each lane adds one fixed 32-bit
   // byte offset, so the loads use the scalar-base addressing form.
-  const int64_t kstr = a.k_st * KGE, vstr = a.v_st * VGE, rstr = a.kr_st * 2;  // row strides in bytes
+  const int64_t kstr = a.k_st * KGE, vstr = a.v_st * VGE, rstr = a.kr_st * (RK8 ? 1 : 2);  // row strides in bytes
   const unsigned char* kg =
       (const unsigned char*)a.k + ((int64_t)c0 * a.k_st + (int64_t)g * a.k_sh) * KE;
   const unsigned char* vg = (const unsigned char*)(a.v + (int64_t)c0 * a.v_st + (int64_t)g * a.v_sh);
-  const unsigned char* rg = DR ? (const unsigned char*)(a.kr + (int64_t)c0 * a.kr_st) : nullptr;
+  const unsigned char* rg = DR ? (const unsigned char*)a.kr + (int64_t)c0 * rstr : nullptr;
   const uint32_t koff = (uint32_t)(krow * kstr) + 16u * kch;
   const uint32_t voff = (uint32_t)(row0 * vstr) + 16u * vch;
   const uint32_t roff = DR ? (uint32_t)(row0r * rstr) + 16u * rch : 0u;
@@ -387,7 +401,10 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
   auto dma4 = [&](const float* gp, float* lp) {
     __builtin_amdgcn_global_load_lds((const void*)gp, (GQAP_LDS void*)((unsigned char*)lp + (wseg >> 2)), 4, 0, 0);
   };
-  const float* ksg = F8 == 2 ? a.ksc + (int64_t)c0 * a.Hk + g : nullptr;
+  // Per-key scales: one per row of a KV head (blockwise fp8 Q.K), or one per
+  // rope row shared by every head (fp8 rope keys).
+  const int64_t sstr = F8 == 2 ? a.Hk : 1;
+  const float* ksg = F8 == 2 ? a.ksc + (int64_t)c0 * a.Hk + g : RK8 ? a.ksc + c0 : nullptr;
   // First byte of key tile kt of K / V.  With PAGED a tile is one page: the
   // 64 x D slab of pool block block_table[b, kt] for KV head g (FlashMLA
   // tensor-shape reference, section 1: tokens 64j .. 64j+63 live in
@@ -438,8 +455,8 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
     unsigned char* kd = BUF ? kbuf1 : kbuf0;
     unsigned char* rd = BUF ? rbuf1 : rbuf0;
     unsigned char* vd = BUF ? vbuf1 : vbuf0;
-    if constexpr (F8 == 2)
-      dma4(ksg + (int64_t)(kt * 64 + min(lane, Lk - 1 - kt * 64)) * a.Hk, BUF ? sbuf1 : sbuf0);
+    if constexpr (KSC)
+      dma4(ksg + (int64_t)(kt * 64 + min(lane, Lk - 1 - kt * 64)) * sstr, BUF ? sbuf1 : sbuf0);
     const int key0 = kt * 64;
     const unsigned char* kt_k = tile_k(kt);
     const unsigned char* kt_v = tile_v(kt);
@@ -464,7 +481,7 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
 #pragma unroll
       for (int i = 0; i < KLD; ++i) dma(kt_k + KRS * i * kstr + koff, kd + 4096 * i + wseg);
 #pragma unroll
-      for (int i = 0; i < RLD; ++i) dma(kt_r + 32 * i * rstr + roff, rd + 4096 * i + wseg);
+      for (int i = 0; i < RLD; ++i) dma(kt_r + RRS * i * rstr + roff, rd + 4096 * i + wseg);
 #pragma unroll
       for (int i = 0; i < VLD; ++i) dma(kt_v + 16 * i * vstr + voff, vd + 4096 * i + wseg);
     } else {
@@ -473,7 +490,7 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
         dma(kt_k + (int64_t)min(krow + KRS * i, Lk - 1 - key0) * kstr + 16 * kch, kd + 4096 * i + wseg);
 #pragma unroll
       for (int i = 0; i < RLD; ++i)
-        dma(kt_r + (int64_t)min(row0r + 32 * i, Lk - 1 - key0) * rstr + 16 * rch, rd + 4096 * i + wseg);
+        dma(kt_r + (int64_t)min(row0r + RRS * i, Lk - 1 - key0) * rstr + 16 * rch, rd + 4096 * i + wseg);
 #pragma unroll
       for (int i = 0; i < VLD; ++i)
         dma(kt_v + (int64_t)min(row0 + 16 * i, Lk - 1 - key0) * vstr + 16 * vch, vd + 4096 * i + wseg);
@@ -524,7 +541,11 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
     for (int s2 = 0; s2 < KSN; ++s2) kra[s2] = l32 * 256 + ((s2 ^ m) << 5) + lo;
   }
   int rra[KSR > 0 ? KSR : 1];
-  if constexpr (DR > 0) {
+  if constexpr (RK8) {  // 8 codes of k-step s2: chunk s2 of a 64-byte row, half hh of it
+    const int m = (l32 >> 2) & 3;
+#pragma unroll
+    for (int s2 = 0; s2 < KSR; ++s2) rra[s2] = l32 * 64 + ((s2 ^ m) << 4) + 8 * hh;
+  } else if constexpr (DR > 0) {
     const int m = (l32 >> 1) & 7;
 #pragma unroll
     for (int s2 = 0; s2 < KSR; ++s2) rra[s2] = l32 * 128 + (((2 * s2 + hh) ^ m) << 4);
@@ -561,7 +582,7 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
     unsigned char* vd = BUF ? vbuf0 : vbuf1;
     const float* sb = BUF ? sbuf1 : sbuf0;
     float* sd = BUF ? sbuf0 : sbuf1;
-    constexpr int NLD = KLD + RLD + VLD + (F8 == 2 ? 1 : 0);
+    constexpr int NLD = KLD + RLD + VLD + (KSC ? 1 : 0);
     const unsigned char* kt_k = WL ? tile_k(kn) : nullptr;
     const unsigned char* kt_v = WL ? tile_v(kn) : nullptr;
     const unsigned char* kt_r = DR && WL ? tile_r(kn) : nullptr;
@@ -578,11 +599,11 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
       if (i < KLD)
         dma(kt_k + KRS * i * kstr + koff, kd + 4096 * i + wseg);
       else if (i < KLD + RLD)
-        dma(kt_r + 32 * (i - KLD) * rstr + roff, rd + 4096 * (i - KLD) + wseg);
+        dma(kt_r + RRS * (i - KLD) * rstr + roff, rd + 4096 * (i - KLD) + wseg);
       else if (i < KLD + RLD + VLD)
         dma(kt_v + 16 * (i - KLD - RLD) * vstr + voff, vd + 4096 * (i - KLD - RLD) + wseg);
-      else if constexpr (F8 == 2)
-        dma4(ksg + (int64_t)(kn * 64 + lane) * a.Hk, sd);
+      else if constexpr (KSC)
+        dma4(ksg + (int64_t)(kn * 64 + lane) * sstr, sd);
     };
     f32x16_t s[2] = {f32x16_t{}, f32x16_t{}};
     if constexpr (!QK8) {
@@ -592,9 +613,42 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
       // before the first rope step of each half.
       constexpr int NS = KSN + KSR;
       constexpr int PF = 8;
-      auto kfrag = [&](int idx) {
-        const int t = idx / NS, ss = idx % NS;
-        return ss < KSN ? load16(kb + t * 8192 + kra[ss]) : load16(rb + t * 4096 + rra[ss - KSN]);
+      // Matrix step idx of the tile: half t, k-step ss (ss >= KSN: rope).
+      // With fp8 rope keys the rope steps of both halves come first.
+      auto step_of = [&](int idx, int& t, int& ss) {
+        if (RK8 && idx < 2 * KSR) {
+          t = idx / KSR;
+          ss = KSN + idx % KSR;
+        } else if (RK8) {
+          t = (idx - 2 * KSR) / KSN;
+          ss = (idx - 2 * KSR) % KSN;
+        } else {
+          t = idx / NS;
+          ss = idx % NS;
+        }
+      };
+      auto kfrag = [&](int idx) -> i32x4 {
+        int t, ss;
+        step_of(idx, t, ss);
+        if (ss < KSN) return load16(kb + t * 8192 + kra[ss]);
+        if constexpr (RK8) {  // 8 codes -> 8 bf16 values (exact)
+          return fp8x8_to_bf16x8_pk(*(const i32x2*)(rb + t * 2048 + rra[ss - KSN]));
+        } else {
+          return load16(rb + t * 4096 + rra[ss - KSN]);
+        }
+      };
+      // The rope sum of half t times its keys' scales (register j of the
+      // half holds key 32 t + 8 (j / 4) + 4 hh + j % 4).
+      auto scale_rope = [&](int t) {
+        if constexpr (RK8) {
+          const float* sp = sb + (wseg >> 4) + 32 * t + 4 * hh;
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const f32x4 w = *(const f32x4*)(sp + 8 * m);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s[t][4 * m + e] *= w[e];
+          }
+        }
       };
       i32x4 kf[PF];
       // Without a rope part the matrix phases run at raised wave priority, so
@@ -609,8 +663,11 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
       for (int idx = 0; idx < 2 * NS; ++idx) {
         const i32x4 cur = kf[idx % PF];
         if (idx + PF < 2 * NS) kf[idx % PF] = kfrag(idx + PF);
-        if (KV8 && KSR > 0 && idx % NS == KSN) s[idx / NS] *= a.qk;
-        s[idx / NS] = mfma32x32x16(__builtin_bit_cast(bf16x8, cur), qop[idx % NS], s[idx / NS]);
+        int t, ss;
+        step_of(idx, t, ss);
+        if (KV8 && KSR > 0 && ss == KSN) s[t] *= a.qk;
+        if (RK8 && ss == 0) scale_rope(t);
+        s[t] = mfma32x32x16(__builtin_bit_cast(bf16x8, cur), qop[ss], s[t]);
         if (WL && idx < NLD) issue_load(idx);
       }
       // Issue order: PF reads, then per MFMA one read (and one tile load
@@ -1042,6 +1099,20 @@ static gqap_status split_setup(int32_t nsplit, int32_t T, int32_t Hq, uint64_t n
   return GQAP_OK;
 }
 
+// Workgroups of a prefill launch: Hq / hpw per (sequence, query tile) item
+// and split.  Up to 64 sequences the kernel ranks the items that exist, so
+// the grid needs no more items than the rows can fill: a sequence of L rows
+// has ceil(L / QT) tiles, at most (L + QT - 1) / QT, and the rows of all
+// sequences are at most T, so sum_b ceil(L_b / QT) <= (T + B (QT - 1)) / QT.
+// Every item past that bound would only return (each costs its compute unit
+// slot a couple of microseconds: the read of the sequence lengths).
+static dim3 prefill_grid(int32_t B, int32_t Hq, int32_t hpw, int32_t q_tiles, int32_t nsplit, int64_t T) {
+  const int64_t QT = 128 / hpw;
+  int64_t items = (int64_t)B * q_tiles;
+  if (B <= 64) items = std::min<int64_t>(items, std::max<int64_t>(B ? 1 : 0, (T + (int64_t)B * (QT - 1)) / QT));
+  return dim3((unsigned)((int64_t)(Hq / hpw) * items * nsplit));
+}
+
 static gqap_status launch_merge(const PrefillArgs& a, int32_t max_len, hipStream_t st) {
   if (a.nsplit <= 1) return GQAP_OK;
   MergeArgs m{};
@@ -1126,7 +1197,7 @@ extern "C" gqap_status gqap_prefill(const gqap_prefill_plan_t* plan, const void*
   a.v = (const uint16_t*)v;
   a.kr = (const uint16_t*)k_rope;
   a.scale_log2 = scale * dev::kLog2e;
-  const dim3 grid((unsigned)(d.num_q_heads / a.hpw) * (unsigned)d.batch * (unsigned)plan->q_tiles * (unsigned)a.nsplit);
+  const dim3 grid = prefill_grid(d.batch, d.num_q_heads, a.hpw, plan->q_tiles, a.nsplit, d.total_tokens);
   hipStream_t st = (hipStream_t)stream;
   if (d.head_dim_rope == 64)
     hipLaunchKernelGGL((prefill_fwd<64, false, 0>), grid, dim3(256), 0, st, a);
@@ -1134,6 +1205,49 @@ extern "C" gqap_status gqap_prefill(const gqap_prefill_plan_t* plan, const void*
     hipLaunchKernelGGL((prefill_fwd<0, false, 0>), grid, dim3(256), 0, st, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(GQAP_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
+  return launch_merge(a, d.max_seq_len, st);
+}
+
+extern "C" gqap_status gqap_prefill_rope_fp8(const gqap_prefill_plan_t* plan, const void* q, const void* k,
+                                             const void* v, const void* k_rope, const float* k_rope_scales,
+                                             const int32_t* cu_seqlens, const uint8_t* block_mask, float scale,
+                                             void* out, float* lse, void* workspace, uint64_t workspace_bytes,
+                                             void* stream) {
+  if (!plan || plan->magic != GQAP_PLAN_MAGIC) return fail(GQAP_ERR_INVALID_ARGUMENT, "invalid prefill plan");
+  const gqap_prefill_desc_t& d = plan->desc;
+  if (d.dtype != GQAP_BF16)
+    return fail(GQAP_ERR_DTYPE, "gqap_prefill_rope_fp8 takes a bf16 plan (q, k and v are bf16)");
+  if (d.head_dim_rope != 64)
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "gqap_prefill_rope_fp8 needs the MLA split head (head_dim_rope 64)");
+  if (d.kr_stride_token % 16 || d.kr_stride_token < 64)
+    return fail(GQAP_ERR_INVALID_ARGUMENT,
+                "the fp8 rope rows need a token stride of at least 64 bytes, a multiple of 16 (got %lld)",
+                (long long)d.kr_stride_token);
+  if (!std::isfinite(scale)) return fail(GQAP_ERR_INVALID_ARGUMENT, "scale must be finite");
+  if (d.batch == 0 || plan->q_tiles == 0) return GQAP_OK;
+  if (!q || !k || !v || !k_rope || !k_rope_scales || !cu_seqlens || !out)
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "null device pointer");
+  if (d.has_block_mask && !block_mask) return fail(GQAP_ERR_INVALID_ARGUMENT, "block mask declared but null");
+  if (misaligned16(q) || misaligned16(k) || misaligned16(v) || misaligned16(out) || misaligned16(k_rope) ||
+      ((uintptr_t)k_rope_scales & 3) || ((uintptr_t)cu_seqlens & 3) || (lse && ((uintptr_t)lse & 3)))
+    return fail(GQAP_ERR_INVALID_ARGUMENT,
+                "device pointers must be 16-byte aligned (k_rope_scales, cu_seqlens, lse 4-byte)");
+  PrefillArgs a = ragged_args(plan, cu_seqlens, block_mask, out, lse);
+  const gqap_status ss =
+      split_setup((int32_t)plan->num_splits, d.total_tokens, d.num_q_heads, plan->workspace_bytes, workspace,
+                  workspace_bytes, &a);
+  if (ss != GQAP_OK) return ss;
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k;
+  a.v = (const uint16_t*)v;
+  a.kr = (const uint16_t*)k_rope;  // e4m3fn codes; the kernel reads bytes
+  a.ksc = k_rope_scales;
+  a.scale_log2 = scale * dev::kLog2e;
+  const dim3 grid = prefill_grid(d.batch, d.num_q_heads, a.hpw, plan->q_tiles, a.nsplit, d.total_tokens);
+  hipStream_t st = (hipStream_t)stream;
+  hipLaunchKernelGGL((prefill_fwd<64, false, 4>), grid, dim3(256), 0, st, a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(GQAP_ERR_HIP, "fp8-rope prefill launch: %s", hipGetErrorString(e));
   return launch_merge(a, d.max_seq_len, st);
 }
 
@@ -1176,7 +1290,7 @@ static gqap_status launch_fp8(const gqap_prefill_plan_t* plan, PrefillArgs& a, v
   const gqap_status ss = split_setup((int32_t)plan->num_splits, d.total_tokens, d.num_q_heads, plan->workspace_bytes,
                                      workspace, workspace_bytes, &a);
   if (ss != GQAP_OK) return ss;
-  const dim3 grid((unsigned)(d.num_q_heads / a.hpw) * (unsigned)d.batch * (unsigned)plan->q_tiles * (unsigned)a.nsplit);
+  const dim3 grid = prefill_grid(d.batch, d.num_q_heads, a.hpw, plan->q_tiles, a.nsplit, d.total_tokens);
   hipStream_t st = (hipStream_t)stream;
   if (d.head_dim_rope == 64)
     hipLaunchKernelGGL((prefill_fwd<64, false, F8>), grid, dim3(256), 0, st, a);
@@ -1361,7 +1475,7 @@ static gqap_status chunk_common(const gqap_chunk_plan_t* plan, const void* q, co
   const gqap_status ss = split_setup((int32_t)plan->num_splits, d.total_q_tokens, d.num_q_heads,
                                      plan->workspace_bytes, workspace, workspace_bytes, &a);
   if (ss != GQAP_OK) return ss;
-  const dim3 grid((unsigned)(d.num_q_heads / a.hpw) * (unsigned)d.batch * (unsigned)plan->q_tiles * (unsigned)a.nsplit);
+  const dim3 grid = prefill_grid(d.batch, d.num_q_heads, a.hpw, plan->q_tiles, a.nsplit, d.total_q_tokens);
   hipStream_t st = (hipStream_t)stream;
   if (d.head_dim_rope == 64) {
     if (fp8)

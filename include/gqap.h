@@ -10,6 +10,8 @@
  *     heads) and an optional 64x64 block-sparse mask;
  *   - the same prefill with the nope parts of Q and K in fp8 e4m3fn, one
  *     scale per tensor or one per row of a head, on the fp8 matrix cores;
+ *   - the MLA prefill with the shared rope key in fp8 e4m3fn, one scale per
+ *     rope row;
  *   - chunked prefill against the paged cache (append the chunk's keys and
  *     values, then attend to the cached prefix and the chunk), with a bf16
  *     cache or an fp8 e4m3fn cache with per-tensor scales;
@@ -367,6 +369,29 @@ gqap_status gqap_prefill_fp8_blockwise(const gqap_prefill_plan_t* plan,
                                        float scale, const float* q_scales, const float* k_scales,
                                        void* out, float* lse, void* workspace, uint64_t workspace_bytes,
                                        void* stream);
+
+/*
+ * Ragged causal MLA prefill with the shared rope key quantised (Modular
+ * flare_mla_prefill, the overload that takes k_rope together with
+ * k_rope_scales).  The plan is a bf16 plan with head_dim_rope 64 (layout as
+ * gqap_prefill); q, k and v are bf16.  k_rope [T, 1, 64] holds e4m3fn codes,
+ * its token stride kr_stride_token counted in bytes (a multiple of 16, at
+ * least 64); k_rope_scales [T] float32 holds one scale per rope row (the page
+ * leaves the scale layout open: one per row is the finest that keeps a row
+ * under one scale; a per-tensor scale is the case of equal entries).  The
+ * value of a code c of row j is e4m3fn(c) * k_rope_scales[j], so
+ *   score = scale * (q[i,h,:128] . k[j,g,:] + k_rope_scales[j] * (q[i,h,128:] . codes of k_rope[j])).
+ * Masking, ragged rows, lse, capacity and key-axis splits behave as in
+ * gqap_prefill.  Errors: INVALID_ARGUMENT (null or misaligned pointers, a
+ * plan without the rope part, a bad rope stride, non-finite scale), DTYPE (an
+ * fp8 plan), HIP.
+ */
+gqap_status gqap_prefill_rope_fp8(const gqap_prefill_plan_t* plan,
+                                  const void* q, const void* k, const void* v,
+                                  const void* k_rope, const float* k_rope_scales,
+                                  const int32_t* cu_seqlens, const uint8_t* block_mask,
+                                  float scale, void* out, float* lse,
+                                  void* workspace, uint64_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Chunked prefill against a paged KV cache                                  */

@@ -615,3 +615,24 @@ def test_noalloc_decode_rejects_a_plan_past_its_scratch_without_a_gpu(gq):
     assert gq.NOALLOC_SCRATCH_BYTES == 32 << 20
     text = open(HEADER).read()
     assert "#define GQAP_NOALLOC_SCRATCH_BYTES (32u << 20)" in text
+
+
+def test_rope_fp8_prefill_rejects_bad_arguments_without_a_gpu(gq):
+    """gqap_prefill_rope_fp8 validates before any device call: a plan of the
+    wrong dtype, one without the rope part, a rope stride that is not a
+    multiple of 16 bytes, null pointers."""
+    lib = gq.lib()
+    fake = 1 << 20
+    call = lambda p, kr=fake, krs=fake: lib.gqap_prefill_rope_fp8(ctypes.byref(p), fake, fake, fake, kr, krs, fake,
+                                                                   None, 0.1, fake, None, None, 0, None)
+    d = baseline_prefill_desc(gq)
+    d.kr_stride_token = 72                      # 72 bytes: not a multiple of 16
+    p = gq.gqap_prefill_plan(d)
+    assert gq.STATUS_NAMES[call(p)] == "INVALID_ARGUMENT" and "stride" in gq.gqap_last_error()
+    d.kr_stride_token = 64
+    p = gq.gqap_prefill_plan(d)
+    assert gq.STATUS_NAMES[call(p, krs=None)] == "INVALID_ARGUMENT"
+    assert gq.STATUS_NAMES[call(p, kr=None)] == "INVALID_ARGUMENT"
+    assert gq.STATUS_NAMES[call(gq.gqap_prefill_plan(baseline_prefill_desc(gq, mla=False)))] == "INVALID_ARGUMENT"
+    f = baseline_fp8_prefill_desc(gq)
+    assert gq.STATUS_NAMES[call(gq.gqap_prefill_plan(f))] == "DTYPE"

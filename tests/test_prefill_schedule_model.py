@@ -5,7 +5,8 @@ hpw workgroups per item: one head with hpw = 1, a pair of heads of one KV
 group with hpw = 2), key-axis split sp = (i // NH) % S, and the
 (i // NH // S)-th existing (sequence, query tile) item, items ranked deepest
 query tile first, then by sequence (for up to 64 sequences a wave ranks them
-with one ballot per depth; past 64 the order is plain).  A query tile has
+with one ballot per depth, and the grid holds only as many items as the rows
+can fill, (T + B (QT - 1)) / QT; past 64 the order is plain).  A query tile has
 QT = 128 / hpw rows; split sp takes key tiles [nkt sp / S, nkt (sp+1) / S)
 of the nkt tiles the tile needs.  Rows of a sequence past the plan's
 capacity are cleared by split 0 of the sequence's last query tile.
@@ -54,7 +55,11 @@ def simulate(lens, max_len, Hq, Hk, hpw, S, nb=None):
     NH = Hq // hpw
     ratio = Hq // Hk
     q_tiles = max(1 if lens else 0, -(-max_len // QT))
-    grid = NH * len(lens) * q_tiles * S
+    items = len(lens) * q_tiles
+    if len(lens) <= 64:   # the launch holds no more items than the rows can fill
+        T = sum(max(L, 0) for L in lens)
+        items = min(items, max(1 if lens else 0, (T + len(lens) * (QT - 1)) // QT))
+    grid = NH * items * S
     computed = {}      # (b, h, row) -> list of (sp, key-tile range)
     cleared = {}       # (b, h, row) -> count
     mask_rows = []     # (b, mask row index) read

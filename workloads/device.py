@@ -70,7 +70,12 @@ class DevicePrefill:
         self.qr = bits_to_tensor(case.q_rope, "bf16").to(device) if case.q_rope is not None else None
         self.k = bits_to_tensor(case.k, case.dtype).to(device)
         self.v = bits_to_tensor(case.v, "bf16").to(device)
-        self.kr = bits_to_tensor(case.k_rope, "bf16").to(device) if case.k_rope is not None else None
+        # the shared rope key: bf16, or e4m3fn codes with one scale per row
+        self.rope8 = getattr(case, "rope_dtype", "bf16") == "e4m3fn"
+        self.kr = (bits_to_tensor(case.k_rope, "e4m3fn" if self.rope8 else "bf16").to(device)
+                   if case.k_rope is not None else None)
+        if self.rope8:
+            self.krs = torch.from_numpy(np.ascontiguousarray(case.k_rope_scale, dtype=np.float32)).to(device)
         # fp8 with one scale per row of a head: [T, Hq] and [T, Hk] float32 arrays on the device
         self.blockwise = self.fp8 and np.ndim(case.q_scale) > 0
         if self.blockwise:
@@ -92,7 +97,10 @@ class DevicePrefill:
 
     def run(self, stream=None):
         ws, wsb = self.ws, self.plan.workspace_bytes
-        if self.blockwise:
+        if self.rope8:
+            gq.gqap_prefill_rope_fp8(self.plan, self.q, self.k, self.v, self.kr, self.krs, self.cu, self.mask,
+                                     self.case.scale, self.out, self.lse, ws, wsb, stream=stream)
+        elif self.blockwise:
             gq.gqap_prefill_fp8_blockwise(self.plan, self.q, self.qr, self.k, self.v, self.kr, self.cu, self.mask,
                                           self.case.scale, self.qsc, self.ksc, self.out, self.lse, ws, wsb,
                                           stream=stream)
