@@ -57,7 +57,7 @@ def _kernel_source_hash(kind: str = "decode") -> str:
 
 
 def _kind_of(workload: str) -> str:
-    return "prefill" if workload.startswith("prefill") else "decode"
+    return "prefill" if workload.startswith("prefill") or workload.startswith("decode_mt") else "decode"
 
 
 def _traffic(workload: str):
@@ -92,6 +92,10 @@ DOMINANT_KERNEL = {
     "prefill_chunk_long_mla_bf16": "prefill_fwd<64, true, 0>",
     "prefill_chunk_fp8kv": "prefill_fwd<0, true, 3>",
     "prefill_mla_rope_fp8": "prefill_fwd<64, false, 4>",
+    "decode_mt1_bf16": "prefill_fwd<0, true, 0>",
+    "decode_mt2_bf16": "prefill_fwd<0, true, 0>",
+    "decode_mt4_bf16": "prefill_fwd<0, true, 0>",
+    "decode_mt2_mla_bf16": "prefill_fwd<64, true, 0>",
 }
 
 
@@ -302,6 +306,37 @@ def bench_chunk(case, steps, warmup, torch, gq, gu, check=True):
     }
 
 
+def bench_mtdecode(case, steps, warmup, torch, gq, gu, check=True):
+    """Multi-token decode: the chunk's new tokens are already in the paged
+    cache (appended once, outside the timing); a step is the attention call.
+    Reported as cache bytes read per second (every key's K and V of every KV
+    head, plus the shared rope row), against the HBM peak."""
+    from workloads import gen
+    dc = gu.DeviceChunk(case)
+    dc.append()
+
+    def run(i):
+        dc.run()
+
+    ms_step, ms_ev, evs = _timed_loop(run, steps, warmup, torch)
+    err = None
+    if check:
+        from oracle import attention as O
+        out, _ = dc.results()
+        pools = dc.pools_bits()
+        rows = list(range(0, case.T, max(1, case.T // 48)))
+        ref, _ = O.chunk_prefill(case.q, pools[0], pools[1], case.block_table, case.cu_seqlens_q, case.kv_lens,
+                                 case.scale, dtype="bf16", rows=rows, kr_pool=pools[2] if len(pools) == 3 else None)
+        err = float(abs(out[rows] - ref).max())
+    nbytes = gen.kv_read_bytes(case)
+    return {
+        "workload": case.name, "bytes": nbytes, "q_len": int(case.q_lens.max()), "ms_per_step": ms_step,
+        "ms_kernel": ms_ev, "ms_kernel_p10": evs[len(evs) // 10], "ms_kernel_p90": evs[(9 * len(evs)) // 10],
+        "gbs_step": nbytes / (ms_step * 1e-3) / 1e9, "gbs_kernel": nbytes / (ms_ev * 1e-3) / 1e9,
+        "splits": int(dc.plan.num_splits), "max_abs_err_sample": err,
+    }
+
+
 def cpu_baseline_decode(case, budget_s: float = 12.0):
     """The oracle, as it is, on the host: whole decode passes over the same
     workload until about `budget_s` seconds have run (at least one)."""
@@ -368,6 +403,25 @@ def cpu_baseline_full(case):
             "sample": f"{what}, {dt:.1f} s"}
 
 
+def cpu_baseline_mtdecode(case):
+    """One full oracle evaluation of a multi-token decode workload (the
+    append and the attention of every query row), in the workload's unit."""
+    from oracle import attention as O
+    from oracle import parallel as OP
+    from workloads import gen
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    t0 = time.perf_counter()
+    pools = O.append_kv(case.k_new, case.v_new, case.k_pool, case.v_pool, case.block_table, case.cu_seqlens_q,
+                        case.kv_lens, kr_new=case.kr_new, kr_pool=case.kr_pool)
+    OP.all_rows(lambda rr: O.chunk_prefill(case.q, pools[0], pools[1], case.block_table, case.cu_seqlens_q,
+                                           case.kv_lens, case.scale, dtype="bf16", rows=rr,
+                                           kr_pool=pools[2] if len(pools) == 3 else None),
+                case.T, block=max(1, case.T // workers), workers=workers)
+    dt = time.perf_counter() - t0
+    return {"value": gen.kv_read_bytes(case) / dt / 1e9, "unit": "GB/s", "cores": workers, "kind": "oracle",
+            "sample": f"one full fp64 append and attention of all {case.T} query rows, {dt:.1f} s"}
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -412,6 +466,7 @@ def main(argv=None) -> int:
         mk = gen.CONFIGS[args.only]
         c = mk()
         fn = (bench_prefill if isinstance(c, gen.PrefillCase) else
+              bench_mtdecode if args.only.startswith("decode_mt") else
               bench_chunk if isinstance(c, gen.ChunkCase) else bench_decode)
         print(json.dumps(fn(c, args.steps, args.warmup, torch, gq, gu)), flush=True)
         if args.copy_calibration_bytes:
@@ -460,6 +515,15 @@ def main(argv=None) -> int:
                 rc["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline_full(cc)
                 secondary.append(rc)
                 del cc
+            # multi-token decode over config 2's cache shape (and its MLA form)
+            for wl in ("decode_mt1_bf16", "decode_mt2_bf16", "decode_mt4_bf16", "decode_mt2_mla_bf16"):
+                mc = gen.CONFIGS[wl]()
+                rm = bench_mtdecode(mc, args.steps, args.warmup, torch, gq, gu)
+                rm["roofline"] = {"bound": "hbm", "achieved": rm["gbs_kernel"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                  "frac": rm["gbs_kernel"] / HBM_PEAK_GBS, "traffic": _traffic(mc.name)}
+                rm["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline_mtdecode(mc)
+                secondary.append(rm)
+                del mc
 
     cpu = None if args.no_cpu_baseline else cpu_baseline_decode(case)
     line = {

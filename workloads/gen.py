@@ -671,6 +671,30 @@ def prefill_chunk_fp8kv(seed: int = 1006, B: int = 8, prefix_range=(1024, 6144),
                            q_lens=[q_len] * B, Hq=32, Hk=8, D=128, kv_dtype="e4m3fn")
 
 
+def decode_multitoken(q_len: int, seed: int = 1013, B: int = 64, len_range=(1024, 4096), Hq: int = 32,
+                      Hk: int = 8, D_rope: int = 0) -> ChunkCase:
+    """Multi-token decode: every sequence holds kv_len ~ U{len_range} keys in a
+    paged cache (config 2's shape: B=64, Hq=32, Hk=8, D=128), the last q_len of
+    them new tokens whose queries attend causally (bottom-right aligned).  With
+    D_rope = 64 it is the MLA form (per-head K plus one shared rope row per
+    token from the rope cache)."""
+    ss = np.random.SeedSequence(seed)
+    kv = np.random.Generator(np.random.PCG64(ss.spawn(1)[0])).integers(len_range[0], len_range[1] + 1, size=B)
+    name = f"decode_mt{q_len}" + ("_mla" if D_rope else "") + "_bf16"
+    c = make_chunk_case(name=name, seed=seed + 1, prefix_lens=(kv - q_len).tolist(), q_lens=[q_len] * B, Hq=Hq,
+                        Hk=Hk, D_rope=D_rope)
+    c.meta["seed"] = seed
+    return c
+
+
+def kv_read_bytes(case: "ChunkCase") -> int:
+    """Bytes of cache rows a decode over the case's keys must read: K and V of
+    every key and KV head (bf16), plus the shared rope row of every key."""
+    n = int(case.kv_lens.astype(np.int64).sum())
+    esz = 1 if case.kv_dtype == "e4m3fn" else 2
+    return n * case.Hk * case.D * 2 * esz + n * case.D_rope * 2
+
+
 CONFIGS = {
     "decode_tiny_f32": decode_tiny_fp32,
     "decode_gqa_bf16": decode_gqa_bf16,
@@ -684,4 +708,8 @@ CONFIGS = {
     "prefill_chunk_long_mla_bf16": prefill_chunk_long_mla_bf16,
     "prefill_chunk_fp8kv": prefill_chunk_fp8kv,
     "prefill_mla_rope_fp8": prefill_mla_rope_fp8,
+    "decode_mt1_bf16": lambda: decode_multitoken(1),
+    "decode_mt2_bf16": lambda: decode_multitoken(2),
+    "decode_mt4_bf16": lambda: decode_multitoken(4),
+    "decode_mt2_mla_bf16": lambda: decode_multitoken(2, Hq=16, Hk=16, D_rope=64),
 }
