@@ -57,7 +57,11 @@ def _kernel_source_hash(kind: str = "decode") -> str:
 
 
 def _kind_of(workload: str) -> str:
-    return "prefill" if workload.startswith("prefill") or workload.startswith("decode_mt") else "decode"
+    """Source set of the workload's dominant kernel: short GQA chunks run on
+    the decode workers, MLA ones on the prefill kernel."""
+    if workload.startswith("decode_mt"):
+        return "prefill" if "_mla" in workload else "decode"
+    return "prefill" if workload.startswith("prefill") else "decode"
 
 
 def _traffic(workload: str):
@@ -80,8 +84,8 @@ def _traffic(workload: str):
 
 # Dominant kernel of each workload, as rocprofv3 names it (substring match).
 DOMINANT_KERNEL = {
-    "decode_gqa_bf16": "decode_worker_mfma<128, false>",
-    "decode_long_fp8": "decode_worker_mfma<128, true>",
+    "decode_gqa_bf16": "decode_worker_mfma<128, false, false>",
+    "decode_long_fp8": "decode_worker_mfma<128, true, false>",
     "decode_tiny_fp32": "decode_worker_f32",
     "prefill_mla_bf16": "prefill_fwd<64, false, 0>",
     "prefill_blocksparse_bf16": "prefill_fwd<0, false, 0>",
@@ -92,9 +96,9 @@ DOMINANT_KERNEL = {
     "prefill_chunk_long_mla_bf16": "prefill_fwd<64, true, 0>",
     "prefill_chunk_fp8kv": "prefill_fwd<0, true, 3>",
     "prefill_mla_rope_fp8": "prefill_fwd<64, false, 4>",
-    "decode_mt1_bf16": "prefill_fwd<0, true, 0>",
-    "decode_mt2_bf16": "prefill_fwd<0, true, 0>",
-    "decode_mt4_bf16": "prefill_fwd<0, true, 0>",
+    "decode_mt1_bf16": "decode_worker_mfma<128, false, true>",
+    "decode_mt2_bf16": "decode_worker_mfma<128, false, true>",
+    "decode_mt4_bf16": "decode_worker_mfma<128, false, true>",
     "decode_mt2_mla_bf16": "prefill_fwd<64, true, 0>",
 }
 
@@ -333,7 +337,8 @@ def bench_mtdecode(case, steps, warmup, torch, gq, gu, check=True):
         "workload": case.name, "bytes": nbytes, "q_len": int(case.q_lens.max()), "ms_per_step": ms_step,
         "ms_kernel": ms_ev, "ms_kernel_p10": evs[len(evs) // 10], "ms_kernel_p90": evs[(9 * len(evs)) // 10],
         "gbs_step": nbytes / (ms_step * 1e-3) / 1e9, "gbs_kernel": nbytes / (ms_ev * 1e-3) / 1e9,
-        "splits": int(dc.plan.num_splits), "max_abs_err_sample": err,
+        "splits": int(dc.plan.num_splits), "kernel": DOMINANT_KERNEL.get(case.name), "plan_kernel": int(dc.plan.kernel),
+        "max_abs_err_sample": err,
     }
 
 
@@ -515,7 +520,7 @@ def main(argv=None) -> int:
                 rc["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline_full(cc)
                 secondary.append(rc)
                 del cc
-            # multi-token decode over config 2's cache shape (and its MLA form)
+            # multi-token decode over the paged-decode workload's cache shape (and its MLA form)
             for wl in ("decode_mt1_bf16", "decode_mt2_bf16", "decode_mt4_bf16", "decode_mt2_mla_bf16"):
                 mc = gen.CONFIGS[wl]()
                 rm = bench_mtdecode(mc, args.steps, args.warmup, torch, gq, gu)

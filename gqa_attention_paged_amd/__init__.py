@@ -110,6 +110,7 @@ class ChunkPlan(ctypes.Structure):
         ("desc", ChunkDesc), ("ratio", ctypes.c_int32), ("q_tiles", ctypes.c_int32),
         ("q_tile_rows", ctypes.c_int32), ("kernel", ctypes.c_int32), ("workspace_bytes", ctypes.c_uint64),
         ("magic", ctypes.c_uint32), ("num_splits", ctypes.c_uint32),
+        ("num_workers", ctypes.c_int32), ("head_chunks", ctypes.c_int32),
     ]
 
 

@@ -52,6 +52,11 @@ struct DecodeArgs {
   int64_t kv_block_bytes, kv_head_bytes, bt_stride;
   int32_t B, Hq, Hk, ratio, head_chunks, hkhc, nworkers;
   int32_t max_len;  // capacity from the plan; a longer (or negative) seq_len empties the sequence
+  // Chunk mode (cu != null): sequence b holds the query rows cu[b] .. cu[b+1]-1
+  // of a chunk aligned to the end of its seq_lens[b] keys; the first max_q of
+  // them are computed.  A unit's 16 columns are then (token, head) pairs.
+  const int32_t* cu;
+  int32_t max_q;
   float score_scale_log2;  // scale * k_scale * log2(e)
   float score_scale;       // scale * k_scale
   float v_scale;
@@ -66,12 +71,24 @@ __device__ __forceinline__ int ld_const(const int32_t* p, int64_t i) {
   return ((const int32_t __attribute__((address_space(4)))*)p)[i];
 }
 
-// Keys of sequence b.  A length outside [0, max_len] (the capacity the plan
-// was made for) is not truncated: the sequence is treated as empty, so its
-// rows come out as 0 with lse = -inf, the same whatever the length was.
-__device__ __forceinline__ int valid_len(const DecodeArgs& a, int b) {
+// Keys that the computed queries of sequence b read.  Decode: seq_lens[b].
+// A length outside [0, max_len] (the capacity the plan was made for) is not
+// truncated: the sequence is treated as empty, so its rows come out as 0 with
+// lse = -inf, the same whatever the length was.  Chunk mode (C): a chunk of
+// Lq rows ends at key seq_lens[b] - 1, and its row i sees the keys up to
+// seq_lens[b] - Lq + i; with only the first min(Lq, max_q) rows computed, the
+// keys read end at seq_lens[b] - Lq + min(Lq, max_q).  An empty chunk, or one
+// with more rows than keys or more keys than the capacity, reads nothing.
+template <bool C>
+__device__ __forceinline__ int seq_keys(const DecodeArgs& a, int b) {
   const int L = ld_const(a.seq_lens, b);
-  return (L < 0 || L > a.max_len) ? 0 : L;
+  if constexpr (!C) {
+    return (L < 0 || L > a.max_len) ? 0 : L;
+  } else {
+    const int Lq = ld_const(a.cu, b + 1) - ld_const(a.cu, b);
+    if (Lq <= 0 || L > a.max_len || L < Lq) return 0;
+    return L - Lq + min(Lq, a.max_q);
+  }
 }
 
 // Position of one work unit.
@@ -80,15 +97,23 @@ struct Unit {
   int ql;    // kv_head * head_chunks + head_chunk
   int j;     // key block within the sequence
   int nblk;  // key blocks of sequence b
-  int L;     // keys of sequence b
+  int L;     // keys read for sequence b
   int phys;  // pool block holding block j
+  int q0;    // first query row of sequence b (chunk mode)
+  int qc;    // computed query rows of sequence b (chunk mode)
 };
 
-__device__ __forceinline__ int seq_blocks(const DecodeArgs& a, int b) { return (valid_len(a, b) + 63) >> 6; }
+template <bool C>
+__device__ __forceinline__ int seq_blocks(const DecodeArgs& a, int b) { return (seq_keys<C>(a, b) + 63) >> 6; }
 
+template <bool C>
 __device__ __forceinline__ void unit_load_seq(const DecodeArgs& a, Unit& u) {
-  u.L = valid_len(a, u.b);
+  u.L = seq_keys<C>(a, u.b);
   u.nblk = (u.L + 63) >> 6;
+  if constexpr (C) {
+    u.q0 = ld_const(a.cu, u.b);
+    u.qc = min(ld_const(a.cu, u.b + 1) - u.q0, a.max_q);
+  }
 }
 
 __device__ __forceinline__ void unit_load_phys(const DecodeArgs& a, Unit& u) {
@@ -107,12 +132,13 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
 }
 
 // Key blocks of sequences [0, b_end), summed by one wave (all lanes get it).
+template <bool C>
 __device__ __forceinline__ int64_t blocks_before(const DecodeArgs& a, int b_end) {
   int64_t total = 0;
   const int lane = __lane_id();
   for (int b0 = 0; b0 < b_end; b0 += 64) {
     const int b = b0 + lane;
-    int nb = b < b_end ? seq_blocks(a, b) : 0;
+    int nb = b < b_end ? seq_blocks<C>(a, b) : 0;
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) nb += __shfl_xor(nb, off);
     total += nb;
@@ -122,12 +148,13 @@ __device__ __forceinline__ int64_t blocks_before(const DecodeArgs& a, int b_end)
 
 // Sequence holding key-block ordinal t (prefix[b] <= t < prefix[b+1]) and
 // prefix[b], found by one wave scanning seq_lens 64 sequences at a time.
+template <bool C>
 __device__ __forceinline__ void locate_block(const DecodeArgs& a, int64_t t, int* b_out, int64_t* before_out) {
   int64_t run = 0;
   const int lane = __lane_id();
   for (int b0 = 0; b0 < a.B; b0 += 64) {
     const int b = b0 + lane;
-    const int nb = b < a.B ? seq_blocks(a, b) : 0;
+    const int nb = b < a.B ? seq_blocks<C>(a, b) : 0;
     const int incl = wave_incl_scan(nb);
     const bool hit = nb > 0 && run + incl - nb <= t && t < run + incl;
     const unsigned long long m = __ballot(hit);
@@ -144,12 +171,13 @@ __device__ __forceinline__ void locate_block(const DecodeArgs& a, int64_t t, int
 }
 
 // Exclusive prefix of the per-sequence block counts -> a.prefix[0..B] (one wave).
+template <bool C>
 __device__ __forceinline__ void write_prefix(const DecodeArgs& a) {
   int64_t run = 0;
   const int lane = __lane_id();
   for (int b0 = 0; b0 < a.B; b0 += 64) {
     const int b = b0 + lane;
-    const int nb = b < a.B ? seq_blocks(a, b) : 0;
+    const int nb = b < a.B ? seq_blocks<C>(a, b) : 0;
     const int incl = wave_incl_scan(nb);
     if (b < a.B) a.prefix[b] = (int32_t)(run + incl - nb);
     run += __shfl(incl, 63);
@@ -158,11 +186,12 @@ __device__ __forceinline__ void write_prefix(const DecodeArgs& a) {
 }
 
 // First unit of a worker whose range starts at unit ub.
+template <bool C>
 __device__ __forceinline__ Unit unit_at(const DecodeArgs& a, int64_t ub) {
   Unit u;
   int64_t before;
-  locate_block(a, ub / a.hkhc, &u.b, &before);
-  unit_load_seq(a, u);
+  locate_block<C>(a, ub / a.hkhc, &u.b, &before);
+  unit_load_seq<C>(a, u);
   const int rem = (int)(ub - before * a.hkhc);
   u.ql = rem / u.nblk;
   u.j = rem - u.ql * u.nblk;
@@ -172,6 +201,7 @@ __device__ __forceinline__ Unit unit_at(const DecodeArgs& a, int64_t ub) {
 
 // Next unit in sequence-major order, skipping sequences without keys.  Only
 // called while the worker's range still holds a unit, so b stays below B.
+template <bool C>
 __device__ __forceinline__ Unit unit_next(const DecodeArgs& a, Unit u) {
   if (++u.j == u.nblk) {
     u.j = 0;
@@ -179,8 +209,8 @@ __device__ __forceinline__ Unit unit_next(const DecodeArgs& a, Unit u) {
       u.ql = 0;
       do {
         ++u.b;
-      } while (u.b < a.B && seq_blocks(a, u.b) == 0);
-      if (u.b < a.B) unit_load_seq(a, u);
+      } while (u.b < a.B && seq_blocks<C>(a, u.b) == 0);
+      if (u.b < a.B) unit_load_seq<C>(a, u);
     }
   }
   if (u.b < a.B) unit_load_phys(a, u);
@@ -213,7 +243,10 @@ __device__ __forceinline__ int vswz(int row, int c) {
 
 using namespace dev;
 
-template <int D, bool FP8>
+// C: chunk mode.  Column col of head chunk hc is then the pair (token i,
+// head hh) with hc * 16 + col = i * ratio + hh, and its keys end at its own
+// causal bound, so every column carries its own key limit.
+template <int D, bool FP8, bool C>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_worker_mfma(DecodeArgs a) {
   constexpr int ESZ = FP8 ? 1 : 2;
   constexpr int RB = D * ESZ;        // bytes per K/V row
@@ -229,8 +262,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   const int lane = threadIdx.x;
   const int col = lane & 15;
   const int G = lane >> 4;
-  if (w == 0) write_prefix(a);  // for the combine pass
-  const int64_t W = blocks_before(a, a.B) * a.hkhc;
+  if (w == 0) write_prefix<C>(a);  // for the combine pass
+  const int64_t W = blocks_before<C>(a, a.B) * a.hkhc;
   const int64_t ub = W * w / a.nworkers;
   const int64_t ue = W * (w + 1) / a.nworkers;
   if (ub >= ue) return;
@@ -245,6 +278,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   float m_run, l_run;
   f32x4 o[NT];
   f32x4 s[2];
+  int klim = 0;  // chunk mode: keys of this lane's column, [0, klim) of the sequence
 
   auto reset = [&]() {
     m_run = -INFINITY;
@@ -258,14 +292,33 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
     return (int64_t)u.phys * a.kv_block_bytes + (int64_t)g * a.kv_head_bytes;
   };
 
+  // (token, head) of this lane's column in the piece's head chunk; decode
+  // has one token, so the column is the head.
+  auto column = [&](const Unit& u, int* tok, int* hl) {
+    const int g = u.ql / a.head_chunks;
+    const int gc = (u.ql - g * a.head_chunks) * 16 + col;
+    *tok = C ? gc / a.ratio : 0;
+    *hl = gc - *tok * a.ratio;
+    return C ? *tok < u.qc : gc < a.ratio;
+  };
+
+  // Chunk mode: row i of the chunk sees keys [0, L - qc + 1 + i); a column
+  // without a query keeps the sequence's whole range (its q is zero).
+  auto set_limit = [&](const Unit& u) {
+    if constexpr (C) {
+      int tok, hl;
+      klim = column(u, &tok, &hl) ? u.L - u.qc + 1 + tok : u.L;
+    }
+  };
+
   // Query heads of the piece's chunk as the B operand (k slots match the K loads).
   auto load_q = [&](const Unit& u) {
     const int g = u.ql / a.head_chunks;
-    const int hc = u.ql - g * a.head_chunks;
-    const int hl = hc * 16 + col;
-    const bool hvalid = hl < a.ratio;
+    int tok, hl;
+    const bool hvalid = column(u, &tok, &hl);
+    const int64_t row = C ? (int64_t)u.q0 + (hvalid ? tok : 0) : (int64_t)u.b;
     const unsigned char* qp = (const unsigned char*)a.q +
-                              ((int64_t)u.b * a.q_sb + (int64_t)(g * a.ratio + (hvalid ? hl : 0)) * a.q_sh) * 2;
+                              (row * a.q_sb + (int64_t)(g * a.ratio + (hvalid ? hl : 0)) * a.q_sh) * 2;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
       const int d0 = FP8 ? (64 * (ks >> 1) + 16 * G + 8 * (ks & 1)) : (32 * ks + 8 * G);
@@ -326,26 +379,30 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   auto softmax_pv = [&](const Unit& u, auto hc_) {
     constexpr int H = decltype(hc_)::value;
     const int valid = min(64, u.L - 64 * u.j) - 32 * H;  // may be <= 0: then the half is all padding
-    // Keys past seq_len are dropped by select: whatever the padding rows hold
-    // never reaches the sums.
+    // Keys past seq_len (chunk mode: past the column's own limit) are dropped
+    // by select: whatever the padding rows hold never reaches the sums.
+    const int kvalid = C ? min(64, klim - 64 * u.j) - 32 * H : valid;
     float bmax = -INFINITY;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float x = token_of<FP8>(t, 4 * G + j) < valid ? s[t][j] * a.score_scale_log2 : -INFINITY;
+        const float x = token_of<FP8>(t, 4 * G + j) < kvalid ? s[t][j] * a.score_scale_log2 : -INFINITY;
         s[t][j] = x;
         bmax = fmaxf(bmax, x);
       }
     bmax = wave_max4(bmax);
     const float m_new = fmaxf(m_run, bmax);
-    const float alpha = fast_exp2(m_run - m_new);
+    // Chunk mode: a column may have seen no key yet (its keys end before this
+    // piece's); subtracting 0 instead of -inf keeps its sums at exactly 0.
+    const float m_sub = C && m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_sub);
     float psum = 0.f;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float p = fast_exp2(s[t][j] - m_new);
+        const float p = fast_exp2(s[t][j] - m_sub);
         s[t][j] = p;
         psum += p;
       }
@@ -401,12 +458,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   // Normalised partial of the finished piece -> its workspace slot.
   auto flush = [&](const Unit& u) {
     const float l_tot = wave_sum4(l_run);
-    const int g = u.ql / a.head_chunks;
-    const int hc = u.ql - g * a.head_chunks;
-    const int rc = min(16, a.ratio - hc * 16);
+    int tok, hl;
+    const bool cvalid = column(u, &tok, &hl);
     const int64_t slot = (int64_t)u.b * a.hkhc + u.ql + w;
-    if (col < rc) {
-      const float inv = a.v_scale / l_tot;
+    if (cvalid) {
+      // A chunk column with no key in this piece leaves 0 and lse -inf.
+      const float inv = C && l_tot == 0.f ? 0.f : a.v_scale / l_tot;
       float* dst = a.ws_o + (slot * 16 + col) * D + 4 * G;
 #pragma unroll
       for (int n = 0; n < NT; ++n) *(f32x4*)(dst + 16 * n) = o[n] * inv;
@@ -426,12 +483,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   // which keeps the compiler's wait counts exact); the last unit is peeled.
   // A new query operand is loaded right after the scores that last used the
   // old one, ahead of that step's K issue.
-  Unit cur = unit_at(a, ub);
+  Unit cur = unit_at<C>(a, ub);
   reset();
+  set_limit(cur);
   load_q(cur);
   issue_k(cur, H0{});
   issue_v(cur, H0{});
-  Unit nx = count > 1 ? unit_next(a, cur) : cur;
+  Unit nx = count > 1 ? unit_next<C>(a, cur) : cur;
   stage_v();
   issue_v(cur, H1{});
   int i = 0;
@@ -453,8 +511,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
     if (boundary) {
       flush(cur);
       reset();
+      set_limit(nx);
     }
-    const Unit nx2 = (i + 2 < count) ? unit_next(a, nx) : nx;
+    const Unit nx2 = (i + 2 < count) ? unit_next<C>(a, nx) : nx;
     cur = nx;
     nx = nx2;
   }
@@ -480,8 +539,8 @@ __global__ __launch_bounds__(64) void decode_worker_f32(DecodeArgs a) {
 
   const int w = blockIdx.x;
   const int lane = threadIdx.x;
-  if (w == 0) write_prefix(a);  // for the combine pass
-  const int64_t W = blocks_before(a, a.B) * a.hkhc;
+  if (w == 0) write_prefix<false>(a);  // for the combine pass
+  const int64_t W = blocks_before<false>(a, a.B) * a.hkhc;
   const int64_t ub = W * w / a.nworkers;
   const int64_t ue = W * (w + 1) / a.nworkers;
   if (ub >= ue) return;
@@ -526,7 +585,7 @@ __global__ __launch_bounds__(64) void decode_worker_f32(DecodeArgs a) {
     }
   };
 
-  Unit u = unit_at(a, ub);
+  Unit u = unit_at<false>(a, ub);
   reset();
   load_q(u);
   for (int i = 0; i < count; ++i) {
@@ -578,7 +637,7 @@ __global__ __launch_bounds__(64) void decode_worker_f32(DecodeArgs a) {
       flush(u);
       break;
     }
-    const Unit nx = unit_next(a, u);
+    const Unit nx = unit_next<false>(a, u);
     if (!same_piece(u, nx)) {
       flush(u);
       reset();
@@ -592,7 +651,11 @@ __global__ __launch_bounds__(64) void decode_worker_f32(DecodeArgs a) {
 // One wave; lane k holds the LSE of piece k (64 pieces per round), and the
 // output rows of all pieces are requested before any arithmetic, so the
 // merge costs one memory round trip for the usual handful of pieces.
-template <int D, bool OUT_BF16>
+// Chunk mode (C): workgroup (sequence, query head, y) takes row y of the
+// sequence's chunk, and the last y also every row past max_q; rows past the
+// computed ones (and every row of a chunk that reads no key) get 0 and lse
+// -inf.
+template <int D, bool OUT_BF16, bool C>
 __global__ __launch_bounds__(64) void decode_combine(DecodeArgs a) {
   constexpr int DC = D / 64;
   const int bh = blockIdx.x;
@@ -601,100 +664,113 @@ __global__ __launch_bounds__(64) void decode_combine(DecodeArgs a) {
   const int lane = threadIdx.x;
   const int g = h / a.ratio;
   const int hh = h - g * a.ratio;
-  const int hc = hh >> 4;
-  const int col = hh & 15;
-  const int ql = g * a.head_chunks + hc;
-  const int64_t qg = (int64_t)b * a.hkhc + ql;
   const int pb = ld_const(a.prefix, b);
   const int nblk = ld_const(a.prefix, b + 1) - pb;
-  float acc[DC];
+  const int row0 = C ? ld_const(a.cu, b) : b;
+  const int rows = C ? ld_const(a.cu, b + 1) - row0 : 1;
+  const int qc = C ? min(rows, a.max_q) : 1;
+  const int i0 = C ? (int)blockIdx.y : 0;
+  const int i_end = !C ? 1 : (int)blockIdx.y + 1 == (int)gridDim.y ? rows : min(rows, i0 + 1);
+  for (int i = i0; i < i_end; ++i) {
+    const bool computed = nblk > 0 && i < qc;
+    const int gc = computed ? i * a.ratio + hh : 0;  // column of (token i, head hh)
+    const int hc = gc >> 4;
+    const int col = gc & 15;
+    const int ql = g * a.head_chunks + hc;
+    const int64_t qg = (int64_t)b * a.hkhc + ql;
+    float acc[DC];
 #pragma unroll
-  for (int c = 0; c < DC; ++c) acc[c] = 0.f;
-  float M = -INFINITY, den = 0.f;
-  if (nblk > 0) {
-    const int64_t W = (int64_t)ld_const(a.prefix, a.B) * a.hkhc;
-    const int64_t u0 = (int64_t)pb * a.hkhc + (int64_t)ql * nblk;
-    const int64_t u1 = u0 + nblk;
-    const int64_t P = a.nworkers;
-    const int w0 = (int)(((u0 + 1) * P - 1) / W);  // worker holding unit u0
-    const int w1 = (int)((u1 * P - 1) / W);        // worker holding unit u1 - 1
-    // With fewer units than workers some workers own no unit; they wrote nothing.
-    auto owns_units = [&](int wk) { return W * wk / P < W * (wk + 1) / P; };
-    if (w1 - w0 < 4) {
-      // Up to four pieces (the usual case): their LSEs and rows are requested
-      // together, so the merge costs a single memory round trip.
-      const int n = w1 - w0 + 1;
-      const bool live = lane < n && owns_units(w0 + lane);
-      const float lse_k = live ? a.ws_lse[(qg + w0 + lane) * 16 + col] : -INFINITY;
-      float v4[4][DC];
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const float* op = a.ws_o + ((qg + w0 + min(kk, n - 1)) * 16 + col) * D;
-#pragma unroll
-        for (int c = 0; c < DC; ++c) v4[kk][c] = op[lane + 64 * c];
-      }
-      M = lse_k;
-#pragma unroll
-      for (int off = 2; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-      M = __shfl(M, 0);
-      const float wt_k = live ? exp2f(lse_k - M) : 0.f;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const float w = __shfl(wt_k, kk);  // 0 for kk >= n or a piece-less worker
-        den += w;
-#pragma unroll
-        for (int c = 0; c < DC; ++c) acc[c] += w > 0.f ? w * v4[kk][c] : 0.f;
-      }
-    } else
-    for (int r0 = w0; r0 <= w1; r0 += 64) {
-      const int wk = r0 + lane;
-      const bool live = wk <= w1 && owns_units(wk);
-      const float lse_k = live ? a.ws_lse[(qg + wk) * 16 + col] : -INFINITY;
-      float m_round = lse_k;
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) m_round = fmaxf(m_round, __shfl_xor(m_round, off));
-      const float M_new = fmaxf(M, m_round);
-      const float scale_old = M == -INFINITY ? 0.f : exp2f(M - M_new);
-#pragma unroll
-      for (int c = 0; c < DC; ++c) acc[c] *= scale_old;
-      den *= scale_old;
-      const float wt_k = live ? exp2f(lse_k - M_new) : 0.f;
-      float wsum = wt_k;
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) wsum += __shfl_xor(wsum, off);
-      den += wsum;
-      const int n = min(64, w1 - r0 + 1);
-      // Four pieces per trip, all loads first.  Slots of empty workers are
-      // read (they are inside the workspace) but dropped by select, so stale
-      // contents never reach the sum.
-      for (int k0 = 0; k0 < n; k0 += 4) {
-        float v4[4][DC], w4[4];
+    for (int c = 0; c < DC; ++c) acc[c] = 0.f;
+    float M = -INFINITY, den = 0.f;
+    if (computed) {
+      const int64_t W = (int64_t)ld_const(a.prefix, a.B) * a.hkhc;
+      const int64_t u0 = (int64_t)pb * a.hkhc + (int64_t)ql * nblk;
+      const int64_t u1 = u0 + nblk;
+      const int64_t P = a.nworkers;
+      const int w0 = (int)(((u0 + 1) * P - 1) / W);  // worker holding unit u0
+      const int w1 = (int)((u1 * P - 1) / W);        // worker holding unit u1 - 1
+      // With fewer units than workers some workers own no unit; they wrote nothing.
+      auto owns_units = [&](int wk) { return W * wk / P < W * (wk + 1) / P; };
+      if (w1 - w0 < 4) {
+        // Up to four pieces (the usual case): their LSEs and rows are requested
+        // together, so the merge costs a single memory round trip.
+        const int n = w1 - w0 + 1;
+        const bool live = lane < n && owns_units(w0 + lane);
+        const float lse_k = live ? a.ws_lse[(qg + w0 + lane) * 16 + col] : -INFINITY;
+        float v4[4][DC];
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-          const int k = min(k0 + kk, n - 1);
-          w4[kk] = k0 + kk < n ? __shfl(wt_k, k) : 0.f;
-          const float* op = a.ws_o + ((qg + r0 + k) * 16 + col) * D;
+          const float* op = a.ws_o + ((qg + w0 + min(kk, n - 1)) * 16 + col) * D;
 #pragma unroll
           for (int c = 0; c < DC; ++c) v4[kk][c] = op[lane + 64 * c];
         }
+        M = lse_k;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
+        for (int off = 2; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+        M = __shfl(M, 0);
+        const float wt_k = live ? exp2f(lse_k - M) : 0.f;
 #pragma unroll
-          for (int c = 0; c < DC; ++c) acc[c] += w4[kk] > 0.f ? w4[kk] * v4[kk][c] : 0.f;
+        for (int kk = 0; kk < 4; ++kk) {
+          const float w = __shfl(wt_k, kk);  // 0 for kk >= n or a piece-less worker
+          den += w;
+#pragma unroll
+          for (int c = 0; c < DC; ++c) acc[c] += w > 0.f ? w * v4[kk][c] : 0.f;
+        }
+      } else
+      for (int r0 = w0; r0 <= w1; r0 += 64) {
+        const int wk = r0 + lane;
+        const bool live = wk <= w1 && owns_units(wk);
+        const float lse_k = live ? a.ws_lse[(qg + wk) * 16 + col] : -INFINITY;
+        float m_round = lse_k;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) m_round = fmaxf(m_round, __shfl_xor(m_round, off));
+        const float M_new = fmaxf(M, m_round);
+        const float scale_old = M == -INFINITY ? 0.f : exp2f(M - M_new);
+#pragma unroll
+        for (int c = 0; c < DC; ++c) acc[c] *= scale_old;
+        den *= scale_old;
+        const float wt_k = live ? exp2f(lse_k - M_new) : 0.f;
+        float wsum = wt_k;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) wsum += __shfl_xor(wsum, off);
+        den += wsum;
+        const int n = min(64, w1 - r0 + 1);
+        // Four pieces per trip, all loads first.  Slots of empty workers are
+        // read (they are inside the workspace) but dropped by select, so stale
+        // contents never reach the sum.
+        for (int k0 = 0; k0 < n; k0 += 4) {
+          float v4[4][DC], w4[4];
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) {
+            const int k = min(k0 + kk, n - 1);
+            w4[kk] = k0 + kk < n ? __shfl(wt_k, k) : 0.f;
+            const float* op = a.ws_o + ((qg + r0 + k) * 16 + col) * D;
+#pragma unroll
+            for (int c = 0; c < DC; ++c) v4[kk][c] = op[lane + 64 * c];
+          }
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+            for (int c = 0; c < DC; ++c) acc[c] += w4[kk] > 0.f ? w4[kk] * v4[kk][c] : 0.f;
+        }
+        M = M_new;
       }
-      M = M_new;
     }
-  }
-  const int64_t obase = (int64_t)b * a.o_sb + (int64_t)h * a.o_sh;
+    // A chunk row can have a zero denominator only if all its pieces saw no
+    // key, which the causal bound rules out; the guard keeps it at 0 anyway.
+    const bool some = computed && den > 0.f;
+    const int64_t row = (int64_t)row0 + i;
+    const int64_t obase = row * a.o_sb + (int64_t)h * a.o_sh;
 #pragma unroll
-  for (int c = 0; c < DC; ++c) {
-    const float v = nblk > 0 ? acc[c] / den : 0.f;
-    if (OUT_BF16)
-      ((uint16_t*)a.out)[obase + lane + 64 * c] = f32_to_bf16(v);
-    else
-      ((float*)a.out)[obase + lane + 64 * c] = v;
+    for (int c = 0; c < DC; ++c) {
+      const float v = some ? acc[c] / den : 0.f;
+      if (OUT_BF16)
+        ((uint16_t*)a.out)[obase + lane + 64 * c] = f32_to_bf16(v);
+      else
+        ((float*)a.out)[obase + lane + 64 * c] = v;
+    }
+    if (a.lse && lane == 0) a.lse[row * a.Hq + h] = some ? (M + log2f(den)) * kLn2 : -INFINITY;
   }
-  if (a.lse && lane == 0) a.lse[bh] = nblk > 0 ? (M + log2f(den)) * kLn2 : -INFINITY;
 }
 
 // Padded block table from the flat CSR page list (MATE msa_interface,
@@ -862,15 +938,15 @@ gqap_status gqap::decode_launch(const gqap_decode_plan_t* plan, const void* q, c
       break;
     case kDecodeBf16Mfma:
       if (d128)
-        hipLaunchKernelGGL((decode_worker_mfma<128, false>), grid, dim3(64), 0, st, a);
+        hipLaunchKernelGGL((decode_worker_mfma<128, false, false>), grid, dim3(64), 0, st, a);
       else
-        hipLaunchKernelGGL((decode_worker_mfma<64, false>), grid, dim3(64), 0, st, a);
+        hipLaunchKernelGGL((decode_worker_mfma<64, false, false>), grid, dim3(64), 0, st, a);
       break;
     case kDecodeFp8Mfma:
       if (d128)
-        hipLaunchKernelGGL((decode_worker_mfma<128, true>), grid, dim3(64), 0, st, a);
+        hipLaunchKernelGGL((decode_worker_mfma<128, true, false>), grid, dim3(64), 0, st, a);
       else
-        hipLaunchKernelGGL((decode_worker_mfma<64, true>), grid, dim3(64), 0, st, a);
+        hipLaunchKernelGGL((decode_worker_mfma<64, true, false>), grid, dim3(64), 0, st, a);
       break;
     default:
       return fail(GQAP_ERR_INVALID_ARGUMENT, "unknown kernel variant %u", plan->kernel);
@@ -881,17 +957,81 @@ gqap_status gqap::decode_launch(const gqap_decode_plan_t* plan, const void* q, c
   const bool bf16_out = d.q_dtype == GQAP_BF16;
   if (d128) {
     if (bf16_out)
-      hipLaunchKernelGGL((decode_combine<128, true>), cgrid, dim3(64), 0, st, a);
+      hipLaunchKernelGGL((decode_combine<128, true, false>), cgrid, dim3(64), 0, st, a);
     else
-      hipLaunchKernelGGL((decode_combine<128, false>), cgrid, dim3(64), 0, st, a);
+      hipLaunchKernelGGL((decode_combine<128, false, false>), cgrid, dim3(64), 0, st, a);
   } else {
     if (bf16_out)
-      hipLaunchKernelGGL((decode_combine<64, true>), cgrid, dim3(64), 0, st, a);
+      hipLaunchKernelGGL((decode_combine<64, true, false>), cgrid, dim3(64), 0, st, a);
     else
-      hipLaunchKernelGGL((decode_combine<64, false>), cgrid, dim3(64), 0, st, a);
+      hipLaunchKernelGGL((decode_combine<64, false, false>), cgrid, dim3(64), 0, st, a);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return fail(GQAP_ERR_HIP, "decode combine launch: %s", hipGetErrorString(e));
+  return GQAP_OK;
+}
+
+gqap_status gqap::chunk_decode_launch(const gqap_chunk_plan_t* plan, const void* q, const void* k_pool,
+                                     const void* v_pool, const int32_t* block_table, const int32_t* cu_seqlens_q,
+                                     const int32_t* kv_lens, float scale, bool fp8, float k_scale, float v_scale,
+                                     void* out, float* lse, void* workspace, uint64_t workspace_bytes,
+                                     void* stream) {
+  const gqap_chunk_desc_t& d = plan->desc;
+  if (!workspace) return fail(GQAP_ERR_INVALID_ARGUMENT, "this plan needs a workspace of %llu bytes",
+                              (unsigned long long)plan->workspace_bytes);
+  if (misaligned(workspace, 256)) return fail(GQAP_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  if (workspace_bytes < plan->workspace_bytes)
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "workspace of %llu bytes < %llu required",
+                (unsigned long long)workspace_bytes, (unsigned long long)plan->workspace_bytes);
+  if (d.head_dim != 128 || d.head_dim_rope != 0 || plan->num_workers <= 0 || plan->head_chunks <= 0)
+    return fail(GQAP_ERR_INVALID_ARGUMENT, "chunk plan is not one for the decode workers");
+  const int kv_esz = fp8 ? 1 : 2;
+  const int64_t pieces = (int64_t)d.batch * d.num_kv_heads * plan->head_chunks + plan->num_workers;
+  const DecodeWorkspace lay = decode_workspace(d.batch, pieces, d.head_dim);
+  if (lay.total > plan->workspace_bytes) return fail(GQAP_ERR_INVALID_ARGUMENT, "chunk plan workspace too small");
+  char* ws = (char*)workspace;
+  DecodeArgs a{};
+  a.q = q;
+  a.k = k_pool;
+  a.v = v_pool;
+  a.block_table = block_table;
+  a.seq_lens = kv_lens;
+  a.prefix = (int32_t*)(ws + lay.prefix);
+  a.ws_lse = (float*)(ws + lay.lse);
+  a.ws_o = (float*)(ws + lay.o);
+  a.out = out;
+  a.lse = lse;
+  a.q_sb = d.q_stride_token;
+  a.q_sh = d.q_stride_head;
+  a.o_sb = d.out_stride_token;
+  a.o_sh = d.out_stride_head;
+  a.kv_block_bytes = d.kv_stride_block * kv_esz;
+  a.kv_head_bytes = d.kv_stride_head * kv_esz;
+  a.bt_stride = d.block_table_stride;
+  a.B = d.batch;
+  a.Hq = d.num_q_heads;
+  a.Hk = d.num_kv_heads;
+  a.ratio = plan->ratio;
+  a.head_chunks = plan->head_chunks;
+  a.hkhc = d.num_kv_heads * plan->head_chunks;
+  a.nworkers = plan->num_workers;
+  a.max_len = d.max_kv_len;
+  a.cu = cu_seqlens_q;
+  a.max_q = d.max_q_len;
+  a.score_scale = scale * (fp8 ? k_scale : 1.f);
+  a.score_scale_log2 = a.score_scale * dev::kLog2e;
+  a.v_scale = fp8 ? v_scale : 1.f;
+  hipStream_t st = (hipStream_t)stream;
+  if (fp8)
+    hipLaunchKernelGGL((decode_worker_mfma<128, true, true>), dim3(plan->num_workers), dim3(64), 0, st, a);
+  else
+    hipLaunchKernelGGL((decode_worker_mfma<128, false, true>), dim3(plan->num_workers), dim3(64), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(GQAP_ERR_HIP, "chunk decode launch: %s", hipGetErrorString(e));
+  hipLaunchKernelGGL((decode_combine<128, true, true>), dim3(d.batch * d.num_q_heads, d.max_q_len), dim3(64), 0, st,
+                     a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return fail(GQAP_ERR_HIP, "chunk decode combine launch: %s", hipGetErrorString(e));
   return GQAP_OK;
 }
 

@@ -337,9 +337,24 @@ extern "C" gqap_status gqap_chunk_plan(const gqap_chunk_desc_t* desc, gqap_chunk
   if ((int64_t)d.total_q_tokens * Hk * (D / 8) > kMaxLaunchItems)
     return fail(GQAP_ERR_UNSUPPORTED, "T * Hk = %lld (token, KV head) rows exceed one append launch",
                 (long long)d.total_q_tokens * Hk);
-  plan->kernel = (Dr ? 2 : 1) + (kv_esz == 1 ? 2 : 0);
+  plan->kernel = (Dr ? kChunkPrefillMla : kChunkPrefill) + (kv_esz == 1 ? 2 : 0);
   plan->num_splits = (uint32_t)ns;
   plan->workspace_bytes = split_workspace(ns, d.total_q_tokens, d.num_q_heads);
+  // Short chunks go to the decode workers when the (token, head) pairs of a
+  // KV head fit in as many 16-column tiles as one token's heads: every K/V
+  // byte is then read once per tile, where the prefill kernel reads it once
+  // per query head.  Forced splits keep the prefill kernel.
+  const int64_t hc_token = ceil_div(plan->ratio, 16);
+  const int64_t hc_chunk = ceil_div((int64_t)d.max_q_len * plan->ratio, 16);
+  if (!Dr && d.num_splits == 0 && d.max_q_len >= 1 && hc_chunk == hc_token) {
+    plan->kernel = kv_esz == 1 ? kChunkDecodeFp8 : kChunkDecode;
+    plan->num_splits = 1;
+    plan->head_chunks = (int32_t)hc_chunk;
+    plan->num_workers = kDefaultCUs * decode_waves_per_cu(kv_esz == 1 ? kDecodeFp8Mfma : kDecodeBf16Mfma, 128);
+    const int64_t pieces = (int64_t)d.batch * Hk * hc_chunk + plan->num_workers;
+    if (pieces > INT32_MAX / 16) return fail(GQAP_ERR_UNSUPPORTED, "too many partial slots for the decode workers");
+    plan->workspace_bytes = decode_workspace(d.batch, pieces, D).total;
+  }
   plan->magic = GQAP_PLAN_MAGIC;
   return GQAP_OK;
 }

@@ -36,6 +36,23 @@ enum DecodeKernel : uint32_t {
   kDecodeFp8Mfma = 3,   // bf16 q / fp8 e4m3fn KV, dequantised to bf16 for the matrix cores
 };
 
+// Kernel variants recorded in a chunked-prefill plan.
+enum ChunkKernel : int32_t {
+  kChunkPrefill = 1,         // prefill kernel over the paged cache
+  kChunkPrefillMla = 2,      // the same with the shared rope cache
+  kChunkPrefillFp8 = 3,      // prefill kernel over an fp8 cache
+  kChunkPrefillMlaFp8 = 4,   // fp8 cache with the bf16 rope cache
+  kChunkDecode = 5,          // short chunks on the decode workers
+  kChunkDecodeFp8 = 6,       // the same over an fp8 cache
+};
+
+// Short chunks on the decode workers (decode.hip).  The caller has checked
+// the plan, the scales, the pointers and their alignment.
+gqap_status chunk_decode_launch(const gqap_chunk_plan_t* plan, const void* q, const void* k_pool,
+                                const void* v_pool, const int32_t* block_table, const int32_t* cu_seqlens_q,
+                                const int32_t* kv_lens, float scale, bool fp8, float k_scale, float v_scale,
+                                void* out, float* lse, void* workspace, uint64_t workspace_bytes, void* stream);
+
 // Byte offsets of the decode workspace regions (shared by planner and launcher).
 //   prefix [B + 1] int32          key blocks before each sequence
 //   lse    [pieces][16] float32   base-2 log-sum-exp of each partial

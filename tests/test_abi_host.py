@@ -355,6 +355,56 @@ def test_chunk_plan_baseline(gq):
     assert p.workspace_bytes == 0
 
 
+@pytest.mark.parametrize("Hq,Hk,max_q,Dr,splits,kernel,head_chunks", [
+    (32, 8, 4, 0, 0, 5, 1),       # 4 tokens x 4 heads: one 16-column tile
+    (32, 8, 5, 0, 0, 1, 0),       # 20 pairs: two tiles where one token takes one -> prefill kernel
+    (32, 8, 1, 0, 0, 5, 1),
+    (16, 16, 16, 0, 0, 5, 1),     # one head per KV head, 16 tokens
+    (16, 2, 2, 0, 0, 5, 1),
+    (16, 2, 3, 0, 0, 1, 0),
+    (10, 2, 3, 0, 0, 5, 1),       # 15 pairs
+    (64, 2, 1, 0, 0, 5, 2),       # 32 heads per KV head take two tiles, as in decode
+    (64, 2, 2, 0, 0, 1, 0),
+    (32, 8, 4, 0, 1, 1, 0),       # forced splits keep the prefill kernel
+    (32, 8, 4, 0, 2, 1, 0),
+    (16, 16, 2, 64, 0, 2, 0),     # rope (MLA) keeps the prefill kernel
+])
+def test_chunk_plan_routes_short_chunks_to_the_decode_workers(gq, Hq, Hk, max_q, Dr, splits, kernel, head_chunks):
+    d = baseline_chunk_desc(gq)
+    d.num_q_heads, d.num_kv_heads, d.max_q_len, d.num_splits = Hq, Hk, max_q, splits
+    d.q_stride_head, d.q_stride_token = 128 + Dr, (128 + Dr) * Hq
+    d.new_stride_head, d.new_stride_token = 128, 128 * Hk
+    d.out_stride_head, d.out_stride_token = 128, 128 * Hq
+    d.kv_stride_block = Hk * 64 * 128
+    if Dr:
+        d.head_dim_rope, d.kr_new_stride_token, d.kr_stride_block = Dr, Dr, 64 * Dr
+    p = gq.gqap_chunk_plan(d)
+    assert (p.kernel, p.head_chunks) == (kernel, head_chunks)
+    if kernel == 5:
+        # the decode workers' workspace: prefix, then per piece 16 LSEs and 16 rows of 128 floats
+        pieces = d.batch * Hk * head_chunks + p.num_workers
+        assert p.num_workers == 1024 and p.num_splits == 1
+        r256 = lambda x: (x + 255) // 256 * 256  # noqa: E731
+        assert p.workspace_bytes == r256((d.batch + 1) * 4) + r256(pieces * 64) + r256(pieces * 16 * 128 * 4)
+        d.kv_dtype = gq.FP8_E4M3FN
+        assert gq.gqap_chunk_plan(d).kernel == 6
+    else:
+        assert p.num_workers == 0
+
+
+def test_chunk_decode_route_needs_a_workspace_without_a_gpu(gq):
+    """The decode workers' route refuses a missing, short or misaligned
+    workspace before touching any pointer."""
+    d = baseline_chunk_desc(gq)
+    d.max_q_len = 4
+    p = gq.gqap_chunk_plan(d)
+    assert p.kernel == 5 and p.workspace_bytes > 0
+    lib = gq.lib()
+    for ws, nbytes in ((None, 0), (256, p.workspace_bytes - 1), (272, p.workspace_bytes)):
+        st = lib.gqap_chunk_prefill(ctypes.byref(p), 16, 16, 16, None, 16, 16, 16, 1.0, 16, None, ws, nbytes, None)
+        assert gq.STATUS_NAMES[st] == "INVALID_ARGUMENT", (ws, nbytes, gq.gqap_last_error())
+
+
 @pytest.mark.parametrize("field,value,status", [
     ("head_dim", 64, "UNSUPPORTED"),
     ("block_size", 32, "UNSUPPORTED"),

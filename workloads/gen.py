@@ -674,7 +674,7 @@ def prefill_chunk_fp8kv(seed: int = 1006, B: int = 8, prefix_range=(1024, 6144),
 def decode_multitoken(q_len: int, seed: int = 1013, B: int = 64, len_range=(1024, 4096), Hq: int = 32,
                       Hk: int = 8, D_rope: int = 0) -> ChunkCase:
     """Multi-token decode: every sequence holds kv_len ~ U{len_range} keys in a
-    paged cache (config 2's shape: B=64, Hq=32, Hk=8, D=128), the last q_len of
+    paged cache (the paged-decode workload's shape: B=64, Hq=32, Hk=8, D=128), the last q_len of
     them new tokens whose queries attend causally (bottom-right aligned).  With
     D_rope = 64 it is the MLA form (per-head K plus one shared rope row per
     token from the rope cache)."""
