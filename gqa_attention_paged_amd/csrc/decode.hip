@@ -44,13 +44,14 @@ struct DecodeArgs {
   const int32_t* block_table;
   const int32_t* seq_lens;
   int32_t* prefix;  // [B + 1] key blocks before each sequence (written by worker 0)
-  float* ws_lse;    // [pieces][16] base 2
-  float* ws_o;      // [pieces][16][D]
+  float* ws_lse;    // [pieces][pcols] base 2
+  float* ws_o;      // [pieces][pcols][D]
   void* out;
   float* lse;
   int64_t q_sb, q_sh, o_sb, o_sh;
   int64_t kv_block_bytes, kv_head_bytes, bt_stride;
   int32_t B, Hq, Hk, ratio, head_chunks, hkhc, nworkers;
+  int32_t pcols;  // columns per piece slot in ws_lse / ws_o
   int32_t max_len;  // capacity from the plan; a longer (or negative) seq_len empties the sequence
   // Chunk mode (cu != null): sequence b holds the query rows cu[b] .. cu[b+1]-1
   // of a chunk aligned to the end of its seq_lens[b] keys; the first max_q of
@@ -464,10 +465,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
     if (cvalid) {
       // A chunk column with no key in this piece leaves 0 and lse -inf.
       const float inv = C && l_tot == 0.f ? 0.f : a.v_scale / l_tot;
-      float* dst = a.ws_o + (slot * 16 + col) * D + 4 * G;
+      float* dst = a.ws_o + (slot * a.pcols + col) * D + 4 * G;
 #pragma unroll
       for (int n = 0; n < NT; ++n) *(f32x4*)(dst + 16 * n) = o[n] * inv;
-      if (G == 0) a.ws_lse[slot * 16 + col] = m_run + log2f(l_tot);
+      if (G == 0) a.ws_lse[slot * a.pcols + col] = m_run + log2f(l_tot);
     }
   };
 
@@ -580,8 +581,9 @@ __global__ __launch_bounds__(64) void decode_worker_f32(DecodeArgs a) {
     for (int hh = 0; hh < 16; ++hh) {
       if (hh >= rc) break;
 #pragma unroll
-      for (int c = 0; c < DC; ++c) a.ws_o[(slot * 16 + hh) * D + lane + 64 * c] = o[hh][c] / l[hh] * a.v_scale;
-      if (lane == 0) a.ws_lse[slot * 16 + hh] = m[hh] * kLog2e + log2f(l[hh]);
+      for (int c = 0; c < DC; ++c)
+        a.ws_o[(slot * a.pcols + hh) * D + lane + 64 * c] = o[hh][c] / l[hh] * a.v_scale;
+      if (lane == 0) a.ws_lse[slot * a.pcols + hh] = m[hh] * kLog2e + log2f(l[hh]);
     }
   };
 
@@ -696,11 +698,11 @@ __global__ __launch_bounds__(64) void decode_combine(DecodeArgs a) {
         // together, so the merge costs a single memory round trip.
         const int n = w1 - w0 + 1;
         const bool live = lane < n && owns_units(w0 + lane);
-        const float lse_k = live ? a.ws_lse[(qg + w0 + lane) * 16 + col] : -INFINITY;
+        const float lse_k = live ? a.ws_lse[(qg + w0 + lane) * a.pcols + col] : -INFINITY;
         float v4[4][DC];
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-          const float* op = a.ws_o + ((qg + w0 + min(kk, n - 1)) * 16 + col) * D;
+          const float* op = a.ws_o + ((qg + w0 + min(kk, n - 1)) * a.pcols + col) * D;
 #pragma unroll
           for (int c = 0; c < DC; ++c) v4[kk][c] = op[lane + 64 * c];
         }
@@ -720,7 +722,7 @@ __global__ __launch_bounds__(64) void decode_combine(DecodeArgs a) {
       for (int r0 = w0; r0 <= w1; r0 += 64) {
         const int wk = r0 + lane;
         const bool live = wk <= w1 && owns_units(wk);
-        const float lse_k = live ? a.ws_lse[(qg + wk) * 16 + col] : -INFINITY;
+        const float lse_k = live ? a.ws_lse[(qg + wk) * a.pcols + col] : -INFINITY;
         float m_round = lse_k;
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) m_round = fmaxf(m_round, __shfl_xor(m_round, off));
@@ -744,7 +746,7 @@ __global__ __launch_bounds__(64) void decode_combine(DecodeArgs a) {
           for (int kk = 0; kk < 4; ++kk) {
             const int k = min(k0 + kk, n - 1);
             w4[kk] = k0 + kk < n ? __shfl(wt_k, k) : 0.f;
-            const float* op = a.ws_o + ((qg + r0 + k) * 16 + col) * D;
+            const float* op = a.ws_o + ((qg + r0 + k) * a.pcols + col) * D;
 #pragma unroll
             for (int c = 0; c < DC; ++c) v4[kk][c] = op[lane + 64 * c];
           }
@@ -894,7 +896,7 @@ gqap_status gqap::decode_launch(const gqap_decode_plan_t* plan, const void* q, c
     return fail(GQAP_ERR_INVALID_ARGUMENT, "k_scale/v_scale apply to fp8 KV only and must be 1.0 otherwise");
 
   const int kv_esz = dtype_size(d.kv_dtype);
-  const DecodeWorkspace lay = decode_workspace(d.batch, plan->max_pieces, d.head_dim);
+  const DecodeWorkspace lay = decode_workspace(d.batch, plan->max_pieces, piece_cols(plan->ratio), d.head_dim);
   char* ws = (char*)workspace;
   DecodeArgs a{};
   a.q = q;
@@ -921,6 +923,7 @@ gqap_status gqap::decode_launch(const gqap_decode_plan_t* plan, const void* q, c
   a.head_chunks = plan->head_chunks;
   a.hkhc = d.num_kv_heads * plan->head_chunks;
   a.nworkers = plan->num_workers;
+  a.pcols = (int32_t)piece_cols(plan->ratio);
   a.max_len = d.max_seq_len;
   a.score_scale = scale * k_scale;
   a.score_scale_log2 = scale * k_scale * dev::kLog2e;
@@ -987,7 +990,8 @@ gqap_status gqap::chunk_decode_launch(const gqap_chunk_plan_t* plan, const void*
     return fail(GQAP_ERR_INVALID_ARGUMENT, "chunk plan is not one for the decode workers");
   const int kv_esz = fp8 ? 1 : 2;
   const int64_t pieces = (int64_t)d.batch * d.num_kv_heads * plan->head_chunks + plan->num_workers;
-  const DecodeWorkspace lay = decode_workspace(d.batch, pieces, d.head_dim);
+  const int64_t pcols = piece_cols((int64_t)d.max_q_len * plan->ratio);
+  const DecodeWorkspace lay = decode_workspace(d.batch, pieces, pcols, d.head_dim);
   if (lay.total > plan->workspace_bytes) return fail(GQAP_ERR_INVALID_ARGUMENT, "chunk plan workspace too small");
   char* ws = (char*)workspace;
   DecodeArgs a{};
@@ -1015,6 +1019,7 @@ gqap_status gqap::chunk_decode_launch(const gqap_chunk_plan_t* plan, const void*
   a.head_chunks = plan->head_chunks;
   a.hkhc = d.num_kv_heads * plan->head_chunks;
   a.nworkers = plan->num_workers;
+  a.pcols = (int32_t)pcols;
   a.max_len = d.max_kv_len;
   a.cu = cu_seqlens_q;
   a.max_q = d.max_q_len;

@@ -121,7 +121,7 @@ extern "C" gqap_status gqap_decode_plan(const gqap_decode_desc_t* desc, gqap_dec
   const int64_t pieces = (int64_t)d.batch * d.num_kv_heads * plan->head_chunks + plan->num_workers;
   if (pieces > INT32_MAX / 16) return fail(GQAP_ERR_INVALID_ARGUMENT, "too many partial slots");
   plan->max_pieces = (int32_t)pieces;
-  plan->workspace_bytes = decode_workspace(d.batch, pieces, d.head_dim).total;
+  plan->workspace_bytes = decode_workspace(d.batch, pieces, piece_cols(plan->ratio), d.head_dim).total;
   plan->magic = GQAP_PLAN_MAGIC;
   return GQAP_OK;
 }
@@ -353,7 +353,8 @@ extern "C" gqap_status gqap_chunk_plan(const gqap_chunk_desc_t* desc, gqap_chunk
     plan->num_workers = kDefaultCUs * decode_waves_per_cu(kv_esz == 1 ? kDecodeFp8Mfma : kDecodeBf16Mfma, 128);
     const int64_t pieces = (int64_t)d.batch * Hk * hc_chunk + plan->num_workers;
     if (pieces > INT32_MAX / 16) return fail(GQAP_ERR_UNSUPPORTED, "too many partial slots for the decode workers");
-    plan->workspace_bytes = decode_workspace(d.batch, pieces, D).total;
+    plan->workspace_bytes =
+        decode_workspace(d.batch, pieces, piece_cols((int64_t)d.max_q_len * plan->ratio), D).total;
   }
   plan->magic = GQAP_PLAN_MAGIC;
   return GQAP_OK;

@@ -54,21 +54,27 @@ gqap_status chunk_decode_launch(const gqap_chunk_plan_t* plan, const void* q, co
                                 void* out, float* lse, void* workspace, uint64_t workspace_bytes, void* stream);
 
 // Byte offsets of the decode workspace regions (shared by planner and launcher).
-//   prefix [B + 1] int32          key blocks before each sequence
-//   lse    [pieces][16] float32   base-2 log-sum-exp of each partial
-//   o      [pieces][16][D] float32 normalised partial outputs
+//   prefix [B + 1] int32              key blocks before each sequence
+//   lse    [pieces][cols] float32     base-2 log-sum-exp of each partial
+//   o      [pieces][cols][D] float32  normalised partial outputs
+// cols = the MFMA columns a piece can hold results for: the query heads of a
+// KV head (times the chunk rows in chunk mode), 16 when that needs more than
+// one 16-column tile.
 struct DecodeWorkspace {
   uint64_t prefix, lse, o, total;
 };
 
 inline uint64_t round256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 
-inline DecodeWorkspace decode_workspace(int64_t B, int64_t pieces, int64_t D) {
+// Columns per piece slot: `pairs` (token, head) pairs per KV head, in tiles of 16.
+inline int64_t piece_cols(int64_t pairs) { return pairs > 16 ? 16 : pairs; }
+
+inline DecodeWorkspace decode_workspace(int64_t B, int64_t pieces, int64_t cols, int64_t D) {
   DecodeWorkspace w;
   w.prefix = 0;
   w.lse = round256((uint64_t)(B + 1) * 4);
-  w.o = w.lse + round256((uint64_t)pieces * 16 * 4);
-  w.total = w.o + round256((uint64_t)pieces * 16 * D * 4);
+  w.o = w.lse + round256((uint64_t)pieces * cols * 4);
+  w.total = w.o + round256((uint64_t)pieces * cols * D * 4);
   return w;
 }
 

@@ -137,9 +137,10 @@ def test_decode_plan_is_a_function_of_the_descriptor(gq):
     assert p.num_workers == 256 * 4        # D=128 bf16: four persistent waves per compute unit
     assert p.head_chunks == 1
     assert p.max_pieces == 64 * 8 * 1 + p.num_workers
-    # prefix (B+1 ints), lse (pieces x 16 floats), partial outputs (pieces x 16 x D floats), 256-byte rounded
+    # prefix (B+1 ints), lse (pieces x 4 floats: one per query head of a KV head), partial
+    # outputs (pieces x 4 x D floats), 256-byte rounded
     r = lambda n: (n + 255) // 256 * 256
-    assert p.workspace_bytes == r(4 * 65) + r(4 * 16 * p.max_pieces) + r(4 * 16 * 128 * p.max_pieces)
+    assert p.workspace_bytes == r(4 * 65) + r(4 * 4 * p.max_pieces) + r(4 * 4 * 128 * p.max_pieces)
     d.num_workers = 77
     assert gq.gqap_decode_plan(d).num_workers == 77
     d.num_workers, d.num_cus = 0, 80
@@ -381,11 +382,13 @@ def test_chunk_plan_routes_short_chunks_to_the_decode_workers(gq, Hq, Hk, max_q,
     p = gq.gqap_chunk_plan(d)
     assert (p.kernel, p.head_chunks) == (kernel, head_chunks)
     if kernel == 5:
-        # the decode workers' workspace: prefix, then per piece 16 LSEs and 16 rows of 128 floats
+        # the decode workers' workspace: prefix, then per piece one LSE and one row of 128
+        # floats per (token, head) column of a tile
         pieces = d.batch * Hk * head_chunks + p.num_workers
+        cols = min(16, max_q * (Hq // Hk))
         assert p.num_workers == 1024 and p.num_splits == 1
         r256 = lambda x: (x + 255) // 256 * 256  # noqa: E731
-        assert p.workspace_bytes == r256((d.batch + 1) * 4) + r256(pieces * 64) + r256(pieces * 16 * 128 * 4)
+        assert p.workspace_bytes == r256((d.batch + 1) * 4) + r256(pieces * cols * 4) + r256(pieces * cols * 128 * 4)
         d.kv_dtype = gq.FP8_E4M3FN
         assert gq.gqap_chunk_plan(d).kernel == 6
     else:
@@ -654,7 +657,7 @@ def test_noalloc_decode_rejects_a_plan_past_its_scratch_without_a_gpu(gq):
     """The allocation-free decode checks the plan's workspace against its fixed
     scratch before any device call."""
     d = baseline_decode_desc(gq)
-    d.num_workers = 5000                         # 5000+ partial slots of 16 x 128 floats: past 32 MiB
+    d.num_workers = 20000                        # 20000+ partial slots of 4 x 128 floats: past 32 MiB
     p = gq.gqap_decode_plan(d)
     assert p.workspace_bytes > gq.NOALLOC_SCRATCH_BYTES
     st = gq.lib().gqap_paged_decode_noalloc(ctypes.byref(p), 16, 16, 16, 16, 16, 1.0, 1.0, 1.0, 16, None, None)

@@ -66,7 +66,7 @@ def test_noalloc_decode_rejects_a_plan_past_the_scratch(gu):
     gq = gu.gq
     case = gen.make_decode_case(name="noalloc_big", seed=421, B=4, Hq=16, Hk=4, D=128, q_dtype="bf16",
                                 kv_dtype="bf16", seq_lens=[64, 64, 64, 64])
-    dd = gu.DeviceDecode(case, num_workers=5000)       # 5000 pieces of 16 x 128 floats: past 32 MiB
+    dd = gu.DeviceDecode(case, num_workers=20000)      # 20000+ pieces of 4 x 128 floats: past 32 MiB
     assert dd.plan.workspace_bytes > gq.NOALLOC_SCRATCH_BYTES
     with pytest.raises(gq.GqapError) as ei:
         gq.gqap_paged_decode_noalloc(dd.plan, dd.q, dd.k, dd.v, dd.bt, dd.sl, case.scale, 1.0, 1.0, dd.out, dd.lse)
