@@ -156,7 +156,8 @@ def pmc_summary(fetch_dir: str, write_dir: str, workload: str, copy_bytes: int, 
     kern = DOMINANT_KERNEL[workload]
     f_k, w_k = _mean_for(fetch, kern), _mean_for(write, kern)
     case = gen.CONFIGS[workload]()
-    alg = case.kv_bytes() if hasattr(case, "kv_bytes") else None
+    alg = (case.kv_bytes() if hasattr(case, "kv_bytes") else
+           gen.kv_read_bytes(case) if workload.startswith("decode_mt") else None)
     ent = {
         "kernel": kern, "source_hash": _kernel_source_hash(_kind_of(workload)),
         "fetch_kib_per_dispatch": f_k, "write_kib_per_dispatch": w_k,
