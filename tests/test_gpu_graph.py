@@ -103,3 +103,26 @@ def test_chunk_step_in_a_graph(gu, kv_dtype):
     scratch = torch.randn(1 << 20, device="cuda")
     _replays_match(gu, g, [dc.out, dc.lse], ref[:2], lambda: scratch.mul_(0.999))
     assert torch.equal(dc.k_pool.detach().cpu().view(torch.uint8), ref[2].view(torch.uint8))
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "e4m3fn"])
+def test_short_chunk_step_in_a_graph(gu, kv_dtype):
+    """A multi-token decode step (append of 1..4 tokens per sequence, then
+    the attention on the decode workers) captured together; every replay
+    reproduces the eager step bit for bit."""
+    case = gen.make_chunk_case(name="graph_short", seed=99, prefix_lens=[100, 0, 640, 63, 2000],
+                               q_lens=[4, 1, 3, 4, 2], Hq=16, Hk=4, kv_dtype=kv_dtype)
+    gu.announce(f"graph short-chunk step, {kv_dtype} cache")
+    dc = gu.DeviceChunk(case)
+    assert dc.plan.kernel == (6 if kv_dtype == "e4m3fn" else 5)
+
+    def step():
+        dc.append()
+        dc.run()
+
+    step()
+    torch.cuda.synchronize()
+    ref = [dc.out.detach().cpu().clone(), dc.lse.detach().cpu().clone()]
+    g = _capture(step)
+    scratch = torch.randn(1 << 20, device="cuda")
+    _replays_match(gu, g, [dc.out, dc.lse], ref, lambda: scratch.mul_(0.999))
