@@ -21,6 +21,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import math
 import os
@@ -46,13 +47,22 @@ KERNEL_SOURCES = {
 }
 
 
+def _strip_comments(src: str) -> str:
+    """C/C++ source without comments and with runs of whitespace collapsed,
+    so that a change to the prose of a file does not make its counters stale
+    (string literals holding comment markers do not occur in these files)."""
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
+
+
 def _kernel_source_hash(kind: str = "decode") -> str:
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kind]:
         p = os.path.join(ROOT, "gqa_attention_paged_amd", "csrc", f)
         if os.path.exists(p):
-            with open(p, "rb") as fh:
-                h.update(fh.read())
+            with open(p, encoding="utf-8") as fh:
+                h.update(_strip_comments(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -26,8 +26,17 @@
 // 16-byte rows, is written to an XOR-swizzled LDS tile once the current
 // block's reads of that tile are issued, and comes back through the LDS
 // transpose read as the token-packed operand of P.V.  All loads are plain
-// register loads, so the compiler's wait counts stay exact.  S^T = K q^T and O^T += V^T P^T run on bf16 MFMA with fp32
-// accumulation; the up-to-16 query heads of a KV head share every K/V byte.
+// register loads, so the compiler's wait counts stay exact.  S^T = K q^T and
+// O^T += V^T P^T run on bf16 MFMA with fp32 accumulation; the up-to-16 query
+// heads of a KV head share every K/V byte.
+//
+// Chunk mode (the same kernels, template flag C): a short chunk of new tokens
+// per sequence at the end of its keys (multi-token decode; FlashMLA
+// tensor-shape reference, section 1, with a query length above 1).  A unit's
+// 16 MFMA columns are then (token, query head) pairs of the KV head, each
+// column with its own causal key limit, and the combine writes the chunk's
+// rows.  The chunked-prefill plan picks this mode when the pairs fit the
+// tiles one token's heads need.
 #include "dev.hpp"
 #include "status.hpp"
 
