@@ -14,7 +14,10 @@
  *     rope row;
  *   - chunked prefill against the paged cache (append the chunk's keys and
  *     values, then attend to the cached prefix and the chunk), with a bf16
- *     cache or an fp8 e4m3fn cache with per-tensor scales;
+ *     cache or an fp8 e4m3fn cache with per-tensor scales; short chunks
+ *     (multi-token decode) run on the paged-decode workers;
+ *   - the decode without a caller workspace, for callers that cannot
+ *     allocate;
  *   - the padded block table built from a CSR page list;
  *   - plan / validation calls that run on the host only;
  *   - a debug gather that exposes the decode kernels' page addressing.
