@@ -26,7 +26,10 @@
 // 16-byte rows, is written to an XOR-swizzled LDS tile once the current
 // block's reads of that tile are issued, and comes back through the LDS
 // transpose read as the token-packed operand of P.V.  All loads are plain
-// register loads, so the compiler's wait counts stay exact.  S^T = K q^T and
+// register loads, so the compiler's wait counts stay exact.  The K/V reads
+// carry the nontemporal hint: every cache byte is read once per pass, and
+// the hinted stream keeps the eight XCDs within a few percent of each other
+// (unhinted, their end times spread by about 10 %).  S^T = K q^T and
 // O^T += V^T P^T run on bf16 MFMA with fp32 accumulation; the up-to-16 query
 // heads of a KV head share every K/V byte.
 //
@@ -130,6 +133,17 @@ __device__ __forceinline__ void unit_load_phys(const DecodeArgs& a, Unit& u) {
   u.phys = ld_const(a.block_table, (int64_t)u.b * a.bt_stride + u.j);
 }
 
+// A value that every lane of the wave holds alike, moved to a scalar
+// register.  What is computed from it then stays scalar, so the unit
+// bookkeeping reads seq_lens and block_table with scalar loads (which wait
+// on their own counter) instead of vector loads queued behind the K/V stream.
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ int64_t uniform(int64_t x) {
+  const uint64_t u = (uint64_t)x;
+  return (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(u >> 32)) << 32) |
+                   (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u));
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave.
 __device__ __forceinline__ int wave_incl_scan(int x) {
   const int lane = __lane_id();
@@ -151,7 +165,7 @@ __device__ __forceinline__ int64_t blocks_before(const DecodeArgs& a, int b_end)
     int nb = b < b_end ? seq_blocks<C>(a, b) : 0;
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) nb += __shfl_xor(nb, off);
-    total += nb;
+    total += uniform(nb);
   }
   return total;
 }
@@ -171,10 +185,10 @@ __device__ __forceinline__ void locate_block(const DecodeArgs& a, int64_t t, int
     if (m) {
       const int l = __ffsll((long long)m) - 1;
       *b_out = b0 + l;
-      *before_out = run + __shfl(incl - nb, l);
+      *before_out = run + uniform(__shfl(incl - nb, l));
       return;
     }
-    run += __shfl(incl, 63);
+    run += uniform(__shfl(incl, 63));
   }
   *b_out = a.B;
   *before_out = run;
@@ -345,7 +359,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
     for (int t = 0; t < 2; ++t) {
       const unsigned char* kp = kblk + token_of<FP8>(2 * H + t, col) * RB + 16 * G;
 #pragma unroll
-      for (int p = 0; p < KLOADS; ++p) kreg[t][p] = load16(kp + 64 * p);
+      for (int p = 0; p < KLOADS; ++p) kreg[t][p] = load16_stream(kp + 64 * p);
     }
   };
 
@@ -354,7 +368,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
     constexpr int H = decltype(hc_)::value;
     const unsigned char* vh = vpool + slab_offset(u) + H * HB;
 #pragma unroll
-    for (int i = 0; i < NV; ++i) vst[i] = load16(vh + 1024 * i + 16 * lane);
+    for (int i = 0; i < NV; ++i) vst[i] = load16_stream(vh + 1024 * i + 16 * lane);
   };
 
   // Staged V rows -> the swizzled LDS tile (rows 0..31 of the half).

