@@ -78,13 +78,16 @@ inline DecodeWorkspace decode_workspace(int64_t B, int64_t pieces, int64_t cols,
   return w;
 }
 
-// Resident worker waves per compute unit for each decode variant (LDS and
-// register budgets of the kernels in decode.hip).
+// Resident worker waves per compute unit for each decode variant.  With the
+// streamed K/V reads, three bf16 D = 128 waves per compute unit already keep
+// HBM busy, and the fewer pieces shorten the combine; fp8 units carry half
+// the bytes, so its workers keep four.  A count that is not a multiple of the
+// compute units leaves some with a wave more than others and runs slower.
 inline int decode_waves_per_cu(uint32_t kernel, int head_dim) {
   switch (kernel) {
     case kDecodeF32Valu: return 2;
-    case kDecodeBf16Mfma: return head_dim == 128 ? 4 : 8;  // 1 or 2 waves per SIMD
-    default: return head_dim == 128 ? 4 : 8;              // fp8 KV
+    case kDecodeBf16Mfma: return head_dim == 128 ? 3 : 8;
+    default: return head_dim == 128 ? 4 : 8;  // fp8 KV
   }
 }
 

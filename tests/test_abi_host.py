@@ -134,7 +134,7 @@ def test_decode_plan_is_a_function_of_the_descriptor(gq):
     d = baseline_decode_desc(gq)
     p = gq.gqap_decode_plan(d)
     assert p.magic == gq.PLAN_MAGIC and p.ratio == 4
-    assert p.num_workers == 256 * 4        # D=128 bf16: four persistent waves per compute unit
+    assert p.num_workers == 256 * 3        # D=128 bf16: three persistent waves per compute unit
     assert p.head_chunks == 1
     assert p.max_pieces == 64 * 8 * 1 + p.num_workers
     # prefix (B+1 ints), lse (pieces x 4 floats: one per query head of a KV head), partial
@@ -144,7 +144,7 @@ def test_decode_plan_is_a_function_of_the_descriptor(gq):
     d.num_workers = 77
     assert gq.gqap_decode_plan(d).num_workers == 77
     d.num_workers, d.num_cus = 0, 80
-    assert gq.gqap_decode_plan(d).num_workers == 80 * 4
+    assert gq.gqap_decode_plan(d).num_workers == 80 * 3
     d.q_dtype = d.kv_dtype = gq.F32
     d.num_cus = 0
     assert gq.gqap_decode_plan(d).num_workers == 256 * 2
@@ -386,7 +386,7 @@ def test_chunk_plan_routes_short_chunks_to_the_decode_workers(gq, Hq, Hk, max_q,
         # floats per (token, head) column of a tile
         pieces = d.batch * Hk * head_chunks + p.num_workers
         cols = min(16, max_q * (Hq // Hk))
-        assert p.num_workers == 1024 and p.num_splits == 1
+        assert p.num_workers == 768 and p.num_splits == 1
         r256 = lambda x: (x + 255) // 256 * 256  # noqa: E731
         assert p.workspace_bytes == r256((d.batch + 1) * 4) + r256(pieces * cols * 4) + r256(pieces * cols * 128 * 4)
         d.kv_dtype = gq.FP8_E4M3FN
