@@ -67,10 +67,8 @@ def _kernel_source_hash(kind: str = "decode") -> str:
 
 
 def _kind_of(workload: str) -> str:
-    """Source set of the workload's dominant kernel: short GQA chunks run on
-    the decode workers, MLA ones on the prefill kernel."""
-    if workload.startswith("decode_mt"):
-        return "prefill" if "_mla" in workload else "decode"
+    """Source set of the workload's dominant kernel: short chunks (plain and
+    MLA) run on the decode workers, the rest on the prefill kernel."""
     return "prefill" if workload.startswith("prefill") else "decode"
 
 
@@ -109,7 +107,7 @@ DOMINANT_KERNEL = {
     "decode_mt1_bf16": "decode_worker_mfma<128, false, true>",
     "decode_mt2_bf16": "decode_worker_mfma<128, false, true>",
     "decode_mt4_bf16": "decode_worker_mfma<128, false, true>",
-    "decode_mt2_mla_bf16": "prefill_fwd<64, true, 0>",
+    "decode_mt2_mla_bf16": "decode_worker_rope<false>",
 }
 
 

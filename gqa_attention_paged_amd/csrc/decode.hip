@@ -70,9 +70,15 @@ struct DecodeArgs {
   // them are computed.  A unit's 16 columns are then (token, head) pairs.
   const int32_t* cu;
   int32_t max_q;
-  float score_scale_log2;  // scale * k_scale * log2(e)
-  float score_scale;       // scale * k_scale
+  float score_scale_log2;  // scale * k_scale * log2(e) (with a rope part: scale * log2(e))
+  float score_scale;       // scale * k_scale (with a rope part: scale)
   float v_scale;
+  // MLA split head (rope kernels): the 64-wide rope row of every key, one
+  // head shared by all query heads, in a paged rope cache of 64-row blocks;
+  // an fp8 cache's k_scale then multiplies the per-head (nope) sum only.
+  const void* kr;
+  int64_t kr_block_bytes;
+  float nope_scale;
 };
 
 namespace dev {
@@ -269,9 +275,10 @@ using namespace dev;
 
 // C: chunk mode.  Column col of head chunk hc is then the pair (token i,
 // head hh) with hc * 16 + col = i * ratio + hh, and its keys end at its own
-// causal bound, so every column carries its own key limit.
-template <int D, bool FP8, bool C>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_worker_mfma(DecodeArgs a) {
+// causal bound, so every column carries its own key limit.  DR: width of the
+// MLA rope part (0 or 64), scored after the per-head part on its own rows.
+template <int D, bool FP8, bool C, int DR>
+__device__ __forceinline__ void decode_worker_body(const DecodeArgs& a) {
   constexpr int ESZ = FP8 ? 1 : 2;
   constexpr int RB = D * ESZ;        // bytes per K/V row
   constexpr int HB = 32 * RB;        // bytes per half slab (32 rows)
@@ -280,6 +287,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   constexpr int KLOADS = RB / 64;    // 16-byte K loads per row and lane group
   constexpr int NT = D / 16;         // 16-wide output tiles
   constexpr int NV = HB / 1024;      // 16-byte V loads per lane and half slab
+  constexpr int KSR = DR / 32;       // MFMA k-steps over the rope part (bf16)
   __shared__ __attribute__((aligned(1024))) unsigned char vlds[HB];
 
   const int w = blockIdx.x;
@@ -298,7 +306,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
 
   i32x4 kreg[2][KLOADS];  // K rows of the half about to be scored (two 16-row tiles)
   i32x4 vst[NV];          // V rows of the next half, on their way to LDS
-  bf16x8 qop[KSTEPS];
+  i32x4 kregr[2][KSR > 0 ? KSR : 1];  // rope rows of the same half
+  bf16x8 qop[KSTEPS + KSR];
   float m_run, l_run;
   f32x4 o[NT];
   f32x4 s[2];
@@ -344,8 +353,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
     const unsigned char* qp = (const unsigned char*)a.q +
                               (row * a.q_sb + (int64_t)(g * a.ratio + (hvalid ? hl : 0)) * a.q_sh) * 2;
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      const int d0 = FP8 ? (64 * (ks >> 1) + 16 * G + 8 * (ks & 1)) : (32 * ks + 8 * G);
+    for (int ks = 0; ks < KSTEPS + KSR; ++ks) {
+      // rope steps (ks >= KSTEPS): the bf16 layout, after the D per-head values
+      const int d0 = ks >= KSTEPS ? D + 32 * (ks - KSTEPS) + 8 * G
+                     : FP8        ? (64 * (ks >> 1) + 16 * G + 8 * (ks & 1))
+                                  : (32 * ks + 8 * G);
       const i32x4 v = hvalid ? load16(qp + 2 * d0) : i32x4{0, 0, 0, 0};
       qop[ks] = __builtin_bit_cast(bf16x8, v);
     }
@@ -360,6 +372,18 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
       const unsigned char* kp = kblk + token_of<FP8>(2 * H + t, col) * RB + 16 * G;
 #pragma unroll
       for (int p = 0; p < KLOADS; ++p) kreg[t][p] = load16_stream(kp + 64 * p);
+    }
+    // The rope rows of the same tokens.  Every query head of the sequence
+    // reads them, so they are read without the streaming hint and may be
+    // served from the caches.
+    if constexpr (DR > 0) {
+      const unsigned char* rblk = (const unsigned char*)a.kr + (int64_t)u.phys * a.kr_block_bytes;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const unsigned char* rp = rblk + token_of<FP8>(2 * H + t, col) * (2 * DR) + 16 * G;
+#pragma unroll
+        for (int r = 0; r < KSR; ++r) kregr[t][r] = load16(rp + 64 * r);
+      }
     }
   };
 
@@ -395,6 +419,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
           ka = __builtin_bit_cast(bf16x8, kreg[t][ks]);
         }
         s[t] = mfma16x16x32(ka, qop[ks], s[t]);
+      }
+      if constexpr (DR > 0) {
+        if constexpr (FP8) s[t] *= a.nope_scale;  // k_scale belongs to the per-head sum only
+#pragma unroll
+        for (int r = 0; r < KSR; ++r)
+          s[t] = mfma16x16x32(__builtin_bit_cast(bf16x8, kregr[t][r]), qop[KSTEPS + r], s[t]);
       }
     }
   };
@@ -548,6 +578,19 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   qk();
   softmax_pv(cur, H1{});
   flush(cur);
+}
+
+template <int D, bool FP8, bool C>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_worker_mfma(DecodeArgs a) {
+  decode_worker_body<D, FP8, C, 0>(a);
+}
+
+// Short chunks with the MLA split head: 128 per-head dims plus the 64-wide
+// rope row of every key from the paged rope cache.  The plan runs at most
+// one worker per SIMD, so the kernel may take a SIMD's whole register file.
+template <bool FP8>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1))) void decode_worker_rope(DecodeArgs a) {
+  decode_worker_body<128, FP8, true, 64>(a);
 }
 
 // fp32 path: one wave per worker, vector ALU, no prefetch.  Lane t scores
@@ -998,7 +1041,8 @@ gqap_status gqap::decode_launch(const gqap_decode_plan_t* plan, const void* q, c
 }
 
 gqap_status gqap::chunk_decode_launch(const gqap_chunk_plan_t* plan, const void* q, const void* k_pool,
-                                     const void* v_pool, const int32_t* block_table, const int32_t* cu_seqlens_q,
+                                     const void* v_pool, const void* kr_pool, const int32_t* block_table,
+                                     const int32_t* cu_seqlens_q,
                                      const int32_t* kv_lens, float scale, bool fp8, float k_scale, float v_scale,
                                      void* out, float* lse, void* workspace, uint64_t workspace_bytes,
                                      void* stream) {
@@ -1009,8 +1053,10 @@ gqap_status gqap::chunk_decode_launch(const gqap_chunk_plan_t* plan, const void*
   if (workspace_bytes < plan->workspace_bytes)
     return fail(GQAP_ERR_INVALID_ARGUMENT, "workspace of %llu bytes < %llu required",
                 (unsigned long long)workspace_bytes, (unsigned long long)plan->workspace_bytes);
-  if (d.head_dim != 128 || d.head_dim_rope != 0 || plan->num_workers <= 0 || plan->head_chunks <= 0)
+  if (d.head_dim != 128 || (d.head_dim_rope != 0 && d.head_dim_rope != 64) || plan->num_workers <= 0 ||
+      plan->head_chunks <= 0)
     return fail(GQAP_ERR_INVALID_ARGUMENT, "chunk plan is not one for the decode workers");
+  const bool rope = d.head_dim_rope == 64;
   const int kv_esz = fp8 ? 1 : 2;
   const int64_t pieces = (int64_t)d.batch * d.num_kv_heads * plan->head_chunks + plan->num_workers;
   const int64_t pcols = piece_cols((int64_t)d.max_q_len * plan->ratio);
@@ -1046,11 +1092,18 @@ gqap_status gqap::chunk_decode_launch(const gqap_chunk_plan_t* plan, const void*
   a.max_len = d.max_kv_len;
   a.cu = cu_seqlens_q;
   a.max_q = d.max_q_len;
-  a.score_scale = scale * (fp8 ? k_scale : 1.f);
+  a.score_scale = scale * (fp8 && !rope ? k_scale : 1.f);
   a.score_scale_log2 = a.score_scale * dev::kLog2e;
   a.v_scale = fp8 ? v_scale : 1.f;
+  a.kr = kr_pool;
+  a.kr_block_bytes = rope ? d.kr_stride_block * 2 : 0;
+  a.nope_scale = fp8 ? k_scale : 1.f;
   hipStream_t st = (hipStream_t)stream;
-  if (fp8)
+  if (rope && fp8)
+    hipLaunchKernelGGL((decode_worker_rope<true>), dim3(plan->num_workers), dim3(64), 0, st, a);
+  else if (rope)
+    hipLaunchKernelGGL((decode_worker_rope<false>), dim3(plan->num_workers), dim3(64), 0, st, a);
+  else if (fp8)
     hipLaunchKernelGGL((decode_worker_mfma<128, true, true>), dim3(plan->num_workers), dim3(64), 0, st, a);
   else
     hipLaunchKernelGGL((decode_worker_mfma<128, false, true>), dim3(plan->num_workers), dim3(64), 0, st, a);

@@ -343,10 +343,11 @@ extern "C" gqap_status gqap_chunk_plan(const gqap_chunk_desc_t* desc, gqap_chunk
   // Short chunks go to the decode workers when the (token, head) pairs of a
   // KV head fit in as many 16-column tiles as one token's heads: every K/V
   // byte is then read once per tile, where the prefill kernel reads it once
-  // per query head.  Forced splits keep the prefill kernel.
+  // per query head.  With the MLA rope cache every query head's tiles also
+  // read the shared rope rows.  Forced splits keep the prefill kernel.
   const int64_t hc_token = ceil_div(plan->ratio, 16);
   const int64_t hc_chunk = ceil_div((int64_t)d.max_q_len * plan->ratio, 16);
-  if (!Dr && d.num_splits == 0 && d.max_q_len >= 1 && hc_chunk == hc_token) {
+  if (d.num_splits == 0 && d.max_q_len >= 1 && hc_chunk == hc_token) {
     plan->kernel = kv_esz == 1 ? kChunkDecodeFp8 : kChunkDecode;
     plan->num_splits = 1;
     plan->head_chunks = (int32_t)hc_chunk;

@@ -1434,8 +1434,8 @@ static gqap_status chunk_common(const gqap_chunk_plan_t* plan, const void* q, co
       (lse && ((uintptr_t)lse & 3)))
     return fail(GQAP_ERR_INVALID_ARGUMENT, "device pointers must be 16-byte aligned (index arrays, lse 4-byte)");
   if (plan->kernel == kChunkDecode || plan->kernel == kChunkDecodeFp8)
-    return chunk_decode_launch(plan, q, k_pool, v_pool, block_table, cu_seqlens_q, kv_lens, scale, fp8, k_scale,
-                               v_scale, out, lse, workspace, workspace_bytes, stream);
+    return chunk_decode_launch(plan, q, k_pool, v_pool, kr_pool, block_table, cu_seqlens_q, kv_lens, scale, fp8,
+                               k_scale, v_scale, out, lse, workspace, workspace_bytes, stream);
   PrefillArgs a{};
   a.q = (const uint16_t*)q;
   a.k = (const uint16_t*)k_pool;

@@ -49,7 +49,8 @@ enum ChunkKernel : int32_t {
 // Short chunks on the decode workers (decode.hip).  The caller has checked
 // the plan, the scales, the pointers and their alignment.
 gqap_status chunk_decode_launch(const gqap_chunk_plan_t* plan, const void* q, const void* k_pool,
-                                const void* v_pool, const int32_t* block_table, const int32_t* cu_seqlens_q,
+                                const void* v_pool, const void* kr_pool, const int32_t* block_table,
+                                const int32_t* cu_seqlens_q,
                                 const int32_t* kv_lens, float scale, bool fp8, float k_scale, float v_scale,
                                 void* out, float* lse, void* workspace, uint64_t workspace_bytes, void* stream);
 

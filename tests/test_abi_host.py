@@ -368,7 +368,10 @@ def test_chunk_plan_baseline(gq):
     (64, 2, 2, 0, 0, 1, 0),
     (32, 8, 4, 0, 1, 1, 0),       # forced splits keep the prefill kernel
     (32, 8, 4, 0, 2, 1, 0),
-    (16, 16, 2, 64, 0, 2, 0),     # rope (MLA) keeps the prefill kernel
+    (16, 16, 2, 64, 0, 5, 1),     # MLA (rope cache): the rope workers, one tile per head
+    (16, 16, 16, 64, 0, 5, 1),
+    (16, 16, 17, 64, 0, 2, 0),    # 17 tokens of one head: two tiles -> the MLA prefill kernel
+    (16, 16, 2, 64, 1, 2, 0),     # forced splits keep the prefill kernel
 ])
 def test_chunk_plan_routes_short_chunks_to_the_decode_workers(gq, Hq, Hk, max_q, Dr, splits, kernel, head_chunks):
     d = baseline_chunk_desc(gq)

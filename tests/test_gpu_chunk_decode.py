@@ -2,10 +2,11 @@
 against the fp64 oracle's chunked prefill.
 
 A chunk plan whose (token, query head) pairs of one KV head fit in as many
-16-wide tiles as one token's heads (no rope, no forced splits) runs
-gqap_chunk_prefill / gqap_chunk_prefill_fp8kv on the decode workers (plan
-kernel 5, or 6 for an fp8 cache).  Every column of a tile is then one (token,
-head) pair with its own causal key bound, kv_len - q_len + i for row i.  The
+16-wide tiles as one token's heads (no forced splits) runs gqap_chunk_prefill
+/ gqap_chunk_prefill_fp8kv on the decode workers (plan kernel 5, or 6 for an
+fp8 cache), the MLA form (64-wide rope rows from the paged rope cache) on
+their rope variant.  Every column of a tile is then one (token, head) pair
+with its own causal key bound, kv_len - q_len + i for row i.  The
 attention is the chunked prefill's, so the bars are the chunk tests': bf16
 max-abs-err 2e-2, fp8 cache 6e-2, LSE 1e-3.  Pool rows past each sequence's
 keys hold NaN, so a read past a row's keys shows up as NaN.
@@ -37,15 +38,17 @@ def gu():
 def _oracle_pools(case):
     fp8 = case.kv_dtype == "e4m3fn"
     return O.append_kv(case.k_new, case.v_new, case.k_pool, case.v_pool, case.block_table, case.cu_seqlens_q,
-                       case.kv_lens, kv_dtype=case.kv_dtype if fp8 else "bf16",
+                       case.kv_lens, kr_new=case.kr_new, kr_pool=case.kr_pool,
+                       kv_dtype=case.kv_dtype if fp8 else "bf16",
                        k_scale=case.k_scale if fp8 else 1.0, v_scale=case.v_scale if fp8 else 1.0)
 
 
 def _oracle(case, pools, rows=None):
     fp8 = case.kv_dtype == "e4m3fn"
     kw = dict(kv_dtype="e4m3fn", k_scale=case.k_scale, v_scale=case.v_scale) if fp8 else {}
+    kr = pools[2] if len(pools) == 3 else None
     fn = lambda rr: O.chunk_prefill(case.q, pools[0], pools[1], case.block_table, case.cu_seqlens_q,  # noqa: E731
-                                    case.kv_lens, case.scale, dtype="bf16", rows=rr, **kw)
+                                    case.kv_lens, case.scale, dtype="bf16", rows=rr, kr_pool=kr, **kw)
     return OR.all_rows(fn, case.T, block=64) if rows is None else fn(rows)
 
 
@@ -60,6 +63,13 @@ def _run(gu, case, num_splits=0, want_kernel=None):
     dc.lse.fill_(NAN)
     dc.append()
     pools = _oracle_pools(case)
+    got = dc.pools_bits()
+    for g, r in zip(got, pools):
+        if fp8 and g.dtype == np.uint8:   # a NaN input may give either NaN code
+            nan_g, nan_r = (g & 0x7F) == 0x7F, (r & 0x7F) == 0x7F
+            assert np.array_equal(nan_g, nan_r) and np.array_equal(g[~nan_r], r[~nan_r]), "appended pool differs"
+        else:
+            assert np.array_equal(g, r), "appended pool differs from the oracle's"
     dc.run()
     out, lse = dc.results()
     ref, ref_lse = _oracle(case, pools)
@@ -77,6 +87,38 @@ def test_multitoken_decode_full_size(gu, q_len):
     1024..4096 keys, 32 query heads on 8 KV heads, the last q_len keys the
     chunk's own."""
     _run(gu, gen.decode_multitoken(q_len))
+
+
+@pytest.mark.parametrize("q_len", [1, 2])
+def test_multitoken_mla_decode_full_size(gu, q_len):
+    """Every row and head of the multi-token MLA decode: the same 64-sequence
+    cache shape with 16 query heads, each its own KV head, and the 64-wide
+    rope rows in the paged rope cache."""
+    _run(gu, gen.decode_multitoken(q_len, Hq=16, Hk=16, D_rope=64))
+
+
+# (Hq, Hk, longest chunk) with the rope cache
+ROPE_SHAPES = [(16, 16, 4), (16, 16, 16), (8, 2, 4), (4, 1, 3)]
+
+
+@pytest.mark.parametrize("Hq,Hk,qmax", ROPE_SHAPES)
+def test_short_mla_chunks_ragged(gu, Hq, Hk, qmax):
+    """The ragged lengths of the plain test below, with the rope part: prefixes
+    on both sides of a page edge, empty chunks, a chunk that is its whole
+    sequence, a sequence of more than 4096 keys."""
+    prefix = [0, 1, 63, 64, 100, 255, 700, 4097, 62, 127]
+    q_lens = [qmax, 1, qmax, 0, max(1, qmax - 1), qmax, 2 if qmax >= 2 else 1, qmax, qmax, 0]
+    case = gen.make_chunk_case(name=f"short_mla_{Hq}x{Hk}_q{qmax}", seed=921 + Hq + Hk + qmax,
+                               prefix_lens=prefix, q_lens=q_lens, Hq=Hq, Hk=Hk, D_rope=64)
+    _run(gu, case)
+
+
+def test_short_mla_chunks_fp8_cache(gu):
+    """fp8 pages with the bf16 rope cache: k_scale multiplies the per-head sum
+    only."""
+    case = gen.make_chunk_case(name="short_mla_fp8", seed=931, prefix_lens=[0, 63, 64, 700, 2000, 5],
+                               q_lens=[2, 2, 1, 2, 2, 0], Hq=16, Hk=16, D_rope=64, kv_dtype="e4m3fn")
+    _run(gu, case)
 
 
 # (Hq, Hk, longest chunk): one 16-column tile of 16, 15 or 12 pairs; ratio
