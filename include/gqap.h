@@ -470,7 +470,8 @@ typedef struct gqap_chunk_plan_t {
   int32_t q_tiles;             /* ceil(max_q_len / q_tile_rows) */
   int32_t q_tile_rows;         /* query rows per workgroup and head: 128 */
   int32_t kernel;             /* 1..4: prefill kernel (2, 4: with rope; 3, 4: fp8 cache);
-                                  5, 6: decode workers (6: fp8 cache) */
+                                  5, 6: decode workers, with the rope cache
+                                  when Dr = 64 (6: fp8 cache) */
   uint64_t workspace_bytes;    /* prefill kernel: 0 unless num_splits > 1 */
   uint32_t magic;
   uint32_t num_splits;         /* key-axis splits the calls will use (1 on the decode workers) */
@@ -488,14 +489,15 @@ typedef struct gqap_chunk_plan_t {
  * (one append launch), with splits T * Hq * 64 >= 2^32); INVALID_ARGUMENT
  * also for num_splits outside 0..16.  Key-axis splits as for the prefill.
  *
- * Short chunks: with Dr = 0 and num_splits = 0, a plan whose chunk rows
- * times Hq / Hk (the (token, query head) pairs of one KV head, max_q_len *
- * Hq / Hk) fit in as many 16-wide tiles as the Hq / Hk heads of one token
- * (for Hq / Hk <= 16: max_q_len * Hq / Hk <= 16; multi-token decode, e.g.
- * speculative verification) runs the calls below on the paged-decode
- * workers: the keys and values of a KV head are then read once per tile
- * instead of once per query head.  The results are the same attention;
- * workspace_bytes is then the decode workers' workspace (never 0).
+ * Short chunks: with num_splits = 0, a plan whose chunk rows times Hq / Hk
+ * (the (token, query head) pairs of one KV head, max_q_len * Hq / Hk) fit in
+ * as many 16-wide tiles as the Hq / Hk heads of one token (for Hq / Hk <= 16:
+ * max_q_len * Hq / Hk <= 16; multi-token decode, e.g. speculative
+ * verification) runs the calls below on the paged-decode workers, plain or
+ * MLA (Dr = 64: the rope rows come from kr_pool): the keys and values of a
+ * KV head are then read once per tile instead of once per query head.  The
+ * results are the same attention; workspace_bytes is then the decode
+ * workers' workspace (never 0).
  *
  * Capacity (both calls below): a chunk whose kv_lens[b] exceeds max_kv_len,
  * or is smaller than its own length q_len_b, is outside the plan: it is not
