@@ -245,7 +245,7 @@ extern "C" gqap_status gqap_prefill_plan(const gqap_prefill_desc_t* desc, gqap_p
     return fail(GQAP_ERR_UNSUPPORTED,
                 "Hq * batch * ceil(max_seq_len/128) * num_splits = %lld workgroups exceeds 2^24",
                 (long long)(grid * ns));
-  // The split merge runs one 64-lane wave per (token, head).
+  // The split merge runs at most one 64-lane wave per (token, head).
   if (ns > 1 && (int64_t)d.total_tokens * d.num_q_heads * 64 > kMaxLaunchItems)
     return fail(GQAP_ERR_UNSUPPORTED, "T * Hq = %lld (token, head) pairs exceed one split-merge launch",
                 (long long)d.total_tokens * d.num_q_heads);

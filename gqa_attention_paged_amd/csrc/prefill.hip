@@ -934,10 +934,13 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
 
 // Merge of the key-axis splits of one (row, head): with w_s = exp(lse_s -
 // max lse), out = sum_s w_s o_s / sum_s w_s and lse = max + log(sum_s w_s);
-// a row that no split saw any key for gets 0 / -inf.  One wave per (row,
-// head), two output columns per lane.  Rows that are not outputs (past
-// cu[B], or past the planned length of their sequence) are skipped, as the
-// attention kernel skips them.
+// a row that no split saw any key for gets 0 / -inf.  One wave merges
+// kMergePairs consecutive (row, head) pairs, two output columns per lane;
+// all their LSEs and partial rows (up to four splits) are requested before
+// the first is used, so a wave costs one memory round trip after its
+// sequence bounds.  Rows that are not outputs (past cu[B], or past the
+// planned length of their sequence) are skipped, as the attention kernel
+// skips them.
 struct MergeArgs {
   const float* ws_o;
   const float* ws_lse;
@@ -949,62 +952,95 @@ struct MergeArgs {
   int32_t T, Hq, B, nsplit, max_len, max_kv;
 };
 
+constexpr int kMergePairs = 4;  // (row, head) pairs per merge wave
+
 __global__ __launch_bounds__(256) void prefill_merge(MergeArgs a) {
-  const int64_t rh = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  constexpr int R = kMergePairs;
+  constexpr int NU = 4;  // splits merged in the single round trip; more take a loop
   const int lane = threadIdx.x & 63;
-  if (rh >= (int64_t)a.T * a.Hq) return;
-  const int row = (int)(rh / a.Hq);
-  const int h = (int)(rh - (int64_t)row * a.Hq);
-  if (row >= a.cu[a.B]) return;
-  int lo = 0, hi = a.B;  // the sequence b with cu[b] <= row < cu[b + 1]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (a.cu[mid] <= row) lo = mid; else hi = mid;
+  const int64_t nrh = (int64_t)a.T * a.Hq;
+  const int64_t rh0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * R;
+  if (rh0 >= nrh) return;
+  // Sequence bounds.  With B <= 64 lane l holds cu[l] (l <= B) and
+  // kvlens[l], read together, and a row's sequence is found by a ballot;
+  // longer batches take a binary search per pair.
+  const bool small = a.B <= 64;
+  int cu_l = 0, kv_l = 0;
+  if (small) {
+    if (lane <= a.B) cu_l = a.cu[lane];
+    if (a.kvlens && lane < a.B) kv_l = a.kvlens[lane];
   }
-  if (row - a.cu[lo] >= a.max_len) return;
-  if (a.kvlens) {  // a chunk outside the capacity was cleared by the attention kernel
-    const int kl = a.kvlens[lo];
-    if (kl > a.max_kv || kl < a.cu[lo + 1] - a.cu[lo]) return;
-  }
-  const int64_t sstride = (int64_t)a.T * a.Hq;
-  // Up to four splits (all the plan chooses by itself): every LSE and row is
-  // requested before the first is used, so the merge costs one memory round
-  // trip.  Forced counts above four take the remaining splits in a loop.
-  constexpr int NU = 4;
-  float ls[NU];
-  f32x2 v[NU];
+  const int cu_end = small ? __shfl(cu_l, a.B) : a.cu[a.B];
+  bool live[R];
 #pragma unroll
-  for (int s = 0; s < NU; ++s) {
-    const bool live = s < a.nsplit;
-    ls[s] = live ? a.ws_lse[s * sstride + rh] : -INFINITY;
-    v[s] = live ? *(const f32x2*)(a.ws_o + (s * sstride + rh) * 128 + 2 * lane) : f32x2{0.f, 0.f};
+  for (int r = 0; r < R; ++r) {
+    const int64_t rh = rh0 + r;
+    const int row = rh < nrh ? (int)(rh / a.Hq) : cu_end;
+    int c0, c1, kl = 0;
+    if (small) {
+      const int b = __popcll(__ballot(lane <= a.B && cu_l <= row)) - 1;  // cu is non-decreasing
+      c0 = __shfl(cu_l, b);
+      c1 = __shfl(cu_l, b + 1);
+      kl = __shfl(kv_l, b);
+    } else {
+      int lo = 0, hi = a.B;  // the sequence b with cu[b] <= row < cu[b + 1]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (a.cu[mid] <= row) lo = mid; else hi = mid;
+      }
+      c0 = a.cu[lo];
+      c1 = a.cu[lo + 1];
+      if (a.kvlens) kl = a.kvlens[lo];
+    }
+    // (a chunk outside the capacity was cleared by the attention kernel)
+    live[r] = row < cu_end && row - c0 < a.max_len && (!a.kvlens || (kl <= a.max_kv && kl >= c1 - c0));
   }
-  float M = -INFINITY;
+  const int64_t sstride = nrh;
+  float ls[R][NU];
+  f32x2 v[R][NU];
 #pragma unroll
-  for (int s = 0; s < NU; ++s) M = fmaxf(M, ls[s]);
-  for (int s = NU; s < a.nsplit; ++s) M = fmaxf(M, a.ws_lse[s * sstride + rh]);
-  float den = 0.f, acc0 = 0.f, acc1 = 0.f;
-  if (M > -INFINITY) {
+  for (int r = 0; r < R; ++r)
 #pragma unroll
     for (int s = 0; s < NU; ++s) {
-      const float wgt = ls[s] == -INFINITY ? 0.f : expf(ls[s] - M);
-      den += wgt;
-      acc0 += wgt * v[s][0];
-      acc1 += wgt * v[s][1];
+      const bool ld = live[r] && s < a.nsplit;
+      const int64_t rh = rh0 + r;
+      ls[r][s] = ld ? a.ws_lse[s * sstride + rh] : -INFINITY;
+      v[r][s] = ld ? *(const f32x2*)(a.ws_o + (s * sstride + rh) * 128 + 2 * lane) : f32x2{0.f, 0.f};
     }
-    for (int s = NU; s < a.nsplit; ++s) {
-      const float lsx = a.ws_lse[s * sstride + rh];
-      if (lsx == -INFINITY) continue;
-      const float wgt = expf(lsx - M);
-      const f32x2 vx = *(const f32x2*)(a.ws_o + (s * sstride + rh) * 128 + 2 * lane);
-      den += wgt;
-      acc0 += wgt * vx[0];
-      acc1 += wgt * vx[1];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if (!live[r]) continue;
+    const int64_t rh = rh0 + r;
+    float M = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < NU; ++s) M = fmaxf(M, ls[r][s]);
+    for (int s = NU; s < a.nsplit; ++s) M = fmaxf(M, a.ws_lse[s * sstride + rh]);
+    float den = 0.f, acc0 = 0.f, acc1 = 0.f;
+    if (M > -INFINITY) {
+#pragma unroll
+      for (int s = 0; s < NU; ++s) {
+        const float wgt = ls[r][s] == -INFINITY ? 0.f : expf(ls[r][s] - M);
+        den += wgt;
+        acc0 += wgt * v[r][s][0];
+        acc1 += wgt * v[r][s][1];
+      }
+      for (int s = NU; s < a.nsplit; ++s) {
+        const float lsx = a.ws_lse[s * sstride + rh];
+        if (lsx == -INFINITY) continue;
+        const float wgt = expf(lsx - M);
+        const f32x2 vx = *(const f32x2*)(a.ws_o + (s * sstride + rh) * 128 + 2 * lane);
+        den += wgt;
+        acc0 += wgt * vx[0];
+        acc1 += wgt * vx[1];
+      }
     }
+    const int row = (int)(rh / a.Hq);
+    const int h = (int)(rh - (int64_t)row * a.Hq);
+    const float inv = den > 0.f ? 1.f / den : 0.f;
+    *(uint32_t*)(a.out + (int64_t)row * a.o_st + (int64_t)h * a.o_sh + 2 * lane) =
+        pack_bf16x2_hw(acc0 * inv, acc1 * inv);
+    if (a.lse && lane == 0) a.lse[rh] = den > 0.f ? M + logf(den) : -INFINITY;
   }
-  const float inv = den > 0.f ? 1.f / den : 0.f;
-  *(uint32_t*)(a.out + (int64_t)row * a.o_st + (int64_t)h * a.o_sh + 2 * lane) = pack_bf16x2_hw(acc0 * inv, acc1 * inv);
-  if (a.lse && lane == 0) a.lse[rh] = den > 0.f ? M + logf(den) : -INFINITY;
 }
 
 // Append a chunk's keys and values to the paged cache (FlashMLA tensor-shape
@@ -1130,7 +1166,7 @@ static gqap_status launch_merge(const PrefillArgs& a, int32_t max_len, hipStream
   m.max_len = max_len;
   m.kvlens = a.kvlens;
   m.max_kv = a.max_kv;
-  const int64_t blocks = ((int64_t)a.T * a.Hq + 3) / 4;
+  const int64_t blocks = ((int64_t)a.T * a.Hq + 4 * kMergePairs - 1) / (4 * kMergePairs);
   if (blocks == 0) return GQAP_OK;
   hipLaunchKernelGGL(prefill_merge, dim3((unsigned)blocks), dim3(256), 0, st, m);
   const hipError_t e = hipGetLastError();
