@@ -961,10 +961,10 @@ __global__ __launch_bounds__(256) void prefill_merge(MergeArgs a) {
   const int64_t nrh = (int64_t)a.T * a.Hq;
   const int64_t rh0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * R;
   if (rh0 >= nrh) return;
-  // Sequence bounds.  With B <= 64 lane l holds cu[l] (l <= B) and
+  // Sequence bounds.  With B < 64 lane l holds cu[l] (l <= B) and
   // kvlens[l], read together, and a row's sequence is found by a ballot;
-  // longer batches take a binary search per pair.
-  const bool small = a.B <= 64;
+  // larger batches take a binary search per pair.
+  const bool small = a.B < 64;
   int cu_l = 0, kv_l = 0;
   if (small) {
     if (lane <= a.B) cu_l = a.cu[lane];

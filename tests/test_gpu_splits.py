@@ -65,6 +65,19 @@ def test_split_ragged_mla(gu):
     _check_prefill(gu, case, (1, 2, 3, 4, 6))
 
 
+@pytest.mark.parametrize("B", [63, 64, 65])
+def test_split_many_sequences(gu, B):
+    """The merge finds a row's sequence from lane-held bounds below 64
+    sequences and by binary search from 64 on: batches on both sides of that
+    edge, with empty and one-row sequences among them."""
+    rng = np.random.default_rng(310 + B)
+    lens = [int(x) for x in rng.integers(0, 140, size=B)]
+    lens[0], lens[-1], lens[B // 2] = 0, 1, 129
+    case = gen.make_prefill_case(name=f"split_b{B}", seed=310 + B, seq_lens=lens, Hq=4, Hk=2, D_qk=128, D_rope=0,
+                                 D_v=128)
+    _check_prefill(gu, case, (1, 2))
+
+
 def test_split_ragged_gqa_with_block_mask(gu):
     case = gen.make_prefill_case(name="split_mask", seed=301, seq_lens=[1100, 333, 64], Hq=8, Hk=2, D_qk=128,
                                  D_rope=0, D_v=128, mask_density=0.3)
