@@ -936,11 +936,10 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
 // max lse), out = sum_s w_s o_s / sum_s w_s and lse = max + log(sum_s w_s);
 // a row that no split saw any key for gets 0 / -inf.  One wave merges
 // kMergePairs consecutive (row, head) pairs, two output columns per lane;
-// all their LSEs and partial rows (up to four splits) are requested before
-// the first is used, so a wave costs one memory round trip after its
-// sequence bounds.  Rows that are not outputs (past cu[B], or past the
-// planned length of their sequence) are skipped, as the attention kernel
-// skips them.
+// all their LSEs and partial rows (up to four splits) and the sequence
+// bounds are requested before any is used, so a wave costs one memory round
+// trip.  Rows that are not outputs (past cu[B], or past the planned length
+// of their sequence) are skipped, as the attention kernel skips them.
 struct MergeArgs {
   const float* ws_o;
   const float* ws_lse;
@@ -961,9 +960,23 @@ __global__ __launch_bounds__(256) void prefill_merge(MergeArgs a) {
   const int64_t nrh = (int64_t)a.T * a.Hq;
   const int64_t rh0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * R;
   if (rh0 >= nrh) return;
-  // Sequence bounds.  With B < 64 lane l holds cu[l] (l <= B) and
-  // kvlens[l], read together, and a row's sequence is found by a ballot;
-  // larger batches take a binary search per pair.
+  // The LSEs and partial rows of the pairs are requested first (every slot
+  // below T * Hq lies inside the workspace; slots of rows that are not
+  // outputs are read but never used), together with the sequence bounds:
+  // with B < 64 lane l holds cu[l] (l <= B) and kvlens[l] and a row's
+  // sequence is found by a ballot; larger batches take a binary search.
+  const int64_t sstride = nrh;
+  float ls[R][NU];
+  f32x2 v[R][NU];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int s = 0; s < NU; ++s) {
+      const int64_t rh = rh0 + r;
+      const bool ld = rh < nrh && s < a.nsplit;
+      ls[r][s] = ld ? a.ws_lse[s * sstride + rh] : -INFINITY;
+      v[r][s] = ld ? *(const f32x2*)(a.ws_o + (s * sstride + rh) * 128 + 2 * lane) : f32x2{0.f, 0.f};
+    }
   const bool small = a.B < 64;
   int cu_l = 0, kv_l = 0;
   if (small) {
@@ -995,18 +1008,6 @@ __global__ __launch_bounds__(256) void prefill_merge(MergeArgs a) {
     // (a chunk outside the capacity was cleared by the attention kernel)
     live[r] = row < cu_end && row - c0 < a.max_len && (!a.kvlens || (kl <= a.max_kv && kl >= c1 - c0));
   }
-  const int64_t sstride = nrh;
-  float ls[R][NU];
-  f32x2 v[R][NU];
-#pragma unroll
-  for (int r = 0; r < R; ++r)
-#pragma unroll
-    for (int s = 0; s < NU; ++s) {
-      const bool ld = live[r] && s < a.nsplit;
-      const int64_t rh = rh0 + r;
-      ls[r][s] = ld ? a.ws_lse[s * sstride + rh] : -INFINITY;
-      v[r][s] = ld ? *(const f32x2*)(a.ws_o + (s * sstride + rh) * 128 + 2 * lane) : f32x2{0.f, 0.f};
-    }
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     if (!live[r]) continue;
