@@ -934,8 +934,8 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
 
 // Merge of the key-axis splits of one (row, head): with w_s = exp(lse_s -
 // max lse), out = sum_s w_s o_s / sum_s w_s and lse = max + log(sum_s w_s);
-// a row that no split saw any key for gets 0 / -inf.  One wave merges
-// kMergePairs consecutive (row, head) pairs, two output columns per lane;
+// a row that no split saw any key for gets 0 / -inf.  One wave merges R
+// consecutive (row, head) pairs, two output columns per lane;
 // all their LSEs and partial rows (up to four splits) and the sequence
 // bounds are requested before any is used, so a wave costs one memory round
 // trip.  Rows that are not outputs (past cu[B], or past the planned length
@@ -951,10 +951,8 @@ struct MergeArgs {
   int32_t T, Hq, B, nsplit, max_len, max_kv;
 };
 
-constexpr int kMergePairs = 4;  // (row, head) pairs per merge wave
-
+template <int R>
 __global__ __launch_bounds__(256) void prefill_merge(MergeArgs a) {
-  constexpr int R = kMergePairs;
   constexpr int NU = 4;  // splits merged in the single round trip; more take a loop
   const int lane = threadIdx.x & 63;
   const int64_t nrh = (int64_t)a.T * a.Hq;
@@ -1167,9 +1165,20 @@ static gqap_status launch_merge(const PrefillArgs& a, int32_t max_len, hipStream
   m.max_len = max_len;
   m.kvlens = a.kvlens;
   m.max_kv = a.max_kv;
-  const int64_t blocks = ((int64_t)a.T * a.Hq + 4 * kMergePairs - 1) / (4 * kMergePairs);
+  // Pairs per wave: a second pair amortises a wave's start and its sequence
+  // lookup, but the merge is one memory round trip per wave, so a small grid
+  // keeps one pair per wave to have more waves in flight.  Measured per merge
+  // (bf16 out, 128 columns): 8192 pairs, 4 splits: 6.8 / 6.9 / 8.0 us with
+  // 1 / 2 / 4 pairs per wave; 32768 pairs, 2 splits: 14.3 / 14.2 / 15.7;
+  // 131072 pairs, 2 splits: 51.5 / 48.1 / 50.9.
+  const int64_t nrh = (int64_t)a.T * a.Hq;
+  const int R = nrh >= 2 * 8192 ? 2 : 1;
+  const int64_t blocks = (nrh + 4 * R - 1) / (4 * R);
   if (blocks == 0) return GQAP_OK;
-  hipLaunchKernelGGL(prefill_merge, dim3((unsigned)blocks), dim3(256), 0, st, m);
+  if (R == 2)
+    hipLaunchKernelGGL(prefill_merge<2>, dim3((unsigned)blocks), dim3(256), 0, st, m);
+  else
+    hipLaunchKernelGGL(prefill_merge<1>, dim3((unsigned)blocks), dim3(256), 0, st, m);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(GQAP_ERR_HIP, "split merge launch: %s", hipGetErrorString(e));
   return GQAP_OK;

@@ -78,6 +78,15 @@ def test_split_many_sequences(gu, B):
     _check_prefill(gu, case, (1, 2))
 
 
+def test_split_merge_odd_pair_count(gu):
+    """Above 16384 (row, head) pairs a merge wave takes two pairs: an odd
+    count (5463 rows of 3 heads) leaves the last wave one pair past the end."""
+    case = gen.make_prefill_case(name="split_odd", seed=320, seq_lens=[683] * 7 + [682], Hq=3, Hk=1, D_qk=128,
+                                 D_rope=0, D_v=128)
+    assert case.T * 3 == 16389
+    _check_prefill(gu, case, (1, 2, 3))
+
+
 def test_split_ragged_gqa_with_block_mask(gu):
     case = gen.make_prefill_case(name="split_mask", seed=301, seq_lens=[1100, 333, 64], Hq=8, Hk=2, D_qk=128,
                                  D_rope=0, D_v=128, mask_density=0.3)
