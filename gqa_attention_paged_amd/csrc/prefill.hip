@@ -73,6 +73,9 @@ struct PrefillArgs {
   // [nsplit][T][Hq], natural log) that prefill_merge combines.
   int32_t nsplit;
   int32_t T;
+  // Paged grids of more than one round of workgroups: items ranked by the
+  // keys their last row sees (see the kernel), else by query tile.
+  int32_t rank_keys;
   float* ws_o;
   float* ws_lse;
   // fp8 KV pages: the value of a V code is e4m3fn(code) * v_scale; k_scale is
@@ -185,11 +188,14 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
   __shared__ __attribute__((aligned(1024))) float sbuf0[KSC ? 256 : 4], sbuf1[KSC ? 256 : 4];
 
   // Work item.  The grid is one-dimensional, Hq / hpw workgroups (times the
-  // key-axis splits) per (query tile, sequence) item; items are ranked
-  // deepest query tile first, then by sequence, and only items that exist
-  // (query tile inside its sequence) are ranked, so all real work precedes
-  // the empty tail of the grid and is spread evenly over the dispatcher's
-  // shader engines.  Within an item the heads of one KV group share an XCD
+  // key-axis splits) per (query tile, sequence) item.  Items are ranked
+  // deepest query tile first, then by sequence; a paged grid of more than
+  // one round of workgroups (up to 64 sequences) ranks them instead by the
+  // keys their last row sees, most first, since there the cached prefixes,
+  // not the query tile, set an item's length and the longest must start
+  // first.  Only items that exist (query tile inside its sequence) are
+  // ranked, so all real work precedes the empty tail of the grid and is
+  // spread evenly over the dispatcher's shader engines.  Within an item the heads of one KV group share an XCD
   // (workgroup i runs on XCD i % 8).
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -213,7 +219,58 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
     return Lq <= 0 ? 0 : Lq > a.max_len ? a.q_tiles : (Lq + QT - 1) / QT;
   };
   int b, qt;
-  if (a.B <= 64) {
+  if (PAGED && a.rank_keys && a.B <= 64) {
+    // Lane l holds sequence l: its query rows, query tiles and key offset
+    // (cached keys before the chunk).  Item (b, qt) costs about as many key
+    // tiles as its last row sees keys, off + min(Lq, (qt + 1) QT): a value
+    // that grows strictly with qt, so a sequence has at most one item per
+    // value.  Items are ranked by that value, largest first (ties by
+    // sequence), so the longest items start first and the grid's end holds
+    // the shortest ones.
+    int nq = 0, lq = 0, koff = 0;
+    if (lane < a.B) {
+      lq = a.cu[lane + 1] - a.cu[lane];
+      nq = item_tiles(lq);
+      if constexpr (PAGED) koff = max(0, a.kvlens[lane] - lq);
+    }
+    // Sums of per-lane counts in [0, 2^nb) by one ballot per bit (no
+    // cross-lane data movement: each step is a compare and a bit count).
+    const int nb = 32 - __builtin_clz((unsigned)a.q_tiles | 1u);
+    auto wave_sum = [&](int v) {
+      int t = 0;
+      for (int k = 0; k < nb; ++k) t += __builtin_popcountll(__ballot((v >> k) & 1)) << k;
+      return t;
+    };
+    auto wave_max = [](int v) {
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
+      return v;
+    };
+    const int qsh = a.hpw == 2 ? 6 : 7;  // log2 QT
+    // items of this lane's sequence whose key count exceeds v
+    auto deeper = [&](int v) {
+      const int y = v - koff;  // need min(lq, (qt + 1) QT) > y
+      if (nq == 0 || lq <= y) return 0;
+      return y < 0 ? nq : max(0, nq - (y >> qsh));
+    };
+    if (item >= wave_sum(nq)) return;  // past the last real item
+    // The key count v of rank `item`: the smallest v with at most `item`
+    // items above it.
+    int lo = -1, hi = wave_max(lane < a.B ? koff + lq : 0);
+    while (hi - lo > 1) {
+      const int mid = lo + ((hi - lo) >> 1);
+      if (wave_sum(deeper(mid)) <= item) hi = mid; else lo = mid;
+    }
+    const int above = wave_sum(deeper(hi));
+    const int at_v = deeper(hi - 1);  // this lane's items with count >= hi
+    uint64_t m = __ballot(at_v > deeper(hi));
+    for (int k = item - above; k > 0; --k) m &= m - 1;  // drop the lower set bits
+    b = __builtin_amdgcn_readfirstlane(__builtin_ctzll(m));
+    qt = __builtin_amdgcn_readfirstlane(__shfl(nq - at_v, b));  // uniform: keeps what follows scalar
+  } else if (a.B <= 64) {
+    // Deepest query tile first, then by sequence: one ballot per tile
+    // index.  Without cached keys this is the key-count order up to ties,
+    // and a single round of workgroups starts together in any order.
     int nq = 0;  // query tiles of sequence `lane`
     if (lane < a.B) nq = item_tiles(a.cu[lane + 1] - a.cu[lane]);
     b = -1;
@@ -1525,6 +1582,9 @@ static gqap_status chunk_common(const gqap_chunk_plan_t* plan, const void* q, co
                                      plan->workspace_bytes, workspace, workspace_bytes, &a);
   if (ss != GQAP_OK) return ss;
   const dim3 grid = prefill_grid(d.batch, d.num_q_heads, a.hpw, plan->q_tiles, a.nsplit, d.total_q_tokens);
+  // Ranking by key count pays when workgroups start in rounds (more than
+  // two per compute unit): it costs a short search per workgroup.
+  a.rank_keys = (int64_t)grid.x > 2 * kDefaultCUs;
   hipStream_t st = (hipStream_t)stream;
   if (d.head_dim_rope == 64) {
     if (fp8)

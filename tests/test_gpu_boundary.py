@@ -159,6 +159,42 @@ def test_chunk_rows_and_chunks_past_the_capacity(gu, num_splits):
     assert e_out <= TOL and e_lse <= LSE_TOL
 
 
+def test_chunk_capacity_edges_in_a_grid_ranked_by_key_count(gu):
+    """64 heads over 10 one-tile chunks: 640 workgroups, more than two per
+    compute unit, so the kernel ranks its items by the keys they see.  The
+    batch holds the edge cases of that ranking: a chunk longer than
+    max_q_len 100 (its last 50 rows 0 / -inf), an empty chunk, a one-token
+    chunk, a chunk with no cached prefix, a chunk exactly at the capacity,
+    and last a chunk whose 1300 keys exceed max_kv_len 1000 (all rows 0 /
+    -inf, not appended)."""
+    prefix = [400, 64, 7, 300, 0, 900, 5, 333, 20, 1200]
+    q_lens = [150, 30, 0, 1, 64, 99, 17, 77, 100, 100]
+    case = gen.make_chunk_case(name="chunk_cap_ranked", seed=404, prefix_lens=prefix, q_lens=q_lens, Hq=64, Hk=8)
+    gu.announce(f"chunk capacity, ranked grid: kv_lens {case.kv_lens.tolist()} q_lens {case.q_lens.tolist()}")
+    dc = gu.DeviceChunk(case, max_q_len=100, max_kv_len=1000, validate=False)
+    assert dc.plan.num_splits == 1
+    dc.out.fill_(NAN)
+    dc.lse.fill_(NAN)
+    dc.append()
+    kp, vp = dc.pools_bits()
+    sub = gen.ChunkCase(**{**case.__dict__, "kv_lens": case.kv_lens[:9], "cu_seqlens_q": case.cu_seqlens_q[:10],
+                           "block_table": case.block_table[:9]})
+    want_k, want_v = O.append_kv(case.k_new, case.v_new, case.k_pool, case.v_pool, sub.block_table,
+                                 sub.cu_seqlens_q, sub.kv_lens)
+    assert np.array_equal(kp, want_k) and np.array_equal(vp, want_v), "append wrote outside the capacity"
+    dc.run()
+    out, lse = dc.results()
+    cu = case.cu_seqlens_q
+    cut = np.concatenate([np.arange(cu[0] + 100, cu[1]), np.arange(cu[9], cu[10])])
+    assert np.all(out[cut] == 0) and np.all(np.isneginf(lse[cut]))
+    keep = np.concatenate([np.arange(cu[0], cu[0] + 100), np.arange(cu[1], cu[9])])
+    ref, ref_lse = O.chunk_prefill(case.q, want_k, want_v, case.block_table, case.cu_seqlens_q, case.kv_lens,
+                                   case.scale, dtype="bf16", rows=keep)
+    e_out, e_lse = gu.max_abs_err(out[keep], ref), gu.lse_err(lse[keep], ref_lse)
+    gu.announce(f"  rows inside the capacity: out {e_out:.3e} lse {e_lse:.3e}")
+    assert e_out <= TOL and e_lse <= LSE_TOL
+
+
 # ---------------------------------------------------------------- strides
 
 @pytest.mark.parametrize("kv", ["bf16", "e4m3fn"])

@@ -6,7 +6,11 @@ group with hpw = 2), key-axis split sp = (i // NH) % S, and the
 (i // NH // S)-th existing (sequence, query tile) item, items ranked deepest
 query tile first, then by sequence (for up to 64 sequences a wave ranks them
 with one ballot per depth, and the grid holds only as many items as the rows
-can fill, (T + B (QT - 1)) / QT; past 64 the order is plain).  A query tile has
+can fill, (T + B (QT - 1)) / QT; past 64 the order is plain).  A paged grid
+of more than one round of workgroups (up to 64 sequences) ranks its items
+instead by the keys the tile's last row sees, off + min(Lq, (qt + 1) QT) with
+off the cached keys before the chunk, most first, ties by sequence; a wave
+finds the item of a rank by a binary search over that key count.  A query tile has
 QT = 128 / hpw rows; split sp takes key tiles [nkt sp / S, nkt (sp+1) / S)
 of the nkt tiles the tile needs.  Rows of a sequence past the plan's
 capacity are cleared by split 0 of the sequence's last query tile.
@@ -18,6 +22,8 @@ This model restates that mapping and checks, on random problems:
   * every row past the capacity is cleared exactly once, by a workgroup of
     its own head, and never also computed;
   * the block-mask reads stay inside the sequence's [nb, nb] slice;
+  * the kernel's binary-search inversion of the ranking gives the item
+    that sorting the items by key count gives, for every rank;
   * the real items precede the empty tail of the grid (ranked path), and
   * the heads of one KV group share an XCD (workgroup i runs on XCD i % 8)
     whenever the group fits in one XCD's share of the heads."""
@@ -29,11 +35,16 @@ def item_tiles(Lq, max_len, q_tiles, QT):
     return 0 if Lq <= 0 else q_tiles if Lq > max_len else -(-Lq // QT)
 
 
-def rank(lens, max_len, q_tiles, QT, item):
+def rank(lens, max_len, q_tiles, QT, item, offs=None, by_keys=False):
     """(b, qt) of grid item `item`, or None (the workgroup returns at once)."""
     B = len(lens)
+    nq = [item_tiles(L, max_len, q_tiles, QT) for L in lens]
+    if B <= 64 and by_keys:
+        offs = offs or [0] * B
+        items = sorted(((offs[b] + min(lens[b], (qt + 1) * QT), b, qt) for b in range(B) for qt in range(nq[b])),
+                       key=lambda e: (-e[0], e[1]))
+        return (items[item][1], items[item][2]) if item < len(items) else None
     if B <= 64:
-        nq = [item_tiles(L, max_len, q_tiles, QT) for L in lens]
         before = 0
         for t in range(q_tiles - 1, -1, -1):
             members = [b for b in range(B) if nq[b] > t]      # ballot(nq > t), lane order
@@ -43,6 +54,36 @@ def rank(lens, max_len, q_tiles, QT, item):
         return None
     b, qt = item % B, q_tiles - 1 - item // B
     return (b, qt) if qt < item_tiles(lens[b], max_len, q_tiles, QT) else None
+
+
+def rank_by_search(lens, max_len, q_tiles, QT, item, offs):
+    """The kernel's steps for up to 64 sequences: lane b holds lq, nq and the
+    key offset; deeper(v) counts its items whose key count exceeds v; a
+    binary search finds the key count of the rank, a ballot the sequence."""
+    B = len(lens)
+    qsh = QT.bit_length() - 1
+    nq = [item_tiles(L, max_len, q_tiles, QT) for L in lens]
+    koff = [max(0, o) for o in offs]
+
+    def deeper(b, v):
+        y = v - koff[b]
+        if nq[b] == 0 or lens[b] <= y:
+            return 0
+        return nq[b] if y < 0 else max(0, nq[b] - (y >> qsh))
+
+    if item >= sum(nq):
+        return None
+    lo, hi = -1, max(koff[b] + lens[b] for b in range(B))
+    while hi - lo > 1:
+        mid = lo + ((hi - lo) >> 1)
+        if sum(deeper(b, mid) for b in range(B)) <= item:
+            hi = mid
+        else:
+            lo = mid
+    above = sum(deeper(b, hi) for b in range(B))
+    members = [b for b in range(B) if deeper(b, hi - 1) > deeper(b, hi)]   # ballot, lane order
+    b = members[item - above]
+    return b, nq[b] - deeper(b, hi - 1)
 
 
 def head_of(x, NH):
@@ -156,3 +197,25 @@ def test_heads_of_one_kv_group_share_an_xcd(Hq, Hk, hpw):
             xcd_of_group.setdefault(h // ratio, set()).add(x % 8)
     if (NH // 8) % max(1, ratio // hpw) == 0:
         assert all(len(s) == 1 for s in xcd_of_group.values())
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_kernel_rank_inversion_matches_the_sorted_order(seed):
+    """The key-count ranking: the binary search and ballot give, rank for
+    rank, the items sorted by key count (most first, ties by sequence), and
+    the ranks past the last item give none."""
+    rng = np.random.default_rng(100 + seed)
+    B = int(rng.integers(1, 65))
+    QT = int(rng.choice([64, 128]))
+    lens = [int(x) for x in rng.integers(0, 700, size=B)]
+    lens[int(rng.integers(0, B))] = 0
+    offs = [int(x) for x in rng.integers(0, 5000, size=B)] if seed % 2 else [0] * B
+    max_len = int(rng.choice([max(lens) + 1, max(1, max(lens) // 2)]))  # some sequences past the capacity
+    q_tiles = max(1, -(-max_len // QT))
+    total = sum(item_tiles(L, max_len, q_tiles, QT) for L in lens)
+    got = [rank_by_search(lens, max_len, q_tiles, QT, i, offs) for i in range(total + 3)]
+    want = [rank(lens, max_len, q_tiles, QT, i, offs, by_keys=True) for i in range(total + 3)]
+    assert got == want
+    assert got[total:] == [None] * 3 and len(set(got[:total])) == total
+    keys = [offs[b] + min(lens[b], (qt + 1) * QT) for b, qt in got[:total]]
+    assert keys == sorted(keys, reverse=True)
