@@ -155,6 +155,14 @@ using namespace dev;
 // with its 64 scales; a rope operand is widened exactly to bf16 when it is
 // read, each half tile runs its rope steps first, multiplies that sum by the
 // keys' scales, then accumulates the bf16 per-head steps.
+// Sum over a wave of per-lane counts in [0, 2^nb): one ballot per bit, so no
+// data moves between lanes (each step is a compare and a bit count).
+__device__ __forceinline__ int wave_sum_small(int v, int nb) {
+  int t = 0;
+  for (int k = 0; k < nb; ++k) t += __builtin_popcountll(__ballot((v >> k) & 1)) << k;
+  return t;
+}
+
 template <int DR, bool PAGED, int F8>
 __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
   constexpr bool QK8 = F8 == 1 || F8 == 2;    // fp8 nope Q.K on the fp8 matrix cores
@@ -235,12 +243,8 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
     }
     // Sums of per-lane counts in [0, 2^nb) by one ballot per bit (no
     // cross-lane data movement: each step is a compare and a bit count).
-    const int nb = 32 - __builtin_clz((unsigned)a.q_tiles | 1u);
-    auto wave_sum = [&](int v) {
-      int t = 0;
-      for (int k = 0; k < nb; ++k) t += __builtin_popcountll(__ballot((v >> k) & 1)) << k;
-      return t;
-    };
+    const int nb = 32 - __builtin_clz((unsigned)a.q_tiles | 1u);  // per-lane counts < 2^nb
+    auto wave_sum = [&](int v) { return wave_sum_small(v, nb); };
     auto wave_max = [](int v) {
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
@@ -275,19 +279,43 @@ __global__ __launch_bounds__(256, 2) void prefill_fwd(PrefillArgs a) {
     if (lane < a.B) nq = item_tiles(a.cu[lane + 1] - a.cu[lane]);
     b = -1;
     qt = -1;
-    int before = 0;
-    for (int t = a.q_tiles - 1; t >= 0; --t) {
-      uint64_t m = __ballot(nq > t);
-      const int cnt = __builtin_popcountll(m);
-      if (item < before + cnt) {
-        for (int k = item - before; k > 0; --k) m &= m - 1;  // drop the lower set bits
-        b = __builtin_ctzll(m);
-        qt = t;
-        break;
+    if (a.q_tiles > 32 && a.B * ((a.q_tiles + 63) >> 6) < a.q_tiles) {
+      // Many tile indices (the walk below would take one dependent ballot
+      // per index, which a workgroup starting beside a busy one issues
+      // slowly: 8-10 us for the last items of a 128-index block-sparse grid).
+      // C(t) = sum_b max(0, nq_b - t) items have a tile index >= t; it falls
+      // with t, so the item's tile index is one less than the number of t
+      // with C(t) > item.  Lane j evaluates t = j (+ 64, ...) from the
+      // sequences' tile counts read one by one as scalars: about 4 B
+      // instructions per 64 tile indices.
+      int above = 0;
+      for (int base = 0; base < a.q_tiles; base += 64) {
+        const int j = base + lane;
+        int c = 0;
+        for (int s = 0; s < a.B; ++s) c += max(0, __builtin_amdgcn_readlane(nq, s) - j);
+        above += __builtin_popcountll(__ballot(j < a.q_tiles && c > item));
       }
-      before += cnt;
+      if (above == 0) return;  // past the last real item
+      qt = above - 1;
+      const int before = wave_sum_small(max(0, nq - above), 32 - __builtin_clz((unsigned)a.q_tiles | 1u));
+      uint64_t m = __ballot(nq > qt);
+      for (int k = item - before; k > 0; --k) m &= m - 1;  // drop the lower set bits
+      b = __builtin_ctzll(m);
+    } else {
+      int before = 0;
+      for (int t = a.q_tiles - 1; t >= 0; --t) {
+        uint64_t m = __ballot(nq > t);
+        const int cnt = __builtin_popcountll(m);
+        if (item < before + cnt) {
+          for (int k = item - before; k > 0; --k) m &= m - 1;  // drop the lower set bits
+          b = __builtin_ctzll(m);
+          qt = t;
+          break;
+        }
+        before += cnt;
+      }
+      if (qt < 0) return;  // past the last real item
     }
-    if (qt < 0) return;  // past the last real item
   } else {
     b = item % a.B;
     qt = a.q_tiles - 1 - item / a.B;

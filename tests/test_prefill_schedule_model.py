@@ -86,6 +86,22 @@ def rank_by_search(lens, max_len, q_tiles, QT, item, offs):
     return b, nq[b] - deeper(b, hi - 1)
 
 
+def rank_parallel(lens, max_len, q_tiles, QT, item):
+    """The kernel's parallel form of the query-tile ranking (used when
+    q_tiles > 32 and B ceil(q_tiles / 64) < q_tiles): C(t) = sum_b max(0, nq_b - t) items have a
+    tile index >= t; the item's tile index is one less than the number of t
+    with C(t) > item; a ballot over nq_b > qt then picks the sequence."""
+    B = len(lens)
+    nq = [item_tiles(L, max_len, q_tiles, QT) for L in lens]
+    above = sum(1 for t in range(q_tiles) if sum(max(0, n - t) for n in nq) > item)
+    if above == 0:
+        return None
+    qt = above - 1
+    before = sum(max(0, n - above) for n in nq)
+    members = [b for b in range(B) if nq[b] > qt]
+    return members[item - before], qt
+
+
 def head_of(x, NH):
     hpx = NH >> 3
     return x if NH & 7 else (x & 7) * hpx + (x >> 3)
@@ -219,3 +235,20 @@ def test_kernel_rank_inversion_matches_the_sorted_order(seed):
     assert got[total:] == [None] * 3 and len(set(got[:total])) == total
     keys = [offs[b] + min(lens[b], (qt + 1) * QT) for b, qt in got[:total]]
     assert keys == sorted(keys, reverse=True)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_parallel_tile_ranking_matches_the_tile_walk(seed):
+    """The parallel query-tile ranking gives, rank for rank, the item of the
+    walk over tile indices (deepest first, then by sequence)."""
+    rng = np.random.default_rng(200 + seed)
+    B = int(rng.integers(1, 65))
+    QT = int(rng.choice([64, 128]))
+    lens = [int(x) for x in rng.integers(0, 9000 if seed % 3 else 700, size=B)]
+    lens[int(rng.integers(0, B))] = 0
+    max_len = int(rng.choice([max(lens) + 1, max(1, max(lens) // 2)]))
+    q_tiles = max(1, -(-max_len // QT))
+    total = sum(item_tiles(L, max_len, q_tiles, QT) for L in lens)
+    got = [rank_parallel(lens, max_len, q_tiles, QT, i) for i in range(total + 3)]
+    want = [rank(lens, max_len, q_tiles, QT, i) for i in range(total + 3)]
+    assert got == want
