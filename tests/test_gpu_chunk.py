@@ -94,6 +94,25 @@ def test_chunk_small_ragged(gu, Hq, Hk):
     _run(gu, case)
 
 
+@pytest.mark.parametrize("seed", [71, 72, 73])
+def test_chunk_grids_ranked_by_key_count(gu, seed):
+    """Grids of more than two workgroups per compute unit (64 heads) rank
+    their items by the keys each query tile sees.  Seeded random batches:
+    prefixes 0..3000 (inside and across pages), chunks 0..400 tokens (some
+    empty, some one token), every row and head compared."""
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(6, 12))
+    prefix = [int(x) for x in rng.integers(0, 3001, size=B)]
+    q_lens = [int(x) for x in rng.integers(0, 401, size=B)]
+    q_lens[0], q_lens[1] = 0, 1
+    q_lens[2] = max(q_lens[2], 260)  # at least one sequence with three query tiles
+    case = gen.make_chunk_case(name=f"chunk_ranked_{seed}", seed=seed, prefix_lens=prefix, q_lens=q_lens,
+                               Hq=64, Hk=8)
+    items = sum(-(-q // 128) for q in q_lens)
+    assert 64 * items > 512, "the grid must run in more than one round"
+    _run(gu, case)
+
+
 def test_chunk_empty_chunks_and_one_token_chunks(gu):
     case = gen.make_chunk_case(name="chunk_edges", seed=62, prefix_lens=[10, 0, 500, 64, 3],
                                q_lens=[0, 1, 1, 0, 257], Hq=8, Hk=2)
