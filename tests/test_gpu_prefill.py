@@ -68,6 +68,18 @@ def test_prefill_mla_config_full_size(gu):
     _check(gu, gen.prefill_mla_bf16())
 
 
+@pytest.mark.parametrize("mask", [None, 0.3])
+def test_prefill_many_query_tile_indices(gu, mask):
+    """Grids with more than 32 query-tile indices, where the kernel finds a
+    workgroup's item by counting, in parallel over tile indices, the items at
+    or past each: ragged lengths with an empty sequence and one of 4500 rows
+    (36 tile indices of 128 rows; 71 of 64 rows with a mask and head pairs).
+    Every row and head compared."""
+    case = gen.make_prefill_case(name=f"many_tiles_{mask}", seed=91, seq_lens=[4500, 0, 2100, 130], Hq=8, Hk=2,
+                                 D_qk=128, D_rope=0, D_v=128, mask_density=mask)
+    _check(gu, case)
+
+
 def test_prefill_blocksparse_config_full_size(gu):
     """Every row and head of the block-sparse workload (2 x 8192 tokens, 32
     query heads): every query tile and head pair the grid ranks is checked."""
